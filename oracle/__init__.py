@@ -1,0 +1,173 @@
+"""CPU oracle of the LUT-6 linear layer -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package.  The product library never does, and this
+package imports nothing from it.
+
+The arithmetic lives in ``lut6_oracle.c`` (plain C, FP64 accumulation, its
+own FP16 codec and unpack; see the header of that file for the passages of
+page "Clef-Flash-ANE-LUT6" it follows).  This module compiles it with gcc and
+marshals numpy arrays into it through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SRC = HERE / "lut6_oracle.c"
+LIB = HERE / "liblut6_oracle.so"
+
+EPI_F32, EPI_F16, EPI_SILU_MUL_F16 = 0, 1, 2
+OK, E_NULL, E_SHAPE, E_SCALE, E_EPILOGUE, E_INDEX_RANGE, E_ROWS, E_NOMEM = 0, 1, 2, 4, 5, 6, 8, 9
+
+CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
+          "-Wall", "-Wextra"]
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(out: Path | None = None, mutant: int = 0) -> Path:
+    """Compile the oracle (``mutant`` > 0 plants a known mistake; tests only)."""
+    out = Path(out) if out is not None else LIB
+    cmd = ["gcc", *CFLAGS, f"-DORA_MUTANT={int(mutant)}", "-o", str(out), str(SRC), "-lm"]
+    tmp = out.with_suffix(out.suffix + f".tmp{os.getpid()}")
+    cmd[cmd.index(str(out))] = str(tmp)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+class Oracle:
+    """ctypes view of one build of the oracle library."""
+
+    def __init__(self, path: Path):
+        lib = ctypes.CDLL(str(path))
+        lib.ora_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.ora_f16_to_f64.restype = ctypes.c_double
+        lib.ora_f64_to_f16.argtypes = [ctypes.c_double]
+        lib.ora_f64_to_f16.restype = ctypes.c_uint16
+        lib.ora_f16_decode_array.argtypes = [_P, _P, _I64]
+        lib.ora_f16_decode_array.restype = None
+        lib.ora_f16_encode_array.argtypes = [_P, _P, _I64]
+        lib.ora_f16_encode_array.restype = None
+        for name in ("ora_pack", "ora_unpack"):
+            getattr(lib, name).argtypes = [_P, _P, _I64, _I64]
+            getattr(lib, name).restype = ctypes.c_int
+        lib.ora_dequant.argtypes = [_P, _P, _P, _I64, _I64]
+        lib.ora_dequant.restype = ctypes.c_int
+        lib.ora_linear.argtypes = [_P, _P, _P, _I64, _I64, _I64, ctypes.c_double,
+                                   ctypes.c_int, _P, _I64, ctypes.c_int, _P, _P]
+        lib.ora_linear.restype = ctypes.c_int
+        lib.ora_packed_bytes.argtypes = [_I64, _I64]
+        lib.ora_packed_bytes.restype = _I64
+        lib.ora_table_bytes.argtypes = [_I64]
+        lib.ora_table_bytes.restype = _I64
+        self.lib = lib
+        self.path = path
+
+    # -- FP16 codec ------------------------------------------------------
+    def f16_to_f64(self, bits: np.ndarray) -> np.ndarray:
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, np.float64)
+        self.lib.ora_f16_decode_array(bits.ctypes.data, out.ctypes.data, bits.size)
+        return out
+
+    def f64_to_f16(self, v: np.ndarray) -> np.ndarray:
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, np.uint16)
+        self.lib.ora_f16_encode_array(v.ctypes.data, out.ctypes.data, v.size)
+        return out
+
+    # -- format ------------------------------------------------------------
+    def pack(self, idx: np.ndarray) -> np.ndarray:
+        idx = np.ascontiguousarray(idx, dtype=np.uint8)
+        n, k = idx.shape
+        out = np.empty((n, 3 * k // 4), np.uint8)
+        st = self.lib.ora_pack(idx.ctypes.data, out.ctypes.data, n, k)
+        if st != OK:
+            raise OracleError(f"ora_pack status {st}")
+        return out
+
+    def unpack(self, packed: np.ndarray, k: int) -> np.ndarray:
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        n = packed.shape[0]
+        out = np.empty((n, k), np.uint8)
+        st = self.lib.ora_unpack(packed.ctypes.data, out.ctypes.data, n, k)
+        if st != OK:
+            raise OracleError(f"ora_unpack status {st}")
+        return out
+
+    def packed_bytes(self, n: int, k: int) -> int:
+        return int(self.lib.ora_packed_bytes(n, k))
+
+    def table_bytes(self, n: int) -> int:
+        return int(self.lib.ora_table_bytes(n))
+
+    # -- dequant / linear --------------------------------------------------
+    def dequant(self, packed: np.ndarray, tables: np.ndarray, k: int) -> np.ndarray:
+        """FP16 bits [N, K] of the dequantized weight."""
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        tables = np.ascontiguousarray(tables).view(np.uint16)
+        n = packed.shape[0]
+        out = np.empty((n, k), np.uint16)
+        st = self.lib.ora_dequant(packed.ctypes.data, tables.ctypes.data, out.ctypes.data, n, k)
+        if st != OK:
+            raise OracleError(f"ora_dequant status {st}")
+        return out
+
+    def linear(self, x: np.ndarray, packed: np.ndarray, tables: np.ndarray, *,
+               epilogue: int, in_scale: float = 1.0, rows=None, threads: int | None = None):
+        """Return (y_exact float64, y_out) for the listed token rows.
+
+        ``x`` is FP16 [L, K] (float16 or uint16 bits), ``packed`` [N, 3K/4] bytes,
+        ``tables`` FP16 [N/16, 64].  ``y_out`` is float32 for EPI_F32 and FP16
+        bits (uint16) otherwise; its width is N, or N/2 for EPI_SILU_MUL_F16.
+        """
+        x = np.ascontiguousarray(x).view(np.uint16)
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        tables = np.ascontiguousarray(tables).view(np.uint16)
+        L, K = x.shape
+        N = packed.shape[0]
+        if packed.shape[1] * 4 != 3 * K:
+            raise OracleError("packed width does not match K")
+        if rows is None:
+            rows_arr, n_rows, rows_ptr = None, L, None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+            n_rows = rows_arr.size
+            rows_ptr = rows_arr.ctypes.data
+        n_out = N // 2 if epilogue == EPI_SILU_MUL_F16 else N
+        y_exact = np.empty((n_rows, n_out), np.float64)
+        y_out = np.empty((n_rows, n_out), np.float32 if epilogue == EPI_F32 else np.uint16)
+        if threads is None:
+            threads = len(os.sched_getaffinity(0))
+        st = self.lib.ora_linear(x.ctypes.data, packed.ctypes.data, tables.ctypes.data,
+                                 L, K, N, float(in_scale), int(epilogue), rows_ptr, n_rows,
+                                 int(threads), y_exact.ctypes.data, y_out.ctypes.data)
+        if st != OK:
+            raise OracleError(f"ora_linear status {st}")
+        return y_exact, y_out
+
+
+_default: Oracle | None = None
+
+
+def load(rebuild: bool = False) -> Oracle:
+    """The default (unmutated) oracle, built on first use."""
+    global _default
+    if _default is None or rebuild:
+        if rebuild or not LIB.exists() or LIB.stat().st_mtime < SRC.stat().st_mtime:
+            build()
+        _default = Oracle(LIB)
+    return _default

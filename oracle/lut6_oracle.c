@@ -1,0 +1,375 @@
+/*
+ * lut6_oracle.c -- plain, slow CPU oracle of the LUT-6 weight-quantized
+ * linear layer.  TEST INFRASTRUCTURE ONLY: nothing but the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load this library.  It
+ * shares no code, header, table or helper with the GPU library.
+ *
+ * What it follows (page "Clef-Flash-ANE-LUT6"):
+ *   - section "Weight precision": the large text linear layers store 6-bit
+ *     indices plus one 64-entry FP16 table per 16 output channels;
+ *   - section "LUT-6 text weights": four 6-bit indices are packed into three
+ *     bytes, little-endian; activations are FP16; the MLP down-projection
+ *     input is scaled up (by at most 16x) and the result scaled back.
+ *
+ * Readings taken where the page leaves a step open:
+ *   - the three bytes form one little-endian 24-bit word
+ *     w = b0 | b1<<8 | b2<<16, and index t (t = 0..3, lowest input column
+ *     first) is bits 6t..6t+5 of w;
+ *   - indices run along the input dimension K of a row-major [N, K] weight;
+ *     each row holds 3K/4 bytes;
+ *   - output rows 16g..16g+15 use table g; tables are stored [N/16, 64];
+ *   - the weight value is table[index], nothing added or scaled;
+ *   - in_scale s: xs = fp16(x * s), y = (sum_k xs * w) / s, s a power of two;
+ *   - the fused MLP epilogue is silu(gate) * up with the gate rows first and
+ *     the up rows second along N, rounded once to FP16;
+ *   - rounding is round-to-nearest-even everywhere; overflow gives +-inf.
+ *
+ * The arithmetic is the plain definition: unpack, table lookup, an FP64 dot
+ * product with k ascending, the scale-back, the epilogue and one rounding.
+ * Threads only split the independent output channels; nothing is blocked,
+ * fused or reordered.
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fPIC -shared -pthread.
+ * ORA_MUTANT (test builds only) plants one known mistake so the pins can be
+ * shown to catch it; the default build defines none.
+ */
+#define _POSIX_C_SOURCE 200809L
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORA_MUTANT
+#define ORA_MUTANT 0
+#endif
+
+enum { ORA_OK = 0, ORA_E_NULL = 1, ORA_E_SHAPE = 2, ORA_E_SCALE = 4,
+       ORA_E_EPILOGUE = 5, ORA_E_INDEX_RANGE = 6, ORA_E_ROWS = 8,
+       ORA_E_NOMEM = 9 };
+enum { ORA_EPI_F32 = 0, ORA_EPI_F16 = 1, ORA_EPI_SILU_MUL_F16 = 2 };
+
+/* ---------------- FP16 codec (IEEE 754 binary16) ---------------- */
+
+/* Decode: sign, 5-bit exponent (bias 15), 10-bit fraction; exponent 0 is
+ * the subnormal range (fraction * 2^-24), exponent 31 is inf / NaN. */
+double ora_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0) {
+#if ORA_MUTANT == 9
+        v = ldexp((double)m, -25);
+#else
+        v = ldexp((double)m, -24);
+#endif
+    } else if (e == 31) {
+        v = m ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + m), e - 25);
+    }
+    return sign ? -v : v;
+}
+
+/* Encode with round-to-nearest, ties to even.  A finite binary16 value is
+ * q * 2^(E-10) with q in [1024, 2048) (normal, E in -14..15) or q * 2^-24
+ * with q in [0, 1024) (subnormal).  Scaling by a power of two is exact in
+ * double, so rounding q to an integer is the only rounding step. */
+static double ora_round_half_even(double q)
+{
+#if ORA_MUTANT == 8
+    return round(q);          /* ties away from zero: a planted mistake */
+#else
+    return nearbyint(q);      /* default IEEE mode: ties to even */
+#endif
+}
+
+uint16_t ora_f64_to_f16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7e00u);
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7c00u);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range; q = 1024 rounds up into the smallest normal,
+         * whose bit pattern is exactly 0x0400 */
+        double q = ora_round_half_even(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int e2;
+    double m = frexp(a, &e2);                 /* a = m * 2^e2, m in [0.5, 1) */
+    int E = e2 - 1;                           /* a = (2m) * 2^E */
+    double q = ora_round_half_even(ldexp(m, 11));   /* in [1024, 2048] */
+    if (q == 2048.0) { q = 1024.0; E += 1; }
+    if (E > 15) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
+void ora_f16_decode_array(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = ora_f16_to_f64(h[i]);
+}
+
+void ora_f16_encode_array(const double *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = ora_f64_to_f16(v[i]);
+}
+
+/* ---------------- packing: four 6-bit indices in three bytes -------- */
+
+int ora_pack(const uint8_t *idx, uint8_t *packed, int64_t n, int64_t k)
+{
+    if (!idx || !packed) return ORA_E_NULL;
+    if (n <= 0 || k <= 0 || k % 4) return ORA_E_SHAPE;
+    int64_t row_bytes = 3 * k / 4;
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t j = 0; j < k / 4; ++j) {
+            uint32_t w = 0;
+            for (int t = 0; t < 4; ++t) {
+                uint32_t v = idx[r * k + 4 * j + t];
+                if (v > 63) return ORA_E_INDEX_RANGE;
+#if ORA_MUTANT == 2
+                w |= v << (6 * (3 - t));   /* index order reversed */
+#else
+                w |= v << (6 * t);
+#endif
+            }
+            uint8_t *p = packed + r * row_bytes + 3 * j;
+#if ORA_MUTANT == 1
+            p[2] = (uint8_t)(w & 0xff);   /* big-endian byte order */
+            p[1] = (uint8_t)((w >> 8) & 0xff);
+            p[0] = (uint8_t)((w >> 16) & 0xff);
+#else
+            p[0] = (uint8_t)(w & 0xff);
+            p[1] = (uint8_t)((w >> 8) & 0xff);
+            p[2] = (uint8_t)((w >> 16) & 0xff);
+#endif
+        }
+    }
+    return ORA_OK;
+}
+
+/* Unpack one row of 3k/4 bytes into k indices. */
+static void ora_unpack_row(const uint8_t *p, uint8_t *idx, int64_t k)
+{
+    for (int64_t j = 0; j < k / 4; ++j) {
+#if ORA_MUTANT == 1
+        uint32_t w = (uint32_t)p[3 * j + 2] | ((uint32_t)p[3 * j + 1] << 8) |
+                     ((uint32_t)p[3 * j] << 16);
+#else
+        uint32_t w = (uint32_t)p[3 * j] | ((uint32_t)p[3 * j + 1] << 8) |
+                     ((uint32_t)p[3 * j + 2] << 16);
+#endif
+        for (int t = 0; t < 4; ++t) {
+#if ORA_MUTANT == 2
+            idx[4 * j + t] = (uint8_t)((w >> (6 * (3 - t))) & 63u);
+#else
+            idx[4 * j + t] = (uint8_t)((w >> (6 * t)) & 63u);
+#endif
+        }
+    }
+}
+
+int ora_unpack(const uint8_t *packed, uint8_t *idx, int64_t n, int64_t k)
+{
+    if (!idx || !packed) return ORA_E_NULL;
+    if (n <= 0 || k <= 0 || k % 4) return ORA_E_SHAPE;
+    for (int64_t r = 0; r < n; ++r)
+        ora_unpack_row(packed + r * (3 * k / 4), idx + r * k, k);
+    return ORA_OK;
+}
+
+/* Table that serves output channel r: one table per 16 channels. */
+static int64_t ora_table_of(int64_t r)
+{
+#if ORA_MUTANT == 3
+    return r / 32;             /* wrong group size */
+#else
+    return r / 16;
+#endif
+}
+
+/* ---------------- dequantization: W[n][k] = T[n/16][idx[n][k]] -------- */
+
+int ora_dequant(const uint8_t *packed, const uint16_t *tables, uint16_t *w,
+                int64_t n, int64_t k)
+{
+    if (!packed || !tables || !w) return ORA_E_NULL;
+    if (n <= 0 || k <= 0 || k % 4 || n % 16) return ORA_E_SHAPE;
+    uint8_t *idx = (uint8_t *)malloc((size_t)k);
+    if (!idx) return ORA_E_NOMEM;
+    for (int64_t r = 0; r < n; ++r) {
+        ora_unpack_row(packed + r * (3 * k / 4), idx, k);
+        const uint16_t *tab = tables + ora_table_of(r) * 64;
+        for (int64_t c = 0; c < k; ++c) w[r * k + c] = tab[idx[c]];
+    }
+    free(idx);
+    return ORA_OK;
+}
+
+/* ---------------- the linear layer ---------------- */
+
+typedef struct {
+    const double *xs;        /* [nr][k] scaled, FP16-rounded activations */
+    const uint8_t *packed;
+    const uint16_t *tables;
+    int64_t k, n, nr;
+    int64_t n_begin, n_end;  /* this thread's output channels */
+    double *acc;             /* [nr][n] */
+    int status;
+} ora_job;
+
+static void *ora_dot_worker(void *arg)
+{
+    ora_job *j = (ora_job *)arg;
+    int64_t k = j->k;
+    uint8_t *idx = (uint8_t *)malloc((size_t)k);
+    double *wd = (double *)malloc((size_t)k * sizeof(double));
+    if (!idx || !wd) { free(idx); free(wd); j->status = ORA_E_NOMEM; return NULL; }
+    for (int64_t r = j->n_begin; r < j->n_end; ++r) {
+        /* dequantize weight row r */
+        ora_unpack_row(j->packed + r * (3 * k / 4), idx, k);
+        const uint16_t *tab = j->tables + ora_table_of(r) * 64;
+        for (int64_t c = 0; c < k; ++c) wd[c] = ora_f16_to_f64(tab[idx[c]]);
+        /* one FP64 dot per token row, k ascending */
+        for (int64_t l = 0; l < j->nr; ++l) {
+            const double *xr = j->xs + l * k;
+            double s = 0.0;
+#if ORA_MUTANT == 7
+            for (int64_t c = 0; c < k - 1; ++c) s += xr[c] * wd[c];  /* last term dropped */
+#else
+            for (int64_t c = 0; c < k; ++c) s += xr[c] * wd[c];
+#endif
+            j->acc[l * j->n + r] = s;
+        }
+    }
+    free(idx);
+    free(wd);
+    j->status = ORA_OK;
+    return NULL;
+}
+
+/*
+ * ora_linear: y = epilogue( (fp16(x*s) . W^T) / s ) for the token rows
+ * listed in `rows` (all L rows when rows == NULL).
+ *   x       FP16 bits [L][K] row-major
+ *   packed  [N][3K/4] bytes; tables FP16 bits [N/16][64]
+ *   y_exact double [nr][n_out], the unrounded epilogue value
+ *   y_out   float [nr][n_out] (epilogue 0) or FP16 bits (epilogues 1, 2)
+ *   n_out = N, or N/2 for the SiLU-multiply epilogue
+ * threads <= 0 means one thread.  Returns ORA_OK or an error code.
+ */
+int ora_linear(const uint16_t *x, const uint8_t *packed, const uint16_t *tables,
+               int64_t L, int64_t K, int64_t N, double in_scale, int epilogue,
+               const int64_t *rows, int64_t n_rows, int threads,
+               double *y_exact, void *y_out)
+{
+    if (!x || !packed || !tables || !y_exact || !y_out) return ORA_E_NULL;
+    if (L < 0 || K <= 0 || N <= 0 || K % 4 || N % 16) return ORA_E_SHAPE;
+    if (epilogue < 0 || epilogue > 2) return ORA_E_EPILOGUE;
+    if (epilogue == ORA_EPI_SILU_MUL_F16 && N % 32) return ORA_E_SHAPE;
+    if (!(in_scale > 0.0) || isinf(in_scale)) return ORA_E_SCALE;
+    int64_t nr = rows ? n_rows : L;
+    if (nr < 0) return ORA_E_ROWS;
+    for (int64_t i = 0; rows && i < nr; ++i)
+        if (rows[i] < 0 || rows[i] >= L) return ORA_E_ROWS;
+    if (nr == 0) return ORA_OK;
+    if (threads <= 0) threads = 1;
+    if (threads > N) threads = (int)N;
+
+    double *xs = (double *)malloc((size_t)(nr * K) * sizeof(double));
+    double *acc = (double *)malloc((size_t)(nr * N) * sizeof(double));
+    ora_job *jobs = (ora_job *)calloc((size_t)threads, sizeof(ora_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (!xs || !acc || !jobs || !tid) {
+        free(xs); free(acc); free(jobs); free(tid);
+        return ORA_E_NOMEM;
+    }
+
+    /* scale the activations and round them to FP16 */
+    for (int64_t l = 0; l < nr; ++l) {
+        int64_t src = rows ? rows[l] : l;
+        for (int64_t c = 0; c < K; ++c) {
+#if ORA_MUTANT == 10
+            double v = ora_f16_to_f64(x[c * L + src]);   /* transposed read */
+#else
+            double v = ora_f16_to_f64(x[src * K + c]);
+#endif
+            xs[l * K + c] = ora_f16_to_f64(ora_f64_to_f16(v * in_scale));
+        }
+    }
+
+    /* FP64 dot products, output channels split over threads */
+    int64_t per = (N + threads - 1) / threads;
+    char *joined = (char *)calloc((size_t)threads, 1);
+    for (int t = 0; t < threads; ++t) {
+        ora_job *j = &jobs[t];
+        j->xs = xs; j->packed = packed; j->tables = tables;
+        j->k = K; j->n = N; j->nr = nr; j->acc = acc;
+        j->n_begin = t * per < N ? t * per : N;
+        j->n_end = (t + 1) * per < N ? (t + 1) * per : N;
+        j->status = ORA_OK;
+        if (j->n_begin >= j->n_end) continue;
+        if (threads > 1 && joined &&
+            pthread_create(&tid[t], NULL, ora_dot_worker, j) == 0)
+            joined[t] = 1;           /* joined below */
+        else
+            ora_dot_worker(j);       /* run on this thread */
+    }
+    int status = ORA_OK;
+    for (int t = 0; t < threads; ++t) {
+        if (joined && joined[t]) pthread_join(tid[t], NULL);
+        if (jobs[t].status != ORA_OK) status = jobs[t].status;
+    }
+    free(joined);
+
+    /* scale back, epilogue, one rounding */
+    if (status == ORA_OK) {
+        int64_t n_out = epilogue == ORA_EPI_SILU_MUL_F16 ? N / 2 : N;
+        for (int64_t l = 0; l < nr; ++l) {
+            for (int64_t c = 0; c < n_out; ++c) {
+                double v;
+                if (epilogue == ORA_EPI_SILU_MUL_F16) {
+#if ORA_MUTANT == 5
+                    double g = acc[l * N + c + N / 2] / in_scale;   /* halves swapped */
+                    double u = acc[l * N + c] / in_scale;
+#else
+                    double g = acc[l * N + c] / in_scale;
+                    double u = acc[l * N + c + N / 2] / in_scale;
+#endif
+#if ORA_MUTANT == 6
+                    v = g / (1.0 + exp(g)) * u;                     /* sign error */
+#else
+                    v = g / (1.0 + exp(-g)) * u;
+#endif
+                } else {
+#if ORA_MUTANT == 4
+                    v = acc[l * N + c];                             /* no scale-back */
+#else
+                    v = acc[l * N + c] / in_scale;
+#endif
+                }
+                y_exact[l * n_out + c] = v;
+                if (epilogue == ORA_EPI_F32) {
+#if ORA_MUTANT == 11
+                    float f = (float)v;                             /* truncation */
+                    if (fabs((double)f) > fabs(v)) f = nextafterf(f, 0.0f);
+                    ((float *)y_out)[l * n_out + c] = f;
+#else
+                    ((float *)y_out)[l * n_out + c] = (float)v;   /* IEEE RNE */
+#endif
+                } else {
+                    ((uint16_t *)y_out)[l * n_out + c] = ora_f64_to_f16(v);
+                }
+            }
+        }
+    }
+    free(xs); free(acc); free(jobs); free(tid);
+    return status;
+}
+
+/* Bytes of a packed [n, k] weight and of its tables (format sizes). */
+int64_t ora_packed_bytes(int64_t n, int64_t k) { return n * (3 * k / 4); }
+int64_t ora_table_bytes(int64_t n) { return (n / 16) * 64 * 2; }

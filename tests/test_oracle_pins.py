@@ -1,0 +1,359 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+The oracle is the plain definition of the LUT-6 linear layer (page
+"Clef-Flash-ANE-LUT6", sections "Weight precision" and "LUT-6 text
+weights").  Nothing here re-types its C code: each pin compares it with
+something independent of it --
+
+  * hand-worked packing examples (tests/golden/pack_worked_examples.txt) and
+    the exhaustive bijection over all 2^24 index tuples / byte triples;
+  * the page's storage figure of about 6.02 bits per weight at K = 4,096
+    (tests/golden/storage_bits_per_weight.txt);
+  * numpy's IEEE binary16 conversions, exhaustively and on every tie;
+  * exact rational (Python integer) brute force on tiny GEMMs;
+  * closed forms: constant, zero, per-group and ramp tables, identity and
+    one-hot activations, the scale invariance of power-of-two in_scale;
+  * the SiLU epilogue against torch's silu in float64.
+
+``test_pins_catch_planted_mistakes`` rebuilds the oracle with each of a list
+of plausible mistakes planted (ORA_MUTANT) and checks that at least one pin
+fails for every one of them.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# ---------------------------------------------------------------------------
+# independent helpers (exact arithmetic; no oracle code)
+# ---------------------------------------------------------------------------
+
+def _frac(v) -> Fraction:
+    return Fraction(float(v))
+
+
+def _round_exact(q: Fraction, dtype) -> np.ndarray:
+    """Correctly rounded (nearest, ties to even) value of the rational q."""
+    c = np.array([float(q)]).astype(dtype)[0]          # within one ulp of the answer
+    cands = [c, np.nextafter(c, dtype(-np.inf)), np.nextafter(c, dtype(np.inf))]
+    cands = [v for v in cands if np.isfinite(v)]
+    best = min(cands, key=lambda v: (abs(_frac(v) - q),
+                                     int(np.array([v], dtype=dtype).view(
+                                         np.uint16 if dtype == np.float16 else np.uint32)[0]) & 1))
+    return np.array([best], dtype=dtype)
+
+
+def _small_problem(L, K, N, seed, *, x_scale=1.0, subnormal_x=False):
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((L, K)) * x_scale).astype(np.float16)
+    if subnormal_x:
+        x.reshape(-1)[:: 7] = (g.integers(1, 1024, size=x.size)[:: 7] * 2.0 ** -24).astype(np.float16)
+    idx = g.integers(0, 64, size=(N, K), dtype=np.uint8)
+    tab = np.sort((g.standard_normal((N // 16, 64)) * 0.02).astype(np.float16), axis=1)
+    return x, idx, tab
+
+
+def _exact_acc(x, idx, tab, s):
+    """Exact sum_k fp16(x*s)[l,k] * T[n//16][idx[n,k]] / s as Fractions."""
+    L, K = x.shape
+    N = idx.shape[0]
+    xs = [[_frac(v) * Fraction(s) for v in row] for row in x]     # exact: s = 2^e, no overflow
+    out = [[None] * N for _ in range(L)]
+    mag = [[None] * N for _ in range(L)]
+    for n in range(N):
+        w = [_frac(tab[n // 16][i]) for i in idx[n]]
+        for l in range(L):
+            terms = [a * b for a, b in zip(xs[l], w)]
+            out[l][n] = sum(terms, Fraction(0)) / Fraction(s)
+            mag[l][n] = sum((abs(t) for t in terms), Fraction(0)) / Fraction(s)
+    return out, mag
+
+
+# ---------------------------------------------------------------------------
+# pins: each takes an Oracle and raises AssertionError on a mismatch
+# ---------------------------------------------------------------------------
+
+def _pack_examples():
+    rows = []
+    for line in (GOLDEN / "pack_worked_examples.txt").read_text().splitlines():
+        if not line.strip() or line.lstrip().startswith("#"):
+            continue
+        left, right = line.split(":")
+        rows.append(([int(v) for v in left.split()], bytes(int(b, 16) for b in right.split())))
+    return rows
+
+
+def pin_pack_worked_examples(ora):
+    ex = _pack_examples()
+    assert len(ex) >= 10
+    idx = np.array([e[0] for e in ex], np.uint8).reshape(1, -1)
+    packed = ora.pack(idx)
+    want = b"".join(e[1] for e in ex)
+    assert packed.tobytes() == want, "packing differs from the hand-worked examples"
+    back = ora.unpack(np.frombuffer(want, np.uint8).reshape(1, -1), idx.shape[1])
+    assert np.array_equal(back, idx), "unpacking differs from the hand-worked examples"
+
+
+def pin_pack_exhaustive(ora):
+    # every 4-tuple of 6-bit indices packs to a distinct 3-byte group and back
+    t = np.arange(64 ** 4, dtype=np.uint32)
+    idx = np.stack([(t // 64 ** i) % 64 for i in range(4)], axis=1).astype(np.uint8).reshape(1, -1)
+    packed = ora.pack(idx)
+    assert packed.size == 3 * 64 ** 4
+    tri = packed.reshape(-1, 3).astype(np.uint32)
+    code = tri[:, 0] + 256 * tri[:, 1] + 65536 * tri[:, 2]
+    assert np.unique(code).size == 2 ** 24, "packing is not injective"
+    assert np.array_equal(ora.unpack(packed, idx.shape[1]), idx), "round trip idx->bytes->idx"
+    # and every byte triple is the packing of exactly one tuple
+    allb = np.arange(2 ** 24, dtype=np.uint32)
+    raw = np.stack([allb % 256, (allb // 256) % 256, allb // 65536], axis=1).astype(np.uint8).reshape(1, -1)
+    again = ora.pack(ora.unpack(raw, 4 * 2 ** 24))
+    assert np.array_equal(again, raw), "round trip bytes->idx->bytes"
+
+
+def pin_storage(ora):
+    want = {}
+    for line in (GOLDEN / "storage_bits_per_weight.txt").read_text().splitlines():
+        if line.strip() and not line.lstrip().startswith("#"):
+            k, v = line.split(":")
+            want[int(k)] = float(v)
+    for K, printed in want.items():
+        N = 256
+        idx = np.zeros((N, K), np.uint8)
+        total = ora.pack(idx).nbytes + ora.table_bytes(N)
+        assert ora.packed_bytes(N, K) == ora.pack(idx).nbytes
+        bpw = total * 8 / (N * K)
+        assert bpw == 6 + 64 / K
+        assert round(bpw, 2) == printed, f"{bpw} bits/weight vs the page's {printed}"
+
+
+def pin_f16_decode(ora):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = ora.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(ours, ref, equal_nan=True), "binary16 decode"
+    assert np.array_equal(np.signbit(ours), np.signbit(ref))
+
+
+def pin_f16_encode(ora):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16).astype(np.float64)
+    pos = np.sort(vals[np.isfinite(vals) & (vals >= 0)])
+    mids = (pos[:-1] + pos[1:]) / 2                          # exact ties
+    up = np.nextafter(mids, np.inf)
+    dn = np.nextafter(mids, -np.inf)
+    g = np.random.default_rng(7)
+    rnd = g.standard_normal(200_000) * 10.0 ** g.uniform(-9, 5, 200_000)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 65504.0, 65519.99, 65520.0,
+                        65536.0, 1e10, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                        2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11 + 2.0 ** -40])
+    v = np.concatenate([vals[np.isfinite(vals)], mids, -mids, up, dn, -up, rnd, special])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    ours = ora.f64_to_f16(v)
+    nan = np.isnan(v)
+    assert np.array_equal(ours[~nan], ref[~nan]), "binary16 encode (round to nearest even)"
+    assert np.all((ours[nan] & 0x7c00) == 0x7c00) and np.all((ours[nan] & 0x3ff) != 0)
+
+
+def pin_dequant(ora):
+    x, idx, tab = _small_problem(1, 192, 96, 11)
+    w = ora.dequant(ora.pack(idx), tab, 192)
+    ref = tab.view(np.uint16)[np.arange(96)[:, None] // 16, idx]
+    assert np.array_equal(w, ref), "dequantized weight != T[n//16][idx]"
+
+
+def pin_linear_bruteforce(ora):
+    for i, (L, K, N) in enumerate([(1, 64, 16), (3, 128, 32), (5, 64, 96), (9, 192, 48)]):
+        x, idx, tab = _small_problem(L, K, N, 100 + i, subnormal_x=(i % 2 == 1))
+        packed = ora.pack(idx)
+        for s in (1.0, 16.0):
+            exact, mag = _exact_acc(x, idx, tab, s)
+            for epi in (oracle.EPI_F32, oracle.EPI_F16):
+                ye, yo = ora.linear(x, packed, tab, epilogue=epi, in_scale=s, threads=2)
+                for l in range(L):
+                    for n in range(N):
+                        q = exact[l][n]
+                        assert abs(_frac(ye[l, n]) - q) <= Fraction(1, 10 ** 12) * mag[l][n] + Fraction(1, 2 ** 80)
+                        dt = np.float32 if epi == oracle.EPI_F32 else np.float16
+                        got = yo[l:l + 1, n] if epi == oracle.EPI_F32 else yo[l:l + 1, n].view(np.float16)
+                        want = _round_exact(q, dt)
+                        assert got.tobytes() == want.tobytes(), (L, K, N, s, epi, l, n)
+
+
+def pin_linear_silu(ora):
+    import torch
+    # One-hot activations read single table entries: a_gate[l, n] = T0[l],
+    # a_up[l, n] = T1[l]; the epilogue must give silu(T0[l]) * T1[l].
+    probes = np.array([0, 0.5, -0.5, 1, -1, 2, -2, 8, -8, 20, -20, 100, -100,
+                       1000, -1000, 0.001, -0.001, 3.14, -3.14], np.float16)
+    ups = np.array([1, 1, 1, 0.5, 0.5, 1, 1, -2, -2, 1, 1, 0.25, 0.25,
+                    1, 1, 3, 3, 1, 1], np.float16)
+    L, K, N = probes.size, 64, 32
+    tab = np.zeros((2, 64), np.float16)
+    tab[0, :L] = probes
+    tab[1, :L] = ups
+    idx = np.tile(np.arange(K, dtype=np.uint8) % 64, (N, 1))
+    x = np.zeros((L, K), np.float16)
+    x[np.arange(L), np.arange(L)] = 1.0
+    ye, yo = ora.linear(x, ora.pack(idx), tab, epilogue=oracle.EPI_SILU_MUL_F16, threads=1)
+    g = torch.tensor(probes.astype(np.float64))
+    ref = (torch.nn.functional.silu(g) * torch.tensor(ups.astype(np.float64))).numpy()
+    for n in range(N // 2):
+        assert np.allclose(ye[:, n], ref, rtol=1e-14, atol=0), "silu(gate) * up"
+        assert np.array_equal(yo[:, n], ref.astype(np.float16).view(np.uint16))
+    # silu(g) - silu(-g) = g and silu(g) ~ g for large g
+    pair = {float(p): ye[i, 0] / float(ups[i]) for i, p in enumerate(probes)}
+    for p in (0.5, 1, 2, 8, 20, 100, 3.14):
+        p16 = float(np.float16(p))
+        assert abs(pair[p16] - pair[-p16] - p16) <= 1e-12 * max(1.0, p16)
+    assert pair[1000.0] == 1000.0 and pair[0.0] == 0.0
+
+
+def pin_special_tables(ora):
+    g = np.random.default_rng(5)
+    L, K, N = 4, 256, 64
+    x = g.standard_normal((L, K)).astype(np.float16)
+    idx = g.integers(0, 64, size=(N, K), dtype=np.uint8)
+    packed = ora.pack(idx)
+    xsum = [sum((_frac(v) for v in row), Fraction(0)) for row in x]
+    # constant tables c = 2^-3: y = c * sum_k x
+    tab = np.full((N // 16, 64), 0.125, np.float16)
+    _, yo = ora.linear(x, packed, tab, epilogue=oracle.EPI_F32, threads=3)
+    for l in range(L):
+        assert np.all(yo[l] == np.float32(float(xsum[l] / 8))), "constant table"
+    # zero tables: +0 everywhere, for every epilogue
+    tab = np.zeros((N // 16, 64), np.float16)
+    for epi in (oracle.EPI_F32, oracle.EPI_F16, oracle.EPI_SILU_MUL_F16):
+        _, yo = ora.linear(x, packed, tab, epilogue=epi, threads=1)
+        assert np.all(yo.view(np.uint32 if epi == oracle.EPI_F32 else np.uint16) == 0)
+    # per-group constant tables T[g][:] = g + 1: y[l, n] = (n // 16 + 1) * sum_k x
+    tab = np.repeat(np.arange(1, N // 16 + 1, dtype=np.float16)[:, None], 64, axis=1)
+    _, yo = ora.linear(x, packed, tab, epilogue=oracle.EPI_F32, threads=2)
+    for l in range(L):
+        want = np.array([float(xsum[l] * (n // 16 + 1)) for n in range(N)], np.float32)
+        assert np.array_equal(yo[l], want), "per-group tables"
+    # ramp tables T[g][j] = j/64 with x = 1: y[l, n] = sum_k idx[n, k] / 64 (raw indices)
+    tab = np.tile((np.arange(64) / 64).astype(np.float16), (N // 16, 1))
+    ones = np.ones((2, K), np.float16)
+    _, yo = ora.linear(ones, packed, tab, epilogue=oracle.EPI_F32, threads=2)
+    want = (idx.astype(np.int64).sum(axis=1) / 64).astype(np.float32)
+    assert np.array_equal(yo[0], want) and np.array_equal(yo[1], want), "ramp tables"
+
+
+def pin_identity_readout(ora):
+    # x = I_K: y[l, n] = W[n, l] bit for bit (one product per output), any s
+    K, N = 64, 48
+    _, idx, tab = _small_problem(1, K, N, 21)
+    W = tab.view(np.uint16)[np.arange(N)[:, None] // 16, idx]
+    eye = np.eye(K, dtype=np.float16)
+    for s in (1.0, 16.0):
+        _, yo = ora.linear(eye, ora.pack(idx), tab, epilogue=oracle.EPI_F16, in_scale=s, threads=2)
+        assert np.array_equal(yo, W.T), "identity readout"
+    # the smallest subnormal activation times 1024 is exactly 2^-14
+    x = np.zeros((1, K), np.float16)
+    x[0, 5] = np.float16(2.0 ** -24)
+    tab1 = np.full((N // 16, 64), 1024, np.float16)
+    _, yo = ora.linear(x, ora.pack(idx), tab1, epilogue=oracle.EPI_F32, threads=1)
+    assert np.all(yo == np.float32(2.0 ** -14)), "subnormal activation"
+
+
+def pin_in_scale(ora):
+    g = np.random.default_rng(9)
+    L, K, N = 6, 128, 64
+    x = g.standard_normal((L, K)).astype(np.float16)
+    idx = g.integers(0, 64, size=(N, K), dtype=np.uint8)
+    tab = np.sort((g.standard_normal((N // 16, 64)) * 0.02).astype(np.float16), axis=1)
+    packed = ora.pack(idx)
+    for epi in (oracle.EPI_F32, oracle.EPI_F16, oracle.EPI_SILU_MUL_F16):
+        _, y1 = ora.linear(x, packed, tab, epilogue=epi, in_scale=1.0, threads=2)
+        for s in (2.0, 4.0, 8.0, 16.0):
+            _, ys = ora.linear(x, packed, tab, epilogue=epi, in_scale=s, threads=2)
+            assert y1.tobytes() == ys.tobytes(), f"power-of-two in_scale {s} changed the result"
+    # overflow: 4096 * 16 = 65536 is beyond FP16, so the scaled input is +inf
+    xo = np.zeros((1, K), np.float16)
+    xo[0, 0] = 4096
+    pos = np.full((N // 16, 64), 0.5, np.float16)
+    _, yf = ora.linear(xo, packed, pos, epilogue=oracle.EPI_F32, in_scale=16.0, threads=1)
+    assert np.all(np.isposinf(yf)), "overflowing scaled input"
+    _, yh = ora.linear(xo, packed, pos, epilogue=oracle.EPI_F16, in_scale=8.0, threads=1)
+    assert np.all(yh.view(np.float16) == np.float16(2048.0)), "largest in-range scale"
+
+
+PINS = [pin_pack_worked_examples, pin_pack_exhaustive, pin_storage, pin_f16_decode,
+        pin_f16_encode, pin_dequant, pin_linear_bruteforce, pin_linear_silu,
+        pin_special_tables, pin_identity_readout, pin_in_scale]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(ora, pin):
+    pin(ora)
+
+
+def test_oracle_refusals(ora):
+    with pytest.raises(oracle.OracleError):
+        ora.pack(np.full((1, 4), 64, np.uint8))                  # index out of range
+    with pytest.raises(oracle.OracleError):
+        ora.pack(np.zeros((1, 6), np.uint8))                     # K not a multiple of 4
+    x = np.zeros((2, 64), np.float16)
+    idx = np.zeros((16, 64), np.uint8)
+    tab = np.zeros((1, 64), np.float16)
+    with pytest.raises(oracle.OracleError):                      # SiLU split needs N % 32
+        ora.linear(x, ora.pack(idx), tab, epilogue=oracle.EPI_SILU_MUL_F16)
+    with pytest.raises(oracle.OracleError):
+        ora.linear(x, ora.pack(idx), tab, epilogue=oracle.EPI_F16, rows=[2])
+
+
+def test_oracle_row_subset(ora):
+    x, idx, tab = _small_problem(9, 128, 64, 3)
+    packed = ora.pack(idx)
+    full_e, full_o = ora.linear(x, packed, tab, epilogue=oracle.EPI_F16)
+    rows = [0, 4, 8]
+    sub_e, sub_o = ora.linear(x, packed, tab, epilogue=oracle.EPI_F16, rows=rows)
+    assert np.array_equal(sub_o, full_o[rows]) and np.array_equal(sub_e, full_e[rows])
+
+
+def test_oracle_threads_do_not_change_result(ora):
+    x, idx, tab = _small_problem(7, 256, 96, 4)
+    packed = ora.pack(idx)
+    a = ora.linear(x, packed, tab, epilogue=oracle.EPI_F32, threads=1)
+    b = ora.linear(x, packed, tab, epilogue=oracle.EPI_F32, threads=5)
+    assert a[0].tobytes() == b[0].tobytes()
+
+
+MUTANTS = {1: "big-endian byte order", 2: "index order reversed", 3: "one table per 32 channels",
+           4: "no scale-back", 5: "gate and up halves swapped", 6: "SiLU sign error",
+           7: "last input column dropped", 8: "ties rounded away from zero",
+           9: "subnormal decode off by 2x", 10: "activations read transposed",
+           11: "f32 output truncated"}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m].replace(" ", "_"))
+def test_pins_catch_planted_mistakes(mutant, tmp_path):
+    lib = oracle.build(tmp_path / f"liblut6_oracle_m{mutant}.so", mutant=mutant)
+    bad = oracle.Oracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(bad)
+        except (AssertionError, oracle.OracleError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught planted mistake {mutant} ({MUTANTS[mutant]})"
+
+
+def test_seeded_inputs_are_reproducible():
+    a = si.gemm_inputs(1, 0, 0, si.Gemm("t", 8, 64, 32, si.EPI_F16))
+    b = si.gemm_inputs(1, 0, 0, si.Gemm("t", 8, 64, 32, si.EPI_F16))
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+    tab = a[2]
+    assert np.all(np.diff(tab.astype(np.float64), axis=1) >= 0), "tables sorted"
+    assert a[1].max() <= 63
