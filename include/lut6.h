@@ -1,0 +1,130 @@
+/*
+ * lut6.h -- C ABI of the LUT-6 weight-quantized linear layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The format (page "Clef-Flash-ANE-LUT6", section "Weight precision"): a
+ * linear layer's weight W[N, K] (N output channels, K input features) is
+ * stored as one 6-bit index per weight plus one table of 64 FP16 values per
+ * 16 consecutive output channels; W[n, k] = table[n / 16][index(n, k)].
+ * Section "LUT-6 text weights": four 6-bit indices are packed into three
+ * bytes, little-endian, so that with its tables a layer with 4,096 inputs
+ * takes about 6.02 bits per weight; activations are FP16, and the MLP
+ * down-projection input is scaled up (by at most 16x) and the result scaled
+ * back.
+ *
+ * Layouts (the readings this library takes where the page is silent):
+ *   idx     uint8 [N, K] row-major, every value in 0..63 (host only).
+ *   packed  uint8 [N, 3K/4] row-major.  Input columns 4j..4j+3 of row n form
+ *           the 24-bit word w = i0 | i1<<6 | i2<<12 | i3<<18 (i0 = column
+ *           4j), stored as bytes 3j, 3j+1, 3j+2 = w & 0xff, (w>>8) & 0xff,
+ *           w >> 16.
+ *   tables  FP16 [N/16, 64] row-major (128 bytes per table); table g serves
+ *           output channels 16g..16g+15; entry = table[index], no offset.
+ *   x       FP16 [L, K] row-major (L tokens).
+ *   y       FP32 [L, N], FP16 [L, N] or FP16 [L, N/2] by epilogue.
+ *
+ * Ownership: the caller allocates, owns and frees every buffer.  Pointers
+ * passed to lut6_linear / lut6_dequant are device pointers of the current
+ * HIP device; pointers passed to lut6_pack / lut6_unpack are host pointers.
+ * The library keeps no per-call state.  It owns one lazily created device
+ * workspace per device for split-K partial sums (created on the first call
+ * that needs it, grown when a later call needs more, freed by
+ * lut6_release()).
+ *
+ * Errors: every function returns LUT6_OK (0) or a named status, and launches
+ * nothing on error.  Arguments are checked on the host; nothing is silently
+ * truncated or padded.  Device-side failures of an enqueued launch surface
+ * as LUT6_E_DEVICE when the launch itself fails, and otherwise at the
+ * caller's next synchronisation, as usual in HIP.
+ */
+#ifndef LUT6_H
+#define LUT6_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LUT6_OK = 0,
+    LUT6_E_NULL = 1,         /* a required pointer is NULL                       */
+    LUT6_E_SHAPE = 2,        /* sizes break a rule below                         */
+    LUT6_E_ALIGN = 3,        /* a device pointer is not 16-byte aligned          */
+    LUT6_E_SCALE = 4,        /* in_scale is not 1, 2, 4, 8 or 16                 */
+    LUT6_E_EPILOGUE = 5,     /* unknown epilogue code                            */
+    LUT6_E_INDEX_RANGE = 6,  /* lut6_pack: an index is above 63                  */
+    LUT6_E_DEVICE = 7,       /* a HIP call or kernel launch failed               */
+    LUT6_E_ALIAS = 8         /* the output overlaps an input                     */
+} lut6_status;
+
+typedef enum {
+    /* y FP32 [L, N]: y = (sum_k fp16(x*s)[l,k] * W[n,k]) / s, rounded once  */
+    LUT6_EPI_STORE_F32 = 0,
+    /* y FP16 [L, N]: the same value rounded once to FP16 (nearest even)    */
+    LUT6_EPI_STORE_F16 = 1,
+    /* y FP16 [L, N/2]: rows [0, N/2) of W are the MLP gate, rows [N/2, N)
+     * the up projection (tables likewise); y[l, j] = silu(a[l, j]) *
+     * a[l, j + N/2] with a the scaled-back FP32 sum and
+     * silu(g) = g / (1 + exp(-g)), rounded once to FP16                   */
+    LUT6_EPI_SILU_MUL_F16 = 2
+} lut6_epilogue;
+
+/* Bytes of a packed [N, K] index matrix: N * 3K/4 (0 if K % 4 or a size
+ * is not positive).                                                       */
+size_t lut6_packed_bytes(int64_t N, int64_t K);
+
+/* Bytes of the tables of an N-channel weight: (N/16) * 64 * 2 (0 if N % 16
+ * or N is not positive).                                                  */
+size_t lut6_table_bytes(int64_t N);
+
+/* Pack idx [N, K] (host) into packed [N, 3K/4] (host), layout above.
+ * N > 0, K > 0, K % 4 == 0 (else LUT6_E_SHAPE); an index above 63 is
+ * refused with LUT6_E_INDEX_RANGE, never masked (packed is then
+ * unspecified).  Synchronous.                                             */
+int lut6_pack(const uint8_t* idx, uint8_t* packed, int64_t N, int64_t K);
+
+/* Inverse of lut6_pack: packed [N, 3K/4] (host) -> idx [N, K] (host).
+ * Every byte string is a valid packing.  Synchronous.                     */
+int lut6_unpack(const uint8_t* packed, uint8_t* idx, int64_t N, int64_t K);
+
+/* The LUT-6 linear layer (page "Clef-Flash-ANE-LUT6", sections "Weight
+ * precision" and "LUT-6 text weights"):
+ *     xs = fp16(x * in_scale)          (round to nearest even, +-inf on overflow)
+ *     a[l, n] = (sum_k xs[l, k] * W[n, k]) / in_scale,  FP32 accumulation
+ *     y = epilogue(a)
+ * Device pointers x (FP16 [L, K]), packed ([N, 3K/4]), tables (FP16
+ * [N/16, 64]), y (see lut6_epilogue); all 16-byte aligned (LUT6_E_ALIGN).
+ * Rules (LUT6_E_SHAPE): L >= 0, K > 0, N > 0, K % 64 == 0, N % 16 == 0, and
+ * N % 32 == 0 for LUT6_EPI_SILU_MUL_F16; L, K and N at most 2^31 - 1 and
+ * every buffer below 2^31 elements per row-major plane.  L == 0 is a no-op.
+ * in_scale must be exactly 1, 2, 4, 8 or 16 (LUT6_E_SCALE), so the scaling
+ * is exact.  y must not overlap x, packed or tables (LUT6_E_ALIAS).
+ * Enqueues the work on `stream` (0 = null stream) and returns; results are
+ * deterministic run to run (no floating-point atomics).                   */
+int lut6_linear(const void* x, const uint8_t* packed, const void* tables, void* y,
+                int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
+                hipStream_t stream);
+
+/* Dequantize: w[n, k] = tables[n/16][index(n, k)] as FP16 bits [N, K] on
+ * the device, with the same device unpack and lookup as lut6_linear.
+ * N % 16 == 0, K % 64 == 0; 16-byte aligned pointers; enqueued on stream.
+ * A bit copy: the result is exact.                                        */
+int lut6_dequant(const uint8_t* packed, const void* tables, void* w,
+                 int64_t N, int64_t K, hipStream_t stream);
+
+/* Free the library's per-device workspaces (after synchronising the
+ * devices that hold one).  Optional; safe to call at any time when no
+ * lut6_linear call is in flight.                                          */
+int lut6_release(void);
+
+/* Name of a status code ("LUT6_OK", "LUT6_E_SHAPE", ...); never NULL.     */
+const char* lut6_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LUT6_H */

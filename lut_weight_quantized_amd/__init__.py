@@ -1,0 +1,191 @@
+"""LUT-6 weight-quantized linear layer on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of the C ABI in ``include/lut6.h`` (library
+``liblut6.so`` in this package, built by ``lut_weight_quantized_amd.build``).
+It only marshals arguments: every step of the computation runs in the HIP
+kernels.  PyTorch is used for device memory and streams.  There is no CPU
+fallback: if the library is missing, every call raises.
+
+Format (page "Clef-Flash-ANE-LUT6", sections "Weight precision" and "LUT-6
+text weights"): 6-bit indices along the input dimension of a row-major
+[N, K] weight, four packed little-endian into three bytes, and one table of
+64 FP16 values per 16 output channels.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import numpy as np
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "liblut6.so"
+
+EPI_STORE_F32 = 0
+EPI_STORE_F16 = 1
+EPI_SILU_MUL_F16 = 2
+
+STATUS = {0: "LUT6_OK", 1: "LUT6_E_NULL", 2: "LUT6_E_SHAPE", 3: "LUT6_E_ALIGN",
+          4: "LUT6_E_SCALE", 5: "LUT6_E_EPILOGUE", 6: "LUT6_E_INDEX_RANGE",
+          7: "LUT6_E_DEVICE", 8: "LUT6_E_ALIAS"}
+
+EXPORTS = ("lut6_packed_bytes", "lut6_table_bytes", "lut6_pack", "lut6_unpack",
+           "lut6_linear", "lut6_dequant", "lut6_release", "lut6_status_string")
+
+
+class Lut6Error(RuntimeError):
+    """A nonzero status from the library; ``.status`` is its name."""
+
+    def __init__(self, status: int, where: str):
+        self.code = int(status)
+        self.status = STATUS.get(self.code, f"LUT6_E_UNKNOWN({status})")
+        super().__init__(f"{where}: {self.status}")
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load ``liblut6.so``; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m lut_weight_quantized_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.lut6_packed_bytes.argtypes = [I64, I64]
+    lib.lut6_packed_bytes.restype = ctypes.c_size_t
+    lib.lut6_table_bytes.argtypes = [I64]
+    lib.lut6_table_bytes.restype = ctypes.c_size_t
+    lib.lut6_pack.argtypes = [P, P, I64, I64]
+    lib.lut6_pack.restype = ctypes.c_int
+    lib.lut6_unpack.argtypes = [P, P, I64, I64]
+    lib.lut6_unpack.restype = ctypes.c_int
+    lib.lut6_linear.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_float, ctypes.c_int, P]
+    lib.lut6_linear.restype = ctypes.c_int
+    lib.lut6_dequant.argtypes = [P, P, P, I64, I64, P]
+    lib.lut6_dequant.restype = ctypes.c_int
+    lib.lut6_release.argtypes = []
+    lib.lut6_release.restype = ctypes.c_int
+    lib.lut6_status_string.argtypes = [ctypes.c_int]
+    lib.lut6_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise Lut6Error(status, where)
+
+
+def status_string(status: int) -> str:
+    return load_library().lut6_status_string(int(status)).decode()
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(load_library().lut6_packed_bytes(N, K))
+
+
+def table_bytes(N: int) -> int:
+    return int(load_library().lut6_table_bytes(N))
+
+
+# ---------------------------------------------------------------------------
+# host format functions (numpy in, numpy out)
+# ---------------------------------------------------------------------------
+
+def pack(idx: np.ndarray) -> np.ndarray:
+    """uint8 indices [N, K] (each 0..63) -> packed bytes [N, 3K/4]."""
+    idx = np.ascontiguousarray(idx)
+    if idx.dtype != np.uint8 or idx.ndim != 2:
+        raise TypeError("idx must be a 2-D uint8 array")
+    N, K = idx.shape
+    out = np.empty((N, 3 * K // 4 if K % 4 == 0 else 0), np.uint8)
+    _check(load_library().lut6_pack(idx.ctypes.data, out.ctypes.data, N, K), "lut6_pack")
+    return out
+
+
+def unpack(packed: np.ndarray, K: int) -> np.ndarray:
+    """packed bytes [N, 3K/4] -> uint8 indices [N, K]."""
+    packed = np.ascontiguousarray(packed)
+    if packed.dtype != np.uint8 or packed.ndim != 2 or packed.shape[1] * 4 != 3 * K:
+        raise TypeError("packed must be a uint8 [N, 3K/4] array")
+    out = np.empty((packed.shape[0], K), np.uint8)
+    _check(load_library().lut6_unpack(packed.ctypes.data, out.ctypes.data, packed.shape[0], K),
+           "lut6_unpack")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# device functions (torch tensors on the current HIP device)
+# ---------------------------------------------------------------------------
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+
+
+def linear(x, packed, tables, *, epilogue: int = EPI_STORE_F16, in_scale: float = 1.0,
+           out=None, stream=None):
+    """y = epilogue((fp16(x * in_scale) @ W^T) / in_scale) on the GPU.
+
+    x: float16 [L, K]; packed: uint8 [N, 3K/4]; tables: float16 [N/16, 64];
+    returns float32 [L, N] (EPI_STORE_F32), float16 [L, N] (EPI_STORE_F16) or
+    float16 [L, N/2] (EPI_SILU_MUL_F16: rows [0, N/2) of W gate, the rest up).
+    """
+    import torch
+    _require(x, torch.float16, "x")
+    _require(packed, torch.uint8, "packed")
+    _require(tables, torch.float16, "tables")
+    if x.dim() != 2 or packed.dim() != 2:
+        raise TypeError("x and packed must be 2-D")
+    L, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != 3 * K or tables.numel() * 16 != N * 64:
+        raise TypeError("packed / tables do not match x's K and packed's N")
+    n_out = N // 2 if epilogue == EPI_SILU_MUL_F16 else N
+    dt = torch.float32 if epilogue == EPI_STORE_F32 else torch.float16
+    if out is None:
+        out = torch.empty((L, n_out), dtype=dt, device=x.device)
+    else:
+        _require(out, dt, "out")
+        if tuple(out.shape) != (L, n_out):
+            raise TypeError(f"out must be [{L}, {n_out}]")
+    st = load_library().lut6_linear(x.data_ptr(), packed.data_ptr(), tables.data_ptr(),
+                                    out.data_ptr(), L, K, N, float(in_scale), int(epilogue),
+                                    _stream_handle(stream))
+    _check(st, "lut6_linear")
+    return out
+
+
+def dequant(packed, tables, K: int, *, out=None, stream=None):
+    """FP16 weight [N, K] with w[n, k] = tables[n/16][index(n, k)] (bit copy)."""
+    import torch
+    _require(packed, torch.uint8, "packed")
+    _require(tables, torch.float16, "tables")
+    N = packed.shape[0]
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
+    else:
+        _require(out, torch.float16, "out")
+    st = load_library().lut6_dequant(packed.data_ptr(), tables.data_ptr(), out.data_ptr(),
+                                     N, K, _stream_handle(stream))
+    _check(st, "lut6_dequant")
+    return out
+
+
+def release() -> None:
+    _check(load_library().lut6_release(), "lut6_release")

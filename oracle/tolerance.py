@@ -1,0 +1,125 @@
+"""Parity criteria between a device result and the oracle -- test
+infrastructure only (used by the tests, the smoke check and the benchmark's
+parity sample).
+
+Criteria, fixed before any device run:
+  * dequantized weights: bit-exact (a lookup has exactly one right answer);
+  * every output: |y - y_ref| <= B_row with
+        B_row = 2e-3 * ||x_row||_2 * max|table| * sqrt(K) / 64
+    where x_row is the unscaled input row, max|table| the largest magnitude
+    over all tables of the weight, and y_ref the oracle's unrounded value;
+  * FP16 outputs: at most 1 unit in the last place from fp16(y_ref)
+    (distance between the ordered bit patterns, +0 == -0).  Where
+    |y_ref| < tau_row = 2^-10 * S_row (S_row = B_row / 2e-3, the natural
+    scale of the row) FP32 summation noise is larger than an FP16 ulp, so
+    the allowance there is the absolute ulp16(tau_row) instead;
+  * SiLU(gate) * up: the bound propagates through h = silu(g) * u as
+        B_h = (1.1 |u_ref| + |silu(g_ref)|) * B_row     (|silu'| <= 1.1)
+    with the same ulp rule on S_h = B_h / 2e-3.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+REL = 2e-3
+
+
+def row_scale(x16: np.ndarray, tables16: np.ndarray, K: int, rows=None) -> np.ndarray:
+    """S_row = ||x_row||_2 * max|table| * sqrt(K) / 64 for the listed rows."""
+    x = np.asarray(x16).view(np.float16)
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    xn = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=1))
+    tmax = float(np.max(np.abs(np.asarray(tables16).view(np.float16).astype(np.float64))))
+    return xn * tmax * np.sqrt(K) / 64.0
+
+
+def _ordered(bits: np.ndarray) -> np.ndarray:
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def ulp16(v: np.ndarray) -> np.ndarray:
+    """Spacing of FP16 numbers at |v| (2^-24 below the normal range)."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+@dataclass
+class Report:
+    ok: bool
+    n: int
+    max_abs_err: float
+    max_err_over_bound: float
+    max_ulp: int
+    strict_ulp_violations: int       # beyond 1 ulp, counted without the floor (diagnostic)
+    floor_cases: int
+    failures: int
+
+    def __str__(self):
+        return (f"ok={self.ok} n={self.n} max|err|={self.max_abs_err:.3g} "
+                f"max err/bound={self.max_err_over_bound:.3g} max_ulp={self.max_ulp} "
+                f"strict>1ulp={self.strict_ulp_violations} floor={self.floor_cases} "
+                f"failures={self.failures}")
+
+
+def check(y_dev: np.ndarray, y_exact: np.ndarray, S_row: np.ndarray, *, fp16: bool,
+          S_elem: np.ndarray | None = None) -> Report:
+    """Compare device outputs with the oracle's unrounded values.
+
+    y_dev: float32 array, or FP16 (float16 / uint16 bits) when fp16=True.
+    S_row: per-row scale [rows]; S_elem (optional, SiLU) per-element scale.
+    """
+    y_exact = np.asarray(y_exact, np.float64)
+    S = np.asarray(S_elem, np.float64) if S_elem is not None else np.asarray(S_row, np.float64)[:, None]
+    S = np.broadcast_to(S, y_exact.shape)
+    bound = REL * S
+    if fp16:
+        bits = np.asarray(y_dev).view(np.uint16)
+        val = bits.view(np.float16).astype(np.float64)
+    else:
+        val = np.asarray(y_dev, np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        err = np.abs(val - y_exact)
+        same_inf = np.isinf(val) & np.isinf(y_exact) & (np.sign(val) == np.sign(y_exact))
+        both_nan = np.isnan(val) & np.isnan(y_exact)
+        special = same_inf | both_nan
+        err = np.where(special, 0.0, err)
+        bad = ~(err <= bound)
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    max_ulp = 0
+    strict = 0
+    floor_cases = 0
+    if fp16:
+        with np.errstate(over="ignore"):
+            ref_bits = y_exact.astype(np.float16).view(np.uint16)
+        d = np.abs(_ordered(bits) - _ordered(ref_bits))
+        d = np.where(special, 0, d)
+        tau = 2.0 ** -10 * S
+        floor = np.abs(y_exact) < tau
+        ref16 = ref_bits.view(np.float16).astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            floor_ok = np.abs(val - ref16) <= ulp16(tau)
+        ulp_bad = np.where(floor, ~floor_ok, d > 1)
+        bad = bad | ulp_bad
+        max_ulp = int(d[~floor].max()) if np.any(~floor) else 0
+        strict = int(np.sum(d > 1))
+        floor_cases = int(np.sum(floor))
+    return Report(ok=not bool(np.any(bad)), n=int(y_exact.size),
+                  max_abs_err=float(np.max(err)) if err.size else 0.0,
+                  max_err_over_bound=float(np.max(ratio)) if ratio.size else 0.0,
+                  max_ulp=max_ulp, strict_ulp_violations=strict, floor_cases=floor_cases,
+                  failures=int(np.sum(bad)))
+
+
+def silu_scale(g_exact: np.ndarray, u_exact: np.ndarray, S_row: np.ndarray) -> np.ndarray:
+    """Per-element S_h = (1.1 |u| + |silu(g)|) * S_row for h = silu(g) * u."""
+    g = np.asarray(g_exact, np.float64)
+    u = np.asarray(u_exact, np.float64)
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(-g))
+    return (1.1 * np.abs(u) + np.abs(silu)) * np.asarray(S_row, np.float64)[:, None]

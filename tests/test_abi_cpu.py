@@ -1,0 +1,121 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+packs and unpacks exactly like the oracle, and refuses bad arguments with
+the named status before touching the device.
+
+No test here launches a kernel: arguments that pass validation are never
+used, and the pointers are fake (aligned integers that are never read).
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import lut_weight_quantized_amd as lq
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "lut6.h"
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(lut6_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = lq.load_library()
+    declared = _declared_functions()
+    assert set(declared) == set(lq.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_strings():
+    for code, name in lq.STATUS.items():
+        assert lq.status_string(code) == name
+    assert lq.status_string(12345) == "LUT6_E_UNKNOWN"
+
+
+def test_sizes():
+    assert lq.packed_bytes(4096, 4096) == 4096 * 3072
+    assert lq.table_bytes(4096) == 256 * 128
+    assert lq.packed_bytes(16, 6) == 0 and lq.table_bytes(20) == 0 and lq.packed_bytes(-1, 4) == 0
+    # bits per weight including tables: 6 + 64 / K
+    assert (lq.packed_bytes(256, 4096) + lq.table_bytes(256)) * 8 / (256 * 4096) == 6 + 64 / 4096
+
+
+def test_pack_matches_oracle_exhaustively(ora):
+    t = np.arange(64 ** 4, dtype=np.uint32)
+    idx = np.stack([(t // 64 ** i) % 64 for i in range(4)], axis=1).astype(np.uint8).reshape(64, -1)
+    ours = lq.pack(idx)
+    assert np.array_equal(ours, ora.pack(idx))
+    assert np.array_equal(lq.unpack(ours, idx.shape[1]), idx)
+
+
+def test_unpack_matches_oracle_on_every_byte_triple(ora):
+    b = np.arange(2 ** 24, dtype=np.uint32)
+    raw = np.stack([b % 256, (b // 256) % 256, b // 65536], axis=1).astype(np.uint8).reshape(16, -1)
+    K = raw.shape[1] * 4 // 3
+    assert np.array_equal(lq.unpack(raw, K), ora.unpack(raw, K))
+
+
+def test_pack_refusals():
+    bad = np.zeros((2, 8), np.uint8)
+    bad[1, 5] = 64
+    with pytest.raises(lq.Lut6Error) as e:
+        lq.pack(bad)
+    assert e.value.status == "LUT6_E_INDEX_RANGE"
+    lib = lq.load_library()
+    buf = np.zeros(64, np.uint8)
+    assert lib.lut6_pack(buf.ctypes.data, buf.ctypes.data, 1, 6) == 2        # K % 4
+    assert lib.lut6_pack(None, buf.ctypes.data, 1, 4) == 1
+    assert lib.lut6_unpack(buf.ctypes.data, None, 1, 4) == 1
+    assert lib.lut6_pack(buf.ctypes.data, buf.ctypes.data, 0, 4) == 2
+
+
+# fake, 16-byte aligned, far-apart device addresses (never dereferenced)
+X, P, T, Y = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000, 0x40_0000_0000
+
+
+def _linear(x=X, p=P, t=T, y=Y, L=128, K=4096, N=4096, s=1.0, epi=1):
+    return lq.load_library().lut6_linear(x, p, t, y, L, K, N, s, epi, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(x=None), 1), (dict(p=None), 1), (dict(t=None), 1), (dict(y=None), 1),
+    (dict(L=-1), 2), (dict(K=0), 2), (dict(N=0), 2), (dict(K=4000), 2), (dict(K=100), 2),
+    (dict(N=4008), 2), (dict(N=48, epi=2), 2), (dict(L=2 ** 31), 2),
+    (dict(epi=3), 5), (dict(epi=-1), 5),
+    (dict(s=3.0), 4), (dict(s=32.0), 4), (dict(s=0.5), 4), (dict(s=-1.0), 4),
+    (dict(x=X + 8), 3), (dict(y=Y + 2), 3), (dict(p=P + 4), 3), (dict(t=T + 1), 3),
+    (dict(y=X), 8), (dict(y=P + 16), 8), (dict(y=T), 8),
+    (dict(L=0), 0),
+])
+def test_linear_validation(kwargs, status):
+    assert _linear(**kwargs) == status
+
+
+def test_dequant_validation():
+    lib = lq.load_library()
+    assert lib.lut6_dequant(None, T, Y, 32, 64, None) == 1
+    assert lib.lut6_dequant(P, T, Y, 20, 64, None) == 2
+    assert lib.lut6_dequant(P, T, Y, 32, 60, None) == 2
+    assert lib.lut6_dequant(P + 4, T, Y, 32, 64, None) == 3
+    assert lib.lut6_dequant(P, T, P, 32, 64, None) == 8
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        lq.linear(x, torch.zeros(16, 48, dtype=torch.uint8), torch.zeros(1, 64, dtype=torch.float16))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(lq, "_lib", None)
+    monkeypatch.setattr(lq, "LIB_PATH", tmp_path / "liblut6.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        lq.load_library()

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every input is seeded and synthetic (seeded_inputs.py).  The oracle gets its
+own packing of the raw indices; the device gets the library's packing.  The
+criteria are those of oracle/tolerance.py: bit-exact dequantization, the
+float bound on every output, 1 FP16 ulp (with the near-zero floor) on FP16
+outputs.  Full-size workloads are checked on every row when the oracle can
+afford it and on seeded sampled rows otherwise.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from oracle import tolerance as tol
+
+torch = pytest.importorskip("torch")
+import lut_weight_quantized_amd as lq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+F32, F16, SILU = lq.EPI_STORE_F32, lq.EPI_STORE_F16, lq.EPI_SILU_MUL_F16
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _dev(a: np.ndarray, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to("cuda")
+
+
+def gpu_linear(x16, idx, tab16, epi, s, packed=None):
+    packed = lq.pack(idx) if packed is None else packed
+    y = lq.linear(_dev(x16), _dev(packed), _dev(tab16), epilogue=epi, in_scale=s)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    return y.view(np.uint16) if epi != F32 else y
+
+
+def oracle_check(ora, x16, idx, tab16, epi, s, y_dev, rows=None, packer=None):
+    """Report whether the device output (all rows, or `rows`) meets the criteria.
+
+    The oracle computes from the raw indices packed by `packer` (an oracle;
+    itself by default)."""
+    K = x16.shape[1]
+    N = idx.shape[0]
+    packed = (packer or ora).pack(idx)
+    S = tol.row_scale(x16, tab16, K, rows)
+    yd = y_dev if rows is None else y_dev[np.asarray(rows)]
+    if epi == SILU:
+        h_exact, _ = ora.linear(x16, packed, tab16, epilogue=oracle.EPI_SILU_MUL_F16, in_scale=s, rows=rows)
+        a_exact, _ = ora.linear(x16, packed, tab16, epilogue=oracle.EPI_F32, in_scale=s, rows=rows)
+        Se = tol.silu_scale(a_exact[:, : N // 2], a_exact[:, N // 2:], S)
+        rep = tol.check(yd, h_exact, S, fp16=True, S_elem=Se)
+    else:
+        y_exact, _ = ora.linear(x16, packed, tab16, epilogue=epi, in_scale=s, rows=rows)
+        rep = tol.check(yd, y_exact, S, fp16=(epi == F16))
+    return rep
+
+
+def _problem(L, K, N, seed, *, sigma=1.0, outliers=0.02, subnormal=False):
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((L, K)) * sigma).astype(np.float16)
+    if subnormal:
+        flat = x.reshape(-1)
+        flat[::13] = (g.integers(1, 1024, size=flat[::13].size) * 2.0 ** -24 *
+                      g.choice([-1, 1], size=flat[::13].size)).astype(np.float16)
+    idx = g.integers(0, 64, size=(N, K), dtype=np.uint8)
+    t = g.standard_normal((N // 16, 64)) * 0.02
+    m = g.random((N // 16, 64)) < outliers
+    tab = np.sort(np.where(m, t * 8, t).astype(np.float16), axis=1)
+    return x, idx, tab
+
+
+# ---------------------------------------------------------------------------
+# dequantization: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(16, 64), (48, 192), (272, 576), (96, 12288), (4096, 4096)])
+def test_dequant_bit_exact(ora, N, K):
+    _say("dequant", N, K)
+    _, idx, tab = _problem(1, K, N, 7 + N + K)
+    w = lq.dequant(_dev(lq.pack(idx)), _dev(tab), K)
+    torch.cuda.synchronize()
+    got = w.cpu().numpy().view(np.uint16)
+    want = ora.dequant(ora.pack(idx), tab, K)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# identity readout: x = I_K gives y = W^T bit for bit (one product per output)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("s", [1.0, 16.0])
+@pytest.mark.parametrize("K", [64, 256])
+def test_identity_readout(ora, K, s):
+    _say("identity", K, s)
+    N = 96
+    _, idx, tab = _problem(1, K, N, 3)
+    eye = np.eye(K, dtype=np.float16)
+    y = gpu_linear(eye, idx, tab, F16, s)
+    W = ora.dequant(ora.pack(idx), tab, K)
+    assert np.array_equal(y, W.T)
+
+
+# ---------------------------------------------------------------------------
+# small and ragged shapes, every epilogue, both regimes
+# ---------------------------------------------------------------------------
+
+SHAPES = [(1, 64, 32), (3, 128, 32), (17, 192, 64), (64, 64, 96), (100, 256, 288),
+          (128, 576, 64), (129, 128, 128), (193, 320, 160), (256, 128, 544),
+          (300, 192, 288), (513, 256, 320), (777, 128, 96)]
+
+
+@pytest.mark.parametrize("L,K,N", SHAPES)
+@pytest.mark.parametrize("epi,s", [(F32, 1.0), (F16, 1.0), (F16, 16.0), (SILU, 1.0), (SILU, 4.0)])
+def test_linear_small(ora, L, K, N, epi, s):
+    _say("small", L, K, N, epi, s)
+    x, idx, tab = _problem(L, K, N, L * 7 + K + N, sigma=0.5 if s > 1 else 1.0,
+                           subnormal=(L % 2 == 1))
+    y = gpu_linear(x, idx, tab, epi, s)
+    rep = oracle_check(ora, x, idx, tab, epi, s, y)
+    assert rep.ok, str(rep)
+
+
+def test_non_aligned_n_tiles(ora):
+    # N = 16 * odd so the last channel tile is partial in both regimes
+    for L in (64, 384):
+        _say("ragged-n", L)
+        x, idx, tab = _problem(L, 128, 16 * 37, 91 + L)
+        y = gpu_linear(x, idx, tab, F16, 1.0)
+        rep = oracle_check(ora, x, idx, tab, F16, 1.0, y)
+        assert rep.ok, str(rep)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the benchmark uses
+# ---------------------------------------------------------------------------
+
+def _workload_gemm_check(ora, cfg, layer, proj, g, n_rows):
+    x, idx, tab = si.gemm_inputs(cfg, layer, proj, g)
+    rows = None if n_rows is None else si.sample_rows(g.L, n_rows, (cfg, layer, proj))
+    y = gpu_linear(x, idx, tab, g.epilogue, g.in_scale)
+    rep = oracle_check(ora, x, idx, tab, g.epilogue, g.in_scale, y, rows)
+    assert rep.ok, f"{g.name}: {rep}"
+    return rep
+
+
+@pytest.mark.parametrize("name,n_rows", [("o_proj_l128", None), ("mlp_gate_up_l512", 24),
+                                         ("mlp_down_l1024", 24), ("hybrid_block_l4096", 12)])
+def test_workload(ora, name, n_rows):
+    w = si.WORKLOADS[name]
+    for li, pi, g in w.gemms():
+        _say(name, g.name, g.L, g.K, g.N)
+        _workload_gemm_check(ora, w.cfg, li, pi, g, n_rows)
+
+
+@pytest.mark.parametrize("layer", [0, 3])
+def test_prefill_sweep_sampled_layers(ora, layer):
+    # one Gated DeltaNet layer (0) and one full-attention layer (3) of the
+    # 32-layer sweep, every projection, at L = 16,384 on 8 sampled rows
+    w = si.WORKLOADS["prefill_sweep_l16384"]
+    for pi, g in enumerate(w.layers[layer]):
+        _say("sweep", layer, g.name)
+        _workload_gemm_check(ora, w.cfg, layer, pi, g, 8)
+
+
+# ---------------------------------------------------------------------------
+# properties
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L,K,N,epi", [(128, 4096, 4096, F32), (1024, 512, 1024, F16),
+                                       (96, 256, 128, SILU)])
+def test_deterministic(L, K, N, epi):
+    _say("determinism", L, K, N, epi)
+    x, idx, tab = _problem(L, K, N, 5)
+    xs, ps, ts = _dev(x), _dev(lq.pack(idx)), _dev(tab)
+    outs = []
+    for _ in range(3):
+        outs.append(lq.linear(xs, ps, ts, epilogue=epi).cpu().numpy().tobytes())
+    assert outs[0] == outs[1] == outs[2]
+
+
+@pytest.mark.parametrize("epi", [F32, F16, SILU])
+@pytest.mark.parametrize("L", [64, 640])
+def test_scale_invariance(L, epi):
+    # power-of-two scaling commutes with rounding when nothing overflows
+    _say("scale-invariance", L, epi)
+    x, idx, tab = _problem(L, 256, 256, 8)
+    y1 = gpu_linear(x, idx, tab, epi, 1.0)
+    for s in (2.0, 16.0):
+        assert gpu_linear(x, idx, tab, epi, s).tobytes() == y1.tobytes()
+
+
+@pytest.mark.parametrize("L", [32, 512])
+def test_overflow_gives_inf(ora, L):
+    _say("overflow", L)
+    x, idx, _ = _problem(L, 128, 64, 2)
+    x[:, 3] = np.float16(4096.0)         # 4096 * 16 = 65536 overflows FP16
+    tab = np.full((4, 64), 0.5, np.float16)
+    for epi in (F32, F16):
+        y = gpu_linear(x, idx, tab, epi, 16.0)
+        yv = y if epi == F32 else y.view(np.float16)
+        _, ref = ora.linear(x, ora.pack(idx), tab, epilogue=epi, in_scale=16.0)
+        rv = ref if epi == F32 else ref.view(np.float16)
+        assert np.all(np.isposinf(yv)) and np.all(np.isposinf(rv))
+
+
+def test_concatenation_invariance():
+    # [W1; W2] gives [y1 | y2] bit for bit: tables belong to 16-row groups
+    L, K = 2048, 256
+    _say("concat", L, K)
+    x, idx1, tab1 = _problem(L, K, 4096, 10)
+    _, idx2, tab2 = _problem(1, K, 2048, 11)
+    y1 = gpu_linear(x, idx1, tab1, F16, 1.0)
+    y2 = gpu_linear(x, idx2, tab2, F16, 1.0)
+    y12 = gpu_linear(x, np.concatenate([idx1, idx2]), np.concatenate([tab1, tab2]), F16, 1.0)
+    assert np.array_equal(y12, np.concatenate([y1, y2], axis=1))
+
+
+# ---------------------------------------------------------------------------
+# the checks see the layout: the device result must FAIL against oracles with
+# a planted mistake (big-endian packing, wrong table group, gate/up swapped,
+# scale not undone)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mutant,epi,s", [(1, F16, 1.0), (2, F16, 1.0), (3, F16, 1.0),
+                                          (4, F16, 16.0), (5, SILU, 1.0)])
+def test_mutation_controls(tmp_path, ora, mutant, epi, s):
+    _say("mutation", mutant)
+    x, idx, tab = _problem(64, 256, 128, 12, sigma=0.5)
+    y = gpu_linear(x, idx, tab, epi, s)
+    assert oracle_check(ora, x, idx, tab, epi, s, y).ok
+    bad = oracle.Oracle(oracle.build(tmp_path / f"m{mutant}.so", mutant=mutant))
+    # the mutant reads bytes packed by the correct oracle
+    assert not oracle_check(bad, x, idx, tab, epi, s, y, packer=ora).ok
