@@ -1,0 +1,308 @@
+"""Benchmark of the LUT-6 dequant-GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of every LUT-6 linear layer of a 32-layer hybrid prefill
+at L = 16,384 tokens (page "Clef-Flash-ANE-LUT6", section "Model
+architecture": 24 Gated DeltaNet layers with qkv|z, out, gate|up and down
+projections, 8 full-attention layers with q|k|v, o, gate|up and down; hidden
+4,096, MLP 12,288), 128 launches of lut6_linear over seeded synthetic weights
+(per-layer seeds) and activations that are resident in HBM before timing
+starts.  The line printed is throughput in TFLOP/s, with
+
+  * roofline: the dominant kernel's algorithmic FLOPs per launch over its
+    average launch time, measured with HIP events on the launch stream,
+    against the FP16 dense MFMA peak (2,516.6 TFLOP/s); its HBM traffic comes
+    from the rocprofv3 counter summary in profiles/ when that summary was
+    taken on the current kernel source, else null;
+  * l128_stream: the L = 128 single projection (4,096 -> 4,096, FP32 out) in
+    algorithmic HBM GB/s, rotating over enough weight sets that the 256 MB
+    last-level cache cannot hold them;
+  * cpu_baseline: the CPU oracle timed on a bounded sample of the same step
+    (sampled token rows of two layers), on this host's cores;
+  * parity_sample: those sampled rows of the GPU result against the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "LUT-6 GEMM TFLOP/s + % FP16 MFMA peak at L>=1024; HBM GB/s at L=128"
+PEAK_FP16_TFLOPS = 2516.6          # 256 CUs x 2.4 GHz x 4,096 FLOP/clk (dense FP16 MFMA)
+PEAK_HBM_GBS = 8000.0              # HBM3E
+STEP_WORKLOAD = "prefill_sweep_l16384"
+STREAM_WORKLOAD = "o_proj_l128"
+TRAFFIC_FILE = ROOT / "profiles" / "gemm_hbm_traffic.json"
+KERNEL_SOURCES = [ROOT / "lut_weight_quantized_amd" / "csrc" / "lut6_linear.hip"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(p.read_bytes())
+    return h.hexdigest()
+
+
+def kernel_class(g) -> str:
+    """Which kernel instance lut6_linear launches for this GEMM."""
+    regime = "stream" if g.L <= 192 else "tiled"
+    epi = {0: "f32", 1: "f16", 2: "silu"}[g.epilogue]
+    return f"{regime}_{epi}"
+
+
+def cpu_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    n = len(os.sched_getaffinity(0))
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="token rows per GEMM in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-iters", type=int, default=200)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run it with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import lut_weight_quantized_amd as lq
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    lq.load_library()
+    stream = torch.cuda.current_stream()
+
+    w = si.WORKLOADS[STEP_WORKLOAD]
+    L = w.layers[0][0].L
+
+    # ---------------- inputs, resident in HBM ----------------
+    t0 = time.time()
+    acts, acts_host = {}, {}
+    for _, _, g in w.gemms():
+        key = (g.K, g.x_tensor)
+        if key not in acts:
+            acts_host[key] = si.gemm_activation(w.cfg, g)
+            acts[key] = torch.from_numpy(acts_host[key]).to("cuda")
+    weights = []
+    for li, layer in enumerate(w.layers):
+        lw = []
+        for pi, g in enumerate(layer):
+            idx, tab = si.gemm_weight(w.cfg, li, pi, g)
+            lw.append((torch.from_numpy(lq.pack(idx)).to("cuda"), torch.from_numpy(tab).to("cuda")))
+            del idx
+        weights.append(lw)
+        if li % 8 == 7:
+            log(f"weights for layers 0..{li} resident ({time.time() - t0:.1f} s)")
+    outs = {}
+    for _, pi, g in w.gemms():
+        key = (g.name, g.n_out)
+        if key not in outs:
+            outs[key] = torch.empty((g.L, g.n_out), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    plan = [(li, pi, g, acts[(g.K, g.x_tensor)], weights[li][pi], outs[(g.name, g.n_out)])
+            for li, pi, g in w.gemms()]
+
+    def step(events=None):
+        for li, pi, g, x, (p, t), y in plan:
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            lq.linear(x, p, t, epilogue=g.epilogue, in_scale=g.in_scale, out=y, stream=stream)
+            if events is not None:
+                e1.record(stream)
+                events.append((g, e0, e1))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms_per_step = t_total * 1e3 / args.steps
+
+    # per kernel class: launches, total time, algorithmic FLOPs
+    per = {}
+    for g, e0, e1 in events:
+        c = per.setdefault(kernel_class(g), {"n": 0, "ms": 0.0, "flops": 0, "bytes": 0})
+        c["n"] += 1
+        c["ms"] += e0.elapsed_time(e1)
+        c["flops"] += g.flops
+        c["bytes"] += g.bytes
+    dom_name = max(per, key=lambda k: per[k]["ms"])
+    dom = per[dom_name]
+    avg_ms = dom["ms"] / dom["n"]
+    flops_per_launch = dom["flops"] / dom["n"]
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    kernels_ms = sum(c["ms"] for c in per.values()) / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms, kernels {kernels_ms:.3f} ms, {value:.1f} TFLOP/s; "
+        + ", ".join(f"{k}: {v['n'] // args.steps}/step {v['ms'] / v['n'] * 1e3:.1f} us avg "
+                    f"{v['flops'] / v['n'] / (v['ms'] / v['n'] * 1e-3) / 1e12:.1f} TFLOP/s"
+                    for k, v in sorted(per.items())))
+
+    traffic = None
+    if TRAFFIC_FILE.exists():
+        rec = json.loads(TRAFFIC_FILE.read_text())
+        if rec.get("kernel_source_sha256") == kernel_source_sha() and rec.get("kernel_class") == dom_name:
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                "traffic": traffic, "kernel": dom_name, "avg_launch_us": round(avg_ms * 1e3, 2),
+                "flops_per_launch": flops_per_launch, "launches_per_step": dom["n"] // args.steps}
+
+    # ---------------- parity sample + CPU baseline (oracle) ----------------
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle import tolerance as tol
+        ora = oracle.load()
+        threads = cpu_threads()
+        layers = (0, 3)               # one Gated DeltaNet and one full-attention layer
+        cpu_s, cpu_flops, worst, n_checked, all_ok = 0.0, 0, 0.0, 0, True
+        for li in layers:
+            for pi, g in enumerate(w.layers[li]):
+                x = acts_host[(g.K, g.x_tensor)]
+                idx, tab = si.gemm_weight(w.cfg, li, pi, g)
+                rows = si.sample_rows(g.L, args.cpu_rows, (w.cfg, li, pi))
+                y = torch.empty((g.L, g.n_out), dtype=torch.float16, device="cuda")
+                p, t = weights[li][pi]
+                lq.linear(acts[(g.K, g.x_tensor)], p, t, epilogue=g.epilogue,
+                          in_scale=g.in_scale, out=y, stream=stream)
+                torch.cuda.synchronize()
+                yd = y[torch.from_numpy(rows).to("cuda")].cpu().numpy().view(np.uint16)
+                packed = ora.pack(idx)
+                tc = time.perf_counter()
+                ye, _ = ora.linear(x, packed, tab, epilogue=g.epilogue, in_scale=g.in_scale,
+                                   rows=rows, threads=threads)
+                cpu_s += time.perf_counter() - tc
+                cpu_flops += 2 * len(rows) * g.K * g.N
+                S = tol.row_scale(x, tab, g.K, rows)
+                if g.epilogue == si.EPI_SILU_MUL_F16:
+                    a, _ = ora.linear(x, packed, tab, epilogue=si.EPI_F32, in_scale=g.in_scale,
+                                      rows=rows, threads=threads)
+                    rep = tol.check(yd, ye, S, fp16=True,
+                                    S_elem=tol.silu_scale(a[:, :g.N // 2], a[:, g.N // 2:], S))
+                else:
+                    rep = tol.check(yd, ye, S, fp16=True)
+                all_ok &= rep.ok
+                worst = max(worst, rep.max_err_over_bound)
+                n_checked += rep.n
+                log(f"layer {li} {g.name}: {rep}")
+                del idx
+        cpu_value = cpu_flops / cpu_s / 1e12
+        cpu = {"value": round(cpu_value, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": (f"{args.cpu_rows} token rows of each of the 4 GEMMs of layers 0 and 3 "
+                          f"({cpu_flops / 1e9:.1f} GFLOP in {cpu_s:.1f} s, FP64 oracle, "
+                          f"{cpu_model()})")}
+        parity = {"ok": bool(all_ok), "outputs_checked": n_checked,
+                  "max_err_over_bound": round(worst, 4)}
+
+    # ---------------- L = 128 weight-streaming projection ----------------
+    sw = si.WORKLOADS[STREAM_WORKLOAD]
+    sg = sw.layers[0][0]
+    sets = 40      # 40 x 15.8 MB working sets > 256 MB last-level cache
+    x128 = torch.from_numpy(si.gemm_activation(sw.cfg, sg)).to("cuda")
+    sets_w = []
+    for i in range(sets):
+        idx, tab = si.gemm_weight(sw.cfg, i, 0, sg)
+        sets_w.append((torch.from_numpy(lq.pack(idx)).to("cuda"), torch.from_numpy(tab).to("cuda"),
+                       x128.clone(), torch.empty((sg.L, sg.N), dtype=torch.float32, device="cuda")))
+    for i in range(2 * sets):
+        p, t, x, y = sets_w[i % sets]
+        lq.linear(x, p, t, epilogue=sg.epilogue, out=y, stream=stream)
+    torch.cuda.synchronize()
+    ev = []
+    for i in range(args.stream_iters):
+        p, t, x, y = sets_w[i % sets]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lq.linear(x, p, t, epilogue=sg.epilogue, out=y, stream=stream)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    us_med = us[len(us) // 2]
+    gbs = sg.bytes / (us_med * 1e-6) / 1e9
+    stream_rec = {"workload": STREAM_WORKLOAD, "us_per_launch_median": round(us_med, 2),
+                  "gb_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                  "tflop_s": round(sg.flops / (us_med * 1e-6) / 1e12, 1),
+                  "algorithmic_bytes": sg.bytes, "weight_sets_rotated": sets,
+                  "note": "event pair spans the GEMM and its split-K reduction"}
+    log(f"L=128 stream: {us_med:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": STEP_WORKLOAD, "L": L, "layers": len(w.layers),
+                   "launches_per_step": len(plan), "flops_per_step": w.flops,
+                   "algorithmic_bytes_per_step": w.bytes,
+                   "frac_fp16_peak": round(value / PEAK_FP16_TFLOPS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "l128_stream": stream_rec,
+        "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

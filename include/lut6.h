@@ -98,8 +98,9 @@ int lut6_unpack(const uint8_t* packed, uint8_t* idx, int64_t N, int64_t K);
  * Device pointers x (FP16 [L, K]), packed ([N, 3K/4]), tables (FP16
  * [N/16, 64]), y (see lut6_epilogue); all 16-byte aligned (LUT6_E_ALIGN).
  * Rules (LUT6_E_SHAPE): L >= 0, K > 0, N > 0, K % 64 == 0, N % 16 == 0, and
- * N % 32 == 0 for LUT6_EPI_SILU_MUL_F16; L, K and N at most 2^31 - 1 and
- * every buffer below 2^31 elements per row-major plane.  L == 0 is a no-op.
+ * N % 32 == 0 for LUT6_EPI_SILU_MUL_F16; L, K, N at most 2^31 - 1, and
+ * x (2LK bytes) and packed (3NK/4 bytes) each smaller than 2^31 bytes.
+ * L == 0 is a no-op.
  * in_scale must be exactly 1, 2, 4, 8 or 16 (LUT6_E_SCALE), so the scaling
  * is exact.  y must not overlap x, packed or tables (LUT6_E_ALIAS).
  * Enqueues the work on `stream` (0 = null stream) and returns; results are

@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include <map>
+#include <type_traits>
 #include <mutex>
 #include <utility>
 
@@ -331,6 +332,321 @@ lut6_gemm_kernel(GemmArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: 256 channels x 256 tokens per workgroup, four waves.
+//   Wave w owns channels [64w, 64w + 64) of the tile as two 32-row MFMA "A"
+//   fragments and all 256 tokens as eight 32-token "B" fragments, contracted
+//   with v_mfma_f32_32x32x16_f16 (on gfx950 the FP16 shape that runs at the
+//   full dense rate; 16x16x32 runs at half of it).  2 x 8 accumulators of 16
+//   floats = 256 accumulation registers per lane.
+//   Over a 64-wide k tile, lane group h = lane / 32 takes k in [32h, 32h + 32),
+//   eight per MFMA step, so its 32 indices are 24 contiguous packed bytes
+//   (a 192-bit little-endian word, index i at bits 6i .. 6i + 5).
+//   A 32-row fragment spans two tables: lanes whose row is in the upper 16
+//   read the second.
+//   Activations go global -> LDS directly (buffer loads with the LDS bit, no
+//   staging registers) into an XOR-swizzled, double-buffered tile.
+//   Pipeline: while the 16 MFMAs of step s run, the operands of step s + 1 are
+//   read from LDS (each B fragment reloaded in place right after its two
+//   MFMAs; the A fragments gathered in the first half of the step).  One
+//   barrier per 64-k tile, before the last step, lets that step already fetch
+//   the first operands of the next tile.
+// ---------------------------------------------------------------------------
+constexpr int T2 = 256;                    // tile channels and tokens
+constexpr int T2_XBYTES = T2 * BK * 2;     // one activation buffer (32 KB)
+constexpr int T2_GROUP_M = 4;              // token tiles per scheduling group
+constexpr int RAW_BUFFER_WORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
+
+// LDS byte offset of 16-byte chunk c (0..7) of activation row r, XOR-swizzled
+// so that eight consecutive rows read at one chunk hit distinct banks.
+__device__ __forceinline__ int xswz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+// Index i (0..31) of the 192-bit little-endian word p.
+template <int I>
+__device__ __forceinline__ uint32_t idx6(const uint32_t (&p)[6])
+{
+    constexpr int bit = 6 * I, w = bit >> 5, o = bit & 31;
+    if constexpr (o <= 26)
+        return (p[w] >> o) & 63u;
+    else
+        return __builtin_amdgcn_alignbit(p[w + 1], p[w], o) & 63u;
+}
+
+template <int EPI, bool SCALED, bool SPLIT>
+__global__ void __launch_bounds__(256, 1)
+lut6_tile256_kernel(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t xl[2 * T2_XBYTES];
+    __shared__ __attribute__((aligned(16))) _Float16 tl[16 * 64];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, h = lane >> 5;
+    const int K = a.K, N = a.N, L = a.L;
+    const int row_bytes = K / 4 * 3;
+
+    // tile: XCD-contiguous ranges, then groups of T2_GROUP_M token tiles so
+    // the workgroups resident on one XCD share activation and weight tiles
+    const int tiles_n = a.n_tiles / a.tiles_m;
+    const int t = xcd_remap(blockIdx.x, a.n_tiles);
+    const int group = t / (T2_GROUP_M * tiles_n);
+    const int first_m = group * T2_GROUP_M;
+    const int gm = min(a.tiles_m - first_m, T2_GROUP_M);
+    const int within = t - group * T2_GROUP_M * tiles_n;
+    const int tm = first_m + within % gm, tn = within / gm;
+    const int m0 = tm * T2;
+    const int kc_begin = blockIdx.y * a.k_chunks_per_split;
+    const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
+
+    // this lane's weight row in fragments 0 and 1, clamped into range (rows
+    // past the end are computed on a copy of the last row and never stored)
+    int lrow0, lrow1;
+    if constexpr (EPI == 2) {
+        const int j = min(tn * 128 + 32 * wave + r32, N / 2 - 1);
+        lrow0 = j;
+        lrow1 = N / 2 + j;
+    } else {
+        const int n = tn * 256 + 64 * wave + r32;
+        lrow0 = min(n, N - 1);
+        lrow1 = min(n + 32, N - 1);
+    }
+    // tables: slot 4w + 2f + half holds the table of rows [16 half, 16 half + 16)
+    // of fragment f of wave w
+    for (int i = tid; i < 16 * 64; i += 256) {
+        const int sl = i >> 6, w = sl >> 2, f = (sl >> 1) & 1, half = sl & 1;
+        int row;
+        if constexpr (EPI == 2) {
+            const int j = min(tn * 128 + 32 * w + 16 * half, N / 2 - 1);
+            row = f ? N / 2 + j : j;
+        } else {
+            row = min(tn * 256 + 64 * w + 32 * f + 16 * half, N - 1);
+        }
+        tl[i] = ((const _Float16*)a.tables)[(row / 16) * 64 + (i & 63)];
+    }
+    const _Float16* tab0 = tl + (4 * wave + 0 + (r32 >> 4)) * 64;
+    const _Float16* tab1 = tl + (4 * wave + 2 + (r32 >> 4)) * 64;
+
+    // buffer descriptors (32-bit offsets; sizes checked on the host)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.x, (short)0, (int)((size_t)L * K * 2), RAW_BUFFER_WORD3);
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.packed, (short)0, (int)((size_t)N * row_bytes), RAW_BUFFER_WORD3);
+    const int poff0 = lrow0 * row_bytes + 24 * h;
+    const int poff1 = lrow1 * row_bytes + 24 * h;
+
+    // global -> LDS copy of a 256 x 64 activation tile: instruction i of wave
+    // w writes rows 32i + 8w .. +8 (1 KB, 16 bytes per lane, lane-linear)
+    const int xrow = 8 * wave + (lane >> 3);
+    const int xchunk = (lane & 7) ^ (lane >> 3);
+    int xgoff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        xgoff[i] = min(m0 + 32 * i + xrow, L - 1) * (K * 2) + xchunk * 16;
+
+    int xoff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xoff[s] = r32 * 128 + (((4 * h + s) ^ (r32 & 7)) << 4);
+
+    f32x16 acc[2][8];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
+
+    uint32_t PC[2][6], PN[2][6];   // packed words of this tile and the next
+    f16x8 XF[8];             // B fragments of the current step
+    f16x8 WF[2];             // A fragments of the current step
+
+    auto issue_tile = [&](int kc, int bufoff) {
+        // activations of tile kc -> the LDS buffer at byte offset bufoff
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (lds_ptr_t)(xl + bufoff + i * 4096 + wave * 1024), 16,
+                xgoff[i] + kc * (BK * 2), 0, 0, 0);
+    };
+    auto load_packed = [&](int kc, uint32_t (&p)[2][6]) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff0 + kc * 48 + 8 * i, 0, 0);
+            const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff1 + kc * 48 + 8 * i, 0, 0);
+            p[0][2 * i] = v0[0];
+            p[0][2 * i + 1] = v0[1];
+            p[1][2 * i] = v1[0];
+            p[1][2 * i + 1] = v1[1];
+        }
+    };
+    auto read_xf = [&](int bufoff, int s, int j) -> f16x8 {
+        return *(const f16x8*)(xl + bufoff + xoff[s] + j * 4096);
+    };
+
+    // One MFMA step on (XF, WF) while the operands of the next step are
+    // fetched: B fragments of chunk NS from LDS buffer NBUF, A fragments
+    // gathered with the packed words NP.  Written as macros so every index
+    // is a compile-time constant.
+#define LUT6_GATHER(NP, NS, J)                                                         \
+    do {                                                                               \
+        w0n[2 * (J)] = tab0[idx6<8 * (NS) + 2 * (J)>(NP[0])];                          \
+        w0n[2 * (J) + 1] = tab0[idx6<8 * (NS) + 2 * (J) + 1>(NP[0])];                  \
+        w1n[2 * (J)] = tab1[idx6<8 * (NS) + 2 * (J)>(NP[1])];                          \
+        w1n[2 * (J) + 1] = tab1[idx6<8 * (NS) + 2 * (J) + 1>(NP[1])];                  \
+    } while (0)
+#define LUT6_MMA(J)                                                                    \
+    do {                                                                               \
+        f16x8 xj = XF[J];                                                              \
+        if constexpr (SCALED) xj = xj * a.scale;                                       \
+        acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(WF[0], xj, acc[0][J], 0, 0, 0); \
+        acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(WF[1], xj, acc[1][J], 0, 0, 0); \
+    } while (0)
+#define LUT6_STEP(NS, NBUF, NP, FETCH)                                                 \
+    do {                                                                               \
+        f16x8 w0n = WF[0], w1n = WF[1];                                                \
+        LUT6_MMA(0); if (FETCH) { XF[0] = read_xf(NBUF, NS, 0); LUT6_GATHER(NP, NS, 0); } \
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 5, 0);                         \
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);                           \
+        LUT6_MMA(1); if (FETCH) { XF[1] = read_xf(NBUF, NS, 1); LUT6_GATHER(NP, NS, 1); } \
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 5, 0);                         \
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);                           \
+        LUT6_MMA(2); if (FETCH) { XF[2] = read_xf(NBUF, NS, 2); LUT6_GATHER(NP, NS, 2); } \
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 5, 0);                         \
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);                           \
+        LUT6_MMA(3); if (FETCH) { XF[3] = read_xf(NBUF, NS, 3); LUT6_GATHER(NP, NS, 3); } \
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 5, 0);                         \
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);                           \
+        LUT6_MMA(4); if (FETCH) { XF[4] = read_xf(NBUF, NS, 4); }                       \
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);                         \
+        LUT6_MMA(5); if (FETCH) { XF[5] = read_xf(NBUF, NS, 5); }                       \
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);                         \
+        LUT6_MMA(6); if (FETCH) { XF[6] = read_xf(NBUF, NS, 6); }                       \
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);                         \
+        LUT6_MMA(7); if (FETCH) { XF[7] = read_xf(NBUF, NS, 7); }                       \
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);                         \
+        WF[0] = w0n;                                                                   \
+        WF[1] = w1n;                                                                   \
+    } while (0)
+
+    // prologue: tile kc_begin in buffer 0, its step-0 operands in registers
+    const bool any = kc_begin < kc_end;
+    if (any) {
+        issue_tile(kc_begin, 0);
+        load_packed(kc_begin, PC);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (any) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) XF[j] = read_xf(0, 0, j);
+        f16x8 w0n, w1n;
+        LUT6_GATHER(PC, 0, 0);
+        LUT6_GATHER(PC, 0, 1);
+        LUT6_GATHER(PC, 0, 2);
+        LUT6_GATHER(PC, 0, 3);
+        WF[0] = w0n;
+        WF[1] = w1n;
+    }
+
+    // main loop, branch-free: the last tile fetches itself again as its
+    // "next" tile (valid memory, into the buffer nobody reads any more)
+    for (int kc = kc_begin; kc < kc_end; ++kc) {
+        const int nk = min(kc + 1, kc_end - 1);
+        const int cur = ((kc - kc_begin) & 1) * T2_XBYTES;
+        const int nxt = T2_XBYTES - cur;
+        issue_tile(nk, nxt);
+        load_packed(nk, PN);
+        LUT6_STEP(1, cur, PC, true);
+        LUT6_STEP(2, cur, PC, true);
+        LUT6_STEP(3, cur, PC, true);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        LUT6_STEP(0, nxt, PN, true);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int i = 0; i < 6; ++i) PC[f][i] = PN[f][i];
+    }
+#undef LUT6_STEP
+#undef LUT6_MMA
+#undef LUT6_GATHER
+
+    // epilogue: lane holds token r32 of each 32-token fragment and channels
+    // 8q + 4h + (0..3), q = 0..3, of each 32-row fragment
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int tok = m0 + 32 * j + r32;
+        if (tok >= L) continue;
+        if constexpr (SPLIT) {
+            // raw FP32 sums of this K range; gate rows at j, up rows at N/2 + j
+            float* prow = a.partial + ((size_t)blockIdx.y * L + tok) * N;
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    int n;
+                    bool ok;
+                    if constexpr (EPI == 2) {
+                        const int jj = tn * 128 + 32 * wave + 8 * q + 4 * h;
+                        ok = jj < N / 2;
+                        n = f ? N / 2 + jj : jj;
+                    } else {
+                        n = tn * 256 + 64 * wave + 32 * f + 8 * q + 4 * h;
+                        ok = n < N;
+                    }
+                    if (!ok) continue;
+                    const f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2],
+                                     acc[f][j][4 * q + 3]};
+                    *(f32x4*)(prow + n) = v;
+                }
+        } else if constexpr (EPI == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int jj = tn * 128 + 32 * wave + 8 * q + 4 * h;
+                if (jj >= N / 2) continue;
+                f16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float g = acc[0][j][4 * q + e] * a.inv_scale;
+                    const float u = acc[1][j][4 * q + e] * a.inv_scale;
+                    hv[e] = (_Float16)(silu_f32(g) * u);
+                }
+                *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + jj) = hv;
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = tn * 256 + 64 * wave + 32 * f + 8 * q + 4 * h;
+                    if (n >= N) continue;
+                    f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2],
+                               acc[f][j][4 * q + 3]};
+                    v *= a.inv_scale;
+                    if constexpr (EPI == 0) {
+                        *(f32x4*)((float*)a.y + (size_t)tok * N + n) = v;
+                    } else {
+                        f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                        *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n) = hv;
+                    }
+                }
+        }
+    }
+}
+
 // Fixed-order sum of split-K partials, then the epilogue.  One thread per
 // four consecutive output columns.
 template <int EPI>
@@ -442,6 +758,19 @@ struct Plan {
     int splits;
 };
 
+int launch_reduce(const GemmArgs& a, int epi, int splits, hipStream_t stream)
+{
+    const int n_out = epi == 2 ? a.N / 2 : a.N;
+    const int64_t total4 = (int64_t)a.L * n_out / 4;
+    dim3 rgrid((unsigned)((total4 + 255) / 256));
+    switch (epi) {
+    case 0: hipLaunchKernelGGL(lut6_reduce_kernel<0>, rgrid, dim3(256), 0, stream, a.partial, a.y, a.L, a.N, splits, a.inv_scale); break;
+    case 1: hipLaunchKernelGGL(lut6_reduce_kernel<1>, rgrid, dim3(256), 0, stream, a.partial, a.y, a.L, a.N, splits, a.inv_scale); break;
+    default: hipLaunchKernelGGL(lut6_reduce_kernel<2>, rgrid, dim3(256), 0, stream, a.partial, a.y, a.L, a.N, splits, a.inv_scale); break;
+    }
+    return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+}
+
 template <int BN, int BM, int WN_W, int WM_W>
 int launch_tiles(GemmArgs a, int epi, int splits, hipStream_t stream)
 {
@@ -464,14 +793,7 @@ int launch_tiles(GemmArgs a, int epi, int splits, hipStream_t stream)
         default: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 2, true>), grid, block, 0, stream, a); break;
         }
         if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
-        const int n_out = epi == 2 ? a.N / 2 : a.N;
-        const int64_t total4 = (int64_t)a.L * n_out / 4;
-        dim3 rgrid((unsigned)((total4 + 255) / 256));
-        switch (epi) {
-        case 0: hipLaunchKernelGGL(lut6_reduce_kernel<0>, rgrid, dim3(256), 0, stream, a.partial, a.y, a.L, a.N, splits, a.inv_scale); break;
-        case 1: hipLaunchKernelGGL(lut6_reduce_kernel<1>, rgrid, dim3(256), 0, stream, a.partial, a.y, a.L, a.N, splits, a.inv_scale); break;
-        default: hipLaunchKernelGGL(lut6_reduce_kernel<2>, rgrid, dim3(256), 0, stream, a.partial, a.y, a.L, a.N, splits, a.inv_scale); break;
-        }
+        return launch_reduce(a, epi, splits, stream);
     } else {
         switch (epi) {
         case 0: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 0, false>), grid, block, 0, stream, a); break;
@@ -501,8 +823,8 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
     const size_t x_bytes = (size_t)L * K * 2, p_bytes = (size_t)N * (K / 4 * 3),
                  t_bytes = (size_t)(N / 16) * 128;
     const size_t y_bytes = (size_t)L * (epilogue == 0 ? N * 4 : epilogue == 1 ? N * 2 : N);
-    if ((size_t)L * K >= ((size_t)1 << 40) || (size_t)N * K >= ((size_t)1 << 40))
-        return LUT6_E_SHAPE;
+    // activation and packed-weight byte sizes must fit 31-bit buffer offsets
+    if (x_bytes >= ((size_t)1 << 31) || p_bytes >= ((size_t)1 << 31)) return LUT6_E_SHAPE;
     if (L == 0) return LUT6_OK;
     if (overlaps(y, y_bytes, x, x_bytes) || overlaps(y, y_bytes, packed, p_bytes) ||
         overlaps(y, y_bytes, tables, t_bytes))
@@ -531,17 +853,47 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
         splits = splits > chunks / 2 ? (chunks / 2 > 0 ? chunks / 2 : 1) : splits;
         return launch_tiles<128, 128, 4, 1>(a, epilogue, splits, stream);
     }
-    // compute regime: 256-channel x 128-token tiles, split K only when the
-    // tile count cannot fill the 256 CUs
+    // compute regime: 256 x 256 tiles; split K (fixed-order reduction) when
+    // the tiles cannot fill most of the 256 CUs
     const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
     const int bn_cov = epilogue == 2 ? 128 : 256;
-    const int tiles = ((n_half + bn_cov - 1) / bn_cov) * (int)((L + 127) / 128);
+    const int tiles_m = (int)((L + T2 - 1) / T2);
+    const int tiles = ((n_half + bn_cov - 1) / bn_cov) * tiles_m;
     int splits = 1;
-    if (tiles < 256) {
-        splits = (512 + tiles - 1) / tiles;
-        if (splits > chunks / 8) splits = chunks / 8 > 0 ? chunks / 8 : 1;
+    if (tiles < 192) {
+        splits = (256 + tiles - 1) / tiles;
+        const int max_splits = chunks / 8 > 0 ? chunks / 8 : 1;
+        if (splits > max_splits) splits = max_splits;
     }
-    return launch_tiles<256, 128, 4, 1>(a, epilogue, splits, stream);
+    a.tiles_m = tiles_m;
+    a.n_tiles = tiles;
+    a.k_chunks_per_split = (chunks + splits - 1) / splits;
+    splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
+    const bool scaled = in_scale != 1.0f;
+    dim3 grid(tiles, splits), block(256);
+    if (splits > 1) {
+        const int st = workspace_for(stream, (size_t)splits * L * N * sizeof(float), &a.partial);
+        if (st != LUT6_OK) return st;
+        switch (epilogue * 2 + (scaled ? 1 : 0)) {
+        case 0: hipLaunchKernelGGL((lut6_tile256_kernel<0, false, true>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((lut6_tile256_kernel<0, true, true>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((lut6_tile256_kernel<1, false, true>), grid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((lut6_tile256_kernel<1, true, true>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((lut6_tile256_kernel<2, false, true>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((lut6_tile256_kernel<2, true, true>), grid, block, 0, stream, a); break;
+        }
+        if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
+        return launch_reduce(a, epilogue, splits, stream);
+    }
+    switch (epilogue * 2 + (scaled ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((lut6_tile256_kernel<0, false, false>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((lut6_tile256_kernel<0, true, false>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((lut6_tile256_kernel<1, false, false>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((lut6_tile256_kernel<1, true, false>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((lut6_tile256_kernel<2, false, false>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((lut6_tile256_kernel<2, true, false>), grid, block, 0, stream, a); break;
+    }
+    return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
 }
 
 extern "C" int lut6_dequant(const uint8_t* packed, const void* tables, void* w, int64_t N,

@@ -17,7 +17,12 @@ tables of section "LUT-6 text weights", whose trained weights are not here.
 
 Every stream comes from ``numpy.random.default_rng([2026, cfg, layer, proj,
 tensor])`` (PCG64) with tensor 0 = x, 1 = a second activation, 2 = indices,
-3 = tables, 4 = outlier mask, 5 = sampled rows.
+3 = tables, 4 = outlier mask, 5 = sampled rows.  Weights are keyed by
+(cfg, layer, projection); activations are shared by every GEMM of a workload
+that reads the same stream at the same width, keyed by (cfg, 0, K): the
+hidden state x, a stand-in `a` for an attention / recurrence output, and a
+stand-in for the MLP down-projection input (its own seeded stream, so every
+GEMM is checked on inputs that come from the generator alone).
 """
 from __future__ import annotations
 
@@ -35,15 +40,15 @@ def rng(cfg: int, layer: int, proj: int, tensor: int) -> np.random.Generator:
 
 
 def activations(L: int, K: int, sigma: float, key: tuple[int, int, int], tensor: int = T_X) -> np.ndarray:
-    """FP16 [L, K] ~ N(0, sigma), rounded to nearest even by numpy's cast."""
+    """FP16 [L, K] ~ N(0, sigma): float32 normals, scaled, rounded to nearest even."""
     g = rng(*key, tensor)
-    return (g.standard_normal((L, K), dtype=np.float64) * sigma).astype(np.float16)
+    return (g.standard_normal((L, K), dtype=np.float32) * np.float32(sigma)).astype(np.float16)
 
 
 def indices(N: int, K: int, key: tuple[int, int, int]) -> np.ndarray:
-    """uint8 [N, K], uniform on 0..63."""
+    """uint8 [N, K], uniform on 0..63 (the low 6 bits of uniform random bytes)."""
     g = rng(*key, T_IDX)
-    return g.integers(0, 64, size=(N, K), dtype=np.uint8)
+    return (np.frombuffer(g.bytes(N * K), np.uint8) & np.uint8(63)).reshape(N, K)
 
 
 def tables(N: int, key: tuple[int, int, int], sigma: float = 0.02,
@@ -178,10 +183,18 @@ WORKLOADS = {
 }
 
 
+def gemm_activation(cfg: int, g: Gemm) -> np.ndarray:
+    """The activation a GEMM of workload `cfg` reads (shared across layers)."""
+    return activations(g.L, g.K, g.x_sigma, (cfg, 0, g.K), g.x_tensor)
+
+
+def gemm_weight(cfg: int, layer: int, proj: int, g: Gemm):
+    """(idx uint8 [N,K], tables fp16 [N/16,64]) of one GEMM."""
+    key = (cfg, layer, proj)
+    return indices(g.N, g.K, key), tables(g.N, key, outlier_p=g.outlier_p)
+
+
 def gemm_inputs(cfg: int, layer: int, proj: int, g: Gemm):
     """(x fp16 [L,K], idx uint8 [N,K], tables fp16 [N/16,64]) for one GEMM."""
-    key = (cfg, layer, proj)
-    x = activations(g.L, g.K, g.x_sigma, key, g.x_tensor)
-    idx = indices(g.N, g.K, key)
-    tab = tables(g.N, key, outlier_p=g.outlier_p)
-    return x, idx, tab
+    idx, tab = gemm_weight(cfg, layer, proj, g)
+    return gemm_activation(cfg, g), idx, tab

@@ -88,6 +88,7 @@ def _linear(x=X, p=P, t=T, y=Y, L=128, K=4096, N=4096, s=1.0, epi=1):
     (dict(x=None), 1), (dict(p=None), 1), (dict(t=None), 1), (dict(y=None), 1),
     (dict(L=-1), 2), (dict(K=0), 2), (dict(N=0), 2), (dict(K=4000), 2), (dict(K=100), 2),
     (dict(N=4008), 2), (dict(N=48, epi=2), 2), (dict(L=2 ** 31), 2),
+    (dict(L=2 ** 18), 2), (dict(N=2 ** 20), 2),
     (dict(epi=3), 5), (dict(epi=-1), 5),
     (dict(s=3.0), 4), (dict(s=32.0), 4), (dict(s=0.5), 4), (dict(s=-1.0), 4),
     (dict(x=X + 8), 3), (dict(y=Y + 2), 3), (dict(p=P + 4), 3), (dict(t=T + 1), 3),
