@@ -344,46 +344,96 @@ lut6_gemm_kernel(GemmArgs a)
 //   (a 192-bit little-endian word, index i at bits 6i .. 6i + 5).
 //   A 32-row fragment spans two tables: lanes whose row is in the upper 16
 //   read the second.
-//   Activations go global -> LDS directly (buffer loads with the LDS bit, no
-//   staging registers) into an XOR-swizzled, double-buffered tile.
-//   Pipeline: while the 16 MFMAs of step s run, the operands of step s + 1 are
-//   read from LDS (each B fragment reloaded in place right after its two
-//   MFMAs; the A fragments gathered in the first half of the step).  One
-//   barrier per 64-k tile, before the last step, lets that step already fetch
-//   the first operands of the next tile.
+//   Memory pipeline: three LDS stages, each holding one 64-k tile of
+//   activations (256 rows x 128 bytes, XOR-swizzled) and of packed indices
+//   (256 rows x 48 bytes), filled by buffer loads that write LDS directly
+//   (no staging registers), issued right after the barrier of the tile
+//   before, so a whole tile of MFMA work hides their latency.
+//   Compute pipeline: while the 16 MFMAs of step s run, the operands of step
+//   s + 1 are read from LDS (each B fragment reloaded in place right after its
+//   two MFMAs; the A entries gathered in the first half of the step and
+//   packed into fragments in the second half).  The barrier sits before the
+//   last step so that step already fetches the first operands of the next
+//   tile.
 // ---------------------------------------------------------------------------
-constexpr int T2 = 256;                    // tile channels and tokens
-constexpr int T2_XBYTES = T2 * BK * 2;     // one activation buffer (32 KB)
-constexpr int T2_GROUP_M = 4;              // token tiles per scheduling group
+constexpr int T2 = 256;                        // tile channels and tokens
+constexpr int T2_XBYTES = T2 * BK * 2;         // activation tile (32 KB)
+constexpr int T2_PBYTES = T2 * BK / 4 * 3;     // packed-index tile (12 KB)
+constexpr int T2_STAGE = T2_XBYTES + T2_PBYTES;
+constexpr int T2_NSTAGE = 3;
+constexpr int T2_TABLES = 2048;                // 16 tables of 128 bytes
+constexpr int T2_LDS = T2_TABLES + T2_NSTAGE * T2_STAGE;
+constexpr int T2_GROUP_M = 4;                  // token tiles per scheduling group
 constexpr int RAW_BUFFER_WORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
+
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
+// LDS byte offset of 16-byte chunk c (0..7) of activation row r.  Rows are
+// 128 bytes; the chunk is XOR-swizzled with (r >> 1) & 7 so that sixteen
+// consecutive rows read at one chunk cover all 64 four-byte banks once (a
+// 16-byte read serves 16 lanes per cycle).
+__device__ __forceinline__ int xswz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-// LDS byte offset of 16-byte chunk c (0..7) of activation row r, XOR-swizzled
-// so that eight consecutive rows read at one chunk hit distinct banks.
-__device__ __forceinline__ int xswz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// (v & 0x7e) | base in one instruction (LLVM would otherwise split the mask
+// and merge into an and plus an add).
+__device__ __forceinline__ uint32_t and_or_7e(uint32_t v, uint32_t base)
+{
+#if __HIP_DEVICE_COMPILE__
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(0x7eu), "v"(base));
+    return r;
+#else
+    return (v & 0x7eu) | base;   // the host pass only parses device code
+#endif
+}
 
-// Index i (0..31) of the 192-bit little-endian word p.
+// Byte offset of table entry "index I" (I = 0..31 of the 192-bit
+// little-endian word p, index I at bits 6I .. 6I + 5) in a 128-byte-aligned
+// LDS table at byte offset tab: the field is shifted to bits 1..6 (one shift
+// or funnel shift), then masked and merged with the table offset.
 template <int I>
-__device__ __forceinline__ uint32_t idx6(const uint32_t (&p)[6])
+__device__ __forceinline__ uint32_t entry_off(const uint32_t (&p)[6], uint32_t tab)
 {
     constexpr int bit = 6 * I, w = bit >> 5, o = bit & 31;
-    if constexpr (o <= 26)
-        return (p[w] >> o) & 63u;
+    uint32_t v;
+    if constexpr (o == 0 && w == 0)
+        v = p[0] << 1;
+    else if constexpr (o == 0)
+        v = __builtin_amdgcn_alignbit(p[w], p[w - 1], 31);
+    else if constexpr (o <= 26)
+        v = p[w] >> (o - 1);
     else
-        return __builtin_amdgcn_alignbit(p[w + 1], p[w], o) & 63u;
+        v = __builtin_amdgcn_alignbit(p[w + 1], p[w], o - 1);
+    return and_or_7e(v, tab);
+}
+
+// Global weight row of tile row t (0..255) of channel tile tn.  Tile row
+// t = 64w + 32f + r is row r of fragment f of wave w.  Rows past the end are
+// clamped (computed on a copy of the last row and never stored).
+template <int EPI>
+__device__ __forceinline__ int tile_row(int t, int tn, int N)
+{
+    if constexpr (EPI == 2) {
+        // fragment 0 of each wave: gate rows, fragment 1: the matching up rows
+        const int w = t >> 6, f = (t >> 5) & 1, r = t & 31;
+        const int j = min(tn * 128 + 32 * w + r, N / 2 - 1);
+        return f ? N / 2 + j : j;
+    } else {
+        return min(tn * 256 + t, N - 1);
+    }
 }
 
 template <int EPI, bool SCALED, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
 lut6_tile256_kernel(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t xl[2 * T2_XBYTES];
-    __shared__ __attribute__((aligned(16))) _Float16 tl[16 * 64];
+    // one LDS block: 16 tables at offset 0 (gather addresses need no base),
+    // then three pipeline stages
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[T2_LDS];
+    _Float16* const tl = (_Float16*)lds;
+    const uint8_t* const tlb = lds;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -404,54 +454,43 @@ lut6_tile256_kernel(GemmArgs a)
     const int kc_begin = blockIdx.y * a.k_chunks_per_split;
     const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
 
-    // this lane's weight row in fragments 0 and 1, clamped into range (rows
-    // past the end are computed on a copy of the last row and never stored)
-    int lrow0, lrow1;
-    if constexpr (EPI == 2) {
-        const int j = min(tn * 128 + 32 * wave + r32, N / 2 - 1);
-        lrow0 = j;
-        lrow1 = N / 2 + j;
-    } else {
-        const int n = tn * 256 + 64 * wave + r32;
-        lrow0 = min(n, N - 1);
-        lrow1 = min(n + 32, N - 1);
-    }
-    // tables: slot 4w + 2f + half holds the table of rows [16 half, 16 half + 16)
-    // of fragment f of wave w
-    for (int i = tid; i < 16 * 64; i += 256) {
-        const int sl = i >> 6, w = sl >> 2, f = (sl >> 1) & 1, half = sl & 1;
-        int row;
-        if constexpr (EPI == 2) {
-            const int j = min(tn * 128 + 32 * w + 16 * half, N / 2 - 1);
-            row = f ? N / 2 + j : j;
-        } else {
-            row = min(tn * 256 + 64 * w + 32 * f + 16 * half, N - 1);
-        }
-        tl[i] = ((const _Float16*)a.tables)[(row / 16) * 64 + (i & 63)];
-    }
-    const _Float16* tab0 = tl + (4 * wave + 0 + (r32 >> 4)) * 64;
-    const _Float16* tab1 = tl + (4 * wave + 2 + (r32 >> 4)) * 64;
+    // tables: slot s = t / 16 holds the table of tile rows 16s .. 16s + 15
+    for (int i = tid; i < 16 * 64; i += 256)
+        tl[i] = ((const _Float16*)a.tables)[(tile_row<EPI>(16 * (i >> 6), tn, N) / 16) * 64 + (i & 63)];
+    // byte offsets (128-aligned) of this lane's two tables
+    const uint32_t tab0 = (uint32_t)((4 * wave + 0 + (r32 >> 4)) * 128);
+    const uint32_t tab1 = (uint32_t)((4 * wave + 2 + (r32 >> 4)) * 128);
 
-    // buffer descriptors (32-bit offsets; sizes checked on the host)
+    // buffer descriptors (31-bit byte offsets; sizes checked on the host)
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.x, (short)0, (int)((size_t)L * K * 2), RAW_BUFFER_WORD3);
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.packed, (short)0, (int)((size_t)N * row_bytes), RAW_BUFFER_WORD3);
-    const int poff0 = lrow0 * row_bytes + 24 * h;
-    const int poff1 = lrow1 * row_bytes + 24 * h;
 
-    // global -> LDS copy of a 256 x 64 activation tile: instruction i of wave
-    // w writes rows 32i + 8w .. +8 (1 KB, 16 bytes per lane, lane-linear)
+    // DMA assignment.  Each instruction writes 1 KB of LDS, 16 bytes per
+    // lane in lane order.  Activations: instruction i of wave w fills rows
+    // 32i + 8w .. +8 (slot = lane & 7 of row 32i + 8w + lane / 8).  Packed
+    // indices: instruction q of wave w fills bytes [1024u, 1024u + 1024) of
+    // the 256 x 48-byte tile, u = 3w + q (each 16-byte piece in one row).
     const int xrow = 8 * wave + (lane >> 3);
-    const int xchunk = (lane & 7) ^ (lane >> 3);
+    const int xchunk = (lane & 7) ^ ((xrow >> 1) & 7);
     int xgoff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         xgoff[i] = min(m0 + 32 * i + xrow, L - 1) * (K * 2) + xchunk * 16;
+    int pgoff[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const int flat = 1024 * (3 * wave + q) + 16 * lane;
+        pgoff[q] = tile_row<EPI>(flat / 48, tn, N) * row_bytes + flat % 48;
+    }
 
+    // this lane's B-fragment offsets inside a stage, per MFMA step
     int xoff[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xoff[s] = r32 * 128 + (((4 * h + s) ^ (r32 & 7)) << 4);
+    for (int s = 0; s < 4; ++s) xoff[s] = xswz(r32, 4 * h + s);
+    // this lane's packed words inside a stage: tile rows 64w + r32 (+32)
+    const int poff = T2_XBYTES + (64 * wave + r32) * 48 + 24 * h;
 
     f32x16 acc[2][8];
 #pragma unroll
@@ -461,127 +500,140 @@ lut6_tile256_kernel(GemmArgs a)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
 
-    uint32_t PC[2][6], PN[2][6];   // packed words of this tile and the next
-    f16x8 XF[8];             // B fragments of the current step
-    f16x8 WF[2];             // A fragments of the current step
+    uint32_t PC[2][6];       // packed words of the current tile
+    // operands, double-buffered by step parity: a step multiplies one set
+    // while the next step's operands are fetched into the other, so no load
+    // ever targets a register an in-flight MFMA still reads
+    f16x8 XA[8], XB[8];      // B fragments
+    f16x8 WA[2], WB[2];      // A fragments
 
-    auto issue_tile = [&](int kc, int bufoff) {
-        // activations of tile kc -> the LDS buffer at byte offset bufoff
+    auto stage_off = [&](int kc) -> int {
+        return T2_TABLES + ((kc - kc_begin) % T2_NSTAGE) * T2_STAGE;
+    };
+    // buffer -> LDS copies of tile kc into its stage (11 loads per wave)
+    auto issue_tile = [&](int kc) {
+        uint8_t* st = lds + stage_off(kc);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (lds_ptr_t)(xl + bufoff + i * 4096 + wave * 1024), 16,
-                xgoff[i] + kc * (BK * 2), 0, 0, 0);
-    };
-    auto load_packed = [&](int kc, uint32_t (&p)[2][6]) {
+                xr, (lds_ptr_t)(st + i * 4096 + wave * 1024), 16, xgoff[i] + kc * (BK * 2), 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff0 + kc * 48 + 8 * i, 0, 0);
-            const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff1 + kc * 48 + 8 * i, 0, 0);
-            p[0][2 * i] = v0[0];
-            p[0][2 * i + 1] = v0[1];
-            p[1][2 * i] = v1[0];
-            p[1][2 * i + 1] = v1[1];
-        }
+        for (int q = 0; q < 3; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                pr, (lds_ptr_t)(st + T2_XBYTES + 1024 * (3 * wave + q)), 16, pgoff[q] + kc * 48, 0, 0, 0);
     };
-    auto read_xf = [&](int bufoff, int s, int j) -> f16x8 {
-        return *(const f16x8*)(xl + bufoff + xoff[s] + j * 4096);
-    };
-
-    // One MFMA step on (XF, WF) while the operands of the next step are
-    // fetched: B fragments of chunk NS from LDS buffer NBUF, A fragments
-    // gathered with the packed words NP.  Written as macros so every index
-    // is a compile-time constant.
-#define LUT6_GATHER(NP, NS, J)                                                         \
-    do {                                                                               \
-        w0n[2 * (J)] = tab0[idx6<8 * (NS) + 2 * (J)>(NP[0])];                          \
-        w0n[2 * (J) + 1] = tab0[idx6<8 * (NS) + 2 * (J) + 1>(NP[0])];                  \
-        w1n[2 * (J)] = tab1[idx6<8 * (NS) + 2 * (J)>(NP[1])];                          \
-        w1n[2 * (J) + 1] = tab1[idx6<8 * (NS) + 2 * (J) + 1>(NP[1])];                  \
-    } while (0)
-#define LUT6_MMA(J)                                                                    \
-    do {                                                                               \
-        f16x8 xj = XF[J];                                                              \
-        if constexpr (SCALED) xj = xj * a.scale;                                       \
-        acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(WF[0], xj, acc[0][J], 0, 0, 0); \
-        acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(WF[1], xj, acc[1][J], 0, 0, 0); \
-    } while (0)
-#define LUT6_STEP(NS, NBUF, NP, FETCH)                                                 \
-    do {                                                                               \
-        f16x8 w0n = WF[0], w1n = WF[1];                                                \
-        LUT6_MMA(0); if (FETCH) { XF[0] = read_xf(NBUF, NS, 0); LUT6_GATHER(NP, NS, 0); } \
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 5, 0);                         \
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);                           \
-        LUT6_MMA(1); if (FETCH) { XF[1] = read_xf(NBUF, NS, 1); LUT6_GATHER(NP, NS, 1); } \
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 5, 0);                         \
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);                           \
-        LUT6_MMA(2); if (FETCH) { XF[2] = read_xf(NBUF, NS, 2); LUT6_GATHER(NP, NS, 2); } \
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 5, 0);                         \
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);                           \
-        LUT6_MMA(3); if (FETCH) { XF[3] = read_xf(NBUF, NS, 3); LUT6_GATHER(NP, NS, 3); } \
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 5, 0);                         \
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 10, 0);                           \
-        LUT6_MMA(4); if (FETCH) { XF[4] = read_xf(NBUF, NS, 4); }                       \
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);                         \
-        LUT6_MMA(5); if (FETCH) { XF[5] = read_xf(NBUF, NS, 5); }                       \
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);                         \
-        LUT6_MMA(6); if (FETCH) { XF[6] = read_xf(NBUF, NS, 6); }                       \
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);                         \
-        LUT6_MMA(7); if (FETCH) { XF[7] = read_xf(NBUF, NS, 7); }                       \
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);                            \
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);                         \
-        WF[0] = w0n;                                                                   \
-        WF[1] = w1n;                                                                   \
-    } while (0)
-
-    // prologue: tile kc_begin in buffer 0, its step-0 operands in registers
-    const bool any = kc_begin < kc_end;
-    if (any) {
-        issue_tile(kc_begin, 0);
-        load_packed(kc_begin, PC);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (any) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) XF[j] = read_xf(0, 0, j);
-        f16x8 w0n, w1n;
-        LUT6_GATHER(PC, 0, 0);
-        LUT6_GATHER(PC, 0, 1);
-        LUT6_GATHER(PC, 0, 2);
-        LUT6_GATHER(PC, 0, 3);
-        WF[0] = w0n;
-        WF[1] = w1n;
-    }
-
-    // main loop, branch-free: the last tile fetches itself again as its
-    // "next" tile (valid memory, into the buffer nobody reads any more)
-    for (int kc = kc_begin; kc < kc_end; ++kc) {
-        const int nk = min(kc + 1, kc_end - 1);
-        const int cur = ((kc - kc_begin) & 1) * T2_XBYTES;
-        const int nxt = T2_XBYTES - cur;
-        issue_tile(nk, nxt);
-        load_packed(nk, PN);
-        LUT6_STEP(1, cur, PC, true);
-        LUT6_STEP(2, cur, PC, true);
-        LUT6_STEP(3, cur, PC, true);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        LUT6_STEP(0, nxt, PN, true);
+    auto read_packed = [&](int so) {
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
-            for (int i = 0; i < 6; ++i) PC[f][i] = PN[f][i];
+            for (int i = 0; i < 3; ++i) {
+                const u32x2 v = *(const u32x2*)(lds + so + poff + f * 32 * 48 + 8 * i);
+                PC[f][2 * i] = v[0];
+                PC[f][2 * i + 1] = v[1];
+            }
+    };
+    auto read_xf = [&](int so, int s, int j) -> f16x8 {
+        return *(const f16x8*)(lds + so + xoff[s] + j * 4096);
+    };
+
+#define LUT6_GATHER(NS, J)                                                             \
+    do {                                                                               \
+        g[4 * (J) + 0] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2 * (J)>(PC[0], tab0)); \
+        g[4 * (J) + 1] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2 * (J) + 1>(PC[0], tab0)); \
+        g[4 * (J) + 2] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2 * (J)>(PC[1], tab1)); \
+        g[4 * (J) + 3] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2 * (J) + 1>(PC[1], tab1)); \
+    } while (0)
+    // fragment dword J of A fragments 0 and 1 from the gathered entries
+#define LUT6_COMBINE(WN, J)                                                            \
+    do {                                                                               \
+        wn0[J] = g[4 * (J) + 0] | (g[4 * (J) + 1] << 16);                              \
+        wn1[J] = g[4 * (J) + 2] | (g[4 * (J) + 3] << 16);                              \
+    } while (0)
+#define LUT6_MMA(X, W, J)                                                              \
+    do {                                                                               \
+        f16x8 xj = X[J];                                                               \
+        if constexpr (SCALED) xj = xj * a.scale;                                       \
+        acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[0], xj, acc[0][J], 0, 0, 0); \
+        acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[1], xj, acc[1][J], 0, 0, 0); \
+    } while (0)
+    // One MFMA step on (X, W) while the operands of step NS are fetched into
+    // (XN, WN) from the stage at byte offset SO (A entries from PC).  The A
+    // entries are gathered in the first half of the step and packed in the
+    // second half, so no VALU waits on a fresh LDS read.  sched_barrier(0)
+    // keeps each block where it is written: left alone the scheduler sinks
+    // the gathers next to their first use.
+#define LUT6_STEP(NS, SO, X, W, XN, WN)                                                \
+    do {                                                                               \
+        uint32_t g[16];                                                                \
+        uint32_t wn0[4], wn1[4];                                                       \
+        LUT6_MMA(X, W, 0); XN[0] = read_xf(SO, NS, 0); LUT6_GATHER(NS, 0);             \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        LUT6_MMA(X, W, 1); XN[1] = read_xf(SO, NS, 1); LUT6_GATHER(NS, 1);             \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        LUT6_MMA(X, W, 2); XN[2] = read_xf(SO, NS, 2); LUT6_GATHER(NS, 2);             \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        LUT6_MMA(X, W, 3); XN[3] = read_xf(SO, NS, 3); LUT6_GATHER(NS, 3);             \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        LUT6_MMA(X, W, 4); XN[4] = read_xf(SO, NS, 4);                                 \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        LUT6_MMA(X, W, 5); XN[5] = read_xf(SO, NS, 5);                                 \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        LUT6_MMA(X, W, 6); XN[6] = read_xf(SO, NS, 6); LUT6_COMBINE(WN, 0); LUT6_COMBINE(WN, 1); \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        LUT6_MMA(X, W, 7); XN[7] = read_xf(SO, NS, 7); LUT6_COMBINE(WN, 2); LUT6_COMBINE(WN, 3); \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        WN[0] = __builtin_bit_cast(f16x8, u32x4{wn0[0], wn0[1], wn0[2], wn0[3]});        \
+        WN[1] = __builtin_bit_cast(f16x8, u32x4{wn1[0], wn1[1], wn1[2], wn1[3]});        \
+    } while (0)
+
+    // prologue: tile kc_begin complete and its step-0 operands in registers,
+    // tile kc_begin + 1 in flight
+    const int last = kc_end - 1;
+    issue_tile(kc_begin);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue_tile(min(kc_begin + 1, last));
+    {
+        const int so = stage_off(kc_begin);
+        read_packed(so);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) XA[j] = read_xf(so, 0, j);
+        uint32_t g[16];
+        uint32_t wn0[4], wn1[4];
+        LUT6_GATHER(0, 0);
+        LUT6_GATHER(0, 1);
+        LUT6_GATHER(0, 2);
+        LUT6_GATHER(0, 3);
+        LUT6_COMBINE(WA, 0);
+        LUT6_COMBINE(WA, 1);
+        LUT6_COMBINE(WA, 2);
+        LUT6_COMBINE(WA, 3);
+        WA[0] = __builtin_bit_cast(f16x8, u32x4{wn0[0], wn0[1], wn0[2], wn0[3]});
+        WA[1] = __builtin_bit_cast(f16x8, u32x4{wn1[0], wn1[1], wn1[2], wn1[3]});
+    }
+
+    // main loop, branch-free: past the end, tiles are fetched again (valid
+    // memory, into a stage that is no longer read).  Tile kc + 1 was issued
+    // right after the previous barrier, a whole tile of MFMA work ago; the
+    // wait before the barrier covers all outstanding loads (the compiler
+    // cannot tell the stages apart, so nothing newer may be in flight), and
+    // the barrier also ends every read of the stage that tile kc + 2 refills.
+    for (int kc = kc_begin; kc < kc_end; ++kc) {
+        const int so = stage_off(kc);
+        LUT6_STEP(1, so, XA, WA, XB, WB);
+        LUT6_STEP(2, so, XB, WB, XA, WA);
+        LUT6_STEP(3, so, XA, WA, XB, WB);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        issue_tile(min(kc + 2, last));
+        const int sn = stage_off(kc + 1);
+        read_packed(sn);
+        __builtin_amdgcn_sched_barrier(0);
+        LUT6_STEP(0, sn, XB, WB, XA, WA);
     }
 #undef LUT6_STEP
 #undef LUT6_MMA
+#undef LUT6_COMBINE
 #undef LUT6_GATHER
 
     // epilogue: lane holds token r32 of each 32-token fragment and channels
@@ -620,9 +672,9 @@ lut6_tile256_kernel(GemmArgs a)
                 f16x4 hv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float g = acc[0][j][4 * q + e] * a.inv_scale;
-                    const float u = acc[1][j][4 * q + e] * a.inv_scale;
-                    hv[e] = (_Float16)(silu_f32(g) * u);
+                    const float gv = acc[0][j][4 * q + e] * a.inv_scale;
+                    const float uv = acc[1][j][4 * q + e] * a.inv_scale;
+                    hv[e] = (_Float16)(silu_f32(gv) * uv);
                 }
                 *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + jj) = hv;
             }
