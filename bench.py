@@ -87,7 +87,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--cpu-rows", type=int, default=64,
+    ap.add_argument("--cpu-rows", type=int, default=512,
                     help="token rows per GEMM in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-iters", type=int, default=200)
