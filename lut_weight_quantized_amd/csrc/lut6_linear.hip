@@ -699,6 +699,268 @@ lut6_tile256_kernel(GemmArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel for few tokens (L <= 192): 128 channels x 128
+// tokens per workgroup over one K slice.  At these sizes the packed weight is
+// most of the traffic and every weight is used by at most 192 tokens, so the
+// K dimension is split across workgroups (fixed-order reduction afterwards)
+// and, inside a workgroup, across waves:
+//   wave w: channel half c = w & 1 (64 channels = two 32-row A fragments),
+//           k half kh = w >> 1 of the workgroup's slice;
+//   each wave contracts all 128 tokens (four 32-token B fragments) with
+//   v_mfma_f32_32x32x16_f16, 2 x 4 x 16 = 128 accumulation registers.
+// No wave shares operands with another, so the main loop has no barrier:
+// activations go straight from global memory to registers (a lane's four
+// steps of one 64-k chunk are 64 contiguous bytes, two lanes per cache
+// line), packed words likewise, and only the tables live in LDS.  The next
+// chunk is loaded while the current one multiplies; the A entries of the
+// next MFMA step are gathered while the current step multiplies.  At the
+// end the two k halves are added in LDS in a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int S_BN = 128, S_BM = 128;
+constexpr int S_CH = 4;                        // most 64-k chunks per wave
+
+template <int EPI, bool SCALED, bool SPLIT>
+__global__ void __launch_bounds__(256, 1)
+lut6_stream_kernel(GemmArgs a)
+{
+    // 8 tables (1 KB) at offset 0, then the k-half exchange area (64 KB)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[1024 + 2 * 128 * 64 * 4];
+    _Float16* const tl = (_Float16*)lds;
+    const uint8_t* const tlb = lds;
+    float* const xch = (float*)(lds + 1024);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = wave & 1, kh = wave >> 1;
+    const int r32 = lane & 31, h = lane >> 5;
+    const int K = a.K, N = a.N, L = a.L;
+    const int row_bytes = K / 4 * 3;
+
+    // one-dimensional grid: consecutive indices (one XCD after the remap)
+    // are the K slices of one tile, whose partial sums then meet in that
+    // XCD's L2
+    const int splits = gridDim.x / a.n_tiles;
+    const int r = xcd_remap(blockIdx.x, gridDim.x);
+    const int t = r / splits, split = r % splits;
+    const int tm = t % a.tiles_m, tn = t / a.tiles_m;
+    const int m0 = tm * S_BM;
+    const int kc_begin = split * a.k_chunks_per_split;
+    const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
+    const int kc_half = (kc_end - kc_begin + 1) / 2;
+    const int w_begin = kh ? min(kc_begin + kc_half, kc_end) : kc_begin;
+    const int w_end = kh ? kc_end : min(kc_begin + kc_half, kc_end);
+
+    // global weight row of tile row tr = 64c + 32f + r (clamped into range)
+    auto trow = [&](int tr) -> int {
+        if constexpr (EPI == 2) {
+            const int cc = tr >> 6, f = (tr >> 5) & 1, r = tr & 31;
+            const int j = min(tn * 64 + 32 * cc + r, N / 2 - 1);
+            return f ? N / 2 + j : j;
+        } else {
+            return min(tn * S_BN + tr, N - 1);
+        }
+    };
+    const uint32_t tab0 = (uint32_t)((4 * c + 0 + (r32 >> 4)) * 128);
+    const uint32_t tab1 = (uint32_t)((4 * c + 2 + (r32 >> 4)) * 128);
+
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.x, (short)0, (int)((size_t)L * K * 2), RAW_BUFFER_WORD3);
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.packed, (short)0, (int)((size_t)N * row_bytes), RAW_BUFFER_WORD3);
+    const int poff0 = trow(64 * c + r32) * row_bytes + 24 * h;
+    const int poff1 = trow(64 * c + 32 + r32) * row_bytes + 24 * h;
+    int xoff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xoff[j] = min(m0 + 32 * j + r32, L - 1) * (K * 2) + 64 * h;
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
+
+    // tables first (their LDS store waits only for them), then every packed
+    // word of this wave's k range (at most S_CH chunks), so the whole weight
+    // stream is in flight at once, then the first activation chunk.  Every
+    // load is unconditional (past the range it re-reads a valid chunk): a
+    // conditional load would make the compiler's wait counting pessimistic
+    // at the join and serialise the chunks.
+    const int nch = w_end - w_begin;
+    const int kc_last = max(w_end - 1, 0);
+    _Float16 tv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + 256 * u;
+        tv[u] = ((const _Float16*)a.tables)[(trow(16 * (i >> 6)) / 16) * 64 + (i & 63)];
+    }
+    uint32_t PW[S_CH][2][6];
+    f16x8 XC[4][4], XN[4][4];      // [token fragment][step]
+    f16x8 WA[2], WB[2];
+#pragma unroll
+    for (int ch = 0; ch < S_CH; ++ch) {
+        const int kc = min(w_begin + ch, kc_last);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff0 + kc * 48 + 8 * i, 0, 0);
+            const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff1 + kc * 48 + 8 * i, 0, 0);
+            PW[ch][0][2 * i] = v0[0];
+            PW[ch][0][2 * i + 1] = v0[1];
+            PW[ch][1][2 * i] = v1[0];
+            PW[ch][1][2 * i + 1] = v1[1];
+        }
+    }
+    auto load_x = [&](int kc, f16x8 (&xf)[4][4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xf[j][s] = __builtin_bit_cast(
+                    f16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j] + kc * 128 + 16 * s, 0, 0));
+    };
+    load_x(min(w_begin, kc_last), XC);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) tl[tid + 256 * u] = tv[u];
+    __syncthreads();
+
+#define S6_GATHER(NS, P)                                                               \
+    do {                                                                               \
+        g[0] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 0>(P[0], tab0));          \
+        g[1] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 1>(P[0], tab0));          \
+        g[2] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2>(P[0], tab0));          \
+        g[3] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 3>(P[0], tab0));          \
+        g[4] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 4>(P[0], tab0));          \
+        g[5] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 5>(P[0], tab0));          \
+        g[6] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 6>(P[0], tab0));          \
+        g[7] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 7>(P[0], tab0));          \
+        g[8] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 0>(P[1], tab1));          \
+        g[9] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 1>(P[1], tab1));          \
+        g[10] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2>(P[1], tab1));         \
+        g[11] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 3>(P[1], tab1));         \
+        g[12] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 4>(P[1], tab1));         \
+        g[13] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 5>(P[1], tab1));         \
+        g[14] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 6>(P[1], tab1));         \
+        g[15] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 7>(P[1], tab1));         \
+    } while (0)
+#define S6_COMBINE(W)                                                                  \
+    do {                                                                               \
+        W[0] = __builtin_bit_cast(f16x8, u32x4{g[0] | (g[1] << 16), g[2] | (g[3] << 16), \
+                                               g[4] | (g[5] << 16), g[6] | (g[7] << 16)}); \
+        W[1] = __builtin_bit_cast(f16x8, u32x4{g[8] | (g[9] << 16), g[10] | (g[11] << 16), \
+                                               g[12] | (g[13] << 16), g[14] | (g[15] << 16)}); \
+    } while (0)
+    // MFMAs of step S on (W, X[.][S]) while the A entries of step NS are
+    // gathered from words NP into WN
+#define S6_STEP(X, S, W, NS, NP, WN)                                                   \
+    do {                                                                               \
+        uint32_t g[16];                                                                \
+        S6_GATHER(NS, NP);                                                             \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                \
+            f16x8 xj = X[j][S];                                                        \
+            if constexpr (SCALED) xj = xj * a.scale;                                   \
+            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[0], xj, acc[0][j], 0, 0, 0); \
+            acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[1], xj, acc[1][j], 0, 0, 0); \
+        }                                                                              \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        S6_COMBINE(WN);                                                                \
+    } while (0)
+    // one 64-k chunk CH with activations X; the next chunk's are loaded into XL
+#define S6_CHUNK(CH, X, XL)                                                            \
+    do {                                                                               \
+        load_x(min(w_begin + (CH) + 1, kc_last), XL);                                  \
+        if ((CH) < nch) {                                                              \
+            S6_STEP(X, 0, WA, 1, PW[CH], WB);                                          \
+            S6_STEP(X, 1, WB, 2, PW[CH], WA);                                          \
+            S6_STEP(X, 2, WA, 3, PW[CH], WB);                                          \
+            S6_STEP(X, 3, WB, 0, PW[(CH) + 1 < S_CH ? (CH) + 1 : (CH)], WA);           \
+        }                                                                              \
+    } while (0)
+
+    {
+        uint32_t g[16];
+        S6_GATHER(0, PW[0]);
+        S6_COMBINE(WA);
+    }
+    S6_CHUNK(0, XC, XN);
+    S6_CHUNK(1, XN, XC);
+    S6_CHUNK(2, XC, XN);
+    S6_CHUNK(3, XN, XC);
+#undef S6_CHUNK
+#undef S6_STEP
+#undef S6_COMBINE
+#undef S6_GATHER
+
+    // add the two k halves in a fixed order: kh = 1 hands its sums over LDS
+    float* mine = xch + c * (128 * 64);
+    if (kh == 1) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mine[((f * 4 + j) * 16 + e) * 64 + lane] = acc[f][j][e];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[f][j][e] += mine[((f * 4 + j) * 16 + e) * 64 + lane];
+
+    // epilogue: lane holds token r32 of each 32-token fragment and channels
+    // 8q + 4h + (0..3), q = 0..3, of each 32-row fragment
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tok = m0 + 32 * j + r32;
+        if (tok >= L) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int n0, n1;
+            bool ok;
+            if constexpr (EPI == 2) {
+                const int jj = tn * 64 + 32 * c + 8 * q + 4 * h;
+                ok = jj < N / 2;
+                n0 = jj;
+                n1 = N / 2 + jj;
+            } else {
+                n0 = tn * S_BN + 64 * c + 8 * q + 4 * h;
+                n1 = n0 + 32;
+                ok = true;
+            }
+            if (!ok) continue;
+            const f32x4 v0 = {acc[0][j][4 * q], acc[0][j][4 * q + 1], acc[0][j][4 * q + 2], acc[0][j][4 * q + 3]};
+            const f32x4 v1 = {acc[1][j][4 * q], acc[1][j][4 * q + 1], acc[1][j][4 * q + 2], acc[1][j][4 * q + 3]};
+            if constexpr (SPLIT) {
+                float* prow = a.partial + ((size_t)split * L + tok) * N;
+                if (n0 < N) *(f32x4*)(prow + n0) = v0;
+                if (n1 < N) *(f32x4*)(prow + n1) = v1;
+            } else if constexpr (EPI == 2) {
+                f16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hv[e] = (_Float16)(silu_f32(v0[e] * a.inv_scale) * (v1[e] * a.inv_scale));
+                *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + n0) = hv;
+            } else if constexpr (EPI == 0) {
+                if (n0 < N) *(f32x4*)((float*)a.y + (size_t)tok * N + n0) = v0 * a.inv_scale;
+                if (n1 < N) *(f32x4*)((float*)a.y + (size_t)tok * N + n1) = v1 * a.inv_scale;
+            } else {
+                const f32x4 u0 = v0 * a.inv_scale, u1 = v1 * a.inv_scale;
+                if (n0 < N)
+                    *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n0) =
+                        f16x4{(_Float16)u0[0], (_Float16)u0[1], (_Float16)u0[2], (_Float16)u0[3]};
+                if (n1 < N)
+                    *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n1) =
+                        f16x4{(_Float16)u1[0], (_Float16)u1[1], (_Float16)u1[2], (_Float16)u1[3]};
+            }
+        }
+    }
+}
+
 // Fixed-order sum of split-K partials, then the epilogue.  One thread per
 // four consecutive output columns.
 template <int EPI>
@@ -896,14 +1158,46 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
     const int chunks = (int)(K / BK);
     if (L <= 192) {
         // weight-streaming regime: 128-channel x 128-token tiles, K split so
-        // that about 512 workgroups stream the weight at once
+        // that about 256 workgroups (one per CU) stream the weight
         const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
-        const int bn_cov = epilogue == 2 ? 64 : 128;
-        const int tiles = ((n_half + bn_cov - 1) / bn_cov) * (int)((L + 127) / 128);
-        int splits = (512 + tiles - 1) / tiles;
-        splits = splits < 1 ? 1 : splits;
-        splits = splits > chunks / 2 ? (chunks / 2 > 0 ? chunks / 2 : 1) : splits;
-        return launch_tiles<128, 128, 4, 1>(a, epilogue, splits, stream);
+        const int bn_cov = epilogue == 2 ? S_BN / 2 : S_BN;
+        const int tiles_m = (int)((L + S_BM - 1) / S_BM);
+        const int tiles = ((n_half + bn_cov - 1) / bn_cov) * tiles_m;
+        int splits = (256 + tiles - 1) / tiles;
+        const int max_splits = chunks / 2 > 0 ? chunks / 2 : 1;
+        const int min_splits = (chunks + 2 * S_CH - 1) / (2 * S_CH);   // <= S_CH chunks per wave
+        splits = splits < min_splits ? min_splits : splits;
+        splits = splits < 1 ? 1 : (splits > max_splits && max_splits >= min_splits ? max_splits : splits);
+        a.tiles_m = tiles_m;
+        a.n_tiles = tiles;
+        a.k_chunks_per_split = (chunks + splits - 1) / splits;
+        splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
+        if ((a.k_chunks_per_split + 1) / 2 > S_CH) return LUT6_E_SHAPE;   // cannot happen
+        const bool scaled = in_scale != 1.0f;
+        dim3 grid(tiles * splits), block(256);
+        if (splits > 1) {
+            const int st = workspace_for(stream, (size_t)splits * L * N * sizeof(float), &a.partial);
+            if (st != LUT6_OK) return st;
+            switch (epilogue * 2 + (scaled ? 1 : 0)) {
+            case 0: hipLaunchKernelGGL((lut6_stream_kernel<0, false, true>), grid, block, 0, stream, a); break;
+            case 1: hipLaunchKernelGGL((lut6_stream_kernel<0, true, true>), grid, block, 0, stream, a); break;
+            case 2: hipLaunchKernelGGL((lut6_stream_kernel<1, false, true>), grid, block, 0, stream, a); break;
+            case 3: hipLaunchKernelGGL((lut6_stream_kernel<1, true, true>), grid, block, 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((lut6_stream_kernel<2, false, true>), grid, block, 0, stream, a); break;
+            default: hipLaunchKernelGGL((lut6_stream_kernel<2, true, true>), grid, block, 0, stream, a); break;
+            }
+            if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
+            return launch_reduce(a, epilogue, splits, stream);
+        }
+        switch (epilogue * 2 + (scaled ? 1 : 0)) {
+        case 0: hipLaunchKernelGGL((lut6_stream_kernel<0, false, false>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((lut6_stream_kernel<0, true, false>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((lut6_stream_kernel<1, false, false>), grid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((lut6_stream_kernel<1, true, false>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((lut6_stream_kernel<2, false, false>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((lut6_stream_kernel<2, true, false>), grid, block, 0, stream, a); break;
+        }
+        return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
     }
     // compute regime: 256 x 256 tiles; split K (fixed-order reduction) when
     // the tiles cannot fill most of the 256 CUs
