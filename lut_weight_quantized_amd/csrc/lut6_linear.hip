@@ -700,46 +700,93 @@ lut6_tile256_kernel(GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Weight-streaming kernel for few tokens (L <= 192): 128 channels x 128
-// tokens per workgroup over one K slice.  At these sizes the packed weight is
-// most of the traffic and every weight is used by at most 192 tokens, so the
-// K dimension is split across workgroups (fixed-order reduction afterwards)
-// and, inside a workgroup, across waves:
-//   wave w: channel half c = w & 1 (64 channels = two 32-row A fragments),
-//           k half kh = w >> 1 of the workgroup's slice;
-//   each wave contracts all 128 tokens (four 32-token B fragments) with
-//   v_mfma_f32_32x32x16_f16, 2 x 4 x 16 = 128 accumulation registers.
-// No wave shares operands with another, so the main loop has no barrier:
-// activations go straight from global memory to registers (a lane's four
-// steps of one 64-k chunk are 64 contiguous bytes, two lanes per cache
-// line), packed words likewise, and only the tables live in LDS.  The next
-// chunk is loaded while the current one multiplies; the A entries of the
-// next MFMA step are gathered while the current step multiplies.  At the
-// end the two k halves are added in LDS in a fixed order.
+// Weight-streaming kernel for few tokens (L <= 192).  Every weight serves at
+// most 192 tokens here, so one read of the packed weight from HBM is the
+// bound, and K is split across workgroups to spread that read over all CUs.
+// A workgroup owns 64 channels x 128 tokens over one K slice and its four
+// waves split the slice again, four ways: each wave contracts all 64
+// channels (two 32-row A fragments) with all 128 tokens (four 32-token B
+// fragments) on v_mfma_f32_32x32x16_f16, 128 accumulation registers.  No two
+// waves read the same activations or packed bytes, so the main loop has no
+// barrier and no LDS staging: activations and packed words go from global
+// memory straight into registers, and only the four tables sit in LDS.  The
+// next chunk's activations load while the current chunk multiplies; the A
+// entries of the next MFMA step are gathered while the current step
+// multiplies.
+//
+// The four k quarters meet in LDS and are added in wave order; wave w
+// finishes token fragment w (both channel fragments).  With one K slice the
+// result goes straight to y; otherwise each workgroup writes its 32 KB
+// partial in accumulator order (1 KB per store instruction) and a second
+// kernel adds the slices in a fixed order.
 // ---------------------------------------------------------------------------
-constexpr int S_BN = 128, S_BM = 128;
-constexpr int S_CH = 4;                        // most 64-k chunks per wave
+// s_waitcnt immediate that waits for vmcnt = 0 and leaves the other counters
+// alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int VMCNT0 = 0x0F70;
+constexpr int S_BN = 64, S_BM = 128;
+constexpr int S_CH = 4;                  // most 64-k chunks per wave
+constexpr int S_PART = 2048;             // f32x4 per workgroup partial: [fragment 8][group 4][lane 64]
+
+// Output of accumulator group q of token fragment j: v0 from channel
+// fragment 0, v1 from channel fragment 1 (for SiLU: gate and up).  Lane
+// `lane` holds token 32j + lane % 32 and channels 8q + 4 (lane / 32) + 0..3
+// of each fragment.
+template <int EPI>
+__device__ __forceinline__ void stream_out(const GemmArgs& a, int tm, int tn, int j, int q,
+                                           int lane, f32x4 v0, f32x4 v1)
+{
+    const int tok = tm * S_BM + 32 * j + (lane & 31);
+    if (tok >= a.L) return;
+    const int c = 8 * q + 4 * (lane >> 5);
+    if constexpr (EPI == 2) {
+        const int jj = tn * (S_BN / 2) + c;
+        if (jj >= a.N / 2) return;
+        f16x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            hv[e] = (_Float16)(silu_f32(v0[e] * a.inv_scale) * (v1[e] * a.inv_scale));
+        *(f16x4*)((_Float16*)a.y + (size_t)tok * (a.N / 2) + jj) = hv;
+    } else {
+        const int n0 = tn * S_BN + c, n1 = n0 + 32;
+        const f32x4 u0 = v0 * a.inv_scale, u1 = v1 * a.inv_scale;
+        if constexpr (EPI == 0) {
+            if (n0 < a.N) *(f32x4*)((float*)a.y + (size_t)tok * a.N + n0) = u0;
+            if (n1 < a.N) *(f32x4*)((float*)a.y + (size_t)tok * a.N + n1) = u1;
+        } else {
+            if (n0 < a.N)
+                *(f16x4*)((_Float16*)a.y + (size_t)tok * a.N + n0) =
+                    f16x4{(_Float16)u0[0], (_Float16)u0[1], (_Float16)u0[2], (_Float16)u0[3]};
+            if (n1 < a.N)
+                *(f16x4*)((_Float16*)a.y + (size_t)tok * a.N + n1) =
+                    f16x4{(_Float16)u1[0], (_Float16)u1[1], (_Float16)u1[2], (_Float16)u1[3]};
+        }
+    }
+}
 
 template <int EPI, bool SCALED, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
 lut6_stream_kernel(GemmArgs a)
 {
-    // 8 tables (1 KB) at offset 0, then the k-half exchange area (64 KB)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[1024 + 2 * 128 * 64 * 4];
-    _Float16* const tl = (_Float16*)lds;
-    const uint8_t* const tlb = lds;
-    float* const xch = (float*)(lds + 1024);
+    // The four tables live in their own LDS array, apart from the activation
+    // ring that buffer->LDS copies write, so the compiler can see that the
+    // gathers never read what an in-flight copy writes and does not make
+    // them wait for it.  Ring: two 16 KB slots per wave, each one 64-k chunk
+    // of 128 token rows (128 bytes per row, 16-byte pieces swizzled by
+    // xswz).  After the main loop the ring is reused for the k-quarter
+    // exchange, [fragment F = 4f + j][source wave][group q][lane] of f32x4.
+    __shared__ __attribute__((aligned(1024))) _Float16 s_tab[4 * 64];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_ring[4 * 2 * 16384];
+    const uint8_t* const tlb = (const uint8_t*)s_tab;
+    f32x4* const xch = (f32x4*)s_ring;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = wave & 1, kh = wave >> 1;
     const int r32 = lane & 31, h = lane >> 5;
     const int K = a.K, N = a.N, L = a.L;
     const int row_bytes = K / 4 * 3;
 
-    // one-dimensional grid: consecutive indices (one XCD after the remap)
-    // are the K slices of one tile, whose partial sums then meet in that
-    // XCD's L2
+    // one-dimensional grid; after the remap consecutive indices (one XCD)
+    // are the K slices of one tile
     const int splits = gridDim.x / a.n_tiles;
     const int r = xcd_remap(blockIdx.x, gridDim.x);
     const int t = r / splits, split = r % splits;
@@ -747,32 +794,48 @@ lut6_stream_kernel(GemmArgs a)
     const int m0 = tm * S_BM;
     const int kc_begin = split * a.k_chunks_per_split;
     const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
-    const int kc_half = (kc_end - kc_begin + 1) / 2;
-    const int w_begin = kh ? min(kc_begin + kc_half, kc_end) : kc_begin;
-    const int w_end = kh ? kc_end : min(kc_begin + kc_half, kc_end);
+    const int per_wave = (kc_end - kc_begin + 3) / 4;
+    const int w_begin = min(kc_begin + wave * per_wave, kc_end);
+    const int w_end = min(w_begin + per_wave, kc_end);
 
-    // global weight row of tile row tr = 64c + 32f + r (clamped into range)
+    // global weight row of tile row tr = 32f + r (clamped into range; such
+    // rows are computed on a copy of the last row and never stored)
     auto trow = [&](int tr) -> int {
         if constexpr (EPI == 2) {
-            const int cc = tr >> 6, f = (tr >> 5) & 1, r = tr & 31;
-            const int j = min(tn * 64 + 32 * cc + r, N / 2 - 1);
+            const int f = tr >> 5, rr = tr & 31;
+            const int j = min(tn * (S_BN / 2) + rr, N / 2 - 1);
             return f ? N / 2 + j : j;
         } else {
             return min(tn * S_BN + tr, N - 1);
         }
     };
-    const uint32_t tab0 = (uint32_t)((4 * c + 0 + (r32 >> 4)) * 128);
-    const uint32_t tab1 = (uint32_t)((4 * c + 2 + (r32 >> 4)) * 128);
+    // LDS table slot of tile rows 16s .. 16s+15 is s; the two tables a lane
+    // group reads sit 128 bytes apart (all 64 banks, no conflicts)
+    const uint32_t tab0 = (uint32_t)((0 + (r32 >> 4)) * 128);
+    const uint32_t tab1 = (uint32_t)((2 + (r32 >> 4)) * 128);
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.x, (short)0, (int)((size_t)L * K * 2), RAW_BUFFER_WORD3);
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.packed, (short)0, (int)((size_t)N * row_bytes), RAW_BUFFER_WORD3);
-    const int poff0 = trow(64 * c + r32) * row_bytes + 24 * h;
-    const int poff1 = trow(64 * c + 32 + r32) * row_bytes + 24 * h;
-    int xoff[4];
+    const int poff0 = trow(r32) * row_bytes + 24 * h;
+    const int poff1 = trow(32 + r32) * row_bytes + 24 * h;
+
+    // activation copies: instruction i fills ring rows 8i .. 8i+7, lane l
+    // row 8i + l / 8, slot l % 8 (the 16-byte piece (l % 8) ^ swizzle), so
+    // one instruction reads eight 128-byte row segments
+    int xg[16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xoff[j] = min(m0 + 32 * j + r32, L - 1) * (K * 2) + 64 * h;
+    for (int i = 0; i < 16; ++i) {
+        const int row = 8 * i + (lane >> 3);
+        xg[i] = min(m0 + row, L - 1) * (K * 2) + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
+    }
+    // this lane's B-fragment pieces in a slot: token 32j + r32, piece 4h + s
+    // (lane group h takes k 32h .. 32h+31 of the chunk, as for the weights)
+    int xo[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xo[s] = r32 * 128 + (((4 * h + s) ^ ((r32 >> 1) & 7)) << 4);
+    uint8_t* const ring = s_ring + wave * 32768;
 
     f32x16 acc[2][4];
 #pragma unroll
@@ -782,22 +845,16 @@ lut6_stream_kernel(GemmArgs a)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
 
-    // tables first (their LDS store waits only for them), then every packed
+    // table entry first (its LDS store waits only for it), then every packed
     // word of this wave's k range (at most S_CH chunks), so the whole weight
     // stream is in flight at once, then the first activation chunk.  Every
     // load is unconditional (past the range it re-reads a valid chunk): a
-    // conditional load would make the compiler's wait counting pessimistic
-    // at the join and serialise the chunks.
+    // conditional load would make the compiler's wait counting pessimistic.
     const int nch = w_end - w_begin;
     const int kc_last = max(w_end - 1, 0);
-    _Float16 tv[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = tid + 256 * u;
-        tv[u] = ((const _Float16*)a.tables)[(trow(16 * (i >> 6)) / 16) * 64 + (i & 63)];
-    }
+    const _Float16 tv = ((const _Float16*)a.tables)[(trow(16 * (tid >> 6)) / 16) * 64 + (tid & 63)];
     uint32_t PW[S_CH][2][6];
-    f16x8 XC[4][4], XN[4][4];      // [token fragment][step]
+    f16x8 XC[4][4], XN[4][4];      // [token fragment][step], by chunk parity
     f16x8 WA[2], WB[2];
 #pragma unroll
     for (int ch = 0; ch < S_CH; ++ch) {
@@ -812,17 +869,22 @@ lut6_stream_kernel(GemmArgs a)
             PW[ch][1][2 * i + 1] = v1[1];
         }
     }
-    auto load_x = [&](int kc, f16x8 (&xf)[4][4]) {
+    auto copy_x = [&](int kc, int slot) {
+        uint8_t* const st = ring + slot * 16384;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(st + i * 1024), 16,
+                                                     xg[i] + kc * (BK * 2), 0, 0, 0);
+    };
+    auto read_x = [&](int slot, f16x8 (&xf)[4][4]) {
+        const uint8_t* const st = ring + slot * 16384;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                xf[j][s] = __builtin_bit_cast(
-                    f16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j] + kc * 128 + 16 * s, 0, 0));
+            for (int s = 0; s < 4; ++s) xf[j][s] = *(const f16x8*)(st + 4096 * j + xo[s]);
     };
-    load_x(min(w_begin, kc_last), XC);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) tl[tid + 256 * u] = tv[u];
+    copy_x(min(w_begin, kc_last), 0);
+    s_tab[tid] = tv;
     __syncthreads();
 
 #define S6_GATHER(NS, P)                                                               \
@@ -867,98 +929,123 @@ lut6_stream_kernel(GemmArgs a)
         __builtin_amdgcn_sched_barrier(0);                                             \
         S6_COMBINE(WN);                                                                \
     } while (0)
-    // one 64-k chunk CH with activations X; the next chunk's are loaded into XL
-#define S6_CHUNK(CH, X, XL)                                                            \
+    // one 64-k chunk CH: once its copy has landed (the only memory operation
+    // still in flight), its activations come from ring slot CH % 2 into X
+    // (the other register set than the previous chunk's, which in-flight
+    // MFMAs may still read); then the next chunk's copy goes to the other
+    // slot, after these reads, so they do not wait for it
+#define S6_CHUNK(CH, X, NC)                                                            \
     do {                                                                               \
-        load_x(min(w_begin + (CH) + 1, kc_last), XL);                                  \
-        if ((CH) < nch) {                                                              \
-            S6_STEP(X, 0, WA, 1, PW[CH], WB);                                          \
-            S6_STEP(X, 1, WB, 2, PW[CH], WA);                                          \
-            S6_STEP(X, 2, WA, 3, PW[CH], WB);                                          \
-            S6_STEP(X, 3, WB, 0, PW[(CH) + 1 < S_CH ? (CH) + 1 : (CH)], WA);           \
-        }                                                                              \
+        __builtin_amdgcn_s_waitcnt(VMCNT0);                                            \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        read_x((CH) & 1, X);                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+        if constexpr ((CH) + 1 < (NC)) copy_x(w_begin + (CH) + 1, ((CH) + 1) & 1);     \
+        S6_STEP(X, 0, WA, 1, PW[CH], WB);                                              \
+        S6_STEP(X, 1, WB, 2, PW[CH], WA);                                              \
+        S6_STEP(X, 2, WA, 3, PW[CH], WB);                                              \
+        S6_STEP(X, 3, WB, 0, PW[(CH) + 1 < S_CH ? (CH) + 1 : (CH)], WA);               \
     } while (0)
 
-    {
-        uint32_t g[16];
-        S6_GATHER(0, PW[0]);
-        S6_COMBINE(WA);
+    // straight-line code for each chunk count: a branch around one chunk
+    // would make the compiler copy every accumulator at the join
+    auto run = [&](auto nc) __attribute__((always_inline)) {
+        constexpr int NC = decltype(nc)::value;
+        {
+            uint32_t g[16];
+            S6_GATHER(0, PW[0]);
+            S6_COMBINE(WA);
+        }
+        S6_CHUNK(0, XC, NC);
+        if constexpr (NC > 1) S6_CHUNK(1, XN, NC);
+        if constexpr (NC > 2) S6_CHUNK(2, XC, NC);
+        if constexpr (NC > 3) S6_CHUNK(3, XN, NC);
+    };
+    static_assert(S_CH == 4, "one case per chunk count");
+    switch (nch) {
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: break;
     }
-    S6_CHUNK(0, XC, XN);
-    S6_CHUNK(1, XN, XC);
-    S6_CHUNK(2, XC, XN);
-    S6_CHUNK(3, XN, XC);
 #undef S6_CHUNK
 #undef S6_STEP
 #undef S6_COMBINE
 #undef S6_GATHER
 
-    // add the two k halves in a fixed order: kh = 1 hands its sums over LDS
-    float* mine = xch + c * (128 * 64);
-    if (kh == 1) {
+    // every copy has landed and every wave is done with its ring before the
+    // ring becomes the exchange area
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // k quarters: each wave hands the fragments of the three token fragments
+    // it does not finish to their owners, then the owner adds the four
+    // quarters in wave order
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j == wave) continue;
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mine[((f * 4 + j) * 16 + e) * 64 + lane] = acc[f][j][e];
+            for (int q = 0; q < 4; ++q)
+                xch[(((4 * f + j) * 4 + wave) * 4 + q) * 64 + lane] =
+                    f32x4{acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2], acc[f][j][4 * q + 3]};
     }
     __syncthreads();
-    if (kh == 1) return;
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[f][j][e] += mine[((f * 4 + j) * 16 + e) * 64 + lane];
-
-    // epilogue: lane holds token r32 of each 32-token fragment and channels
-    // 8q + 4h + (0..3), q = 0..3, of each 32-row fragment
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tok = m0 + 32 * j + r32;
-        if (tok >= L) continue;
+    auto finish = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            int n0, n1;
-            bool ok;
-            if constexpr (EPI == 2) {
-                const int jj = tn * 64 + 32 * c + 8 * q + 4 * h;
-                ok = jj < N / 2;
-                n0 = jj;
-                n1 = N / 2 + jj;
-            } else {
-                n0 = tn * S_BN + 64 * c + 8 * q + 4 * h;
-                n1 = n0 + 32;
-                ok = true;
-            }
-            if (!ok) continue;
-            const f32x4 v0 = {acc[0][j][4 * q], acc[0][j][4 * q + 1], acc[0][j][4 * q + 2], acc[0][j][4 * q + 3]};
-            const f32x4 v1 = {acc[1][j][4 * q], acc[1][j][4 * q + 1], acc[1][j][4 * q + 2], acc[1][j][4 * q + 3]};
-            if constexpr (SPLIT) {
-                float* prow = a.partial + ((size_t)split * L + tok) * N;
-                if (n0 < N) *(f32x4*)(prow + n0) = v0;
-                if (n1 < N) *(f32x4*)(prow + n1) = v1;
-            } else if constexpr (EPI == 2) {
-                f16x4 hv;
+            f32x4 s0, s1;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    hv[e] = (_Float16)(silu_f32(v0[e] * a.inv_scale) * (v1[e] * a.inv_scale));
-                *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + n0) = hv;
-            } else if constexpr (EPI == 0) {
-                if (n0 < N) *(f32x4*)((float*)a.y + (size_t)tok * N + n0) = v0 * a.inv_scale;
-                if (n1 < N) *(f32x4*)((float*)a.y + (size_t)tok * N + n1) = v1 * a.inv_scale;
+            for (int src = 0; src < 4; ++src) {
+                f32x4 v0, v1;
+                if (src == j) {
+                    v0 = f32x4{acc[0][j][4 * q], acc[0][j][4 * q + 1], acc[0][j][4 * q + 2], acc[0][j][4 * q + 3]};
+                    v1 = f32x4{acc[1][j][4 * q], acc[1][j][4 * q + 1], acc[1][j][4 * q + 2], acc[1][j][4 * q + 3]};
+                } else {
+                    v0 = xch[(((0 + j) * 4 + src) * 4 + q) * 64 + lane];
+                    v1 = xch[(((4 + j) * 4 + src) * 4 + q) * 64 + lane];
+                }
+                s0 = src == 0 ? v0 : s0 + v0;
+                s1 = src == 0 ? v1 : s1 + v1;
+            }
+            if constexpr (SPLIT) {
+                f32x4* part = (f32x4*)a.partial + (size_t)(t * splits + split) * S_PART;
+                part[((0 + j) * 4 + q) * 64 + lane] = s0;
+                part[((4 + j) * 4 + q) * 64 + lane] = s1;
             } else {
-                const f32x4 u0 = v0 * a.inv_scale, u1 = v1 * a.inv_scale;
-                if (n0 < N)
-                    *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n0) =
-                        f16x4{(_Float16)u0[0], (_Float16)u0[1], (_Float16)u0[2], (_Float16)u0[3]};
-                if (n1 < N)
-                    *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n1) =
-                        f16x4{(_Float16)u1[0], (_Float16)u1[1], (_Float16)u1[2], (_Float16)u1[3]};
+                stream_out<EPI>(a, tm, tn, j, q, lane, s0, s1);
             }
         }
+    };
+    switch (wave) {
+    case 0: finish(std::integral_constant<int, 0>{}); break;
+    case 1: finish(std::integral_constant<int, 1>{}); break;
+    case 2: finish(std::integral_constant<int, 2>{}); break;
+    default: finish(std::integral_constant<int, 3>{}); break;
     }
+}
+
+// Fixed-order sum of the streaming kernel's K-slice partials (accumulator
+// order), then the epilogue.  One thread per lane of one accumulator group:
+// (tile, token fragment j, group q, lane).
+template <int EPI>
+__global__ void __launch_bounds__(256)
+lut6_stream_reduce_kernel(GemmArgs a, int splits)
+{
+    const int g = blockIdx.x * 256 + threadIdx.x;
+    if (g >= a.n_tiles * 1024) return;
+    const int lane = g & 63, q = (g >> 6) & 3, j = (g >> 8) & 3, t = g >> 10;
+    const f32x4* p0 = (const f32x4*)a.partial + (size_t)t * splits * S_PART + (j * 4 + q) * 64 + lane;
+    const f32x4* p1 = p0 + 4 * 4 * 64;     // channel fragment 1
+    f32x4 s0 = p0[0], s1 = p1[0];
+    for (int s = 1; s < splits; ++s) {
+        s0 += p0[(size_t)s * S_PART];
+        s1 += p1[(size_t)s * S_PART];
+    }
+    stream_out<EPI>(a, t % a.tiles_m, t / a.tiles_m, j, q, lane, s0, s1);
 }
 
 // Fixed-order sum of split-K partials, then the epilogue.  One thread per
@@ -1157,26 +1244,27 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
 
     const int chunks = (int)(K / BK);
     if (L <= 192) {
-        // weight-streaming regime: 128-channel x 128-token tiles, K split so
-        // that about 256 workgroups (one per CU) stream the weight
+        // weight-streaming regime: 64-channel x 128-token tiles, K split so
+        // that about 256 workgroups (one per CU) stream the weight, each wave
+        // holding at most S_CH chunks
         const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
         const int bn_cov = epilogue == 2 ? S_BN / 2 : S_BN;
         const int tiles_m = (int)((L + S_BM - 1) / S_BM);
         const int tiles = ((n_half + bn_cov - 1) / bn_cov) * tiles_m;
+        const int min_splits = (chunks + 4 * S_CH - 1) / (4 * S_CH);
+        const int max_splits = chunks / 4 > min_splits ? chunks / 4 : min_splits;
         int splits = (256 + tiles - 1) / tiles;
-        const int max_splits = chunks / 2 > 0 ? chunks / 2 : 1;
-        const int min_splits = (chunks + 2 * S_CH - 1) / (2 * S_CH);   // <= S_CH chunks per wave
-        splits = splits < min_splits ? min_splits : splits;
-        splits = splits < 1 ? 1 : (splits > max_splits && max_splits >= min_splits ? max_splits : splits);
+        splits = splits < min_splits ? min_splits : splits > max_splits ? max_splits : splits;
         a.tiles_m = tiles_m;
         a.n_tiles = tiles;
         a.k_chunks_per_split = (chunks + splits - 1) / splits;
         splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
-        if ((a.k_chunks_per_split + 1) / 2 > S_CH) return LUT6_E_SHAPE;   // cannot happen
+        if ((a.k_chunks_per_split + 3) / 4 > S_CH) return LUT6_E_SHAPE;   // cannot happen
+        if ((int64_t)tiles * splits > INT32_MAX / 1024) return LUT6_E_SHAPE;
         const bool scaled = in_scale != 1.0f;
-        dim3 grid(tiles * splits), block(256);
+        dim3 grid((unsigned)(tiles * splits)), block(256);
         if (splits > 1) {
-            const int st = workspace_for(stream, (size_t)splits * L * N * sizeof(float), &a.partial);
+            const int st = workspace_for(stream, (size_t)tiles * splits * S_PART * 16, &a.partial);
             if (st != LUT6_OK) return st;
             switch (epilogue * 2 + (scaled ? 1 : 0)) {
             case 0: hipLaunchKernelGGL((lut6_stream_kernel<0, false, true>), grid, block, 0, stream, a); break;
@@ -1187,7 +1275,13 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
             default: hipLaunchKernelGGL((lut6_stream_kernel<2, true, true>), grid, block, 0, stream, a); break;
             }
             if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
-            return launch_reduce(a, epilogue, splits, stream);
+            dim3 rgrid((unsigned)(tiles * 4));
+            switch (epilogue) {
+            case 0: hipLaunchKernelGGL(lut6_stream_reduce_kernel<0>, rgrid, block, 0, stream, a, splits); break;
+            case 1: hipLaunchKernelGGL(lut6_stream_reduce_kernel<1>, rgrid, block, 0, stream, a, splits); break;
+            default: hipLaunchKernelGGL(lut6_stream_reduce_kernel<2>, rgrid, block, 0, stream, a, splits); break;
+            }
+            return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
         }
         switch (epilogue * 2 + (scaled ? 1 : 0)) {
         case 0: hipLaunchKernelGGL((lut6_stream_kernel<0, false, false>), grid, block, 0, stream, a); break;

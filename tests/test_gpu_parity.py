@@ -116,7 +116,8 @@ def test_identity_readout(ora, K, s):
 SHAPES = [(1, 64, 32), (3, 128, 32), (17, 192, 64), (64, 64, 96), (100, 256, 288),
           (128, 576, 64), (129, 128, 128), (193, 320, 160), (256, 128, 544),
           (300, 192, 288), (513, 256, 320), (777, 128, 96), (300, 1024, 96),
-          (513, 2048, 160), (260, 4096, 544)]
+          (513, 2048, 160), (260, 4096, 544), (192, 12288, 96), (160, 3072, 1056),
+          (128, 1024, 2080)]
 
 
 @pytest.mark.parametrize("L,K,N", SHAPES)
