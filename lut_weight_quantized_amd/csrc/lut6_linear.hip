@@ -336,36 +336,37 @@ lut6_gemm_kernel(GemmArgs a)
 // Large-tile kernel: 256 channels x 256 tokens per workgroup, four waves.
 //   Wave w owns channels [64w, 64w + 64) of the tile as two 32-row MFMA "A"
 //   fragments and all 256 tokens as eight 32-token "B" fragments, contracted
-//   with v_mfma_f32_32x32x16_f16 (on gfx950 the FP16 shape that runs at the
-//   full dense rate; 16x16x32 runs at half of it).  2 x 8 accumulators of 16
-//   floats = 256 accumulation registers per lane.
+//   with v_mfma_f32_32x32x16_f16 (the FP16 shape with the most work per
+//   operand byte on gfx950).  2 x 8 accumulators of 16 floats = 256
+//   accumulation registers per lane.
 //   Over a 64-wide k tile, lane group h = lane / 32 takes k in [32h, 32h + 32),
 //   eight per MFMA step, so its 32 indices are 24 contiguous packed bytes
-//   (a 192-bit little-endian word, index i at bits 6i .. 6i + 5).
+//   (a 192-bit little-endian word, index i at bits 6i .. 6i + 5), loaded from
+//   global memory straight into registers two tiles ahead.
 //   A 32-row fragment spans two tables: lanes whose row is in the upper 16
 //   read the second.
-//   Memory pipeline: three LDS stages, each holding one 64-k tile of
-//   activations (256 rows x 128 bytes, XOR-swizzled) and of packed indices
-//   (256 rows x 48 bytes), filled by buffer loads that write LDS directly
-//   (no staging registers), issued right after the barrier of the tile
-//   before, so a whole tile of MFMA work hides their latency.
-//   Compute pipeline: while the 16 MFMAs of step s run, the operands of step
-//   s + 1 are read from LDS (each B fragment reloaded in place right after its
-//   two MFMAs; the A entries gathered in the first half of the step and
-//   packed into fragments in the second half).  The barrier sits before the
-//   last step so that step already fetches the first operands of the next
-//   tile.
+//   Memory pipeline: three LDS stages of activations (256 rows x 128 bytes,
+//   XOR-swizzled), filled by buffer loads that write LDS directly (no
+//   staging registers), issued two tiles ahead.
+//   Compute pipeline (one wave per SIMD, so the MFMA unit only stays busy if
+//   nothing the wave issues has to wait): each step of 16 MFMAs also reads
+//   the B fragments of the next step, gathers the A entries of the step after
+//   it, and packs the entries gathered one step earlier into the next step's
+//   A fragments, all spread evenly over the step (two gathers, one B read and
+//   one pack per MFMA pair), so every LDS read has a whole step to land.  The
+//   barrier sits before the last step of a tile, which reads the first B
+//   fragments of the next tile.
 // ---------------------------------------------------------------------------
 constexpr int T2 = 256;                        // tile channels and tokens
 constexpr int T2_XBYTES = T2 * BK * 2;         // activation tile (32 KB)
-constexpr int T2_PBYTES = T2 * BK / 4 * 3;     // packed-index tile (12 KB)
-constexpr int T2_STAGE = T2_XBYTES + T2_PBYTES;
 constexpr int T2_NSTAGE = 3;
 constexpr int T2_TABLES = 2048;                // 16 tables of 128 bytes
-constexpr int T2_LDS = T2_TABLES + T2_NSTAGE * T2_STAGE;
+constexpr int T2_LDS = T2_TABLES + T2_NSTAGE * T2_XBYTES;
 constexpr int T2_GROUP_M = 4;                  // token tiles per scheduling group
 constexpr int RAW_BUFFER_WORD3 = 0x00020000;   // gfx9 raw buffer descriptor word 3
-
+// s_waitcnt immediate that waits for vmcnt = 0 and leaves the other counters
+// alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int VMCNT0 = 0x0F70;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -430,7 +431,7 @@ __global__ void __launch_bounds__(256, 1)
 lut6_tile256_kernel(GemmArgs a)
 {
     // one LDS block: 16 tables at offset 0 (gather addresses need no base),
-    // then three pipeline stages
+    // then three activation stages
     __shared__ __attribute__((aligned(1024))) uint8_t lds[T2_LDS];
     _Float16* const tl = (_Float16*)lds;
     const uint8_t* const tlb = lds;
@@ -467,30 +468,25 @@ lut6_tile256_kernel(GemmArgs a)
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.packed, (short)0, (int)((size_t)N * row_bytes), RAW_BUFFER_WORD3);
 
-    // DMA assignment.  Each instruction writes 1 KB of LDS, 16 bytes per
-    // lane in lane order.  Activations: instruction i of wave w fills rows
-    // 32i + 8w .. +8 (slot = lane & 7 of row 32i + 8w + lane / 8).  Packed
-    // indices: instruction q of wave w fills bytes [1024u, 1024u + 1024) of
-    // the 256 x 48-byte tile, u = 3w + q (each 16-byte piece in one row).
+    // Activation DMA: each instruction writes 1 KB of LDS, 16 bytes per lane
+    // in lane order; instruction i of wave w fills rows 32i + 8w .. +8 (slot
+    // = lane & 7 of row 32i + 8w + lane / 8).
     const int xrow = 8 * wave + (lane >> 3);
     const int xchunk = (lane & 7) ^ ((xrow >> 1) & 7);
     int xgoff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         xgoff[i] = min(m0 + 32 * i + xrow, L - 1) * (K * 2) + xchunk * 16;
-    int pgoff[3];
+    // this lane's packed words: 24 bytes at tile offset 24h of weight rows
+    // 64w + r32 (fragment 0) and 64w + 32 + r32 (fragment 1)
+    int pgoff[2];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        const int flat = 1024 * (3 * wave + q) + 16 * lane;
-        pgoff[q] = tile_row<EPI>(flat / 48, tn, N) * row_bytes + flat % 48;
-    }
+    for (int f = 0; f < 2; ++f) pgoff[f] = tile_row<EPI>(64 * wave + 32 * f + r32, tn, N) * row_bytes + 24 * h;
 
     // this lane's B-fragment offsets inside a stage, per MFMA step
     int xoff[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) xoff[s] = xswz(r32, 4 * h + s);
-    // this lane's packed words inside a stage: tile rows 64w + r32 (+32)
-    const int poff = T2_XBYTES + (64 * wave + r32) * 48 + 24 * h;
 
     f32x16 acc[2][8];
 #pragma unroll
@@ -500,141 +496,150 @@ lut6_tile256_kernel(GemmArgs a)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
 
-    uint32_t PC[2][6];       // packed words of the current tile
-    // operands, double-buffered by step parity: a step multiplies one set
-    // while the next step's operands are fetched into the other, so no load
-    // ever targets a register an in-flight MFMA still reads
-    f16x8 XA[8], XB[8];      // B fragments
-    f16x8 WA[2], WB[2];      // A fragments
+    // packed words of three tiles (tile kc_begin + i in set i % 3), operands
+    // by step parity: step s multiplies X[s & 1], W[s & 1] while X[~s & 1]
+    // and W[~s & 1] are refilled and G[s & 1] gathers for step s + 2
+    uint32_t PC[3][2][6];
+    f16x8 X[2][8];
+    f16x8 W[2][2];
+    uint32_t G[2][16];
 
-    auto stage_off = [&](int kc) -> int {
-        return T2_TABLES + ((kc - kc_begin) % T2_NSTAGE) * T2_STAGE;
-    };
-    // buffer -> LDS copies of tile kc into its stage (11 loads per wave)
-    auto issue_tile = [&](int kc) {
-        uint8_t* st = lds + stage_off(kc);
+    // buffer -> LDS copies of the activations of tile kc into stage st
+    auto issue_x = [&](int st, int kc) {
+        uint8_t* const sp = lds + T2_TABLES + st * T2_XBYTES;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (lds_ptr_t)(st + i * 4096 + wave * 1024), 16, xgoff[i] + kc * (BK * 2), 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                pr, (lds_ptr_t)(st + T2_XBYTES + 1024 * (3 * wave + q)), 16, pgoff[q] + kc * 48, 0, 0, 0);
+                xr, (lds_ptr_t)(sp + i * 4096 + wave * 1024), 16, xgoff[i], kc * (BK * 2), 0, 0);
     };
-    auto read_packed = [&](int so) {
+    // packed words of tile kc into set PS (a constant)
+    auto load_pc = [&](auto ps_c, int kc) {
+        constexpr int PS = decltype(ps_c)::value;
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const u32x2 v = *(const u32x2*)(lds + so + poff + f * 32 * 48 + 8 * i);
-                PC[f][2 * i] = v[0];
-                PC[f][2 * i + 1] = v[1];
-            }
+        for (int f = 0; f < 2; ++f) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(pr, pgoff[f], kc * 48, 0);
+            const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(pr, pgoff[f] + 16, kc * 48, 0);
+            PC[PS][f][0] = v[0];
+            PC[PS][f][1] = v[1];
+            PC[PS][f][2] = v[2];
+            PC[PS][f][3] = v[3];
+            PC[PS][f][4] = u[0];
+            PC[PS][f][5] = u[1];
+        }
     };
     auto read_xf = [&](int so, int s, int j) -> f16x8 {
         return *(const f16x8*)(lds + so + xoff[s] + j * 4096);
     };
 
-#define LUT6_GATHER(NS, J)                                                             \
+    // gather q (0..15) of step NS from packed set PS: fragment q / 8, index
+    // 8 NS + q % 8 of the lane's 32
+#define LUT6_GATHER(GP, PS, NS, Q)                                                     \
+    G[GP][Q] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + (Q) % 8>(PC[PS][(Q) / 8], (Q) / 8 ? tab1 : tab0))
+    // pack c (0..7) of the A fragments of the next step: fragment c / 4,
+    // dword c % 4 from gathers 2c, 2c + 1
+#define LUT6_PACK(GP, C) wn[(C) / 4][(C) % 4] = G[GP][2 * (C)] | (G[GP][2 * (C) + 1] << 16)
+#define LUT6_MMA(P, J)                                                                 \
     do {                                                                               \
-        g[4 * (J) + 0] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2 * (J)>(PC[0], tab0)); \
-        g[4 * (J) + 1] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2 * (J) + 1>(PC[0], tab0)); \
-        g[4 * (J) + 2] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2 * (J)>(PC[1], tab1)); \
-        g[4 * (J) + 3] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2 * (J) + 1>(PC[1], tab1)); \
-    } while (0)
-    // fragment dword J of A fragments 0 and 1 from the gathered entries
-#define LUT6_COMBINE(WN, J)                                                            \
-    do {                                                                               \
-        wn0[J] = g[4 * (J) + 0] | (g[4 * (J) + 1] << 16);                              \
-        wn1[J] = g[4 * (J) + 2] | (g[4 * (J) + 3] << 16);                              \
-    } while (0)
-#define LUT6_MMA(X, W, J)                                                              \
-    do {                                                                               \
-        f16x8 xj = X[J];                                                               \
+        f16x8 xj = X[P][J];                                                            \
         if constexpr (SCALED) xj = xj * a.scale;                                       \
-        acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[0], xj, acc[0][J], 0, 0, 0); \
-        acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[1], xj, acc[1][J], 0, 0, 0); \
+        acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[P][0], xj, acc[0][J], 0, 0, 0); \
+        acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[P][1], xj, acc[1][J], 0, 0, 0); \
     } while (0)
-    // One MFMA step on (X, W) while the operands of step NS are fetched into
-    // (XN, WN) from the stage at byte offset SO (A entries from PC).  The A
-    // entries are gathered in the first half of the step and packed in the
-    // second half, so no VALU waits on a fresh LDS read.  sched_barrier(0)
-    // keeps each block where it is written: left alone the scheduler sinks
-    // the gathers next to their first use.
-#define LUT6_STEP(NS, SO, X, W, XN, WN)                                                \
+    // One step: MFMAs on parity P; B fragments of the next step from stage
+    // byte offset SN (step NB of its tile); gathers for the step after next
+    // (step NG of the tile whose packed words are in set PG); packs of the
+    // entries gathered one step ago.  sched_barrier(0) keeps each MFMA pair
+    // with its share of the other work: left alone the scheduler clusters the
+    // LDS reads.
+#define LUT6_PAIR(P, SN, NB, PG, NG, J)                                                \
     do {                                                                               \
-        uint32_t g[16];                                                                \
-        uint32_t wn0[4], wn1[4];                                                       \
-        LUT6_MMA(X, W, 0); XN[0] = read_xf(SO, NS, 0); LUT6_GATHER(NS, 0);             \
+        LUT6_MMA(P, J);                                                                \
+        X[1 - (P)][J] = read_xf(SN, NB, J);                                            \
+        LUT6_GATHER(P, PG, NG, 2 * (J));                                               \
+        LUT6_GATHER(P, PG, NG, 2 * (J) + 1);                                           \
+        LUT6_PACK(1 - (P), J);                                                         \
         __builtin_amdgcn_sched_barrier(0);                                             \
-        LUT6_MMA(X, W, 1); XN[1] = read_xf(SO, NS, 1); LUT6_GATHER(NS, 1);             \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        LUT6_MMA(X, W, 2); XN[2] = read_xf(SO, NS, 2); LUT6_GATHER(NS, 2);             \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        LUT6_MMA(X, W, 3); XN[3] = read_xf(SO, NS, 3); LUT6_GATHER(NS, 3);             \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        LUT6_MMA(X, W, 4); XN[4] = read_xf(SO, NS, 4);                                 \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        LUT6_MMA(X, W, 5); XN[5] = read_xf(SO, NS, 5);                                 \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        LUT6_MMA(X, W, 6); XN[6] = read_xf(SO, NS, 6); LUT6_COMBINE(WN, 0); LUT6_COMBINE(WN, 1); \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        LUT6_MMA(X, W, 7); XN[7] = read_xf(SO, NS, 7); LUT6_COMBINE(WN, 2); LUT6_COMBINE(WN, 3); \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        WN[0] = __builtin_bit_cast(f16x8, u32x4{wn0[0], wn0[1], wn0[2], wn0[3]});        \
-        WN[1] = __builtin_bit_cast(f16x8, u32x4{wn1[0], wn1[1], wn1[2], wn1[3]});        \
+    } while (0)
+#define LUT6_STEP(P, SN, NB, PG, NG)                                                   \
+    do {                                                                               \
+        uint32_t wn[2][4];                                                             \
+        LUT6_PAIR(P, SN, NB, PG, NG, 0);                                               \
+        LUT6_PAIR(P, SN, NB, PG, NG, 1);                                               \
+        LUT6_PAIR(P, SN, NB, PG, NG, 2);                                               \
+        LUT6_PAIR(P, SN, NB, PG, NG, 3);                                               \
+        LUT6_PAIR(P, SN, NB, PG, NG, 4);                                               \
+        LUT6_PAIR(P, SN, NB, PG, NG, 5);                                               \
+        LUT6_PAIR(P, SN, NB, PG, NG, 6);                                               \
+        LUT6_PAIR(P, SN, NB, PG, NG, 7);                                               \
+        W[1 - (P)][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]}); \
+        W[1 - (P)][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]}); \
     } while (0)
 
-    // prologue: tile kc_begin complete and its step-0 operands in registers,
-    // tile kc_begin + 1 in flight
+    // prologue: activations and packed words of the first two tiles in
+    // flight; the first tile's step-0 operands in registers and its step-1
+    // entries gathered
     const int last = kc_end - 1;
-    issue_tile(kc_begin);
+    issue_x(0, kc_begin);
+    load_pc(std::integral_constant<int, 0>{}, kc_begin);
+    issue_x(1, min(kc_begin + 1, last));
+    load_pc(std::integral_constant<int, 1>{}, min(kc_begin + 1, last));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    issue_tile(min(kc_begin + 1, last));
     {
-        const int so = stage_off(kc_begin);
-        read_packed(so);
+        constexpr int so = T2_TABLES;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) XA[j] = read_xf(so, 0, j);
-        uint32_t g[16];
-        uint32_t wn0[4], wn1[4];
-        LUT6_GATHER(0, 0);
-        LUT6_GATHER(0, 1);
-        LUT6_GATHER(0, 2);
-        LUT6_GATHER(0, 3);
-        LUT6_COMBINE(WA, 0);
-        LUT6_COMBINE(WA, 1);
-        LUT6_COMBINE(WA, 2);
-        LUT6_COMBINE(WA, 3);
-        WA[0] = __builtin_bit_cast(f16x8, u32x4{wn0[0], wn0[1], wn0[2], wn0[3]});
-        WA[1] = __builtin_bit_cast(f16x8, u32x4{wn1[0], wn1[1], wn1[2], wn1[3]});
+        for (int j = 0; j < 8; ++j) X[0][j] = read_xf(so, 0, j);
+        uint32_t wn[2][4];
+#define LUT6_PRO(Q)                                                                    \
+    do {                                                                               \
+        LUT6_GATHER(0, 0, 0, Q);                                                       \
+        LUT6_GATHER(1, 0, 1, Q);                                                       \
+    } while (0)
+        LUT6_PRO(0); LUT6_PRO(1); LUT6_PRO(2); LUT6_PRO(3); LUT6_PRO(4); LUT6_PRO(5); LUT6_PRO(6); LUT6_PRO(7);
+        LUT6_PRO(8); LUT6_PRO(9); LUT6_PRO(10); LUT6_PRO(11); LUT6_PRO(12); LUT6_PRO(13); LUT6_PRO(14); LUT6_PRO(15);
+#undef LUT6_PRO
+        LUT6_PACK(0, 0); LUT6_PACK(0, 1); LUT6_PACK(0, 2); LUT6_PACK(0, 3);
+        LUT6_PACK(0, 4); LUT6_PACK(0, 5); LUT6_PACK(0, 6); LUT6_PACK(0, 7);
+        W[0][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]});
+        W[0][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]});
     }
 
-    // main loop, branch-free: past the end, tiles are fetched again (valid
-    // memory, into a stage that is no longer read).  Tile kc + 1 was issued
-    // right after the previous barrier, a whole tile of MFMA work ago; the
-    // wait before the barrier covers all outstanding loads (the compiler
-    // cannot tell the stages apart, so nothing newer may be in flight), and
-    // the barrier also ends every read of the stage that tile kc + 2 refills.
-    for (int kc = kc_begin; kc < kc_end; ++kc) {
-        const int so = stage_off(kc);
-        LUT6_STEP(1, so, XA, WA, XB, WB);
-        LUT6_STEP(2, so, XB, WB, XA, WA);
-        LUT6_STEP(3, so, XA, WA, XB, WB);
-        __builtin_amdgcn_s_waitcnt(0);
+    // One tile: tile kc in stage ST (a constant; its packed words in set ST).
+    // Past the end, tiles are fetched again (valid memory, into a stage and a
+    // set that are no longer read).  The barrier before step 3: this wave's
+    // copies of tile kc + 1 landed long ago (its packed words, issued after
+    // them, were already waited for by step 2's gathers); after it, all of
+    // tile kc + 1 is in LDS and every read of the stage that tile kc + 2
+    // refills (tile kc - 1's) has completed.
+    auto tile_step = [&](auto st_c, int kc) {
+        constexpr int ST = decltype(st_c)::value;
+        constexpr int S1 = (ST + 1) % T2_NSTAGE, S2 = (ST + 2) % T2_NSTAGE;
+        constexpr int so = T2_TABLES + ST * T2_XBYTES;
+        constexpr int sn = T2_TABLES + S1 * T2_XBYTES;
+        LUT6_STEP(0, so, 1, ST, 2);
+        LUT6_STEP(1, so, 2, ST, 3);
+        LUT6_STEP(0, so, 3, S1, 0);
+        __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
-        issue_tile(min(kc + 2, last));
-        const int sn = stage_off(kc + 1);
-        read_packed(sn);
-        __builtin_amdgcn_sched_barrier(0);
-        LUT6_STEP(0, sn, XB, WB, XA, WA);
+        issue_x(S2, min(kc + 2, last));
+        load_pc(std::integral_constant<int, S2>{}, min(kc + 2, last));
+        LUT6_STEP(1, sn, 0, S1, 1);
+    };
+    int kc = kc_begin;
+    for (; kc + T2_NSTAGE <= kc_end; kc += T2_NSTAGE) {
+        tile_step(std::integral_constant<int, 0>{}, kc);
+        tile_step(std::integral_constant<int, 1>{}, kc + 1);
+        tile_step(std::integral_constant<int, 2>{}, kc + 2);
     }
+    if (kc < kc_end) tile_step(std::integral_constant<int, 0>{}, kc);
+    if (kc + 1 < kc_end) tile_step(std::integral_constant<int, 1>{}, kc + 1);
 #undef LUT6_STEP
+#undef LUT6_PAIR
 #undef LUT6_MMA
-#undef LUT6_COMBINE
+#undef LUT6_PACK
 #undef LUT6_GATHER
+    // the last tiles' refetches are still in flight
+    __builtin_amdgcn_s_waitcnt(0);
 
     // epilogue: lane holds token r32 of each 32-token fragment and channels
     // 8q + 4h + (0..3), q = 0..3, of each 32-row fragment
@@ -720,9 +725,6 @@ lut6_tile256_kernel(GemmArgs a)
 // partial in accumulator order (1 KB per store instruction) and a second
 // kernel adds the slices in a fixed order.
 // ---------------------------------------------------------------------------
-// s_waitcnt immediate that waits for vmcnt = 0 and leaves the other counters
-// alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int VMCNT0 = 0x0F70;
 constexpr int S_BN = 64, S_BM = 128;
 constexpr int S_CH = 4;                  // most 64-k chunks per wave
 constexpr int S_PART = 2048;             // f32x4 per workgroup partial: [fragment 8][group 4][lane 64]
