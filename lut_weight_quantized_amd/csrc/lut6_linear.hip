@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include <map>
+#include <tuple>
 #include <type_traits>
 #include <mutex>
 #include <utility>
@@ -104,6 +105,18 @@ __device__ __forceinline__ void gather16(uint32_t d0, uint32_t d1, uint32_t d2,
     hi = __builtin_bit_cast(f16x8, b);
 }
 
+// Workgroup barrier for the main loops: each wave has already waited for its
+// own LDS copies (vmcnt), and LDS needs no cache maintenance, so the LDS
+// fence that __syncthreads() adds (a wait for every outstanding LDS read,
+// including the prefetches of the next step) is not needed.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float silu_f32(float g)
 {
     // g / (1 + e^-g); e^-g = 2^(-g log2 e) on the hardware exp2
@@ -117,6 +130,7 @@ struct GemmArgs {
     const uint16_t* tables;   // FP16 [N/16, 64]
     void* y;                  // output (epilogue layout) when not split
     float* partial;           // FP32 [splits, L, N] when split
+    const uint16_t* w16;      // FP16 [N, K], the expanded weight (two-pass path)
     int L, K, N;
     int k_chunks_per_split;   // BK-chunks per split
     int tiles_m;              // token tiles
@@ -426,6 +440,145 @@ __device__ __forceinline__ int tile_row(int t, int tn, int N)
     }
 }
 
+// Epilogue of the 256 x 256 tiles: lane (r32, h) of wave w holds token r32
+// of each 32-token fragment j and channels 8q + 4h + (0..3), q = 0..3, of
+// each 32-row fragment f (tile rows 64w + 32f + ...).  SPLIT: raw FP32 sums
+// of K slice ks into the partial buffer.
+template <int EPI, bool SPLIT>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, const f32x16 (&acc)[2][8], int m0, int tn,
+                                              int wave, int r32, int h, int ks)
+{
+    const int L = a.L, N = a.N;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int tok = m0 + 32 * j + r32;
+        if (tok >= L) continue;
+        if constexpr (SPLIT) {
+            // raw FP32 sums of this K range; gate rows at j, up rows at N/2 + j
+            float* prow = a.partial + ((size_t)ks * L + tok) * N;
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    int n;
+                    bool ok;
+                    if constexpr (EPI == 2) {
+                        const int jj = tn * 128 + 32 * wave + 8 * q + 4 * h;
+                        ok = jj < N / 2;
+                        n = f ? N / 2 + jj : jj;
+                    } else {
+                        n = tn * 256 + 64 * wave + 32 * f + 8 * q + 4 * h;
+                        ok = n < N;
+                    }
+                    if (!ok) continue;
+                    const f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2],
+                                     acc[f][j][4 * q + 3]};
+                    *(f32x4*)(prow + n) = v;
+                }
+        } else if constexpr (EPI == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int jj = tn * 128 + 32 * wave + 8 * q + 4 * h;
+                if (jj >= N / 2) continue;
+                f16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float gv = acc[0][j][4 * q + e] * a.inv_scale;
+                    const float uv = acc[1][j][4 * q + e] * a.inv_scale;
+                    hv[e] = (_Float16)(silu_f32(gv) * uv);
+                }
+                *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + jj) = hv;
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = tn * 256 + 64 * wave + 32 * f + 8 * q + 4 * h;
+                    if (n >= N) continue;
+                    f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2],
+                               acc[f][j][4 * q + 3]};
+                    v *= a.inv_scale;
+                    if constexpr (EPI == 0) {
+                        *(f32x4*)((float*)a.y + (size_t)tok * N + n) = v;
+                    } else {
+                        f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                        *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n) = hv;
+                    }
+                }
+        }
+    }
+}
+
+
+// Epilogue through LDS (not split): each wave writes its 64 output channels
+// (32 for silu(gate) * up) of 64 tokens at a time into an LDS block with
+// padded rows (16 spare bytes per row: the 32 lanes of one fragment write
+// 32 different rows without bank conflicts), then reads whole row segments
+// back and stores them, 16 bytes per lane, so every store instruction
+// writes whole cache lines (instead of 16-byte pieces of 32 rows).  The
+// caller has synchronised the workgroup: the pipeline stages are free.
+template <int EPI>
+__device__ __forceinline__ void tile_store_rows(const GemmArgs& a, const f32x16 (&acc)[2][8], int m0, int tn,
+                                               int wave, int lane, uint8_t* lds)
+{
+    constexpr int OUTC = EPI == 2 ? 32 : 64;      // output channels per wave
+    constexpr int ESZ = EPI == 0 ? 4 : 2;         // output element bytes
+    constexpr int ROWB = OUTC * ESZ;              // one token's bytes
+    constexpr int PITCH = ROWB + 16;
+    constexpr int LPR = ROWB / 16;                // lanes per row when reading back
+    constexpr int NREAD = 64 * ROWB / 1024;       // read/store instructions per 64 tokens
+    const int r32 = lane & 31, h = lane >> 5;
+    uint8_t* const wl = lds + wave * (64 * PITCH);
+    const int L = a.L;
+    const int ncols = EPI == 2 ? a.N / 2 : a.N;
+    const int n0 = EPI == 2 ? tn * 128 + 32 * wave : tn * 256 + 64 * wave;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * p + jj;
+            uint8_t* const row = wl + (32 * jj + r32) * PITCH;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (EPI == 2) {
+                    f16x4 hv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float gv = acc[0][j][4 * q + e] * a.inv_scale;
+                        const float uv = acc[1][j][4 * q + e] * a.inv_scale;
+                        hv[e] = (_Float16)(silu_f32(gv) * uv);
+                    }
+                    *(f16x4*)(row + (8 * q + 4 * h) * 2) = hv;
+                } else {
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2], acc[f][j][4 * q + 3]};
+                        v *= a.inv_scale;
+                        const int col = 32 * f + 8 * q + 4 * h;
+                        if constexpr (EPI == 0) {
+                            *(f32x4*)(row + col * 4) = v;
+                        } else {
+                            const f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+                            *(f16x4*)(row + col * 2) = hv;
+                        }
+                    }
+                }
+            }
+        }
+        // the wave reads back what its own lanes wrote (LDS executes a
+        // wave's accesses in order)
+#pragma unroll
+        for (int i = 0; i < NREAD; ++i) {
+            const int idx = i * 64 + lane, r = idx / LPR, seg = idx % LPR;
+            const u32x4 v = *(const u32x4*)(wl + r * PITCH + seg * 16);
+            const int tok = m0 + 64 * p + r, col = n0 + seg * (16 / ESZ);
+            if (tok < L && col < ncols)
+                *(u32x4*)((uint8_t*)a.y + ((size_t)tok * ncols + col) * ESZ) = v;
+        }
+    }
+}
+
 template <int EPI, bool SCALED, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
 lut6_tile256_kernel(GemmArgs a)
@@ -620,7 +773,7 @@ lut6_tile256_kernel(GemmArgs a)
         LUT6_STEP(1, so, 2, ST, 3);
         LUT6_STEP(0, so, 3, S1, 0);
         __builtin_amdgcn_s_waitcnt(VMCNT0);
-        __syncthreads();
+        lds_barrier();
         issue_x(S2, min(kc + 2, last));
         load_pc(std::integral_constant<int, S2>{}, min(kc + 2, last));
         LUT6_STEP(1, sn, 0, S1, 1);
@@ -641,65 +794,267 @@ lut6_tile256_kernel(GemmArgs a)
     // the last tiles' refetches are still in flight
     __builtin_amdgcn_s_waitcnt(0);
 
-    // epilogue: lane holds token r32 of each 32-token fragment and channels
-    // 8q + 4h + (0..3), q = 0..3, of each 32-row fragment
+    if constexpr (SPLIT) {
+        tile_epilogue<EPI, SPLIT>(a, acc, m0, tn, wave, r32, h, blockIdx.y);
+    } else {
+        __syncthreads();
+        tile_store_rows<EPI>(a, acc, m0, tn, wave, lane, lds);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Two-pass path for many tokens.  The fused kernel above gathers every weight
+// once per 256-token tile, so at L = 16,384 each weight is looked up 64
+// times, and each lookup costs an LDS gather and about three VALU
+// instructions per MFMA: with one wave per SIMD (all 512 registers of a lane
+// go to one wave so that it can hold 64 x 256 accumulators) the wave's issue
+// slots, not the matrix unit, set the pace.  For many tokens the weight is
+// therefore expanded once per call (lut6_expand_kernel: the same unpack and
+// table lookup, FP16 [N, K] into a library workspace) and the contraction
+// reads both operands as FP16 tiles.
+//
+// The GEMM keeps the large-tile kernel's shape: 256 channels x 256 tokens per
+// workgroup, wave w owning channels [64w, 64w + 64) as two 32-row A fragments
+// and all 256 tokens as eight B fragments of v_mfma_f32_32x32x16_f16.  A
+// pipeline stage holds one 64-k tile of the activations and one of the
+// expanded weight (each 256 rows x 128 bytes, XOR-swizzled), filled by
+// buffer -> LDS copies; two stages.  Per MFMA pair a wave issues one B read
+// and, twice per step, one A read: about 0.6 LDS reads per MFMA instead of
+// the fused kernel's 1.5 LDS and 2.5 VALU instructions.  The barrier sits
+// before the last step of a tile: every wave then has its operands of that
+// step in registers, so the stage it read is refilled with the tile after
+// next right away.
+// ---------------------------------------------------------------------------
+constexpr int EXPAND_MIN_L = 1024;   // token count from which the two-pass path runs
+// s_waitcnt immediate: vmcnt <= 8, other counters not waited for
+constexpr int VMCNT8 = 0x0F78;
+
+template <int EPI, bool SCALED, bool SPLIT>
+__global__ void __launch_bounds__(256, 1)
+lut6_expanded_gemm_kernel(GemmArgs a)
+{
+    // three activation stages (tables are not needed here)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[T2_NSTAGE * T2_XBYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, h = lane >> 5;
+    const int K = a.K, N = a.N, L = a.L;
+
+    // tile order as in the large-tile kernel
+    const int tiles_n = a.n_tiles / a.tiles_m;
+    const int t = xcd_remap(blockIdx.x, a.n_tiles);
+    const int group = t / (T2_GROUP_M * tiles_n);
+    const int first_m = group * T2_GROUP_M;
+    const int gm = min(a.tiles_m - first_m, T2_GROUP_M);
+    const int within = t - group * T2_GROUP_M * tiles_n;
+    const int tm = first_m + within % gm, tn = within / gm;
+    const int m0 = tm * T2;
+    const int kc_begin = blockIdx.y * a.k_chunks_per_split;
+    const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
+
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.x, (short)0, (int)((size_t)L * K * 2), RAW_BUFFER_WORD3);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.w16, (short)0, (int)((size_t)tiles_n * 8 * (K / BK + 1) * 4096), RAW_BUFFER_WORD3);
+
+    // activation copies: instruction i of wave w fills rows 32i + 8w .. +8 of
+    // the tile (slot lane & 7 of row 32i + 8w + lane / 8)
+    const int xrow = 8 * wave + (lane >> 3);
+    const int xchunk = (lane & 7) ^ ((xrow >> 1) & 7);
+    int xgoff[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int tok = m0 + 32 * j + r32;
-        if (tok >= L) continue;
-        if constexpr (SPLIT) {
-            // raw FP32 sums of this K range; gate rows at j, up rows at N/2 + j
-            float* prow = a.partial + ((size_t)blockIdx.y * L + tok) * N;
+    for (int i = 0; i < 8; ++i) xgoff[i] = min(m0 + 32 * i + xrow, L - 1) * (K * 2) + xchunk * 16;
+    // A fragments straight from the expanded weight, which is stored in
+    // fragment order (lut6_expand_kernel): fragment (tile tn, wave w,
+    // fragment f, chunk kc, step s) is 1 KB, 16 bytes per lane in lane
+    // order, so each load is contiguous
+    const int bstride = (K / BK + 1) * 4096;   // one fragment block (see lut6_expand_kernel)
+    int wgoff[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) wgoff[f] = ((tn * 4 + wave) * 2 + f) * bstride + lane * 16;
+    // B-fragment offsets inside a stage per step (token r32 of each block)
+    int xoff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xoff[s] = xswz(r32, 4 * h + s);
+
+    f32x16 acc[2][8];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
+    // B fragments by step parity; A fragments of three tiles (tile
+    // kc_begin + i in set i % 3), [step][fragment]
+    f16x8 X[2][8];
+    f16x8 WA[3][4][2];
+
+    auto issue_x = [&](int st, int kc, int i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (lds_ptr_t)(lds + st * T2_XBYTES + i * 4096 + wave * 1024), 16, xgoff[i], kc * (BK * 2), 0, 0);
+    };
+    auto load_w = [&](auto ws_c, int kc) {
+        constexpr int WS = decltype(ws_c)::value;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int f = 0; f < 2; ++f)
+                WA[WS][s][f] = __builtin_bit_cast(
+                    f16x8, __builtin_amdgcn_raw_buffer_load_b128(wr, wgoff[f] + 1024 * s, kc * 4096, 0));
+    };
+    auto read_x = [&](int so, int s, int j) -> f16x8 { return *(const f16x8*)(lds + so + xoff[s] + j * 4096); };
+
+#define E_MMA(P, WS, S, J)                                                             \
+    do {                                                                               \
+        f16x8 xj = X[P][J];                                                            \
+        if constexpr (SCALED) xj = xj * a.scale;                                       \
+        acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(WA[WS][S][0], xj, acc[0][J], 0, 0, 0); \
+        acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(WA[WS][S][1], xj, acc[1][J], 0, 0, 0); \
+    } while (0)
+    // MFMA pair J of step S (parity P, A fragments of set WS), then the B
+    // fragment J of the next step (step NB of the tile in stage SN)
+#define E_PAIR(P, WS, S, SN, NB, J)                                                    \
+    do {                                                                               \
+        E_MMA(P, WS, S, J);                                                            \
+        X[1 - (P)][J] = read_x(SN, NB, J);                                             \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+    } while (0)
+#define E_STEP(P, WS, S, SN, NB)                                                       \
+    do {                                                                               \
+        E_PAIR(P, WS, S, SN, NB, 0); E_PAIR(P, WS, S, SN, NB, 1);                      \
+        E_PAIR(P, WS, S, SN, NB, 2); E_PAIR(P, WS, S, SN, NB, 3);                      \
+        E_PAIR(P, WS, S, SN, NB, 4); E_PAIR(P, WS, S, SN, NB, 5);                      \
+        E_PAIR(P, WS, S, SN, NB, 6); E_PAIR(P, WS, S, SN, NB, 7);                      \
+    } while (0)
+    // the last step of a tile also issues the copies of tile KN into stage
+    // S2 and the A fragments of tile KN into set S2, one copy per MFMA pair
+#define E_PAIR_ISSUE(P, WS, S, SN, NB, J, S2, KN)                                      \
+    do {                                                                               \
+        E_MMA(P, WS, S, J);                                                            \
+        X[1 - (P)][J] = read_x(SN, NB, J);                                             \
+        issue_x(S2, KN, J);                                                            \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+    } while (0)
+
+    // prologue: activations and A fragments of the first two tiles in
+    // flight, the first tile's step-0 B fragments in registers
+    const int last = kc_end - 1;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    int n;
-                    bool ok;
-                    if constexpr (EPI == 2) {
-                        const int jj = tn * 128 + 32 * wave + 8 * q + 4 * h;
-                        ok = jj < N / 2;
-                        n = f ? N / 2 + jj : jj;
-                    } else {
-                        n = tn * 256 + 64 * wave + 32 * f + 8 * q + 4 * h;
-                        ok = n < N;
-                    }
-                    if (!ok) continue;
-                    const f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2],
-                                     acc[f][j][4 * q + 3]};
-                    *(f32x4*)(prow + n) = v;
-                }
-        } else if constexpr (EPI == 2) {
+    for (int i = 0; i < 8; ++i) issue_x(0, kc_begin, i);
+    load_w(std::integral_constant<int, 0>{}, kc_begin);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int jj = tn * 128 + 32 * wave + 8 * q + 4 * h;
-                if (jj >= N / 2) continue;
-                f16x4 hv;
+    for (int i = 0; i < 8; ++i) issue_x(1, min(kc_begin + 1, last), i);
+    load_w(std::integral_constant<int, 1>{}, min(kc_begin + 1, last));
+    // wait for the first tile's copies (tile 2's and the A fragments, issued
+    // after them, may still be in flight)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float gv = acc[0][j][4 * q + e] * a.inv_scale;
-                    const float uv = acc[1][j][4 * q + e] * a.inv_scale;
-                    hv[e] = (_Float16)(silu_f32(gv) * uv);
-                }
-                *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + jj) = hv;
+    for (int j = 0; j < 8; ++j) X[0][j] = read_x(0, 0, j);
+
+    // One tile: tile kc in stage ST, its A fragments in set ST (constants).
+    // The barrier before step 3: this wave's copies of tile kc + 1 have
+    // landed (issued a tile ago; only the A fragments issued after them may
+    // be outstanding) and every wave has read its step-3 operands of stage
+    // ST - 1's tile, so after it tile kc + 2 goes to stage (ST + 2) % 3.
+    auto tile_step = [&](auto st_c, int kc) {
+        constexpr int ST = decltype(st_c)::value;
+        constexpr int S1 = (ST + 1) % T2_NSTAGE, S2 = (ST + 2) % T2_NSTAGE;
+        constexpr int so = ST * T2_XBYTES, sn = S1 * T2_XBYTES;
+        E_STEP(0, ST, 0, so, 1);
+        E_STEP(1, ST, 1, so, 2);
+        E_STEP(0, ST, 2, so, 3);
+        __builtin_amdgcn_s_waitcnt(VMCNT8);
+        lds_barrier();
+        const int kn = min(kc + 2, last);
+        E_PAIR_ISSUE(1, ST, 3, sn, 0, 0, S2, kn);
+        E_PAIR_ISSUE(1, ST, 3, sn, 0, 1, S2, kn);
+        E_PAIR_ISSUE(1, ST, 3, sn, 0, 2, S2, kn);
+        E_PAIR_ISSUE(1, ST, 3, sn, 0, 3, S2, kn);
+        E_PAIR_ISSUE(1, ST, 3, sn, 0, 4, S2, kn);
+        E_PAIR_ISSUE(1, ST, 3, sn, 0, 5, S2, kn);
+        E_PAIR_ISSUE(1, ST, 3, sn, 0, 6, S2, kn);
+        E_PAIR_ISSUE(1, ST, 3, sn, 0, 7, S2, kn);
+        load_w(std::integral_constant<int, S2>{}, kn);
+    };
+    int kc = kc_begin;
+    for (; kc + T2_NSTAGE <= kc_end; kc += T2_NSTAGE) {
+        tile_step(std::integral_constant<int, 0>{}, kc);
+        tile_step(std::integral_constant<int, 1>{}, kc + 1);
+        tile_step(std::integral_constant<int, 2>{}, kc + 2);
+    }
+    if (kc < kc_end) tile_step(std::integral_constant<int, 0>{}, kc);
+    if (kc + 1 < kc_end) tile_step(std::integral_constant<int, 1>{}, kc + 1);
+#undef E_PAIR_ISSUE
+#undef E_STEP
+#undef E_PAIR
+#undef E_MMA
+    __builtin_amdgcn_s_waitcnt(0);
+
+    if constexpr (SPLIT) {
+        tile_epilogue<EPI, SPLIT>(a, acc, m0, tn, wave, r32, h, blockIdx.y);
+    } else {
+        __syncthreads();
+        tile_store_rows<EPI>(a, acc, m0, tn, wave, lane, lds);
+    }
+}
+
+// Weight expansion for the two-pass path, written in the order the GEMM
+// reads its A fragments: for channel tile tn, wave w, fragment f (tile rows
+// 64w + 32f + r, r = lane % 32, as chosen by tile_row), 64-k chunk kc and
+// MFMA step s, lane l holds the FP16 weights k = 64 kc + 32 (l / 32) + 8s ..
+// +8 of its row: 16 bytes, lanes in order, 1 KB per fragment.  The chunks of
+// one (tn, w, f) form a block of K / 64 + 1 chunks of 4 KB: the spare chunk
+// keeps the blocks that concurrent workgroups read from sitting a power of
+// two apart, which would map them onto the same memory channels.
+// Workgroup (tn, g) expands chunks [8g, 8g + 8) of the 256 rows of channel
+// tile tn; a thread takes one (w, f, chunk, lane): 24 contiguous packed bytes
+// (32 indices) in, four 16-byte stores (one per step) out, each store
+// instruction contiguous across the wave.
+constexpr int X_CHUNKS = 8;   // chunks per expansion workgroup
+
+template <int EPI>
+__global__ void __launch_bounds__(256)
+lut6_expand_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ tables,
+                   uint16_t* __restrict__ w16, int N, int K)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t tab[16 * 64];
+    const int tn = blockIdx.x, g = blockIdx.y;
+    const int chunks = K / BK;
+    const int row_bytes = K / 4 * 3;
+    // the 16 tables of the tile: slot s = tile row / 16
+    for (int i = threadIdx.x; i < 16 * 64; i += 256)
+        tab[i] = tables[(tile_row<EPI>(16 * (i >> 6), tn, N) / 16) * 64 + (i & 63)];
+    __syncthreads();
+    const int nch = min(X_CHUNKS, chunks - g * X_CHUNKS);
+    for (int u = threadIdx.x; u < 8 * nch * 64; u += 256) {
+        const int lane = u & 63, kl = (u >> 6) % nch, wf = (u >> 6) / nch;
+        const int kc = g * X_CHUNKS + kl;
+        const int trow = 64 * (wf >> 1) + 32 * (wf & 1) + (lane & 31);
+        const int row = tile_row<EPI>(trow, tn, N);
+        const uint8_t* src = packed + (size_t)row * row_bytes + 48 * kc + 24 * (lane >> 5);
+        // 8-byte aligned (rows are 48-byte multiples, the offset 48 kc + 24h)
+        const u32x2* const q = (const u32x2*)__builtin_assume_aligned(src, 8);
+        const u32x2 v0 = q[0], v1 = q[1], v2 = q[2];
+        const uint32_t pw[6] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1]};
+        const uint16_t* const t = tab + 64 * (trow >> 4);
+        uint16_t* const dst = w16 + ((((size_t)tn * 8 + wf) * (chunks + 1) + kc) * 4096 + lane * 16) / 2;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            // indices 8 st .. 8 st + 7 of the 192-bit word
+            uint32_t e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int bit = 6 * (8 * st + i), wd = bit >> 5, o = bit & 31;
+                const uint32_t lo = pw[wd] >> o;
+                const uint32_t hi = (o > 26 && wd + 1 < 6) ? (pw[wd + 1] << (32 - o)) : 0u;
+                e[i] = (lo | hi) & 63u;
             }
-        } else {
+            u32x4 out;
 #pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = tn * 256 + 64 * wave + 32 * f + 8 * q + 4 * h;
-                    if (n >= N) continue;
-                    f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2],
-                               acc[f][j][4 * q + 3]};
-                    v *= a.inv_scale;
-                    if constexpr (EPI == 0) {
-                        *(f32x4*)((float*)a.y + (size_t)tok * N + n) = v;
-                    } else {
-                        f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                        *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n) = hv;
-                    }
-                }
+            for (int i = 0; i < 4; ++i) out[i] = (uint32_t)t[e[2 * i]] | ((uint32_t)t[e[2 * i + 1]] << 16);
+            *(u32x4*)(dst + st * 512) = out;
         }
     }
 }
@@ -1118,19 +1473,22 @@ lut6_dequant_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restri
 // ---------------------------------------------------------------------------
 
 struct Workspace {
-    float* ptr = nullptr;
+    void* ptr = nullptr;
     size_t bytes = 0;
 };
 
-std::mutex g_ws_mutex;
-std::map<std::pair<int, uintptr_t>, Workspace> g_ws;   // key: (device, stream)
+// workspace kinds: split-K partial sums, expanded FP16 weight
+enum { WS_PARTIAL = 0, WS_EXPANDED = 1 };
 
-int workspace_for(hipStream_t stream, size_t bytes, float** out)
+std::mutex g_ws_mutex;
+std::map<std::tuple<int, uintptr_t, int>, Workspace> g_ws;   // key: (device, stream, kind)
+
+int workspace_for(hipStream_t stream, int kind, size_t bytes, void** out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return LUT6_E_DEVICE;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[std::make_pair(dev, (uintptr_t)stream)];
+    Workspace& w = g_ws[std::make_tuple(dev, (uintptr_t)stream, kind)];
     if (w.bytes < bytes) {
         if (w.ptr) {
             // a previous launch on this stream may still use the old buffer
@@ -1141,7 +1499,7 @@ int workspace_for(hipStream_t stream, size_t bytes, float** out)
         }
         void* p = nullptr;
         if (hipMalloc(&p, bytes) != hipSuccess) return LUT6_E_DEVICE;
-        w.ptr = (float*)p;
+        w.ptr = p;
         w.bytes = bytes;
     }
     *out = w.ptr;
@@ -1188,7 +1546,7 @@ int launch_tiles(GemmArgs a, int epi, int splits, hipStream_t stream)
     dim3 grid(a.n_tiles, splits), block(64 * WN_W * WM_W);
     if (splits > 1) {
         const size_t bytes = (size_t)splits * a.L * a.N * sizeof(float);
-        const int st = workspace_for(stream, bytes, &a.partial);
+        const int st = workspace_for(stream, WS_PARTIAL, bytes, (void**)&a.partial);
         if (st != LUT6_OK) return st;
         switch (epi) {
         case 0: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 0, true>), grid, block, 0, stream, a); break;
@@ -1205,6 +1563,40 @@ int launch_tiles(GemmArgs a, int epi, int splits, hipStream_t stream)
         }
     }
     return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+}
+
+// Launch the 256 x 256 tile kernel, fused or on the expanded weight.
+template <bool SPLIT>
+void launch_tiles_t(const GemmArgs& a, bool two_pass, int epilogue, bool scaled, dim3 grid, hipStream_t stream)
+{
+    const dim3 block(256);
+    const int sel = epilogue * 2 + (scaled ? 1 : 0);
+    if (two_pass) {
+        switch (sel) {
+        case 0: hipLaunchKernelGGL((lut6_expanded_gemm_kernel<0, false, SPLIT>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((lut6_expanded_gemm_kernel<0, true, SPLIT>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((lut6_expanded_gemm_kernel<1, false, SPLIT>), grid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((lut6_expanded_gemm_kernel<1, true, SPLIT>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((lut6_expanded_gemm_kernel<2, false, SPLIT>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((lut6_expanded_gemm_kernel<2, true, SPLIT>), grid, block, 0, stream, a); break;
+        }
+    } else {
+        switch (sel) {
+        case 0: hipLaunchKernelGGL((lut6_tile256_kernel<0, false, SPLIT>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((lut6_tile256_kernel<0, true, SPLIT>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((lut6_tile256_kernel<1, false, SPLIT>), grid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((lut6_tile256_kernel<1, true, SPLIT>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((lut6_tile256_kernel<2, false, SPLIT>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((lut6_tile256_kernel<2, true, SPLIT>), grid, block, 0, stream, a); break;
+        }
+    }
+}
+
+void launch_tiles(const GemmArgs& a, bool two_pass, int epilogue, bool scaled, bool split, dim3 grid,
+                  hipStream_t stream)
+{
+    if (split) launch_tiles_t<true>(a, two_pass, epilogue, scaled, grid, stream);
+    else launch_tiles_t<false>(a, two_pass, epilogue, scaled, grid, stream);
 }
 
 }  // namespace
@@ -1266,7 +1658,7 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
         const bool scaled = in_scale != 1.0f;
         dim3 grid((unsigned)(tiles * splits)), block(256);
         if (splits > 1) {
-            const int st = workspace_for(stream, (size_t)tiles * splits * S_PART * 16, &a.partial);
+            const int st = workspace_for(stream, WS_PARTIAL, (size_t)tiles * splits * S_PART * 16, (void**)&a.partial);
             if (st != LUT6_OK) return st;
             switch (epilogue * 2 + (scaled ? 1 : 0)) {
             case 0: hipLaunchKernelGGL((lut6_stream_kernel<0, false, true>), grid, block, 0, stream, a); break;
@@ -1313,29 +1705,32 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
     splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
     const bool scaled = in_scale != 1.0f;
     dim3 grid(tiles, splits), block(256);
-    if (splits > 1) {
-        const int st = workspace_for(stream, (size_t)splits * L * N * sizeof(float), &a.partial);
+    // many tokens: expand the weight once, then the FP16 GEMM; otherwise the
+    // fused kernel
+    const int tiles_n = tiles / tiles_m;
+    const size_t w16_bytes = (size_t)tiles_n * 8 * (chunks + 1) * 4096;   // whole tiles, fragment order
+    const bool two_pass = L >= EXPAND_MIN_L && w16_bytes <= (size_t)INT32_MAX;
+    if (two_pass) {
+        void* w16 = nullptr;
+        const int st = workspace_for(stream, WS_EXPANDED, w16_bytes, &w16);
         if (st != LUT6_OK) return st;
-        switch (epilogue * 2 + (scaled ? 1 : 0)) {
-        case 0: hipLaunchKernelGGL((lut6_tile256_kernel<0, false, true>), grid, block, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((lut6_tile256_kernel<0, true, true>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((lut6_tile256_kernel<1, false, true>), grid, block, 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((lut6_tile256_kernel<1, true, true>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((lut6_tile256_kernel<2, false, true>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((lut6_tile256_kernel<2, true, true>), grid, block, 0, stream, a); break;
+        const dim3 xgrid((unsigned)tiles_n, (unsigned)((chunks + X_CHUNKS - 1) / X_CHUNKS));
+        switch (epilogue) {
+        case 2: hipLaunchKernelGGL(lut6_expand_kernel<2>, xgrid, dim3(256), 0, stream,
+                                   packed, (const uint16_t*)tables, (uint16_t*)w16, (int)N, (int)K); break;
+        default: hipLaunchKernelGGL(lut6_expand_kernel<0>, xgrid, dim3(256), 0, stream,
+                                    packed, (const uint16_t*)tables, (uint16_t*)w16, (int)N, (int)K); break;
         }
         if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
-        return launch_reduce(a, epilogue, splits, stream);
+        a.w16 = (const uint16_t*)w16;
     }
-    switch (epilogue * 2 + (scaled ? 1 : 0)) {
-    case 0: hipLaunchKernelGGL((lut6_tile256_kernel<0, false, false>), grid, block, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((lut6_tile256_kernel<0, true, false>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((lut6_tile256_kernel<1, false, false>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((lut6_tile256_kernel<1, true, false>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((lut6_tile256_kernel<2, false, false>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((lut6_tile256_kernel<2, true, false>), grid, block, 0, stream, a); break;
+    if (splits > 1) {
+        const int st = workspace_for(stream, WS_PARTIAL, (size_t)splits * L * N * sizeof(float), (void**)&a.partial);
+        if (st != LUT6_OK) return st;
     }
-    return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+    launch_tiles(a, two_pass, epilogue, scaled, splits > 1, grid, stream);
+    if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
+    return splits > 1 ? launch_reduce(a, epilogue, splits, stream) : LUT6_OK;
 }
 
 extern "C" int lut6_dequant(const uint8_t* packed, const void* tables, void* w, int64_t N,
@@ -1362,7 +1757,7 @@ extern "C" int lut6_release(void)
     (void)hipGetDevice(&cur);
     for (auto& kv : g_ws) {
         if (!kv.second.ptr) continue;
-        const int dev = kv.first.first;
+        const int dev = std::get<0>(kv.first);
         if (hipSetDevice(dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
             status = LUT6_E_DEVICE;
         (void)hipFree(kv.second.ptr);

@@ -98,7 +98,7 @@ def test_dequant_bit_exact(ora, N, K):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("s", [1.0, 16.0])
-@pytest.mark.parametrize("K", [64, 256])
+@pytest.mark.parametrize("K", [64, 256, 1024])
 def test_identity_readout(ora, K, s):
     _say("identity", K, s)
     N = 96
@@ -131,9 +131,26 @@ def test_linear_small(ora, L, K, N, epi, s):
     assert rep.ok, str(rep)
 
 
+# many tokens: the weight is expanded once and the GEMM reads FP16 tiles;
+# ragged L and N, split K (few tiles), every epilogue and scale
+SHAPES_MANY = [(1024, 64, 32), (1029, 256, 160), (1100, 576, 544), (2047, 128, 96),
+               (1536, 1024, 288), (1280, 12288, 64)]
+
+
+@pytest.mark.parametrize("L,K,N", SHAPES_MANY)
+@pytest.mark.parametrize("epi,s", [(F32, 1.0), (F16, 1.0), (F16, 16.0), (SILU, 1.0), (SILU, 4.0)])
+def test_linear_many_tokens(ora, L, K, N, epi, s):
+    _say("many", L, K, N, epi, s)
+    x, idx, tab = _problem(L, K, N, L * 5 + K + N, sigma=0.5 if s > 1 else 1.0,
+                           subnormal=(L % 2 == 1))
+    y = gpu_linear(x, idx, tab, epi, s)
+    rep = oracle_check(ora, x, idx, tab, epi, s, y)
+    assert rep.ok, str(rep)
+
+
 def test_non_aligned_n_tiles(ora):
     # N = 16 * odd so the last channel tile is partial in both regimes
-    for L in (64, 384):
+    for L in (64, 384, 1088):
         _say("ragged-n", L)
         x, idx, tab = _problem(L, 128, 16 * 37, 91 + L)
         y = gpu_linear(x, idx, tab, F16, 1.0)
@@ -178,7 +195,7 @@ def test_prefill_sweep_sampled_layers(ora, layer):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("L,K,N,epi", [(128, 4096, 4096, F32), (1024, 512, 1024, F16),
-                                       (96, 256, 128, SILU)])
+                                       (96, 256, 128, SILU), (1500, 768, 160, F32)])
 def test_deterministic(L, K, N, epi):
     _say("determinism", L, K, N, epi)
     x, idx, tab = _problem(L, K, N, 5)
@@ -190,7 +207,7 @@ def test_deterministic(L, K, N, epi):
 
 
 @pytest.mark.parametrize("epi", [F32, F16, SILU])
-@pytest.mark.parametrize("L", [64, 640])
+@pytest.mark.parametrize("L", [64, 640, 1024])
 def test_scale_invariance(L, epi):
     # power-of-two scaling commutes with rounding when nothing overflows
     _say("scale-invariance", L, epi)
@@ -200,7 +217,7 @@ def test_scale_invariance(L, epi):
         assert gpu_linear(x, idx, tab, epi, s).tobytes() == y1.tobytes()
 
 
-@pytest.mark.parametrize("L", [32, 512])
+@pytest.mark.parametrize("L", [32, 512, 1024])
 def test_overflow_gives_inf(ora, L):
     _say("overflow", L)
     x, idx, _ = _problem(L, 128, 64, 2)
