@@ -10,11 +10,12 @@ projections, 8 full-attention layers with q|k|v, o, gate|up and down; hidden
 (per-layer seeds) and activations that are resident in HBM before timing
 starts.  The line printed is throughput in TFLOP/s, with
 
-  * roofline: the dominant kernel's algorithmic FLOPs per launch over its
-    average launch time, measured with HIP events on the launch stream,
-    against the FP16 dense MFMA peak (2,516.6 TFLOP/s); its HBM traffic comes
-    from the rocprofv3 counter summary in profiles/ when that summary was
-    taken on the current kernel source, else null;
+  * roofline: the dominant launch class's algorithmic FLOPs per lut6_linear
+    call over the call's average time (HIP events around the call on its
+    stream, so for the many-token path the weight expansion and the GEMM
+    together), against the FP16 dense MFMA peak (2,516.6 TFLOP/s); its HBM
+    traffic comes from the rocprofv3 counter summary in profiles/ when that
+    summary was taken on the current kernel source, else null;
   * l128_stream: the L = 128 single projection (4,096 -> 4,096, FP32 out) in
     algorithmic HBM GB/s over back-to-back launches, rotating over enough
     weight sets that the 256 MB last-level cache cannot hold them;
@@ -60,10 +61,18 @@ def kernel_source_sha() -> str:
 
 
 def kernel_class(g) -> str:
-    """Which kernel instance lut6_linear launches for this GEMM."""
-    regime = "stream" if g.L <= 192 else "tiled"
+    """Which kernels lut6_linear launches for this GEMM (path and epilogue)."""
+    import lut_weight_quantized_amd as lq
+    regime = {lq.PATH_STREAM: "stream", lq.PATH_FUSED: "fused",
+              lq.PATH_EXPANDED: "expanded"}[lq.linear_path(g.L, g.K, g.N, g.epilogue)]
     epi = {0: "f32", 1: "f16", 2: "silu"}[g.epilogue]
     return f"{regime}_{epi}"
+
+
+# the kernels one lut6_linear call of each path runs (for the roofline record)
+PATH_KERNELS = {"stream": ["lut6_stream_kernel", "lut6_stream_reduce_kernel (split K)"],
+                "fused": ["lut6_tile256_kernel"],
+                "expanded": ["lut6_expand_kernel", "lut6_expanded_gemm_kernel"]}
 
 
 def cpu_threads() -> int:
@@ -211,8 +220,11 @@ def main() -> int:
 
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                "traffic": traffic, "kernel": dom_name, "avg_launch_us": round(avg_ms * 1e3, 2),
-                "flops_per_launch": flops_per_launch, "launches_per_step": dom["n"] // args.steps}
+                "traffic": traffic, "kernel": dom_name,
+                "kernels_per_launch": PATH_KERNELS[dom_name.split("_")[0]],
+                "avg_launch_us": round(avg_ms * 1e3, 2),
+                "flops_per_launch": flops_per_launch, "launches_per_step": dom["n"] // args.steps,
+                "timing": "HIP events around each lut6_linear call on its stream (all its kernels)"}
 
     # ---------------- parity sample + CPU baseline (oracle) ----------------
     cpu = None

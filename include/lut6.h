@@ -26,10 +26,12 @@
  * Ownership: the caller allocates, owns and frees every buffer.  Pointers
  * passed to lut6_linear / lut6_dequant are device pointers of the current
  * HIP device; pointers passed to lut6_pack / lut6_unpack are host pointers.
- * The library keeps no per-call state.  It owns one lazily created device
- * workspace per device for split-K partial sums (created on the first call
- * that needs it, grown when a later call needs more, freed by
- * lut6_release()).
+ * The library keeps no per-call state.  It owns lazily created device
+ * workspaces, one of each kind per (device, stream): split-K partial sums,
+ * and the expanded FP16 weight of the many-token path (see
+ * lut6_linear_path); each is created on the first call that needs it,
+ * grown when a later call needs more (after synchronising that stream) and
+ * freed by lut6_release().
  *
  * Errors: every function returns LUT6_OK (0) or a named status, and launches
  * nothing on error.  Arguments are checked on the host; nothing is silently
@@ -108,6 +110,27 @@ int lut6_unpack(const uint8_t* packed, uint8_t* idx, int64_t N, int64_t K);
 int lut6_linear(const void* x, const uint8_t* packed, const void* tables, void* y,
                 int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
                 hipStream_t stream);
+
+/* Kernel paths of lut6_linear (what lut6_linear_path returns).            */
+typedef enum {
+    /* L <= 192: the weight-streaming kernel (K split across workgroups,
+     * fixed-order reduction)                                              */
+    LUT6_PATH_STREAM = 0,
+    /* the fused kernel: 256 x 256 tiles, packed indices unpacked and looked
+     * up in LDS per tile, FP16 MFMA                                       */
+    LUT6_PATH_FUSED = 1,
+    /* L >= 1024: the weight is expanded once per call (the same unpack and
+     * lookup) into a workspace of tiles_n * 8 * (K/64 + 1) * 4 KB, then an
+     * FP16 MFMA GEMM reads it (tiles_n = ceil(N / 256); for
+     * LUT6_EPI_SILU_MUL_F16 a tile holds 128 gate|up row pairs, the same
+     * count); the fused kernel instead if that workspace would reach 2 GB */
+    LUT6_PATH_EXPANDED = 2
+} lut6_path;
+
+/* The path lut6_linear takes for these sizes (a lut6_path value), or the
+ * negated status lut6_linear would return for them (-LUT6_E_SHAPE,
+ * -LUT6_E_EPILOGUE).  Host only; no device work.                          */
+int lut6_linear_path(int64_t L, int64_t K, int64_t N, int epilogue);
 
 /* Dequantize: w[n, k] = tables[n/16][index(n, k)] as FP16 bits [N, K] on
  * the device, with the same device unpack and lookup as lut6_linear.

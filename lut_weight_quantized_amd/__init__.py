@@ -30,7 +30,13 @@ STATUS = {0: "LUT6_OK", 1: "LUT6_E_NULL", 2: "LUT6_E_SHAPE", 3: "LUT6_E_ALIGN",
           7: "LUT6_E_DEVICE", 8: "LUT6_E_ALIAS"}
 
 EXPORTS = ("lut6_packed_bytes", "lut6_table_bytes", "lut6_pack", "lut6_unpack",
-           "lut6_linear", "lut6_dequant", "lut6_release", "lut6_status_string")
+           "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_release",
+           "lut6_status_string")
+
+# kernel paths of lut6_linear (lut6_linear_path)
+PATH_STREAM = 0
+PATH_FUSED = 1
+PATH_EXPANDED = 2
 
 
 class Lut6Error(RuntimeError):
@@ -65,6 +71,8 @@ def load_library() -> ctypes.CDLL:
     lib.lut6_unpack.restype = ctypes.c_int
     lib.lut6_linear.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_float, ctypes.c_int, P]
     lib.lut6_linear.restype = ctypes.c_int
+    lib.lut6_linear_path.argtypes = [I64, I64, I64, ctypes.c_int]
+    lib.lut6_linear_path.restype = ctypes.c_int
     lib.lut6_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.lut6_dequant.restype = ctypes.c_int
     lib.lut6_release.argtypes = []
@@ -169,6 +177,15 @@ def linear(x, packed, tables, *, epilogue: int = EPI_STORE_F16, in_scale: float 
                                     _stream_handle(stream))
     _check(st, "lut6_linear")
     return out
+
+
+def linear_path(L: int, K: int, N: int, epilogue: int = EPI_STORE_F16) -> int:
+    """Which kernels lut6_linear runs for these sizes (PATH_*); raises on
+    sizes it would refuse."""
+    r = int(load_library().lut6_linear_path(L, K, N, int(epilogue)))
+    if r < 0:
+        raise Lut6Error(-r, "lut6_linear_path")
+    return r
 
 
 def dequant(packed, tables, K: int, *, out=None, stream=None):

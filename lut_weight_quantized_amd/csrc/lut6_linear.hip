@@ -7,35 +7,37 @@
 //     a[l, n]  = (sum_k xs[l, k] * W[n, k]) / s       (FP32 accumulation)
 //     y        = epilogue(a): FP32, FP16, or silu(gate) * up in FP16.
 //
-// Mapping onto the hardware
-//   * The contraction runs on v_mfma_f32_16x16x32_f16 (FP16 inputs, FP32
-//     accumulate).  The weight is the MFMA "A" operand (16 output channels x
-//     32 k) and the activations the "B" operand (32 k x 16 tokens), so each
-//     accumulator lane holds four consecutive channels of one token and the
-//     store is a 16-byte (FP32) or 8-byte (FP16) vector per lane.
-//   * A 16-channel fragment uses exactly one table, because fragments are
-//     16-aligned.  The tables of a workgroup's channels sit in LDS (128 bytes
-//     each: one table spans the 32 four-byte banks once, so a wave's lookups
-//     into one table never conflict).
-//   * Index tiles are never materialised: each lane loads the 12 packed bytes
-//     that hold 16 consecutive indices of one channel (three aligned dwords,
-//     a 96-bit little-endian word whose field t is index t), extracts each
-//     6-bit field and gathers its table entry from LDS straight into the
-//     FP16 fragment registers.  Workgroup waves own disjoint channels, so
-//     every weight is dequantised once per workgroup.
-//   * The sum over k is insensitive to the order of k inside one MFMA as long
-//     as A and B agree; lane group g (= lane / 16) takes k0+16g .. k0+16g+15
-//     for a pair of MFMAs, which keeps its 12 packed bytes contiguous.
-//   * Activation tiles (BM tokens x 64 k) are double-buffered in LDS with a
-//     16-byte row pad (144-byte rows), which keeps the 16-byte fragment reads
-//     conflict-free.  The input scale is applied while staging, in FP16
-//     (one rounding, exactly as fp16(x * s)).
-//   * Small token counts split K across workgroups; partial sums go to a
-//     workspace and a second kernel adds them in a fixed order (no atomics),
-//     so results are bit-identical run to run.
-//   * Workgroups are dispatched round-robin over the 8 XCDs; the tile index
-//     is remapped so that consecutive tiles (which share a weight tile) run
-//     on the same XCD and share its L2.
+// Mapping onto the hardware (one MI355X: 256 CUs in 8 XCDs, 4 SIMDs per CU)
+//   * Every contraction runs on v_mfma_f32_32x32x16_f16 (FP16 operands,
+//     FP32 accumulation): the weight is the MFMA "A" operand (32 channels x
+//     16 k), the activations the "B" operand (16 k x 32 tokens).  The k order
+//     inside an MFMA is free as long as A and B agree; lane group h = lane /
+//     32 takes k in [32h, 32h + 32) of a 64-k chunk, so its 32 indices are
+//     24 contiguous packed bytes (a 192-bit little-endian word).
+//   * Tables sit in LDS, 128 bytes each; a lookup is one shift or funnel
+//     shift, one v_and_or_b32 into an LDS byte offset and one ds_read_u16,
+//     a bit copy (dequantisation is exact).
+//   * Three paths by token count (lut6_linear_path):
+//       - L <= 192, lut6_stream_kernel: each weight serves few tokens, so K
+//         is split across workgroups until ~256 of them (one per CU) stream
+//         the packed weight; partial sums are added by a second kernel in a
+//         fixed order (no atomics, bit-identical run to run).
+//       - 192 < L < 1024, lut6_tile256_kernel: 256 x 256 tiles, four waves
+//         (one per SIMD, 64 x 256 accumulators each); packed words go
+//         straight to registers, activations through three LDS stages, and
+//         the table lookups are spread over the MFMA stream.
+//       - L >= 1024, lut6_expand_kernel + lut6_expanded_gemm_kernel: the
+//         fused kernel repeats every lookup once per 256-token tile, and one
+//         wave per SIMD cannot issue those lookups and keep the matrix unit
+//         fed; with many tokens the weight is expanded once per call into
+//         FP16 MFMA fragments (1 KB each, contiguous) and the GEMM loads them
+//         straight into registers.
+//   * Tiles are remapped from the round-robin XCD dispatch to contiguous
+//     ranges per XCD and grouped by 4 token tiles, so the workgroups resident
+//     on one XCD share activation and weight tiles in its L2.
+//   * Outputs go through LDS so that each store instruction writes whole
+//     rows; the input scale is applied to the FP16 activation fragments
+//     (exactly fp16(x * s)) and undone on the FP32 sums.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,7 +58,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;          // k per main-loop step (two MFMA k-steps of 32)
-constexpr int XROW = BK + 8;    // LDS activation row, in halves (144 bytes)
 constexpr int NUM_XCD = 8;
 
 // ---------------------------------------------------------------------------
@@ -138,213 +139,6 @@ struct GemmArgs {
     _Float16 scale;           // in_scale as FP16 (exact)
     float inv_scale;          // 1 / in_scale (exact)
 };
-
-// ---------------------------------------------------------------------------
-// The GEMM kernel.
-//   BN x BM tile of (channels x tokens); WN_W x WM_W waves; each wave owns
-//   BN/WN_W channels (FN fragments of 16) and BM/WM_W tokens (FM of 16).
-//   EPI: 0 = FP32, 1 = FP16, 2 = SiLU(gate) * up FP16.  SPLIT: write FP32
-//   partial sums instead of the epilogue.
-//   For EPI 2 a tile covers gate channels [j0, j0 + BN/2) and the matching
-//   up channels [N/2 + j0, ...); wave fragments f < FN/2 are gate, the rest up,
-//   so each lane holds both operands of its outputs.
-// ---------------------------------------------------------------------------
-template <int BN, int BM, int WN_W, int WM_W, int EPI, bool SPLIT>
-__global__ void __launch_bounds__(64 * WN_W * WM_W)
-lut6_gemm_kernel(GemmArgs a)
-{
-    constexpr int NT = 64 * WN_W * WM_W;
-    constexpr int WN = BN / WN_W, WM = BM / WM_W;
-    constexpr int FN = WN / 16, FM = WM / 16;
-    constexpr int XCH = BM * BK / 8;            // 16-byte chunks per activation tile
-    constexpr int XPT = (XCH + NT - 1) / NT;    // chunks per thread
-    static_assert(BN % (16 * WN_W) == 0 && BM % (16 * WM_W) == 0, "tile shape");
-    static_assert(EPI != 2 || FN % 2 == 0, "SiLU needs an even fragment count");
-
-    __shared__ __attribute__((aligned(16))) _Float16 xs_lds[2][BM * XROW];
-    __shared__ __attribute__((aligned(16))) uint16_t tab_lds[BN / 16 * 64];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % WN_W, wm = wave / WN_W;
-    const int r16 = lane & 15, g4 = lane >> 4;
-
-    const int tile = xcd_remap(blockIdx.x, a.n_tiles);
-    const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
-    const int m0 = tm * BM;
-    const int K = a.K, N = a.N, L = a.L;
-    const int kc_begin = blockIdx.y * a.k_chunks_per_split;
-    const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
-    const int row_bytes = K / 4 * 3;
-
-    // First channel of fragment f of wave w (may be >= the valid range:
-    // such fragments are computed on a clamped row and never stored).
-    auto frag_row = [&](int w, int f) -> int {
-        if constexpr (EPI == 2) {
-            const int j = tn * (BN / 2) + w * (WN / 2) + 16 * (f % (FN / 2));
-            return f < FN / 2 ? j : N / 2 + j;
-        } else {
-            return tn * BN + w * WN + 16 * f;
-        }
-    };
-    auto frag_valid = [&](int w, int f) -> bool {
-        if constexpr (EPI == 2) return tn * (BN / 2) + w * (WN / 2) + 16 * (f % (FN / 2)) < N / 2;
-        else return frag_row(w, f) < N;
-    };
-
-    // tables of this workgroup's fragments -> LDS (slot = wave * FN + f)
-    for (int i = tid; i < BN / 16 * 64; i += NT) {
-        const int s = i / 64, w = s / FN, f = s % FN;
-        const int row = frag_valid(w, f) ? frag_row(w, f) : 0;
-        tab_lds[i] = a.tables[(row / 16) * 64 + (i % 64)];
-    }
-
-    // per-lane packed-byte pointers for each fragment
-    const uint8_t* prow[FN];
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-        const int row = (frag_valid(wn, f) ? frag_row(wn, f) : 0) + r16;
-        prow[f] = a.packed + (size_t)row * row_bytes + 12 * g4;
-    }
-
-    f32x4 acc[FN][FM];
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-#pragma unroll
-        for (int m = 0; m < FM; ++m) acc[f][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const bool scaled = a.scale != (_Float16)1.0f;
-
-    // activation chunk c of k-step kc -> registers
-    auto load_x = [&](int kc, u32x4 (&xr)[XPT]) {
-#pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int c = tid + i * NT;
-            const int r = c / (BK / 8), cc = c % (BK / 8);
-            const int tok = m0 + r;
-            if (c < XCH && tok < L)
-                xr[i] = *(const u32x4*)(a.x + (size_t)tok * K + kc * BK + cc * 8);
-            else
-                xr[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store_x = [&](int buf, u32x4 (&xr)[XPT]) {
-#pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int c = tid + i * NT;
-            if (c < XCH) {
-                const int r = c / (BK / 8), cc = c % (BK / 8);
-                u32x4 v = xr[i];
-                if (scaled) {
-                    f16x8 h = __builtin_bit_cast(f16x8, v);
-                    h = h * a.scale;
-                    v = __builtin_bit_cast(u32x4, h);
-                }
-                *(u32x4*)(&xs_lds[buf][r * XROW + cc * 8]) = v;
-            }
-        }
-    };
-    auto load_p = [&](int kc, uint32_t (&p)[FN][3]) {
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-            const uint32_t* q = (const uint32_t*)(prow[f] + (size_t)kc * (BK / 4 * 3));
-            p[f][0] = q[0];
-            p[f][1] = q[1];
-            p[f][2] = q[2];
-        }
-    };
-
-    u32x4 xr[XPT];
-    uint32_t pk[FN][3], pn[FN][3];
-    if (kc_begin < kc_end) {
-        load_x(kc_begin, xr);
-        load_p(kc_begin, pk);
-        store_x(0, xr);
-    }
-    __syncthreads();
-
-    const uint16_t* tab_w = tab_lds + wn * FN * 64;
-    for (int kc = kc_begin; kc < kc_end; ++kc) {
-        const int cur = (kc - kc_begin) & 1;
-        const bool more = kc + 1 < kc_end;
-        if (more) {
-            load_x(kc + 1, xr);
-            load_p(kc + 1, pn);
-        }
-        // activation fragments of this wave: token r16 of each 16-token block
-        f16x8 xb[FM][2];
-#pragma unroll
-        for (int m = 0; m < FM; ++m) {
-            const _Float16* src = &xs_lds[cur][(wm * WM + 16 * m + r16) * XROW + 16 * g4];
-            xb[m][0] = *(const f16x8*)(src);
-            xb[m][1] = *(const f16x8*)(src + 8);
-        }
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-            f16x8 w0, w1;
-            gather16(pk[f][0], pk[f][1], pk[f][2], tab_w + f * 64, w0, w1);
-#pragma unroll
-            for (int m = 0; m < FM; ++m) {
-                acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w0, xb[m][0], acc[f][m], 0, 0, 0);
-                acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w1, xb[m][1], acc[f][m], 0, 0, 0);
-            }
-        }
-        if (more) {
-            store_x(cur ^ 1, xr);
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                pk[f][0] = pn[f][0];
-                pk[f][1] = pn[f][1];
-                pk[f][2] = pn[f][2];
-            }
-        }
-        __syncthreads();
-    }
-
-    // epilogue: lane holds channels frag_row + 4*g4 + (0..3) of token r16
-#pragma unroll
-    for (int m = 0; m < FM; ++m) {
-        const int tok = m0 + wm * WM + 16 * m + r16;
-        if (tok >= L) continue;
-        if constexpr (SPLIT) {
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                if (!frag_valid(wn, f)) continue;
-                const int n = frag_row(wn, f) + 4 * g4;
-                float* dst = a.partial + ((size_t)blockIdx.y * L + tok) * N + n;
-                *(f32x4*)dst = acc[f][m];
-            }
-        } else if constexpr (EPI == 0) {
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                if (!frag_valid(wn, f)) continue;
-                const int n = frag_row(wn, f) + 4 * g4;
-                *(f32x4*)((float*)a.y + (size_t)tok * N + n) = acc[f][m] * a.inv_scale;
-            }
-        } else if constexpr (EPI == 1) {
-#pragma unroll
-            for (int f = 0; f < FN; ++f) {
-                if (!frag_valid(wn, f)) continue;
-                const int n = frag_row(wn, f) + 4 * g4;
-                const f32x4 v = acc[f][m] * a.inv_scale;
-                f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n) = h;
-            }
-        } else {
-#pragma unroll
-            for (int f = 0; f < FN / 2; ++f) {
-                if (!frag_valid(wn, f)) continue;
-                const int j = frag_row(wn, f) + 4 * g4;
-                const f32x4 gv = acc[f][m] * a.inv_scale;
-                const f32x4 uv = acc[f + FN / 2][m] * a.inv_scale;
-                f16x4 h;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) h[r] = (_Float16)(silu_f32(gv[r]) * uv[r]);
-                *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + j) = h;
-            }
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Large-tile kernel: 256 channels x 256 tokens per workgroup, four waves.
@@ -440,18 +234,19 @@ __device__ __forceinline__ int tile_row(int t, int tn, int N)
     }
 }
 
-// Epilogue of the 256 x 256 tiles: lane (r32, h) of wave w holds token r32
-// of each 32-token fragment j and channels 8q + 4h + (0..3), q = 0..3, of
-// each 32-row fragment f (tile rows 64w + 32f + ...).  SPLIT: raw FP32 sums
-// of K slice ks into the partial buffer.
-template <int EPI, bool SPLIT>
-__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, const f32x16 (&acc)[2][8], int m0, int tn,
+// Epilogue of the 256 x 256 tiles: lane (r32, h) of a wave whose channels
+// are tile rows 64w + [0, 64) and whose tokens start at tok0 holds token
+// tok0 + 32j + r32 of each 32-token fragment j and channels 8q + 4h + (0..3),
+// q = 0..3, of each 32-row fragment f (tile rows 64w + 32f + ...).  SPLIT:
+// raw FP32 sums of K slice ks into the partial buffer.
+template <int EPI, bool SPLIT, int NJ>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, const f32x16 (&acc)[2][NJ], int tok0, int tn,
                                               int wave, int r32, int h, int ks)
 {
     const int L = a.L, N = a.N;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int tok = m0 + 32 * j + r32;
+    for (int j = 0; j < NJ; ++j) {
+        const int tok = tok0 + 32 * j + r32;
         if (tok >= L) continue;
         if constexpr (SPLIT) {
             // raw FP32 sums of this K range; gate rows at j, up rows at N/2 + j
@@ -518,26 +313,29 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, const f32x16 (&
 // back and stores them, 16 bytes per lane, so every store instruction
 // writes whole cache lines (instead of 16-byte pieces of 32 rows).  The
 // caller has synchronised the workgroup: the pipeline stages are free.
-template <int EPI>
-__device__ __forceinline__ void tile_store_rows(const GemmArgs& a, const f32x16 (&acc)[2][8], int m0, int tn,
-                                               int wave, int lane, uint8_t* lds)
+// NJ 32-token fragments per wave, JP of them per pass; the wave's channels
+// are tile rows 64w + [0, 64), its tokens start at tok0, its LDS block is
+// number slot.
+template <int EPI, int NJ, int JP>
+__device__ __forceinline__ void tile_store_rows(const GemmArgs& a, const f32x16 (&acc)[2][NJ], int tok0, int tn,
+                                               int w, int slot, int lane, uint8_t* lds)
 {
     constexpr int OUTC = EPI == 2 ? 32 : 64;      // output channels per wave
     constexpr int ESZ = EPI == 0 ? 4 : 2;         // output element bytes
     constexpr int ROWB = OUTC * ESZ;              // one token's bytes
     constexpr int PITCH = ROWB + 16;
     constexpr int LPR = ROWB / 16;                // lanes per row when reading back
-    constexpr int NREAD = 64 * ROWB / 1024;       // read/store instructions per 64 tokens
+    constexpr int NREAD = 32 * JP * ROWB / 1024;  // read/store instructions per pass
     const int r32 = lane & 31, h = lane >> 5;
-    uint8_t* const wl = lds + wave * (64 * PITCH);
+    uint8_t* const wl = lds + slot * (32 * JP * PITCH);
     const int L = a.L;
     const int ncols = EPI == 2 ? a.N / 2 : a.N;
-    const int n0 = EPI == 2 ? tn * 128 + 32 * wave : tn * 256 + 64 * wave;
+    const int n0 = EPI == 2 ? tn * 128 + 32 * w : tn * 256 + 64 * w;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < NJ / JP; ++p) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * p + jj;
+        for (int jj = 0; jj < JP; ++jj) {
+            const int j = JP * p + jj;
             uint8_t* const row = wl + (32 * jj + r32) * PITCH;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -572,7 +370,7 @@ __device__ __forceinline__ void tile_store_rows(const GemmArgs& a, const f32x16 
         for (int i = 0; i < NREAD; ++i) {
             const int idx = i * 64 + lane, r = idx / LPR, seg = idx % LPR;
             const u32x4 v = *(const u32x4*)(wl + r * PITCH + seg * 16);
-            const int tok = m0 + 64 * p + r, col = n0 + seg * (16 / ESZ);
+            const int tok = tok0 + 32 * JP * p + r, col = n0 + seg * (16 / ESZ);
             if (tok < L && col < ncols)
                 *(u32x4*)((uint8_t*)a.y + ((size_t)tok * ncols + col) * ESZ) = v;
         }
@@ -795,10 +593,10 @@ lut6_tile256_kernel(GemmArgs a)
     __builtin_amdgcn_s_waitcnt(0);
 
     if constexpr (SPLIT) {
-        tile_epilogue<EPI, SPLIT>(a, acc, m0, tn, wave, r32, h, blockIdx.y);
+        tile_epilogue<EPI, SPLIT, 8>(a, acc, m0, tn, wave, r32, h, blockIdx.y);
     } else {
         __syncthreads();
-        tile_store_rows<EPI>(a, acc, m0, tn, wave, lane, lds);
+        tile_store_rows<EPI, 8, 2>(a, acc, m0, tn, wave, wave, lane, lds);
     }
 }
 
@@ -993,10 +791,10 @@ lut6_expanded_gemm_kernel(GemmArgs a)
     __builtin_amdgcn_s_waitcnt(0);
 
     if constexpr (SPLIT) {
-        tile_epilogue<EPI, SPLIT>(a, acc, m0, tn, wave, r32, h, blockIdx.y);
+        tile_epilogue<EPI, SPLIT, 8>(a, acc, m0, tn, wave, r32, h, blockIdx.y);
     } else {
         __syncthreads();
-        tile_store_rows<EPI>(a, acc, m0, tn, wave, lane, lds);
+        tile_store_rows<EPI, 8, 2>(a, acc, m0, tn, wave, wave, lane, lds);
     }
 }
 
@@ -1532,39 +1330,6 @@ int launch_reduce(const GemmArgs& a, int epi, int splits, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
 }
 
-template <int BN, int BM, int WN_W, int WM_W>
-int launch_tiles(GemmArgs a, int epi, int splits, hipStream_t stream)
-{
-    const int n_half = epi == 2 ? a.N / 2 : a.N;
-    const int bn_cov = epi == 2 ? BN / 2 : BN;
-    const int tiles_n = (n_half + bn_cov - 1) / bn_cov;
-    a.tiles_m = (a.L + BM - 1) / BM;
-    a.n_tiles = a.tiles_m * tiles_n;
-    const int chunks = a.K / BK;
-    a.k_chunks_per_split = (chunks + splits - 1) / splits;
-    splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
-    dim3 grid(a.n_tiles, splits), block(64 * WN_W * WM_W);
-    if (splits > 1) {
-        const size_t bytes = (size_t)splits * a.L * a.N * sizeof(float);
-        const int st = workspace_for(stream, WS_PARTIAL, bytes, (void**)&a.partial);
-        if (st != LUT6_OK) return st;
-        switch (epi) {
-        case 0: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 0, true>), grid, block, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 1, true>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 2, true>), grid, block, 0, stream, a); break;
-        }
-        if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
-        return launch_reduce(a, epi, splits, stream);
-    } else {
-        switch (epi) {
-        case 0: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 0, false>), grid, block, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 1, false>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((lut6_gemm_kernel<BN, BM, WN_W, WM_W, 2, false>), grid, block, 0, stream, a); break;
-        }
-    }
-    return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
-}
-
 // Launch the 256 x 256 tile kernel, fused or on the expanded weight.
 template <bool SPLIT>
 void launch_tiles_t(const GemmArgs& a, bool two_pass, int epilogue, bool scaled, dim3 grid, hipStream_t stream)
@@ -1599,7 +1364,32 @@ void launch_tiles(const GemmArgs& a, bool two_pass, int epilogue, bool scaled, b
     else launch_tiles_t<false>(a, two_pass, epilogue, scaled, grid, stream);
 }
 
+// Which kernels lut6_linear runs for a (valid) shape: the weight-streaming
+// kernel for few tokens, the fused tile kernel, or weight expansion plus the
+// FP16 GEMM for many tokens (when the expanded weight fits 31-bit offsets).
+int choose_path(int64_t L, int64_t K, int64_t N, int epilogue)
+{
+    if (L <= 192) return LUT6_PATH_STREAM;
+    if (L < EXPAND_MIN_L) return LUT6_PATH_FUSED;
+    const int64_t n_half = epilogue == 2 ? N / 2 : N;
+    const int64_t bn_cov = epilogue == 2 ? 128 : 256;
+    const int64_t tiles_n = (n_half + bn_cov - 1) / bn_cov;
+    const size_t w16_bytes = (size_t)tiles_n * 8 * (K / BK + 1) * 4096;
+    return w16_bytes <= (size_t)INT32_MAX ? LUT6_PATH_EXPANDED : LUT6_PATH_FUSED;
+}
+
 }  // namespace
+
+extern "C" int lut6_linear_path(int64_t L, int64_t K, int64_t N, int epilogue)
+{
+    if (L < 0 || K <= 0 || N <= 0 || K % 64 || N % 16) return -LUT6_E_SHAPE;
+    if (L > INT32_MAX || K > INT32_MAX || N > INT32_MAX) return -LUT6_E_SHAPE;
+    if (epilogue < 0 || epilogue > 2) return -LUT6_E_EPILOGUE;
+    if (epilogue == LUT6_EPI_SILU_MUL_F16 && N % 32) return -LUT6_E_SHAPE;
+    if ((size_t)L * K * 2 >= ((size_t)1 << 31) || (size_t)N * (K / 4 * 3) >= ((size_t)1 << 31))
+        return -LUT6_E_SHAPE;
+    return choose_path(L, K, N, epilogue);
+}
 
 extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tables, void* y,
                            int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
@@ -1637,7 +1427,8 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
     a.inv_scale = 1.0f / in_scale;
 
     const int chunks = (int)(K / BK);
-    if (L <= 192) {
+    const int path = choose_path(L, K, N, epilogue);
+    if (path == LUT6_PATH_STREAM) {
         // weight-streaming regime: 64-channel x 128-token tiles, K split so
         // that about 256 workgroups (one per CU) stream the weight, each wave
         // holding at most S_CH chunks
@@ -1709,7 +1500,7 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
     // fused kernel
     const int tiles_n = tiles / tiles_m;
     const size_t w16_bytes = (size_t)tiles_n * 8 * (chunks + 1) * 4096;   // whole tiles, fragment order
-    const bool two_pass = L >= EXPAND_MIN_L && w16_bytes <= (size_t)INT32_MAX;
+    const bool two_pass = path == LUT6_PATH_EXPANDED;
     if (two_pass) {
         void* w16 = nullptr;
         const int st = workspace_for(stream, WS_EXPANDED, w16_bytes, &w16);

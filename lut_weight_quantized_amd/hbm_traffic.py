@@ -47,10 +47,16 @@ def source_sha() -> str:
 
 
 def classify(name: str) -> str | None:
-    """bench.py's kernel class of a LUT-6 kernel name, None for anything else."""
+    """bench.py's kernel class of a LUT-6 kernel name, None for anything else.
+
+    "reduce" (a split-K reduction, after its GEMM) and "expand" (the weight
+    expansion, before its GEMM) belong to the neighbouring GEMM's launch."""
     if "lut6_stream_reduce_kernel" in name or "lut6_reduce_kernel" in name:
         return "reduce"
-    for kind, regime in (("lut6_tile256_kernel<", "tiled"), ("lut6_stream_kernel<", "stream")):
+    if "lut6_expand_kernel" in name:
+        return "expand"
+    for kind, regime in (("lut6_expanded_gemm_kernel<", "expanded"), ("lut6_tile256_kernel<", "fused"),
+                         ("lut6_stream_kernel<", "stream")):
         if kind in name:
             epi = name.split(kind, 1)[1].split(",", 1)[0].strip()
             return f"{regime}_" + {"0": "f32", "1": "f16", "2": "silu"}[epi]
@@ -115,18 +121,23 @@ def main() -> int:
     fetch_factor = COPY_BYTES / (fetch[-1][1] * 1024)
     write_factor = COPY_BYTES / (write[-1][1] * 1024)
 
-    # LUT-6 dispatches: layer 0's launches first, then layer 3's; a GEMM and
-    # its reduction (if any) are consecutive dispatches
+    # LUT-6 dispatches: layer 0's launches first, then layer 3's; a GEMM, the
+    # weight expansion before it and the reduction after it (if any) are
+    # consecutive dispatches
     lut = [(n, f * 1024 * fetch_factor, w * 1024 * write_factor)
            for (n, f), (_, w) in zip(fetch[:-1], write[:-1]) if classify(n) is not None]
     launches = []                      # [class, bytes read, bytes written]
+    pending = [0.0, 0.0]               # an expansion waiting for its GEMM
     for n, rb, wb in lut:
         c = classify(n)
         if c == "reduce":
             launches[-1][1] += rb
             launches[-1][2] += wb
+        elif c == "expand":
+            pending = [pending[0] + rb, pending[1] + wb]
         else:
-            launches.append([c, rb, wb])
+            launches.append([c, rb + pending[0], wb + pending[1]])
+            pending = [0.0, 0.0]
     if len(launches) != 8:
         raise RuntimeError(f"expected 8 GEMM launches (4 per layer), saw {len(launches)}")
     per_class: dict[str, dict] = {}

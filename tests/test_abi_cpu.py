@@ -99,6 +99,27 @@ def test_linear_validation(kwargs, status):
     assert _linear(**kwargs) == status
 
 
+def test_linear_path():
+    # few tokens stream the weight; mid-size L runs the fused kernel; from
+    # 1024 tokens the weight is expanded once, unless the expansion would
+    # not fit 31-bit offsets
+    assert lq.linear_path(1, 4096, 4096) == lq.PATH_STREAM
+    assert lq.linear_path(192, 12288, 4096) == lq.PATH_STREAM
+    assert lq.linear_path(193, 4096, 4096) == lq.PATH_FUSED
+    assert lq.linear_path(1023, 4096, 24576, lq.EPI_SILU_MUL_F16) == lq.PATH_FUSED
+    assert lq.linear_path(1024, 4096, 4096) == lq.PATH_EXPANDED
+    assert lq.linear_path(16384, 12288, 4096) == lq.PATH_EXPANDED
+    assert lq.linear_path(16384, 4096, 24576, lq.EPI_SILU_MUL_F16) == lq.PATH_EXPANDED
+    # 8 * (K/64 + 1) * 4 KB per 256-channel tile: 2 GB at N = 96 * 256, K = 2^16
+    assert lq.linear_path(4096, 65536, 96 * 256, lq.EPI_STORE_F32) == lq.PATH_FUSED
+    with pytest.raises(lq.Lut6Error) as e:
+        lq.linear_path(1024, 100, 4096)
+    assert e.value.status == "LUT6_E_SHAPE"
+    with pytest.raises(lq.Lut6Error) as e:
+        lq.linear_path(1024, 4096, 4096, 7)
+    assert e.value.status == "LUT6_E_EPILOGUE"
+
+
 def test_dequant_validation():
     lib = lq.load_library()
     assert lib.lut6_dequant(None, T, Y, 32, 64, None) == 1

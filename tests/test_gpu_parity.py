@@ -124,6 +124,7 @@ SHAPES = [(1, 64, 32), (3, 128, 32), (17, 192, 64), (64, 64, 96), (100, 256, 288
 @pytest.mark.parametrize("epi,s", [(F32, 1.0), (F16, 1.0), (F16, 16.0), (SILU, 1.0), (SILU, 4.0)])
 def test_linear_small(ora, L, K, N, epi, s):
     _say("small", L, K, N, epi, s)
+    assert lq.linear_path(L, K, N, epi) in (lq.PATH_STREAM, lq.PATH_FUSED)
     x, idx, tab = _problem(L, K, N, L * 7 + K + N, sigma=0.5 if s > 1 else 1.0,
                            subnormal=(L % 2 == 1))
     y = gpu_linear(x, idx, tab, epi, s)
@@ -141,6 +142,7 @@ SHAPES_MANY = [(1024, 64, 32), (1029, 256, 160), (1100, 576, 544), (2047, 128, 9
 @pytest.mark.parametrize("epi,s", [(F32, 1.0), (F16, 1.0), (F16, 16.0), (SILU, 1.0), (SILU, 4.0)])
 def test_linear_many_tokens(ora, L, K, N, epi, s):
     _say("many", L, K, N, epi, s)
+    assert lq.linear_path(L, K, N, epi) == lq.PATH_EXPANDED
     x, idx, tab = _problem(L, K, N, L * 5 + K + N, sigma=0.5 if s > 1 else 1.0,
                            subnormal=(L % 2 == 1))
     y = gpu_linear(x, idx, tab, epi, s)
