@@ -175,6 +175,10 @@ constexpr int RAW_BUFFER_WORD3 = 0x00020000;   // gfx9 raw buffer descriptor wor
 // s_waitcnt immediate that waits for vmcnt = 0 and leaves the other counters
 // alone (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int VMCNT0 = 0x0F70;
+// vmcnt <= 16 (bits 3:0 = 0, bits 15:14 = 1), other counters not waited for
+constexpr int VMCNT16 = 0x4F70;
+// lgkmcnt = 0, other counters not waited for
+constexpr int LGKMCNT0 = 0xC07F;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -928,11 +932,15 @@ lut6_stream_kernel(GemmArgs a)
     // them wait for it.  Ring: two 16 KB slots per wave, each one 64-k chunk
     // of 128 token rows (128 bytes per row, 16-byte pieces swizzled by
     // xswz).  After the main loop the ring is reused for the k-quarter
-    // exchange, [fragment F = 4f + j][source wave][group q][lane] of f32x4.
+    // exchange: array f holds channel fragment f, [token fragment j][source
+    // wave][group q][lane] of f32x4.
     __shared__ __attribute__((aligned(1024))) _Float16 s_tab[4 * 64];
-    __shared__ __attribute__((aligned(1024))) uint8_t s_ring[4 * 2 * 16384];
+    // ring slot 0 of every wave in one array, slot 1 in another: the
+    // compiler tracks copies into LDS per array, so reads of one slot then
+    // do not wait for the copy in flight into the other
+    __shared__ __attribute__((aligned(1024))) uint8_t s_ring0[4 * 16384];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_ring1[4 * 16384];
     const uint8_t* const tlb = (const uint8_t*)s_tab;
-    f32x4* const xch = (f32x4*)s_ring;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -990,7 +998,8 @@ lut6_stream_kernel(GemmArgs a)
     int xo[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) xo[s] = r32 * 128 + (((4 * h + s) ^ ((r32 >> 1) & 7)) << 4);
-    uint8_t* const ring = s_ring + wave * 32768;
+    uint8_t* const ring0 = s_ring0 + wave * 16384;
+    uint8_t* const ring1 = s_ring1 + wave * 16384;
 
     f32x16 acc[2][4];
 #pragma unroll
@@ -1000,106 +1009,127 @@ lut6_stream_kernel(GemmArgs a)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
 
-    // table entry first (its LDS store waits only for it), then every packed
-    // word of this wave's k range (at most S_CH chunks), so the whole weight
-    // stream is in flight at once, then the first activation chunk.  Every
-    // load is unconditional (past the range it re-reads a valid chunk): a
-    // conditional load would make the compiler's wait counting pessimistic.
+    // table entry first (its LDS store waits only for it), then, chunk by
+    // chunk, the packed words and the first two activation copies, so the
+    // first chunk can start while the rest of the weight stream is still in
+    // flight.  Every load is unconditional (past the range it re-reads a
+    // valid chunk): a conditional load would make the compiler's wait
+    // counting pessimistic.
     const int nch = w_end - w_begin;
     const int kc_last = max(w_end - 1, 0);
     const _Float16 tv = ((const _Float16*)a.tables)[(trow(16 * (tid >> 6)) / 16) * 64 + (tid & 63)];
     uint32_t PW[S_CH][2][6];
     f16x8 XC[4][4], XN[4][4];      // [token fragment][step], by chunk parity
-    f16x8 WA[2], WB[2];
-#pragma unroll
-    for (int ch = 0; ch < S_CH; ++ch) {
+    f16x8 W[2][2];                 // A fragments by step parity
+    uint32_t G[2][16];             // gathered entries by step parity
+    // packed words of chunk ch: exactly four VMEM instructions (the chunk
+    // waits below count them)
+    auto load_pw = [&](int ch) {
         const int kc = min(w_begin + ch, kc_last);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff0 + kc * 48 + 8 * i, 0, 0);
-            const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff1 + kc * 48 + 8 * i, 0, 0);
-            PW[ch][0][2 * i] = v0[0];
-            PW[ch][0][2 * i + 1] = v0[1];
-            PW[ch][1][2 * i] = v1[0];
-            PW[ch][1][2 * i + 1] = v1[1];
-        }
-    }
+        const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(pr, poff0, kc * 48, 0);
+        const u32x2 b0 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff0 + 16, kc * 48, 0);
+        const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(pr, poff1, kc * 48, 0);
+        const u32x2 b1 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff1 + 16, kc * 48, 0);
+        PW[ch][0][0] = a0[0]; PW[ch][0][1] = a0[1]; PW[ch][0][2] = a0[2]; PW[ch][0][3] = a0[3];
+        PW[ch][0][4] = b0[0]; PW[ch][0][5] = b0[1];
+        PW[ch][1][0] = a1[0]; PW[ch][1][1] = a1[1]; PW[ch][1][2] = a1[2]; PW[ch][1][3] = a1[3];
+        PW[ch][1][4] = b1[0]; PW[ch][1][5] = b1[1];
+    };
+    // keeps the memory operations before it ahead of those after it (the
+    // chunk waits count the operations issued after each copy)
+    auto order = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
     auto copy_x = [&](int kc, int slot) {
-        uint8_t* const st = ring + slot * 16384;
+        uint8_t* const st = slot ? ring1 : ring0;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(st + i * 1024), 16,
-                                                     xg[i] + kc * (BK * 2), 0, 0, 0);
+                                                     xg[i], kc * (BK * 2), 0, 0);
     };
     auto read_x = [&](int slot, f16x8 (&xf)[4][4]) {
-        const uint8_t* const st = ring + slot * 16384;
+        const uint8_t* const st = slot ? ring1 : ring0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int s = 0; s < 4; ++s) xf[j][s] = *(const f16x8*)(st + 4096 * j + xo[s]);
     };
+    static_assert(S_CH == 4, "load order and wait counts assume four chunks per wave");
+    load_pw(0);
+    order();
     copy_x(min(w_begin, kc_last), 0);
+    order();
+    load_pw(1);
+    order();
+    copy_x(min(w_begin + 1, kc_last), 1);
+    order();
+    load_pw(2);
+    load_pw(3);
+    order();
+    // the tables are the only LDS data shared between waves here (each wave
+    // waits for its own ring copies), so a plain barrier after the stores
     s_tab[tid] = tv;
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(LGKMCNT0);
+    lds_barrier();
 
-#define S6_GATHER(NS, P)                                                               \
+    // gather q (0..15) of step NS from packed words P into G[GP]: fragment
+    // q / 8, index 8 NS + q % 8 of the lane's 32
+#define S6_GATHER(GP, NS, P, Q)                                                        \
+    G[GP][Q] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + (Q) % 8>(P[(Q) / 8], (Q) / 8 ? tab1 : tab0))
+    // pack c (0..7) of the next step's A fragments: fragment c / 4, dword c % 4
+#define S6_PACK(GP, C) wn[(C) / 4][(C) % 4] = G[GP][2 * (C)] | (G[GP][2 * (C) + 1] << 16)
+#define S6_MMA(X, S, P, J)                                                             \
     do {                                                                               \
-        g[0] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 0>(P[0], tab0));          \
-        g[1] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 1>(P[0], tab0));          \
-        g[2] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2>(P[0], tab0));          \
-        g[3] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 3>(P[0], tab0));          \
-        g[4] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 4>(P[0], tab0));          \
-        g[5] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 5>(P[0], tab0));          \
-        g[6] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 6>(P[0], tab0));          \
-        g[7] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 7>(P[0], tab0));          \
-        g[8] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 0>(P[1], tab1));          \
-        g[9] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 1>(P[1], tab1));          \
-        g[10] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 2>(P[1], tab1));         \
-        g[11] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 3>(P[1], tab1));         \
-        g[12] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 4>(P[1], tab1));         \
-        g[13] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 5>(P[1], tab1));         \
-        g[14] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 6>(P[1], tab1));         \
-        g[15] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + 7>(P[1], tab1));         \
+        f16x8 xj = X[J][S];                                                            \
+        if constexpr (SCALED) xj = xj * a.scale;                                       \
+        acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[P][0], xj, acc[0][J], 0, 0, 0); \
+        acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[P][1], xj, acc[1][J], 0, 0, 0); \
     } while (0)
-#define S6_COMBINE(W)                                                                  \
+    // step S of a chunk (parity P = S & 1) on activations X: after each MFMA
+    // pair, four gathers for step NS (two steps ahead, packed words NP) and
+    // two packs of the entries gathered one step ago into the next step's
+    // fragments
+#define S6_PAIR(X, S, P, NS, NP, J)                                                    \
     do {                                                                               \
-        W[0] = __builtin_bit_cast(f16x8, u32x4{g[0] | (g[1] << 16), g[2] | (g[3] << 16), \
-                                               g[4] | (g[5] << 16), g[6] | (g[7] << 16)}); \
-        W[1] = __builtin_bit_cast(f16x8, u32x4{g[8] | (g[9] << 16), g[10] | (g[11] << 16), \
-                                               g[12] | (g[13] << 16), g[14] | (g[15] << 16)}); \
-    } while (0)
-    // MFMAs of step S on (W, X[.][S]) while the A entries of step NS are
-    // gathered from words NP into WN
-#define S6_STEP(X, S, W, NS, NP, WN)                                                   \
-    do {                                                                               \
-        uint32_t g[16];                                                                \
-        S6_GATHER(NS, NP);                                                             \
+        S6_MMA(X, S, P, J);                                                            \
+        S6_GATHER(P, NS, NP, 4 * (J) + 0); S6_GATHER(P, NS, NP, 4 * (J) + 1);          \
+        S6_GATHER(P, NS, NP, 4 * (J) + 2); S6_GATHER(P, NS, NP, 4 * (J) + 3);          \
+        S6_PACK(1 - (P), 2 * (J)); S6_PACK(1 - (P), 2 * (J) + 1);                      \
         __builtin_amdgcn_sched_barrier(0);                                             \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                \
-            f16x8 xj = X[j][S];                                                        \
-            if constexpr (SCALED) xj = xj * a.scale;                                   \
-            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[0], xj, acc[0][j], 0, 0, 0); \
-            acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[1], xj, acc[1][j], 0, 0, 0); \
-        }                                                                              \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        S6_COMBINE(WN);                                                                \
     } while (0)
-    // one 64-k chunk CH: once its copy has landed (the only memory operation
-    // still in flight), its activations come from ring slot CH % 2 into X
-    // (the other register set than the previous chunk's, which in-flight
-    // MFMAs may still read); then the next chunk's copy goes to the other
-    // slot, after these reads, so they do not wait for it
+#define S6_STEP(X, S, NS, NP)                                                          \
+    do {                                                                               \
+        uint32_t wn[2][4];                                                             \
+        S6_PAIR(X, S, (S) & 1, NS, NP, 0); S6_PAIR(X, S, (S) & 1, NS, NP, 1);          \
+        S6_PAIR(X, S, (S) & 1, NS, NP, 2); S6_PAIR(X, S, (S) & 1, NS, NP, 3);          \
+        W[1 - ((S) & 1)][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]}); \
+        W[1 - ((S) & 1)][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]}); \
+    } while (0)
+    // one 64-k chunk CH: once its copy has landed (later copies and packed
+    // words may still be in flight), its activations come from ring slot
+    // CH % 2 into X (the other register set than the previous chunk's, which
+    // in-flight MFMAs may still read); once those reads are done the slot
+    // takes chunk CH + 2.  VMEM operations issued after chunk CH's copy:
+    // CH = 0: packed words 1, copy 1, packed words 2 and 3 (4 + 16 + 8);
+    // CH = 1: packed words 2 and 3, copy 2 if any; CH = 2: copy 3 if any.
 #define S6_CHUNK(CH, X, NC)                                                            \
     do {                                                                               \
-        __builtin_amdgcn_s_waitcnt(VMCNT0);                                            \
+        constexpr int later_ = (CH) == 0 ? 28 : (CH) == 1 ? 8 + ((NC) > 2 ? 16 : 0)     \
+                             : (CH) == 2 ? ((NC) > 3 ? 16 : 0) : 0;                    \
+        __builtin_amdgcn_s_waitcnt((later_ & 15) | ((later_ >> 4) << 14) | 0x0F70);    \
         __builtin_amdgcn_sched_barrier(0);                                             \
         read_x((CH) & 1, X);                                                           \
         __builtin_amdgcn_sched_barrier(0);                                             \
-        if constexpr ((CH) + 1 < (NC)) copy_x(w_begin + (CH) + 1, ((CH) + 1) & 1);     \
-        S6_STEP(X, 0, WA, 1, PW[CH], WB);                                              \
-        S6_STEP(X, 1, WB, 2, PW[CH], WA);                                              \
-        S6_STEP(X, 2, WA, 3, PW[CH], WB);                                              \
-        S6_STEP(X, 3, WB, 0, PW[(CH) + 1 < S_CH ? (CH) + 1 : (CH)], WA);               \
+        if constexpr ((CH) + 2 < (NC)) {                                               \
+            __builtin_amdgcn_s_waitcnt(LGKMCNT0);                                      \
+            copy_x(w_begin + (CH) + 2, (CH) & 1);                                      \
+            order();                                                                   \
+        }                                                                              \
+        S6_STEP(X, 0, 2, PW[CH]);                                                      \
+        S6_STEP(X, 1, 3, PW[CH]);                                                      \
+        S6_STEP(X, 2, 0, PW[(CH) + 1 < S_CH ? (CH) + 1 : (CH)]);                       \
+        S6_STEP(X, 3, 1, PW[(CH) + 1 < S_CH ? (CH) + 1 : (CH)]);                       \
     } while (0)
 
     // straight-line code for each chunk count: a branch around one chunk
@@ -1107,16 +1137,26 @@ lut6_stream_kernel(GemmArgs a)
     auto run = [&](auto nc) __attribute__((always_inline)) {
         constexpr int NC = decltype(nc)::value;
         {
-            uint32_t g[16];
-            S6_GATHER(0, PW[0]);
-            S6_COMBINE(WA);
+            // step 0's fragments, step 1's entries
+            uint32_t wn[2][4];
+            S6_GATHER(0, 0, PW[0], 0); S6_GATHER(0, 0, PW[0], 1); S6_GATHER(0, 0, PW[0], 2); S6_GATHER(0, 0, PW[0], 3);
+            S6_GATHER(0, 0, PW[0], 4); S6_GATHER(0, 0, PW[0], 5); S6_GATHER(0, 0, PW[0], 6); S6_GATHER(0, 0, PW[0], 7);
+            S6_GATHER(0, 0, PW[0], 8); S6_GATHER(0, 0, PW[0], 9); S6_GATHER(0, 0, PW[0], 10); S6_GATHER(0, 0, PW[0], 11);
+            S6_GATHER(0, 0, PW[0], 12); S6_GATHER(0, 0, PW[0], 13); S6_GATHER(0, 0, PW[0], 14); S6_GATHER(0, 0, PW[0], 15);
+            S6_GATHER(1, 1, PW[0], 0); S6_GATHER(1, 1, PW[0], 1); S6_GATHER(1, 1, PW[0], 2); S6_GATHER(1, 1, PW[0], 3);
+            S6_GATHER(1, 1, PW[0], 4); S6_GATHER(1, 1, PW[0], 5); S6_GATHER(1, 1, PW[0], 6); S6_GATHER(1, 1, PW[0], 7);
+            S6_GATHER(1, 1, PW[0], 8); S6_GATHER(1, 1, PW[0], 9); S6_GATHER(1, 1, PW[0], 10); S6_GATHER(1, 1, PW[0], 11);
+            S6_GATHER(1, 1, PW[0], 12); S6_GATHER(1, 1, PW[0], 13); S6_GATHER(1, 1, PW[0], 14); S6_GATHER(1, 1, PW[0], 15);
+            S6_PACK(0, 0); S6_PACK(0, 1); S6_PACK(0, 2); S6_PACK(0, 3);
+            S6_PACK(0, 4); S6_PACK(0, 5); S6_PACK(0, 6); S6_PACK(0, 7);
+            W[0][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]});
+            W[0][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]});
         }
         S6_CHUNK(0, XC, NC);
         if constexpr (NC > 1) S6_CHUNK(1, XN, NC);
         if constexpr (NC > 2) S6_CHUNK(2, XC, NC);
         if constexpr (NC > 3) S6_CHUNK(3, XN, NC);
     };
-    static_assert(S_CH == 4, "one case per chunk count");
     switch (nch) {
     case 4: run(std::integral_constant<int, 4>{}); break;
     case 3: run(std::integral_constant<int, 3>{}); break;
@@ -1126,7 +1166,9 @@ lut6_stream_kernel(GemmArgs a)
     }
 #undef S6_CHUNK
 #undef S6_STEP
-#undef S6_COMBINE
+#undef S6_PAIR
+#undef S6_MMA
+#undef S6_PACK
 #undef S6_GATHER
 
     // every copy has landed and every wave is done with its ring before the
@@ -1144,7 +1186,7 @@ lut6_stream_kernel(GemmArgs a)
         for (int f = 0; f < 2; ++f)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                xch[(((4 * f + j) * 4 + wave) * 4 + q) * 64 + lane] =
+                (f ? (f32x4*)s_ring1 : (f32x4*)s_ring0)[((j * 4 + wave) * 4 + q) * 64 + lane] =
                     f32x4{acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2], acc[f][j][4 * q + 3]};
     }
     __syncthreads();
@@ -1160,8 +1202,8 @@ lut6_stream_kernel(GemmArgs a)
                     v0 = f32x4{acc[0][j][4 * q], acc[0][j][4 * q + 1], acc[0][j][4 * q + 2], acc[0][j][4 * q + 3]};
                     v1 = f32x4{acc[1][j][4 * q], acc[1][j][4 * q + 1], acc[1][j][4 * q + 2], acc[1][j][4 * q + 3]};
                 } else {
-                    v0 = xch[(((0 + j) * 4 + src) * 4 + q) * 64 + lane];
-                    v1 = xch[(((4 + j) * 4 + src) * 4 + q) * 64 + lane];
+                    v0 = ((const f32x4*)s_ring0)[((j * 4 + src) * 4 + q) * 64 + lane];
+                    v1 = ((const f32x4*)s_ring1)[((j * 4 + src) * 4 + q) * 64 + lane];
                 }
                 s0 = src == 0 ? v0 : s0 + v0;
                 s1 = src == 0 ? v1 : s1 + v1;
