@@ -16,12 +16,14 @@
 //     24 contiguous packed bytes (a 192-bit little-endian word).
 //   * Tables sit in LDS, 128 bytes each; a lookup is one shift or funnel
 //     shift, one v_and_or_b32 into an LDS byte offset and one ds_read_u16,
-//     a bit copy (dequantisation is exact).
+//     a bit copy (dequantisation is exact).  The streaming kernel uses
+//     4096-word pair tables instead (two consecutive k per lookup).
 //   * Three paths by token count (lut6_linear_path):
-//       - L <= 192, lut6_stream_kernel: each weight serves few tokens, so K
-//         is split across workgroups until ~256 of them (one per CU) stream
-//         the packed weight; partial sums are added by a second kernel in a
-//         fixed order (no atomics, bit-identical run to run).
+//       - L <= 192, lut6_stream_kernel: each weight serves few tokens;
+//         64-token x 32-channel tiles over the whole K range (one kernel,
+//         outputs finished in place), K split into slices added by a second
+//         kernel in a fixed order only when the tiles are too few to fill
+//         the CUs (no atomics, bit-identical run to run).
 //       - 192 < L < 1024, lut6_tile256_kernel: 256 x 256 tiles, four waves
 //         (one per SIMD, 64 x 256 accumulators each); packed words go
 //         straight to registers, activations through three LDS stages, and
@@ -220,6 +222,40 @@ __device__ __forceinline__ uint32_t entry_off(const uint32_t (&p)[6], uint32_t t
     else
         v = __builtin_amdgcn_alignbit(p[w + 1], p[w], o - 1);
     return and_or_7e(v, tab);
+}
+
+// (v & 0x3ffc) | base in one instruction.
+__device__ __forceinline__ uint32_t and_or_3ffc(uint32_t v, uint32_t base)
+{
+#if __HIP_DEVICE_COMPILE__
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(0x3ffcu), "v"(base));
+    return r;
+#else
+    return (v & 0x3ffcu) | base;
+#endif
+}
+
+// Byte offset of a pair-table word in a 16 KB-aligned LDS pair table at
+// byte offset tab.  The word for the 12-bit field at bit B of the 192-bit
+// little-endian word p (indices i0 at bits B .. B+5 and i1 at B+6 .. B+11,
+// two consecutive k) is entry i0 | i1 << 6, holding T[i0] in its low half
+// and T[i1] in its high half: the field is shifted to bits 2 .. 13 (one
+// shift or funnel shift), then masked and merged with the table offset.
+template <int B>
+__device__ __forceinline__ uint32_t pair_off(const uint32_t (&p)[6], uint32_t tab)
+{
+    constexpr int w = B >> 5, o = B & 31;
+    uint32_t v;
+    if constexpr (o == 0 && w == 0)
+        v = p[0] << 2;
+    else if constexpr (o == 0)
+        v = __builtin_amdgcn_alignbit(p[w], p[w - 1], 30);
+    else if constexpr (o <= 20)
+        v = p[w] >> (o - 2);
+    else
+        v = __builtin_amdgcn_alignbit(p[w + 1], p[w], o - 2);
+    return and_or_3ffc(v, tab);
 }
 
 // Global weight row of tile row t (0..255) of channel tile tn.  Tile row
@@ -863,84 +899,43 @@ lut6_expand_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restric
 
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel for few tokens (L <= 192).  Every weight serves at
-// most 192 tokens here, so one read of the packed weight from HBM is the
-// bound, and K is split across workgroups to spread that read over all CUs.
-// A workgroup owns 64 channels x 128 tokens over one K slice and its four
-// waves split the slice again, four ways: each wave contracts all 64
-// channels (two 32-row A fragments) with all 128 tokens (four 32-token B
-// fragments) on v_mfma_f32_32x32x16_f16, 128 accumulation registers.  No two
-// waves read the same activations or packed bytes, so the main loop has no
-// barrier and no LDS staging: activations and packed words go from global
-// memory straight into registers, and only the four tables sit in LDS.  The
-// next chunk's activations load while the current chunk multiplies; the A
-// entries of the next MFMA step are gathered while the current step
-// multiplies.
+// most 192 tokens here, so streaming the packed weight once from HBM, and
+// the activations from L2, bound the kernel.  A workgroup owns 32 channels
+// (one A fragment: two tables) x 64 tokens (two B fragments) over the whole
+// K range, so that the outputs leave the kernel finished: no partial sums,
+// no second kernel (a launch costs more than the whole weight read at this
+// size).  With 64 tokens per tile the activation re-reads from L2 (one per
+// 32 channels) stay within what 256 CUs draw from their L2s while the packed
+// weight streams once, and the A fragment of each MFMA step serves two
+// MFMAs.  The four waves split K four ways and meet in LDS at the end.
 //
-// The four k quarters meet in LDS and are added in wave order; wave w
-// finishes token fragment w (both channel fragments).  With one K slice the
-// result goes straight to y; otherwise each workgroup writes its 32 KB
-// partial in accumulator order (1 KB per store instruction) and a second
-// kernel adds the slices in a fixed order.
+// Lookups use pair tables: entry i0 | i1 << 6 of a 4096-word LDS table holds
+// T[i0] and T[i1], so two consecutive k of one channel cost one 12-bit field
+// extraction (shift, v_and_or_b32) and one ds_read_b32, and the word is
+// already the packed FP16 pair an MFMA fragment takes.  Activations go
+// through per-wave LDS rings by buffer->LDS copies (whole 128-byte rows per
+// instruction), four 64-k chunks in flight per wave; each ring slot is its
+// own LDS array, so the compiler's wait for a slot's copy does not also wait
+// for the copies into the other slots.
+//
+// Few tiles (small N or L) split K into slices with FP32 partial planes
+// added by lut6_reduce_kernel in a fixed order.
 // ---------------------------------------------------------------------------
-constexpr int S_BN = 64, S_BM = 128;
-constexpr int S_CH = 4;                  // most 64-k chunks per wave
-constexpr int S_PART = 2048;             // f32x4 per workgroup partial: [fragment 8][group 4][lane 64]
-
-// Output of accumulator group q of token fragment j: v0 from channel
-// fragment 0, v1 from channel fragment 1 (for SiLU: gate and up).  Lane
-// `lane` holds token 32j + lane % 32 and channels 8q + 4 (lane / 32) + 0..3
-// of each fragment.
-template <int EPI>
-__device__ __forceinline__ void stream_out(const GemmArgs& a, int tm, int tn, int j, int q,
-                                           int lane, f32x4 v0, f32x4 v1)
-{
-    const int tok = tm * S_BM + 32 * j + (lane & 31);
-    if (tok >= a.L) return;
-    const int c = 8 * q + 4 * (lane >> 5);
-    if constexpr (EPI == 2) {
-        const int jj = tn * (S_BN / 2) + c;
-        if (jj >= a.N / 2) return;
-        f16x4 hv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            hv[e] = (_Float16)(silu_f32(v0[e] * a.inv_scale) * (v1[e] * a.inv_scale));
-        *(f16x4*)((_Float16*)a.y + (size_t)tok * (a.N / 2) + jj) = hv;
-    } else {
-        const int n0 = tn * S_BN + c, n1 = n0 + 32;
-        const f32x4 u0 = v0 * a.inv_scale, u1 = v1 * a.inv_scale;
-        if constexpr (EPI == 0) {
-            if (n0 < a.N) *(f32x4*)((float*)a.y + (size_t)tok * a.N + n0) = u0;
-            if (n1 < a.N) *(f32x4*)((float*)a.y + (size_t)tok * a.N + n1) = u1;
-        } else {
-            if (n0 < a.N)
-                *(f16x4*)((_Float16*)a.y + (size_t)tok * a.N + n0) =
-                    f16x4{(_Float16)u0[0], (_Float16)u0[1], (_Float16)u0[2], (_Float16)u0[3]};
-            if (n1 < a.N)
-                *(f16x4*)((_Float16*)a.y + (size_t)tok * a.N + n1) =
-                    f16x4{(_Float16)u1[0], (_Float16)u1[1], (_Float16)u1[2], (_Float16)u1[3]};
-        }
-    }
-}
+constexpr int S_BN = 32, S_BM = 64;
+constexpr int S_WAVE_SLOT = 8192;        // one 64-k chunk of 64 token rows
+constexpr int S_SLOT = 4 * S_WAVE_SLOT;  // one ring slot of all four waves
+constexpr int S_MIN_CHUNKS = 16;         // fewest 64-k chunks per K slice
 
 template <int EPI, bool SCALED, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
 lut6_stream_kernel(GemmArgs a)
 {
-    // The four tables live in their own LDS array, apart from the activation
-    // ring that buffer->LDS copies write, so the compiler can see that the
-    // gathers never read what an in-flight copy writes and does not make
-    // them wait for it.  Ring: two 16 KB slots per wave, each one 64-k chunk
-    // of 128 token rows (128 bytes per row, 16-byte pieces swizzled by
-    // xswz).  After the main loop the ring is reused for the k-quarter
-    // exchange: array f holds channel fragment f, [token fragment j][source
-    // wave][group q][lane] of f32x4.
-    __shared__ __attribute__((aligned(1024))) _Float16 s_tab[4 * 64];
-    // ring slot 0 of every wave in one array, slot 1 in another: the
-    // compiler tracks copies into LDS per array, so reads of one slot then
-    // do not wait for the copy in flight into the other
-    __shared__ __attribute__((aligned(1024))) uint8_t s_ring0[4 * 16384];
-    __shared__ __attribute__((aligned(1024))) uint8_t s_ring1[4 * 16384];
-    const uint8_t* const tlb = (const uint8_t*)s_tab;
+    // pair tables (slot s: tile rows 16s .. 16s+15), then the four ring slots
+    __shared__ __attribute__((aligned(1024))) uint8_t s_pair[2 * 16384];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_x0[S_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_x1[S_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_x2[S_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_x3[S_SLOT];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -949,7 +944,7 @@ lut6_stream_kernel(GemmArgs a)
     const int row_bytes = K / 4 * 3;
 
     // one-dimensional grid; after the remap consecutive indices (one XCD)
-    // are the K slices of one tile
+    // are the token tiles, then the K slices, of one channel tile
     const int splits = gridDim.x / a.n_tiles;
     const int r = xcd_remap(blockIdx.x, gridDim.x);
     const int t = r / splits, split = r % splits;
@@ -959,261 +954,264 @@ lut6_stream_kernel(GemmArgs a)
     const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
     const int per_wave = (kc_end - kc_begin + 3) / 4;
     const int w_begin = min(kc_begin + wave * per_wave, kc_end);
-    const int w_end = min(w_begin + per_wave, kc_end);
+    const int nch = min(w_begin + per_wave, kc_end) - w_begin;
+    const int kc_last = max(w_begin + nch - 1, 0);
 
-    // global weight row of tile row tr = 32f + r (clamped into range; such
-    // rows are computed on a copy of the last row and never stored)
-    auto trow = [&](int tr) -> int {
+    // global weight row of tile row i (clamped into range; such rows are
+    // computed on a copy of the last row and never stored): for SiLU, rows
+    // 0..15 are gate channels and 16..31 the matching up channels
+    auto trow = [&](int i) -> int {
         if constexpr (EPI == 2) {
-            const int f = tr >> 5, rr = tr & 31;
-            const int j = min(tn * (S_BN / 2) + rr, N / 2 - 1);
-            return f ? N / 2 + j : j;
+            const int j = min(tn * (S_BN / 2) + (i & 15), N / 2 - 1);
+            return i >= 16 ? N / 2 + j : j;
         } else {
-            return min(tn * S_BN + tr, N - 1);
+            return min(tn * S_BN + i, N - 1);
         }
     };
-    // LDS table slot of tile rows 16s .. 16s+15 is s; the two tables a lane
-    // group reads sit 128 bytes apart (all 64 banks, no conflicts)
-    const uint32_t tab0 = (uint32_t)((0 + (r32 >> 4)) * 128);
-    const uint32_t tab1 = (uint32_t)((2 + (r32 >> 4)) * 128);
+
+    // Table entries for the pair tables, loaded first: this thread builds
+    // words 16 tid .. 16 tid + 15 of both slots, whose low halves are
+    // entries 16 (tid % 4) .. +15 and whose high half is entry tid / 4.
+    u32x4 tlo[2][2];
+    uint32_t thi[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint16_t* T = a.tables + (size_t)(trow(16 * s) / 16) * 64;
+        tlo[s][0] = *(const u32x4*)(T + 16 * (tid & 3));
+        tlo[s][1] = *(const u32x4*)(T + 16 * (tid & 3) + 8);
+        thi[s] = T[tid >> 2];
+    }
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.x, (short)0, (int)((size_t)L * K * 2), RAW_BUFFER_WORD3);
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.packed, (short)0, (int)((size_t)N * row_bytes), RAW_BUFFER_WORD3);
-    const int poff0 = trow(r32) * row_bytes + 24 * h;
-    const int poff1 = trow(32 + r32) * row_bytes + 24 * h;
-
+    const int poff = trow(r32) * row_bytes + 24 * h;
     // activation copies: instruction i fills ring rows 8i .. 8i+7, lane l
-    // row 8i + l / 8, slot l % 8 (the 16-byte piece (l % 8) ^ swizzle), so
-    // one instruction reads eight 128-byte row segments
-    int xg[16];
+    // row 8i + l / 8, position l % 8, which holds the row's 16-byte piece
+    // (l % 8) ^ ((row >> 1) & 7)
+    int xg[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
         const int row = 8 * i + (lane >> 3);
         xg[i] = min(m0 + row, L - 1) * (K * 2) + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
     }
-    // this lane's B-fragment pieces in a slot: token 32j + r32, piece 4h + s
-    // (lane group h takes k 32h .. 32h+31 of the chunk, as for the weights)
+    // this lane's B-fragment pieces: token 32j + r32, piece 4h + s (lane
+    // group h takes k 32h .. 32h + 31 of the chunk, as for the weights)
     int xo[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xo[s] = r32 * 128 + (((4 * h + s) ^ ((r32 >> 1) & 7)) << 4);
-    uint8_t* const ring0 = s_ring0 + wave * 16384;
-    uint8_t* const ring1 = s_ring1 + wave * 16384;
+    for (int s = 0; s < 4; ++s) xo[s] = wave * S_WAVE_SLOT + r32 * 128 + (((4 * h + s) ^ ((r32 >> 1) & 7)) << 4);
 
-    f32x16 acc[2][4];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
-
-    // table entry first (its LDS store waits only for it), then, chunk by
-    // chunk, the packed words and the first two activation copies, so the
-    // first chunk can start while the rest of the weight stream is still in
-    // flight.  Every load is unconditional (past the range it re-reads a
-    // valid chunk): a conditional load would make the compiler's wait
-    // counting pessimistic.
-    const int nch = w_end - w_begin;
-    const int kc_last = max(w_end - 1, 0);
-    const _Float16 tv = ((const _Float16*)a.tables)[(trow(16 * (tid >> 6)) / 16) * 64 + (tid & 63)];
-    uint32_t PW[S_CH][2][6];
-    f16x8 XC[4][4], XN[4][4];      // [token fragment][step], by chunk parity
-    f16x8 W[2][2];                 // A fragments by step parity
-    uint32_t G[2][16];             // gathered entries by step parity
-    // packed words of chunk ch: exactly four VMEM instructions (the chunk
-    // waits below count them)
-    auto load_pw = [&](int ch) {
+    auto slot_base = [&](auto sc) -> uint8_t* {
+        constexpr int SL = decltype(sc)::value;
+        return SL == 0 ? s_x0 : SL == 1 ? s_x1 : SL == 2 ? s_x2 : s_x3;
+    };
+    // copies and packed words of chunk ch; past the range (only in the
+    // prologue) a valid chunk is re-read and never used
+    auto copy_x = [&](int ch, auto sc) {
+        uint8_t* const st = slot_base(sc) + wave * S_WAVE_SLOT;
         const int kc = min(w_begin + ch, kc_last);
-        const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(pr, poff0, kc * 48, 0);
-        const u32x2 b0 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff0 + 16, kc * 48, 0);
-        const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(pr, poff1, kc * 48, 0);
-        const u32x2 b1 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff1 + 16, kc * 48, 0);
-        PW[ch][0][0] = a0[0]; PW[ch][0][1] = a0[1]; PW[ch][0][2] = a0[2]; PW[ch][0][3] = a0[3];
-        PW[ch][0][4] = b0[0]; PW[ch][0][5] = b0[1];
-        PW[ch][1][0] = a1[0]; PW[ch][1][1] = a1[1]; PW[ch][1][2] = a1[2]; PW[ch][1][3] = a1[3];
-        PW[ch][1][4] = b1[0]; PW[ch][1][5] = b1[1];
-    };
-    // keeps the memory operations before it ahead of those after it (the
-    // chunk waits count the operations issued after each copy)
-    auto order = [] {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto copy_x = [&](int kc, int slot) {
-        uint8_t* const st = slot ? ring1 : ring0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(st + i * 1024), 16,
-                                                     xg[i], kc * (BK * 2), 0, 0);
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(st + i * 1024), 16, xg[i],
+                                                     kc * (BK * 2), 0, 0);
     };
-    auto read_x = [&](int slot, f16x8 (&xf)[4][4]) {
-        const uint8_t* const st = slot ? ring1 : ring0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) xf[j][s] = *(const f16x8*)(st + 4096 * j + xo[s]);
+    uint32_t PW[4][6];
+    auto load_pw = [&](int ch, auto sc) {
+        constexpr int SL = decltype(sc)::value;
+        const int kc = min(w_begin + ch, kc_last);
+        const u32x4 q4 = __builtin_amdgcn_raw_buffer_load_b128(pr, poff, kc * 48, 0);
+        const u32x2 q2 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff + 16, kc * 48, 0);
+        PW[SL][0] = q4[0]; PW[SL][1] = q4[1]; PW[SL][2] = q4[2]; PW[SL][3] = q4[3];
+        PW[SL][4] = q2[0]; PW[SL][5] = q2[1];
     };
-    static_assert(S_CH == 4, "load order and wait counts assume four chunks per wave");
-    load_pw(0);
-    order();
-    copy_x(min(w_begin, kc_last), 0);
-    order();
-    load_pw(1);
-    order();
-    copy_x(min(w_begin + 1, kc_last), 1);
-    order();
-    load_pw(2);
-    load_pw(3);
-    order();
-    // the tables are the only LDS data shared between waves here (each wave
-    // waits for its own ring copies), so a plain barrier after the stores
-    s_tab[tid] = tv;
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    // every prologue load is unconditional, so the main loop is entered
+    // with the same loads in flight, in the same order, as it leaves each
+    // iteration (the compiler's waits stay exact)
+    load_pw(0, C0{});
+    copy_x(0, C0{});
+    load_pw(1, C1{});
+    copy_x(1, C1{});
+    load_pw(2, C2{});
+    copy_x(2, C2{});
+    load_pw(3, C3{});
+    copy_x(3, C3{});
+
+    // pair tables: word p of slot s = T[p % 64] | T[p / 64] << 16
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t hi = thi[s] << 16;
+        uint32_t wv[16];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            const uint32_t lo2 = tlo[s][d >> 2][d & 3];
+            wv[2 * d] = (lo2 & 0xffffu) | hi;
+            wv[2 * d + 1] = (lo2 >> 16) | hi;
+        }
+        u32x4* dst = (u32x4*)(s_pair + s * 16384 + tid * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = u32x4{wv[4 * q], wv[4 * q + 1], wv[4 * q + 2], wv[4 * q + 3]};
+    }
+    // the pair tables are the only LDS data shared between waves (each wave
+    // waits for its own ring copies): a plain barrier after the stores
     __builtin_amdgcn_s_waitcnt(LGKMCNT0);
     lds_barrier();
 
-    // gather q (0..15) of step NS from packed words P into G[GP]: fragment
-    // q / 8, index 8 NS + q % 8 of the lane's 32
-#define S6_GATHER(GP, NS, P, Q)                                                        \
-    G[GP][Q] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + (Q) % 8>(P[(Q) / 8], (Q) / 8 ? tab1 : tab0))
-    // pack c (0..7) of the next step's A fragments: fragment c / 4, dword c % 4
-#define S6_PACK(GP, C) wn[(C) / 4][(C) % 4] = G[GP][2 * (C)] | (G[GP][2 * (C) + 1] << 16)
-#define S6_MMA(X, S, P, J)                                                             \
-    do {                                                                               \
-        f16x8 xj = X[J][S];                                                            \
-        if constexpr (SCALED) xj = xj * a.scale;                                       \
-        acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[P][0], xj, acc[0][J], 0, 0, 0); \
-        acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[P][1], xj, acc[1][J], 0, 0, 0); \
-    } while (0)
-    // step S of a chunk (parity P = S & 1) on activations X: after each MFMA
-    // pair, four gathers for step NS (two steps ahead, packed words NP) and
-    // two packs of the entries gathered one step ago into the next step's
-    // fragments
-#define S6_PAIR(X, S, P, NS, NP, J)                                                    \
-    do {                                                                               \
-        S6_MMA(X, S, P, J);                                                            \
-        S6_GATHER(P, NS, NP, 4 * (J) + 0); S6_GATHER(P, NS, NP, 4 * (J) + 1);          \
-        S6_GATHER(P, NS, NP, 4 * (J) + 2); S6_GATHER(P, NS, NP, 4 * (J) + 3);          \
-        S6_PACK(1 - (P), 2 * (J)); S6_PACK(1 - (P), 2 * (J) + 1);                      \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-    } while (0)
-#define S6_STEP(X, S, NS, NP)                                                          \
-    do {                                                                               \
-        uint32_t wn[2][4];                                                             \
-        S6_PAIR(X, S, (S) & 1, NS, NP, 0); S6_PAIR(X, S, (S) & 1, NS, NP, 1);          \
-        S6_PAIR(X, S, (S) & 1, NS, NP, 2); S6_PAIR(X, S, (S) & 1, NS, NP, 3);          \
-        W[1 - ((S) & 1)][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]}); \
-        W[1 - ((S) & 1)][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]}); \
-    } while (0)
-    // one 64-k chunk CH: once its copy has landed (later copies and packed
-    // words may still be in flight), its activations come from ring slot
-    // CH % 2 into X (the other register set than the previous chunk's, which
-    // in-flight MFMAs may still read); once those reads are done the slot
-    // takes chunk CH + 2.  VMEM operations issued after chunk CH's copy:
-    // CH = 0: packed words 1, copy 1, packed words 2 and 3 (4 + 16 + 8);
-    // CH = 1: packed words 2 and 3, copy 2 if any; CH = 2: copy 3 if any.
-#define S6_CHUNK(CH, X, NC)                                                            \
-    do {                                                                               \
-        constexpr int later_ = (CH) == 0 ? 28 : (CH) == 1 ? 8 + ((NC) > 2 ? 16 : 0)     \
-                             : (CH) == 2 ? ((NC) > 3 ? 16 : 0) : 0;                    \
-        __builtin_amdgcn_s_waitcnt((later_ & 15) | ((later_ >> 4) << 14) | 0x0F70);    \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        read_x((CH) & 1, X);                                                           \
-        __builtin_amdgcn_sched_barrier(0);                                             \
-        if constexpr ((CH) + 2 < (NC)) {                                               \
-            __builtin_amdgcn_s_waitcnt(LGKMCNT0);                                      \
-            copy_x(w_begin + (CH) + 2, (CH) & 1);                                      \
-            order();                                                                   \
-        }                                                                              \
-        S6_STEP(X, 0, 2, PW[CH]);                                                      \
-        S6_STEP(X, 1, 3, PW[CH]);                                                      \
-        S6_STEP(X, 2, 0, PW[(CH) + 1 < S_CH ? (CH) + 1 : (CH)]);                       \
-        S6_STEP(X, 3, 1, PW[(CH) + 1 < S_CH ? (CH) + 1 : (CH)]);                       \
-    } while (0)
-
-    // straight-line code for each chunk count: a branch around one chunk
-    // would make the compiler copy every accumulator at the join
-    auto run = [&](auto nc) __attribute__((always_inline)) {
-        constexpr int NC = decltype(nc)::value;
-        {
-            // step 0's fragments, step 1's entries
-            uint32_t wn[2][4];
-            S6_GATHER(0, 0, PW[0], 0); S6_GATHER(0, 0, PW[0], 1); S6_GATHER(0, 0, PW[0], 2); S6_GATHER(0, 0, PW[0], 3);
-            S6_GATHER(0, 0, PW[0], 4); S6_GATHER(0, 0, PW[0], 5); S6_GATHER(0, 0, PW[0], 6); S6_GATHER(0, 0, PW[0], 7);
-            S6_GATHER(0, 0, PW[0], 8); S6_GATHER(0, 0, PW[0], 9); S6_GATHER(0, 0, PW[0], 10); S6_GATHER(0, 0, PW[0], 11);
-            S6_GATHER(0, 0, PW[0], 12); S6_GATHER(0, 0, PW[0], 13); S6_GATHER(0, 0, PW[0], 14); S6_GATHER(0, 0, PW[0], 15);
-            S6_GATHER(1, 1, PW[0], 0); S6_GATHER(1, 1, PW[0], 1); S6_GATHER(1, 1, PW[0], 2); S6_GATHER(1, 1, PW[0], 3);
-            S6_GATHER(1, 1, PW[0], 4); S6_GATHER(1, 1, PW[0], 5); S6_GATHER(1, 1, PW[0], 6); S6_GATHER(1, 1, PW[0], 7);
-            S6_GATHER(1, 1, PW[0], 8); S6_GATHER(1, 1, PW[0], 9); S6_GATHER(1, 1, PW[0], 10); S6_GATHER(1, 1, PW[0], 11);
-            S6_GATHER(1, 1, PW[0], 12); S6_GATHER(1, 1, PW[0], 13); S6_GATHER(1, 1, PW[0], 14); S6_GATHER(1, 1, PW[0], 15);
-            S6_PACK(0, 0); S6_PACK(0, 1); S6_PACK(0, 2); S6_PACK(0, 3);
-            S6_PACK(0, 4); S6_PACK(0, 5); S6_PACK(0, 6); S6_PACK(0, 7);
-            W[0][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]});
-            W[0][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]});
-        }
-        S6_CHUNK(0, XC, NC);
-        if constexpr (NC > 1) S6_CHUNK(1, XN, NC);
-        if constexpr (NC > 2) S6_CHUNK(2, XC, NC);
-        if constexpr (NC > 3) S6_CHUNK(3, XN, NC);
+    // pair table of this lane's channel row
+    const uint32_t tab = (uint32_t)((r32 >> 4) * 16384);
+    // A fragment of step S from packed words P
+    auto gather = [&](const uint32_t (&p)[6], auto stc) -> f16x8 {
+        constexpr int S = decltype(stc)::value;
+        const u32x4 d = {*(const uint32_t*)(s_pair + pair_off<48 * S + 0>(p, tab)),
+                         *(const uint32_t*)(s_pair + pair_off<48 * S + 12>(p, tab)),
+                         *(const uint32_t*)(s_pair + pair_off<48 * S + 24>(p, tab)),
+                         *(const uint32_t*)(s_pair + pair_off<48 * S + 36>(p, tab))};
+        return __builtin_bit_cast(f16x8, d);
     };
-    switch (nch) {
-    case 4: run(std::integral_constant<int, 4>{}); break;
-    case 3: run(std::integral_constant<int, 3>{}); break;
-    case 2: run(std::integral_constant<int, 2>{}); break;
-    case 1: run(std::integral_constant<int, 1>{}); break;
-    default: break;
-    }
-#undef S6_CHUNK
-#undef S6_STEP
-#undef S6_PAIR
-#undef S6_MMA
-#undef S6_PACK
-#undef S6_GATHER
 
-    // every copy has landed and every wave is done with its ring before the
-    // ring becomes the exchange area
+    f32x16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+
+    // chunk c on ring slot SL = c % 4: its B fragments leave the slot, which
+    // then takes chunk c + 4 when PF; its A fragments are gathered one MFMA
+    // step ahead (step 0 during the previous chunk's step 3, from the next
+    // slot's packed words, possibly of a chunk past the range: a harmless
+    // lookup); once its steps are gathered, the packed words of chunk c + 4
+    // (clamped) replace it
+    f16x8 Wc = gather(PW[0], C0{});
+    auto chunk = [&](int c, auto sc, auto pf) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sc)::value, NS = (SL + 1) & 3;
+        const uint8_t* const st = slot_base(sc);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 X[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) X[j][s] = *(const f16x8*)(st + 4096 * j + xo[s]);
+        if constexpr (decltype(pf)::value) {
+            // the slot's reads have completed before the copy may land
+            __builtin_amdgcn_s_waitcnt(LGKMCNT0);
+            copy_x(c + 4, sc);
+        }
+        if constexpr (SCALED) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) X[j][s] = X[j][s] * a.scale;
+        }
+        // the scheduling barriers keep each step's lookups in that step, so
+        // no lookup (and its wait for packed words) is hoisted ahead
+        f16x8 Wn;
+#define S8_STEP(S, NEXT)                                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        Wn = NEXT;                                                                       \
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wc, X[0][S], acc[0], 0, 0, 0);   \
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Wc, X[1][S], acc[1], 0, 0, 0);   \
+        Wc = Wn;
+        S8_STEP(0, gather(PW[SL], C1{}));
+        S8_STEP(1, gather(PW[SL], C2{}));
+        S8_STEP(2, gather(PW[SL], C3{}));
+        S8_STEP(3, gather(PW[NS], C0{}));
+#undef S8_STEP
+        __builtin_amdgcn_sched_barrier(0);
+        load_pw(c + 4, sc);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using Y = std::true_type;
+    using Nn = std::false_type;
+    // G groups of four chunks, then R more: the groups before the last copy
+    // all four successors, the last one only the R that exist
+    const int G = nch >> 2, R = nch & 3;
+    for (int g = 0; g + 1 < G; ++g) {
+        chunk(4 * g + 0, C0{}, Y{});
+        chunk(4 * g + 1, C1{}, Y{});
+        chunk(4 * g + 2, C2{}, Y{});
+        chunk(4 * g + 3, C3{}, Y{});
+    }
+    if (G > 0) {
+        const int c = 4 * (G - 1);
+        switch (R) {
+        case 0: chunk(c, C0{}, Nn{}); chunk(c + 1, C1{}, Nn{}); chunk(c + 2, C2{}, Nn{}); chunk(c + 3, C3{}, Nn{}); break;
+        case 1: chunk(c, C0{}, Y{}); chunk(c + 1, C1{}, Nn{}); chunk(c + 2, C2{}, Nn{}); chunk(c + 3, C3{}, Nn{}); break;
+        case 2: chunk(c, C0{}, Y{}); chunk(c + 1, C1{}, Y{}); chunk(c + 2, C2{}, Nn{}); chunk(c + 3, C3{}, Nn{}); break;
+        default: chunk(c, C0{}, Y{}); chunk(c + 1, C1{}, Y{}); chunk(c + 2, C2{}, Y{}); chunk(c + 3, C3{}, Nn{}); break;
+        }
+    }
+    {
+        const int c = 4 * G;
+        switch (R) {
+        case 1: chunk(c, C0{}, Nn{}); break;
+        case 2: chunk(c, C0{}, Nn{}); chunk(c + 1, C1{}, Nn{}); break;
+        case 3: chunk(c, C0{}, Nn{}); chunk(c + 1, C1{}, Nn{}); chunk(c + 2, C2{}, Nn{}); break;
+        default: break;
+        }
+    }
+
+    // k quarters meet in slot 0 of the ring, [token fragment j][group q]
+    // [source wave][lane] of f32x4; wave 2j + (q & 1) owns (j, q) and adds
+    // the four quarters in wave order.  Every copy has landed and every wave
+    // is done with its ring before the exchange.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    // k quarters: each wave hands the fragments of the three token fragments
-    // it does not finish to their owners, then the owner adds the four
-    // quarters in wave order
+    f32x4* const xa = (f32x4*)s_x0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j == wave) continue;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                (f ? (f32x4*)s_ring1 : (f32x4*)s_ring0)[((j * 4 + wave) * 4 + q) * 64 + lane] =
-                    f32x4{acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2], acc[f][j][4 * q + 3]};
-    }
+        for (int q = 0; q < 4; ++q)
+            if (2 * j + (q & 1) != wave)
+                xa[((j * 4 + q) * 4 + wave) * 64 + lane] =
+                    f32x4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
     __syncthreads();
-    auto finish = [&](auto jc) {
-        constexpr int j = decltype(jc)::value;
+    auto finish = [&](auto wc) {
+        constexpr int w = decltype(wc)::value, j = w >> 1, q0 = w & 1;
+        f32x4 v[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            f32x4 s0, s1;
+        for (int u = 0; u < 2; ++u) {
+            const int q = q0 + 2 * u;
 #pragma unroll
             for (int src = 0; src < 4; ++src) {
-                f32x4 v0, v1;
-                if (src == j) {
-                    v0 = f32x4{acc[0][j][4 * q], acc[0][j][4 * q + 1], acc[0][j][4 * q + 2], acc[0][j][4 * q + 3]};
-                    v1 = f32x4{acc[1][j][4 * q], acc[1][j][4 * q + 1], acc[1][j][4 * q + 2], acc[1][j][4 * q + 3]};
-                } else {
-                    v0 = ((const f32x4*)s_ring0)[((j * 4 + src) * 4 + q) * 64 + lane];
-                    v1 = ((const f32x4*)s_ring1)[((j * 4 + src) * 4 + q) * 64 + lane];
-                }
-                s0 = src == 0 ? v0 : s0 + v0;
-                s1 = src == 0 ? v1 : s1 + v1;
+                const f32x4 o = src == w ? f32x4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]}
+                                         : xa[((j * 4 + q) * 4 + src) * 64 + lane];
+                v[u] = src == 0 ? o : v[u] + o;
             }
+        }
+        // v[u]: rows 8 (q0 + 2u) + 4h + 0..3 of the fragment, token 32j + r32
+        const int tok = m0 + 32 * j + r32;
+        if (tok >= L) return;
+        if constexpr (EPI == 2) {
+            const int c = tn * (S_BN / 2) + 8 * q0 + 4 * h;   // gate rows, up rows 16 further
             if constexpr (SPLIT) {
-                f32x4* part = (f32x4*)a.partial + (size_t)(t * splits + split) * S_PART;
-                part[((0 + j) * 4 + q) * 64 + lane] = s0;
-                part[((4 + j) * 4 + q) * 64 + lane] = s1;
+                float* const pp = a.partial + (size_t)split * L * N + (size_t)tok * N;
+                *(f32x4*)(pp + c) = v[0];
+                *(f32x4*)(pp + N / 2 + c) = v[1];
             } else {
-                stream_out<EPI>(a, tm, tn, j, q, lane, s0, s1);
+                f16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hv[e] = (_Float16)(silu_f32(v[0][e] * a.inv_scale) * (v[1][e] * a.inv_scale));
+                *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + c) = hv;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int c = tn * S_BN + 8 * (q0 + 2 * u) + 4 * h;
+                if (c >= N) continue;
+                if constexpr (SPLIT) {
+                    *(f32x4*)(a.partial + (size_t)split * L * N + (size_t)tok * N + c) = v[u];
+                } else if constexpr (EPI == 0) {
+                    *(f32x4*)((float*)a.y + (size_t)tok * N + c) = v[u] * a.inv_scale;
+                } else {
+                    const f32x4 o = v[u] * a.inv_scale;
+                    *(f16x4*)((_Float16*)a.y + (size_t)tok * N + c) =
+                        f16x4{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
+                }
             }
         }
     };
@@ -1223,26 +1221,6 @@ lut6_stream_kernel(GemmArgs a)
     case 2: finish(std::integral_constant<int, 2>{}); break;
     default: finish(std::integral_constant<int, 3>{}); break;
     }
-}
-
-// Fixed-order sum of the streaming kernel's K-slice partials (accumulator
-// order), then the epilogue.  One thread per lane of one accumulator group:
-// (tile, token fragment j, group q, lane).
-template <int EPI>
-__global__ void __launch_bounds__(256)
-lut6_stream_reduce_kernel(GemmArgs a, int splits)
-{
-    const int g = blockIdx.x * 256 + threadIdx.x;
-    if (g >= a.n_tiles * 1024) return;
-    const int lane = g & 63, q = (g >> 6) & 3, j = (g >> 8) & 3, t = g >> 10;
-    const f32x4* p0 = (const f32x4*)a.partial + (size_t)t * splits * S_PART + (j * 4 + q) * 64 + lane;
-    const f32x4* p1 = p0 + 4 * 4 * 64;     // channel fragment 1
-    f32x4 s0 = p0[0], s1 = p1[0];
-    for (int s = 1; s < splits; ++s) {
-        s0 += p0[(size_t)s * S_PART];
-        s1 += p1[(size_t)s * S_PART];
-    }
-    stream_out<EPI>(a, t % a.tiles_m, t / a.tiles_m, j, q, lane, s0, s1);
 }
 
 // Fixed-order sum of split-K partials, then the epilogue.  One thread per
@@ -1259,12 +1237,23 @@ lut6_reduce_kernel(const float* __restrict__ partial, void* __restrict__ y, int 
     const int tok = (int)(i4 / (n_out / 4));
     const int c = (int)(i4 % (n_out / 4)) * 4;
     const size_t plane = (size_t)L * N;
-    if constexpr (EPI == 2) {
-        f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s) {
-            g += *(const f32x4*)(partial + s * plane + (size_t)tok * N + c);
-            u += *(const f32x4*)(partial + s * plane + (size_t)tok * N + N / 2 + c);
+    // slices four at a time, loaded before the adds (one wait per four);
+    // past the last slice a valid re-read, for which zero is added
+    auto sum = [&](size_t off) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < splits; s += 4) {
+            f32x4 b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                b[i] = *(const f32x4*)(partial + (size_t)min(s + i, splits - 1) * plane + off);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v += s + i < splits ? b[i] : z;
         }
+        return v;
+    };
+    if constexpr (EPI == 2) {
+        f32x4 g = sum((size_t)tok * N + c), u = sum((size_t)tok * N + N / 2 + c);
         g *= inv_scale;
         u *= inv_scale;
         f16x4 h;
@@ -1272,9 +1261,7 @@ lut6_reduce_kernel(const float* __restrict__ partial, void* __restrict__ y, int 
         for (int r = 0; r < 4; ++r) h[r] = (_Float16)(silu_f32(g[r]) * u[r]);
         *(f16x4*)((_Float16*)y + (size_t)tok * n_out + c) = h;
     } else {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s)
-            v += *(const f32x4*)(partial + s * plane + (size_t)tok * N + c);
+        f32x4 v = sum((size_t)tok * N + c);
         v *= inv_scale;
         if constexpr (EPI == 0) {
             *(f32x4*)((float*)y + (size_t)tok * N + c) = v;
@@ -1471,54 +1458,46 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
     const int chunks = (int)(K / BK);
     const int path = choose_path(L, K, N, epilogue);
     if (path == LUT6_PATH_STREAM) {
-        // weight-streaming regime: 64-channel x 128-token tiles, K split so
-        // that about 256 workgroups (one per CU) stream the weight, each wave
-        // holding at most S_CH chunks
+        // weight-streaming regime: 64-token x 32-channel tiles over the whole
+        // K range; K is split into slices (partial planes, fixed-order sum)
+        // only when the tiles would leave most of the 256 CUs idle
         const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
         const int bn_cov = epilogue == 2 ? S_BN / 2 : S_BN;
         const int tiles_m = (int)((L + S_BM - 1) / S_BM);
         const int tiles = ((n_half + bn_cov - 1) / bn_cov) * tiles_m;
-        const int min_splits = (chunks + 4 * S_CH - 1) / (4 * S_CH);
-        const int max_splits = chunks / 4 > min_splits ? chunks / 4 : min_splits;
-        int splits = (256 + tiles - 1) / tiles;
-        splits = splits < min_splits ? min_splits : splits > max_splits ? max_splits : splits;
+        int splits = 1;
+        if (tiles < 192) {
+            splits = (256 + tiles - 1) / tiles;
+            const int max_splits = chunks / S_MIN_CHUNKS > 0 ? chunks / S_MIN_CHUNKS : 1;
+            if (splits > max_splits) splits = max_splits;
+        }
         a.tiles_m = tiles_m;
         a.n_tiles = tiles;
         a.k_chunks_per_split = (chunks + splits - 1) / splits;
         splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
-        if ((a.k_chunks_per_split + 3) / 4 > S_CH) return LUT6_E_SHAPE;   // cannot happen
-        if ((int64_t)tiles * splits > INT32_MAX / 1024) return LUT6_E_SHAPE;
-        const bool scaled = in_scale != 1.0f;
-        dim3 grid((unsigned)(tiles * splits)), block(256);
+        if ((int64_t)tiles * splits > INT32_MAX) return LUT6_E_SHAPE;
         if (splits > 1) {
-            const int st = workspace_for(stream, WS_PARTIAL, (size_t)tiles * splits * S_PART * 16, (void**)&a.partial);
+            const int st = workspace_for(stream, WS_PARTIAL, (size_t)splits * L * N * sizeof(float), (void**)&a.partial);
             if (st != LUT6_OK) return st;
-            switch (epilogue * 2 + (scaled ? 1 : 0)) {
-            case 0: hipLaunchKernelGGL((lut6_stream_kernel<0, false, true>), grid, block, 0, stream, a); break;
-            case 1: hipLaunchKernelGGL((lut6_stream_kernel<0, true, true>), grid, block, 0, stream, a); break;
-            case 2: hipLaunchKernelGGL((lut6_stream_kernel<1, false, true>), grid, block, 0, stream, a); break;
-            case 3: hipLaunchKernelGGL((lut6_stream_kernel<1, true, true>), grid, block, 0, stream, a); break;
-            case 4: hipLaunchKernelGGL((lut6_stream_kernel<2, false, true>), grid, block, 0, stream, a); break;
-            default: hipLaunchKernelGGL((lut6_stream_kernel<2, true, true>), grid, block, 0, stream, a); break;
-            }
-            if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
-            dim3 rgrid((unsigned)(tiles * 4));
-            switch (epilogue) {
-            case 0: hipLaunchKernelGGL(lut6_stream_reduce_kernel<0>, rgrid, block, 0, stream, a, splits); break;
-            case 1: hipLaunchKernelGGL(lut6_stream_reduce_kernel<1>, rgrid, block, 0, stream, a, splits); break;
-            default: hipLaunchKernelGGL(lut6_stream_reduce_kernel<2>, rgrid, block, 0, stream, a, splits); break;
-            }
-            return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
         }
-        switch (epilogue * 2 + (scaled ? 1 : 0)) {
+        const bool scaled = in_scale != 1.0f;
+        const dim3 grid((unsigned)(tiles * splits)), block(256);
+        switch ((epilogue * 2 + (scaled ? 1 : 0)) * 2 + (splits > 1 ? 1 : 0)) {
         case 0: hipLaunchKernelGGL((lut6_stream_kernel<0, false, false>), grid, block, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((lut6_stream_kernel<0, true, false>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((lut6_stream_kernel<1, false, false>), grid, block, 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((lut6_stream_kernel<1, true, false>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((lut6_stream_kernel<2, false, false>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((lut6_stream_kernel<2, true, false>), grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((lut6_stream_kernel<0, false, true>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((lut6_stream_kernel<0, true, false>), grid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((lut6_stream_kernel<0, true, true>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((lut6_stream_kernel<1, false, false>), grid, block, 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((lut6_stream_kernel<1, false, true>), grid, block, 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((lut6_stream_kernel<1, true, false>), grid, block, 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((lut6_stream_kernel<1, true, true>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((lut6_stream_kernel<2, false, false>), grid, block, 0, stream, a); break;
+        case 9: hipLaunchKernelGGL((lut6_stream_kernel<2, false, true>), grid, block, 0, stream, a); break;
+        case 10: hipLaunchKernelGGL((lut6_stream_kernel<2, true, false>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((lut6_stream_kernel<2, true, true>), grid, block, 0, stream, a); break;
         }
-        return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+        if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
+        return splits > 1 ? launch_reduce(a, epilogue, splits, stream) : LUT6_OK;
     }
     // compute regime: 256 x 256 tiles; split K (fixed-order reduction) when
     // the tiles cannot fill most of the 256 CUs
