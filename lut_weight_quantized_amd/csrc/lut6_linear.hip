@@ -926,10 +926,15 @@ constexpr int S_WAVE_SLOT = 8192;        // one 64-k chunk of 64 token rows
 constexpr int S_SLOT = 4 * S_WAVE_SLOT;  // one ring slot of all four waves
 constexpr int S_MIN_CHUNKS = 16;         // fewest 64-k chunks per K slice
 
-template <int EPI, bool SCALED, bool SPLIT>
+template <int EPI, bool SCALED, bool SPLIT, bool F16>
 __global__ void __launch_bounds__(256, 1)
 lut6_stream_kernel(GemmArgs a)
 {
+    // F16: every wave has exactly 16 chunks (K slice of 4096); all their
+    // packed words are loaded up front, so that the copies of activations,
+    // which hit in L2, never wait behind a packed-word load from HBM in
+    // the wave's in-order load queue.
+    //
     // pair tables (slot s: tile rows 16s .. 16s+15), then the four ring slots
     __shared__ __attribute__((aligned(1024))) uint8_t s_pair[2 * 16384];
     __shared__ __attribute__((aligned(1024))) uint8_t s_x0[S_SLOT];
@@ -953,8 +958,11 @@ lut6_stream_kernel(GemmArgs a)
     const int kc_begin = split * a.k_chunks_per_split;
     const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
     const int per_wave = (kc_end - kc_begin + 3) / 4;
-    const int w_begin = min(kc_begin + wave * per_wave, kc_end);
-    const int nch = min(w_begin + per_wave, kc_end) - w_begin;
+    // k quarter of this wave, rotated by tile so that the workgroups of one
+    // XCD do not all read the same activation chunk at the same time
+    const int quarter = (wave + r) & 3;
+    const int w_begin = min(kc_begin + quarter * per_wave, kc_end);
+    const int nch = F16 ? 16 : min(w_begin + per_wave, kc_end) - w_begin;
     const int kc_last = max(w_begin + nch - 1, 0);
 
     // global weight row of tile row i (clamped into range; such rows are
@@ -1029,17 +1037,44 @@ lut6_stream_kernel(GemmArgs a)
     using C1 = std::integral_constant<int, 1>;
     using C2 = std::integral_constant<int, 2>;
     using C3 = std::integral_constant<int, 3>;
-    // every prologue load is unconditional, so the main loop is entered
-    // with the same loads in flight, in the same order, as it leaves each
-    // iteration (the compiler's waits stay exact)
-    load_pw(0, C0{});
-    copy_x(0, C0{});
-    load_pw(1, C1{});
-    copy_x(1, C1{});
-    load_pw(2, C2{});
-    copy_x(2, C2{});
-    load_pw(3, C3{});
-    copy_x(3, C3{});
+    // F16: packed words of all 16 chunks, then the copies of chunks 0..3
+    uint32_t P16[F16 ? 16 : 1][6];
+    auto load_p16 = [&](auto cc) {
+        constexpr int C = decltype(cc)::value;
+        const int kc = w_begin + C;
+        const u32x4 q4 = __builtin_amdgcn_raw_buffer_load_b128(pr, poff, kc * 48, 0);
+        const u32x2 q2 = __builtin_amdgcn_raw_buffer_load_b64(pr, poff + 16, kc * 48, 0);
+        P16[C][0] = q4[0]; P16[C][1] = q4[1]; P16[C][2] = q4[2]; P16[C][3] = q4[3];
+        P16[C][4] = q2[0]; P16[C][5] = q2[1];
+    };
+    if constexpr (F16) {
+        // the first four chunks' words and copies lead, so the loop can
+        // start while the other twelve chunks' words stream in behind them
+        load_p16(std::integral_constant<int, 0>{});  load_p16(std::integral_constant<int, 1>{});
+        load_p16(std::integral_constant<int, 2>{});  load_p16(std::integral_constant<int, 3>{});
+        copy_x(0, C0{});
+        copy_x(1, C1{});
+        copy_x(2, C2{});
+        copy_x(3, C3{});
+        load_p16(std::integral_constant<int, 4>{});  load_p16(std::integral_constant<int, 5>{});
+        load_p16(std::integral_constant<int, 6>{});  load_p16(std::integral_constant<int, 7>{});
+        load_p16(std::integral_constant<int, 8>{});  load_p16(std::integral_constant<int, 9>{});
+        load_p16(std::integral_constant<int, 10>{}); load_p16(std::integral_constant<int, 11>{});
+        load_p16(std::integral_constant<int, 12>{}); load_p16(std::integral_constant<int, 13>{});
+        load_p16(std::integral_constant<int, 14>{}); load_p16(std::integral_constant<int, 15>{});
+    } else {
+        // every prologue load is unconditional, so the main loop is entered
+        // with the same loads in flight, in the same order, as it leaves
+        // each iteration (the compiler's waits stay exact)
+        load_pw(0, C0{});
+        copy_x(0, C0{});
+        load_pw(1, C1{});
+        copy_x(1, C1{});
+        load_pw(2, C2{});
+        copy_x(2, C2{});
+        load_pw(3, C3{});
+        copy_x(3, C3{});
+    }
 
     // pair tables: word p of slot s = T[p % 64] | T[p / 64] << 16
 #pragma unroll
@@ -1079,6 +1114,52 @@ lut6_stream_kernel(GemmArgs a)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
+    if constexpr (F16) {
+        // chunk C computes on fragments read during chunk C - 1 (register
+        // set C % 2); at its start those reads are complete, its slot takes
+        // chunk C + 4, and the fragments of chunk C + 1 are read while its
+        // eight MFMAs run
+        f16x8 A[2][4], B[2][2][4];
+        auto fetch = [&](auto cc) __attribute__((always_inline)) {
+            constexpr int C = decltype(cc)::value, RS = C & 1;
+            const uint8_t* const st = slot_base(std::integral_constant<int, C & 3>{});
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) B[RS][j][s] = *(const f16x8*)(st + 4096 * j + xo[s]);
+            A[RS][0] = gather(P16[C], C0{});
+            A[RS][1] = gather(P16[C], C1{});
+            A[RS][2] = gather(P16[C], C2{});
+            A[RS][3] = gather(P16[C], C3{});
+        };
+        auto step16 = [&](auto cc) __attribute__((always_inline)) {
+            constexpr int C = decltype(cc)::value, RS = C & 1;
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(LGKMCNT0);
+            if constexpr (C + 4 < 16) copy_x(C + 4, std::integral_constant<int, C & 3>{});
+            if constexpr (SCALED) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) B[RS][j][s] = B[RS][j][s] * a.scale;
+            }
+            if constexpr (C + 1 < 16) fetch(std::integral_constant<int, C + 1>{});
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[RS][s], B[RS][0][s], acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[RS][s], B[RS][1][s], acc[1], 0, 0, 0);
+            }
+        };
+        fetch(C0{});
+        step16(std::integral_constant<int, 0>{});  step16(std::integral_constant<int, 1>{});
+        step16(std::integral_constant<int, 2>{});  step16(std::integral_constant<int, 3>{});
+        step16(std::integral_constant<int, 4>{});  step16(std::integral_constant<int, 5>{});
+        step16(std::integral_constant<int, 6>{});  step16(std::integral_constant<int, 7>{});
+        step16(std::integral_constant<int, 8>{});  step16(std::integral_constant<int, 9>{});
+        step16(std::integral_constant<int, 10>{}); step16(std::integral_constant<int, 11>{});
+        step16(std::integral_constant<int, 12>{}); step16(std::integral_constant<int, 13>{});
+        step16(std::integral_constant<int, 14>{}); step16(std::integral_constant<int, 15>{});
+    } else {
     // chunk c on ring slot SL = c % 4: its B fragments leave the slot, which
     // then takes chunk c + 4 when PF; its A fragments are gathered one MFMA
     // step ahead (step 0 during the previous chunk's step 3, from the next
@@ -1153,11 +1234,12 @@ lut6_stream_kernel(GemmArgs a)
         default: break;
         }
     }
+    }
 
     // k quarters meet in slot 0 of the ring, [token fragment j][group q]
-    // [source wave][lane] of f32x4; wave 2j + (q & 1) owns (j, q) and adds
-    // the four quarters in wave order.  Every copy has landed and every wave
-    // is done with its ring before the exchange.
+    // [k quarter][lane] of f32x4; wave 2j + (q & 1) owns (j, q) and adds the
+    // four quarters in k order.  Every copy has landed and every wave is
+    // done with its ring before the exchange.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x4* const xa = (f32x4*)s_x0;
@@ -1166,7 +1248,7 @@ lut6_stream_kernel(GemmArgs a)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (2 * j + (q & 1) != wave)
-                xa[((j * 4 + q) * 4 + wave) * 64 + lane] =
+                xa[((j * 4 + q) * 4 + quarter) * 64 + lane] =
                     f32x4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
     __syncthreads();
     auto finish = [&](auto wc) {
@@ -1175,11 +1257,11 @@ lut6_stream_kernel(GemmArgs a)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int q = q0 + 2 * u;
+            const f32x4 own = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
 #pragma unroll
-            for (int src = 0; src < 4; ++src) {
-                const f32x4 o = src == w ? f32x4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]}
-                                         : xa[((j * 4 + q) * 4 + src) * 64 + lane];
-                v[u] = src == 0 ? o : v[u] + o;
+            for (int kq = 0; kq < 4; ++kq) {
+                const f32x4 o = kq == quarter ? own : xa[((j * 4 + q) * 4 + kq) * 64 + lane];
+                v[u] = kq == 0 ? o : v[u] + o;
             }
         }
         // v[u]: rows 8 (q0 + 2u) + 4h + 0..3 of the fragment, token 32j + r32
@@ -1482,19 +1564,17 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
         }
         const bool scaled = in_scale != 1.0f;
         const dim3 grid((unsigned)(tiles * splits)), block(256);
-        switch ((epilogue * 2 + (scaled ? 1 : 0)) * 2 + (splits > 1 ? 1 : 0)) {
-        case 0: hipLaunchKernelGGL((lut6_stream_kernel<0, false, false>), grid, block, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((lut6_stream_kernel<0, false, true>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((lut6_stream_kernel<0, true, false>), grid, block, 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((lut6_stream_kernel<0, true, true>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((lut6_stream_kernel<1, false, false>), grid, block, 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((lut6_stream_kernel<1, false, true>), grid, block, 0, stream, a); break;
-        case 6: hipLaunchKernelGGL((lut6_stream_kernel<1, true, false>), grid, block, 0, stream, a); break;
-        case 7: hipLaunchKernelGGL((lut6_stream_kernel<1, true, true>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((lut6_stream_kernel<2, false, false>), grid, block, 0, stream, a); break;
-        case 9: hipLaunchKernelGGL((lut6_stream_kernel<2, false, true>), grid, block, 0, stream, a); break;
-        case 10: hipLaunchKernelGGL((lut6_stream_kernel<2, true, false>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((lut6_stream_kernel<2, true, true>), grid, block, 0, stream, a); break;
+        // every wave holds exactly 16 chunks: the fully preloaded variant
+        const bool f16 = a.k_chunks_per_split == 64 && chunks % 64 == 0;
+        switch (((epilogue * 2 + (scaled ? 1 : 0)) * 2 + (splits > 1 ? 1 : 0)) * 2 + (f16 ? 1 : 0)) {
+#define S8_CASE(I, E, S, P)                                                                                   \
+        case 2 * (I): hipLaunchKernelGGL((lut6_stream_kernel<E, S, P, false>), grid, block, 0, stream, a); break; \
+        case 2 * (I) + 1: hipLaunchKernelGGL((lut6_stream_kernel<E, S, P, true>), grid, block, 0, stream, a); break;
+        S8_CASE(0, 0, false, false) S8_CASE(1, 0, false, true) S8_CASE(2, 0, true, false) S8_CASE(3, 0, true, true)
+        S8_CASE(4, 1, false, false) S8_CASE(5, 1, false, true) S8_CASE(6, 1, true, false) S8_CASE(7, 1, true, true)
+        S8_CASE(8, 2, false, false) S8_CASE(9, 2, false, true) S8_CASE(10, 2, true, false) S8_CASE(11, 2, true, true)
+#undef S8_CASE
+        default: return LUT6_E_EPILOGUE;
         }
         if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
         return splits > 1 ? launch_reduce(a, epilogue, splits, stream) : LUT6_OK;
