@@ -70,7 +70,7 @@ def kernel_class(g) -> str:
 
 
 # the kernels one lut6_linear call of each path runs (for the roofline record)
-PATH_KERNELS = {"stream": ["lut6_stream_kernel", "lut6_stream_reduce_kernel (split K)"],
+PATH_KERNELS = {"stream": ["lut6_stream_kernel", "lut6_reduce_kernel (only when K is split)"],
                 "fused": ["lut6_tile256_kernel"],
                 "expanded": ["lut6_expand_kernel", "lut6_expanded_gemm_kernel"]}
 
@@ -289,7 +289,7 @@ def main() -> int:
         lq.linear(x, p, t, epilogue=sg.epilogue, out=y, stream=stream)
     torch.cuda.synchronize()
     # back-to-back launches between one event pair: the per-launch time
-    # includes the split-K reduction and the gaps between kernels, and none
+    # includes every kernel of a call and the gaps between calls, and none
     # of the host's launch latency
     reps = []
     for r in range(3):
@@ -309,7 +309,7 @@ def main() -> int:
                   "tflop_s": round(sg.flops / (us_med * 1e-6) / 1e12, 1),
                   "algorithmic_bytes": sg.bytes, "weight_sets_rotated": sets,
                   "note": (f"median of 3 runs of {args.stream_iters} back-to-back launches; "
-                           "spans the GEMM, its split-K reduction and the gaps between kernels")}
+                           "spans each call's kernels and the gaps between calls")}
     log(f"L=128 stream: {us_med:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
 
     line = {

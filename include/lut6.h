@@ -113,8 +113,9 @@ int lut6_linear(const void* x, const uint8_t* packed, const void* tables, void* 
 
 /* Kernel paths of lut6_linear (what lut6_linear_path returns).            */
 typedef enum {
-    /* L <= 192: the weight-streaming kernel (K split across workgroups,
-     * fixed-order reduction)                                              */
+    /* L <= 192: the weight-streaming kernel (64-token x 32-channel tiles
+     * over the whole K range; K split into slices, added by a second
+     * kernel in a fixed order, only when the tiles are too few)           */
     LUT6_PATH_STREAM = 0,
     /* the fused kernel: 256 x 256 tiles, packed indices unpacked and looked
      * up in LDS per tile, FP16 MFMA                                       */

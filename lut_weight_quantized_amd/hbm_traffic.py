@@ -51,7 +51,7 @@ def classify(name: str) -> str | None:
 
     "reduce" (a split-K reduction, after its GEMM) and "expand" (the weight
     expansion, before its GEMM) belong to the neighbouring GEMM's launch."""
-    if "lut6_stream_reduce_kernel" in name or "lut6_reduce_kernel" in name:
+    if "lut6_reduce_kernel" in name:
         return "reduce"
     if "lut6_expand_kernel" in name:
         return "expand"
