@@ -846,11 +846,14 @@ lut6_expanded_gemm_kernel(GemmArgs a)
 // one (tn, w, f) form a block of K / 64 + 1 chunks of 4 KB: the spare chunk
 // keeps the blocks that concurrent workgroups read from sitting a power of
 // two apart, which would map them onto the same memory channels.
-// Workgroup (tn, g) expands chunks [8g, 8g + 8) of the 256 rows of channel
-// tile tn; a thread takes one (w, f, chunk, lane): 24 contiguous packed bytes
-// (32 indices) in, four 16-byte stores (one per step) out, each store
-// instruction contiguous across the wave.
-constexpr int X_CHUNKS = 8;   // chunks per expansion workgroup
+// Workgroup (tn, g) expands chunks [2g, 2g + 2) of the 256 rows of channel
+// tile tn (small workgroups, so that even a 4096 x 4096 weight spreads over
+// 512 of them); a thread takes up to four (w, f, chunk, lane) units: 24
+// contiguous packed bytes (32 indices) in, four 16-byte stores (one per
+// step) out, each store instruction contiguous across the wave.  All four
+// units' packed bytes are loaded before the first lookup.
+constexpr int X_CHUNKS = 2;                       // chunks per expansion workgroup
+constexpr int X_UNITS = 8 * X_CHUNKS * 64 / 256;  // units per thread
 
 template <int EPI>
 __global__ void __launch_bounds__(256)
@@ -861,37 +864,61 @@ lut6_expand_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restric
     const int tn = blockIdx.x, g = blockIdx.y;
     const int chunks = K / BK;
     const int row_bytes = K / 4 * 3;
-    // the 16 tables of the tile: slot s = tile row / 16
-    for (int i = threadIdx.x; i < 16 * 64; i += 256)
-        tab[i] = tables[(tile_row<EPI>(16 * (i >> 6), tn, N) / 16) * 64 + (i & 63)];
-    __syncthreads();
+    // the 16 tables of the tile: slot s = tile row / 16 (four entries per
+    // thread, all loaded before the first store)
+    uint16_t tv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        tv[j] = tables[(tile_row<EPI>(16 * (i >> 6), tn, N) / 16) * 64 + (i & 63)];
+    }
     const int nch = min(X_CHUNKS, chunks - g * X_CHUNKS);
-    for (int u = threadIdx.x; u < 8 * nch * 64; u += 256) {
+    // unit u = threadIdx.x + 256 i: lane u % 64, chunk (u / 64) % nch of the
+    // group, fragment wf = (u / 64) / nch; past 512 nch units a thread
+    // re-reads unit 0's bytes and stores nothing
+    u32x2 q[X_UNITS][3];
+    int trow[X_UNITS], dsto[X_UNITS];
+#pragma unroll
+    for (int i = 0; i < X_UNITS; ++i) {
+        const int uu = threadIdx.x + 256 * i;
+        const int u = uu < 8 * nch * 64 ? uu : 0;
         const int lane = u & 63, kl = (u >> 6) % nch, wf = (u >> 6) / nch;
         const int kc = g * X_CHUNKS + kl;
-        const int trow = 64 * (wf >> 1) + 32 * (wf & 1) + (lane & 31);
-        const int row = tile_row<EPI>(trow, tn, N);
+        trow[i] = 64 * (wf >> 1) + 32 * (wf & 1) + (lane & 31);
+        const int row = tile_row<EPI>(trow[i], tn, N);
         const uint8_t* src = packed + (size_t)row * row_bytes + 48 * kc + 24 * (lane >> 5);
         // 8-byte aligned (rows are 48-byte multiples, the offset 48 kc + 24h)
-        const u32x2* const q = (const u32x2*)__builtin_assume_aligned(src, 8);
-        const u32x2 v0 = q[0], v1 = q[1], v2 = q[2];
-        const uint32_t pw[6] = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1]};
-        const uint16_t* const t = tab + 64 * (trow >> 4);
-        uint16_t* const dst = w16 + ((((size_t)tn * 8 + wf) * (chunks + 1) + kc) * 4096 + lane * 16) / 2;
+        const u32x2* const qp = (const u32x2*)__builtin_assume_aligned(src, 8);
+        q[i][0] = qp[0];
+        q[i][1] = qp[1];
+        q[i][2] = qp[2];
+        dsto[i] = uu < 8 * nch * 64 ? (int)(((size_t)(tn * 8 + wf) * (chunks + 1) + kc) * 2048 + lane * 8) : -1;
+    }
+    // the table entries go to LDS once every load is in flight
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tab[threadIdx.x + 256 * j] = tv[j];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < X_UNITS; ++i) {
+        if (dsto[i] < 0) continue;
+        const uint32_t pw[6] = {q[i][0][0], q[i][0][1], q[i][1][0], q[i][1][1], q[i][2][0], q[i][2][1]};
+        const uint16_t* const t = tab + 64 * (trow[i] >> 4);
+        uint16_t* const dst = w16 + (size_t)dsto[i];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             // indices 8 st .. 8 st + 7 of the 192-bit word
             uint32_t e[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int bit = 6 * (8 * st + i), wd = bit >> 5, o = bit & 31;
+            for (int j = 0; j < 8; ++j) {
+                const int bit = 6 * (8 * st + j), wd = bit >> 5, o = bit & 31;
                 const uint32_t lo = pw[wd] >> o;
                 const uint32_t hi = (o > 26 && wd + 1 < 6) ? (pw[wd + 1] << (32 - o)) : 0u;
-                e[i] = (lo | hi) & 63u;
+                e[j] = (lo | hi) & 63u;
             }
             u32x4 out;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) out[i] = (uint32_t)t[e[2 * i]] | ((uint32_t)t[e[2 * i + 1]] << 16);
+            for (int j = 0; j < 4; ++j) out[j] = (uint32_t)t[e[2 * j]] | ((uint32_t)t[e[2 * j + 1]] << 16);
             *(u32x4*)(dst + st * 512) = out;
         }
     }
