@@ -19,6 +19,11 @@ starts.  The line printed is throughput in TFLOP/s, with
   * l128_stream: the L = 128 single projection (4,096 -> 4,096, FP32 out) in
     algorithmic HBM GB/s over back-to-back launches, rotating over enough
     weight sets that the 256 MB last-level cache cannot hold them;
+  * per_config: the three other workloads (L = 512 gate|up, L = 1,024 down,
+    one L = 4,096 block's three projections), each timed over back-to-back
+    launches that rotate through enough buffer copies (at least 512 MB) that
+    the last-level cache cannot hold them: TFLOP/s and algorithmic GB/s
+    against the FP16 peak and HBM bandwidth;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same step
     (sampled token rows of two layers), on this host's cores;
   * parity_sample: those sampled rows of the GPU result against the oracle.
@@ -43,6 +48,8 @@ PEAK_FP16_TFLOPS = 2516.6          # 256 CUs x 2.4 GHz x 4,096 FLOP/clk (dense F
 PEAK_HBM_GBS = 8000.0              # HBM3E
 STEP_WORKLOAD = "prefill_sweep_l16384"
 STREAM_WORKLOAD = "o_proj_l128"
+OTHER_WORKLOADS = ("mlp_gate_up_l512", "mlp_down_l1024", "hybrid_block_l4096")
+ROTATE_BYTES = 512 << 20           # at least twice the 256 MB last-level cache
 TRAFFIC_FILE = ROOT / "profiles" / "gemm_hbm_traffic.json"
 KERNEL_SOURCES = [ROOT / "lut_weight_quantized_amd" / "csrc" / "lut6_linear.hip"]
 TRAFFIC_LAYERS = (0, 3)            # one Gated DeltaNet and one full-attention layer
@@ -91,6 +98,59 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def time_workload(lq, si, torch, stream, name: str, launches: int = 20) -> dict:
+    """Median time of one pass over a workload's GEMMs (one launch each),
+    over back-to-back passes that rotate through copies of every buffer
+    (at least ROTATE_BYTES in all), so each launch reads from HBM."""
+    w = si.WORKLOADS[name]
+    gemms = [g for _, _, g in w.gemms()]
+    per_set = sum(g.bytes for g in gemms)
+    sets = max(2, -(-ROTATE_BYTES // per_set))
+    base = []
+    for li, pi, g in w.gemms():
+        idx, tab = si.gemm_weight(w.cfg, li, pi, g)
+        base.append((torch.from_numpy(lq.pack(idx)).to("cuda"), torch.from_numpy(tab).to("cuda"),
+                     torch.from_numpy(si.gemm_activation(w.cfg, g)).to("cuda")))
+        del idx
+    bufs = []
+    for _ in range(sets):
+        bufs.append([(p.clone(), t.clone(), x.clone(),
+                      torch.empty((g.L, g.n_out), device="cuda",
+                                  dtype=torch.float32 if g.epilogue == 0 else torch.float16))
+                     for (p, t, x), g in zip(base, gemms)])
+    del base
+
+    def one_pass(i):
+        for (p, t, x, y), g in zip(bufs[i % sets], gemms):
+            lq.linear(x, p, t, epilogue=g.epilogue, in_scale=g.in_scale, out=y, stream=stream)
+
+    for i in range(2 * sets):
+        one_pass(i)
+    torch.cuda.synchronize()
+    reps = []
+    for r in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(launches):
+            one_pass(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1) * 1e3 / launches)
+    us = sorted(reps)[1]
+    del bufs
+    torch.cuda.empty_cache()
+    tf = w.flops / (us * 1e-6) / 1e12
+    gbs = w.bytes / (us * 1e-6) / 1e9
+    return {"workload": name, "gemms": [f"{g.name} L={g.L} K={g.K} N={g.N}" for g in gemms],
+            "paths": [{lq.PATH_STREAM: "stream", lq.PATH_FUSED: "fused", lq.PATH_EXPANDED: "expanded"}[
+                lq.linear_path(g.L, g.K, g.N, g.epilogue)] for g in gemms],
+            "us_per_pass": round(us, 2), "tflop_s": round(tf, 1),
+            "frac_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4), "gb_s": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "flops": w.flops, "algorithmic_bytes": w.bytes,
+            "buffer_sets_rotated": sets}
 
 
 def main() -> int:
@@ -311,6 +371,15 @@ def main() -> int:
                   "note": (f"median of 3 runs of {args.stream_iters} back-to-back launches; "
                            "spans each call's kernels and the gaps between calls")}
     log(f"L=128 stream: {us_med:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+    del sets_w
+
+    # ---------------- the other workloads ----------------
+    per_config = []
+    for name in OTHER_WORKLOADS:
+        rec = time_workload(lq, si, torch, stream, name)
+        per_config.append(rec)
+        log(f"{name}: {rec['us_per_pass']:.1f} us, {rec['tflop_s']:.0f} TFLOP/s "
+            f"({rec['frac_fp16_peak']:.1%} of FP16 peak)")
 
     line = {
         "metric": METRIC,
@@ -332,6 +401,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "l128_stream": stream_rec,
+        "per_config": per_config,
         "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)
