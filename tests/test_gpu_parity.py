@@ -132,6 +132,25 @@ def test_linear_small(ora, L, K, N, epi, s):
     assert rep.ok, str(rep)
 
 
+# few tokens over a whole 4096-wide K slice per wave group: the streaming
+# kernel's variant that loads every chunk's packed words up front (enough
+# tiles: no K split; 64 tokens and 4,096 channels at K = 8,192: two slices);
+# ragged L, every epilogue and scale
+SHAPES_STREAM16 = [(128, 4096, 4096), (40, 4096, 6144), (64, 8192, 4096)]
+
+
+@pytest.mark.parametrize("L,K,N", SHAPES_STREAM16)
+@pytest.mark.parametrize("epi,s", [(F32, 1.0), (F16, 1.0), (F16, 16.0), (SILU, 1.0), (SILU, 4.0)])
+def test_linear_stream_whole_slices(ora, L, K, N, epi, s):
+    _say("stream16", L, K, N, epi, s)
+    assert lq.linear_path(L, K, N, epi) == lq.PATH_STREAM
+    x, idx, tab = _problem(L, K, N, L * 11 + K + N, sigma=0.5 if s > 1 else 1.0,
+                           subnormal=(L % 2 == 1))
+    y = gpu_linear(x, idx, tab, epi, s)
+    rep = oracle_check(ora, x, idx, tab, epi, s, y)
+    assert rep.ok, str(rep)
+
+
 # many tokens: the weight is expanded once and the GEMM reads FP16 tiles;
 # ragged L and N, split K (few tiles), every epilogue and scale
 SHAPES_MANY = [(1024, 64, 32), (1029, 256, 160), (1100, 576, 544), (2047, 128, 96),
