@@ -357,3 +357,50 @@ def test_seeded_inputs_are_reproducible():
     tab = a[2]
     assert np.all(np.diff(tab.astype(np.float64), axis=1) >= 0), "tables sorted"
     assert a[1].max() <= 63
+
+
+# ---------------------------------------------------------------------------
+# the parity criterion itself: the exactly rounded oracle passes, a result one
+# rounding step or more beyond it does not
+# ---------------------------------------------------------------------------
+
+def test_tolerance_accepts_rounded_oracle_and_rejects_drift(ora):
+    from oracle import tolerance as tol
+    # K = 64 and no table outliers: half an FP16 ulp of the largest outputs
+    # exceeds 2e-3 * S_row, the tightest case of the criterion
+    for (L, K, N, seed) in [(256, 64, 32, 11), (64, 4096, 64, 12)]:
+        x, idx, tab = _small_problem(L, K, N, seed)
+        packed = ora.pack(idx)
+        S = tol.row_scale(x, tab, K)
+        y, _ = ora.linear(x, packed, tab, epilogue=oracle.EPI_F32)
+        y = np.asarray(y, np.float64)
+        r16 = y.astype(np.float16)
+        assert tol.check(r16, y, S, fp16=True).ok
+        assert tol.check(y.astype(np.float32), y, S, fp16=False).ok
+        # pick the element with the largest |y| relative to its row scale
+        i, j = np.unravel_index(np.argmax(np.abs(y) / S[:, None]), y.shape)
+        # FP32: one bound beyond fails
+        bad32 = y.astype(np.float32)
+        bad32[i, j] = y[i, j] + 1.01 * 2e-3 * S[i] * np.sign(y[i, j])
+        assert not tol.check(bad32, y, S, fp16=False).ok
+        # FP16: the neighbours of fp16(y_ref) away from y_ref, one and two
+        # ulps out: two always fail (ulp rule), one fails where the FP32
+        # bound is below half an ulp (error >= 1 ulp > bound + ulp / 2)
+        away = np.float16(np.inf if r16[i, j] >= y[i, j] else -np.inf)
+        for steps in (2, 1):
+            v = r16[i, j]
+            for _ in range(steps):
+                v = np.nextafter(v, away)
+            bad16 = r16.copy()
+            bad16[i, j] = v
+            rep = tol.check(bad16, y, S, fp16=True)
+            if steps == 2 or 2e-3 * S[i] < 0.5 * tol.ulp16(y[i, j]):
+                assert not rep.ok, (L, K, N, steps, str(rep))
+    # SiLU(gate) * up rounded once to FP16 passes
+    x, idx, tab = _small_problem(128, 64, 64, 13)
+    packed = ora.pack(idx)
+    S = tol.row_scale(x, tab, 64)
+    h, _ = ora.linear(x, packed, tab, epilogue=oracle.EPI_SILU_MUL_F16)
+    a, _ = ora.linear(x, packed, tab, epilogue=oracle.EPI_F32)
+    Se = tol.silu_scale(a[:, :32], a[:, 32:], S)
+    assert tol.check(np.asarray(h, np.float64).astype(np.float16), h, S, fp16=True, S_elem=Se).ok
