@@ -120,11 +120,12 @@ typedef enum {
     /* the fused kernel: 256 x 256 tiles, packed indices unpacked and looked
      * up in LDS per tile, FP16 MFMA                                       */
     LUT6_PATH_FUSED = 1,
-    /* L >= 1024: the weight is expanded once per call (the same unpack and
-     * lookup) into a workspace of tiles_n * 8 * (K/64 + 1) * 4 KB, then an
-     * FP16 MFMA GEMM reads it (tiles_n = ceil(N / 256); for
-     * LUT6_EPI_SILU_MUL_F16 a tile holds 128 gate|up row pairs, the same
-     * count); the fused kernel instead if that workspace would reach 2 GB */
+    /* L >= 1536 (L >= 3072 when K >= 8192): the weight is expanded once
+     * per call (the same unpack and lookup) into a workspace of
+     * tiles_n * 8 * (K/64 + 1) * 4 KB, then an FP16 MFMA GEMM reads it
+     * (tiles_n = ceil(N / 256); for LUT6_EPI_SILU_MUL_F16 a tile holds 128
+     * gate|up row pairs, the same count); the fused kernel instead if that
+     * workspace would reach 2 GB                                          */
     LUT6_PATH_EXPANDED = 2
 } lut6_path;
 

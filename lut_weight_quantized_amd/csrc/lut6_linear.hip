@@ -663,7 +663,13 @@ lut6_tile256_kernel(GemmArgs a)
 // step in registers, so the stage it read is refilled with the tile after
 // next right away.
 // ---------------------------------------------------------------------------
-constexpr int EXPAND_MIN_L = 1024;   // token count from which the two-pass path runs
+// Token counts from which the two-pass path runs.  Below them the fused
+// kernel is as fast or faster: one expansion pass costs about as much as the
+// fused kernel's extra LDS and VALU work over that many tokens, and for a
+// deep K (a down-projection) the fused kernel keeps up to about 3000 tokens.
+constexpr int EXPAND_MIN_L = 1536;
+constexpr int EXPAND_MIN_L_DEEP_K = 3072;
+constexpr int DEEP_K = 8192;
 // s_waitcnt immediate: vmcnt <= 8, other counters not waited for
 constexpr int VMCNT8 = 0x0F78;
 
@@ -1508,7 +1514,7 @@ void launch_tiles(const GemmArgs& a, bool two_pass, int epilogue, bool scaled, b
 int choose_path(int64_t L, int64_t K, int64_t N, int epilogue)
 {
     if (L <= 192) return LUT6_PATH_STREAM;
-    if (L < EXPAND_MIN_L) return LUT6_PATH_FUSED;
+    if (L < (K >= DEEP_K ? EXPAND_MIN_L_DEEP_K : EXPAND_MIN_L)) return LUT6_PATH_FUSED;
     const int64_t n_half = epilogue == 2 ? N / 2 : N;
     const int64_t bn_cov = epilogue == 2 ? 128 : 256;
     const int64_t tiles_n = (n_half + bn_cov - 1) / bn_cov;

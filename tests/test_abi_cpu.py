@@ -101,13 +101,16 @@ def test_linear_validation(kwargs, status):
 
 def test_linear_path():
     # few tokens stream the weight; mid-size L runs the fused kernel; from
-    # 1024 tokens the weight is expanded once, unless the expansion would
-    # not fit 31-bit offsets
+    # 1536 tokens (3072 when K >= 8192) the weight is expanded once, unless
+    # the expansion would not fit 31-bit offsets
     assert lq.linear_path(1, 4096, 4096) == lq.PATH_STREAM
     assert lq.linear_path(192, 12288, 4096) == lq.PATH_STREAM
     assert lq.linear_path(193, 4096, 4096) == lq.PATH_FUSED
-    assert lq.linear_path(1023, 4096, 24576, lq.EPI_SILU_MUL_F16) == lq.PATH_FUSED
-    assert lq.linear_path(1024, 4096, 4096) == lq.PATH_EXPANDED
+    assert lq.linear_path(1535, 4096, 24576, lq.EPI_SILU_MUL_F16) == lq.PATH_FUSED
+    assert lq.linear_path(1536, 4096, 4096) == lq.PATH_EXPANDED
+    assert lq.linear_path(1536, 8128, 4096) == lq.PATH_EXPANDED
+    assert lq.linear_path(3071, 8192, 4096) == lq.PATH_FUSED
+    assert lq.linear_path(3072, 12288, 4096) == lq.PATH_EXPANDED
     assert lq.linear_path(16384, 12288, 4096) == lq.PATH_EXPANDED
     assert lq.linear_path(16384, 4096, 24576, lq.EPI_SILU_MUL_F16) == lq.PATH_EXPANDED
     # 8 * (K/64 + 1) * 4 KB per 256-channel tile: 2 GB at N = 96 * 256, K = 2^16

@@ -117,7 +117,8 @@ SHAPES = [(1, 64, 32), (3, 128, 32), (17, 192, 64), (64, 64, 96), (100, 256, 288
           (128, 576, 64), (129, 128, 128), (193, 320, 160), (256, 128, 544),
           (300, 192, 288), (513, 256, 320), (777, 128, 96), (300, 1024, 96),
           (513, 2048, 160), (260, 4096, 544), (192, 12288, 96), (160, 3072, 1056),
-          (128, 1024, 2080)]
+          (128, 1024, 2080), (1024, 64, 32), (1029, 256, 160), (1535, 576, 544),
+          (1280, 12288, 64)]
 
 
 @pytest.mark.parametrize("L,K,N", SHAPES)
@@ -153,8 +154,8 @@ def test_linear_stream_whole_slices(ora, L, K, N, epi, s):
 
 # many tokens: the weight is expanded once and the GEMM reads FP16 tiles;
 # ragged L and N, split K (few tiles), every epilogue and scale
-SHAPES_MANY = [(1024, 64, 32), (1029, 256, 160), (1100, 576, 544), (2047, 128, 96),
-               (1536, 1024, 288), (1280, 12288, 64)]
+SHAPES_MANY = [(1536, 64, 32), (1541, 256, 160), (1600, 576, 544), (2047, 128, 96),
+               (1536, 1024, 288), (3072, 8192, 64)]
 
 
 @pytest.mark.parametrize("L,K,N", SHAPES_MANY)
