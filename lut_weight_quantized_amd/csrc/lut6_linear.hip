@@ -670,8 +670,6 @@ lut6_tile256_kernel(GemmArgs a)
 constexpr int EXPAND_MIN_L = 1536;
 constexpr int EXPAND_MIN_L_DEEP_K = 3072;
 constexpr int DEEP_K = 8192;
-// s_waitcnt immediate: vmcnt <= 8, other counters not waited for
-constexpr int VMCNT8 = 0x0F78;
 
 template <int EPI, bool SCALED, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
@@ -771,8 +769,19 @@ lut6_expanded_gemm_kernel(GemmArgs a)
         E_PAIR(P, WS, S, SN, NB, 4); E_PAIR(P, WS, S, SN, NB, 5);                      \
         E_PAIR(P, WS, S, SN, NB, 6); E_PAIR(P, WS, S, SN, NB, 7);                      \
     } while (0)
-    // the last step of a tile also issues the copies of tile KN into stage
-    // S2 and the A fragments of tile KN into set S2, one copy per MFMA pair
+    // the first step of a tile also loads the A fragments of tile KN into
+    // set S2 (step J / 2, fragment J % 2), the last step issues the copies of
+    // tile KN into stage S2: one memory instruction per MFMA pair.  (Eight
+    // loads per wave in a row, 32 per CU at once, held up the MFMAs queued
+    // behind them; two per pair, loads and copies in the same step, too.)
+#define E_PAIR_LOADW(P, WS, S, SN, NB, J, S2, KN)                                      \
+    do {                                                                               \
+        E_MMA(P, WS, S, J);                                                            \
+        X[1 - (P)][J] = read_x(SN, NB, J);                                             \
+        WA[S2][(J) / 2][(J) % 2] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128( \
+            wr, wgoff[(J) % 2] + 1024 * ((J) / 2), (KN) * 4096, 0));                   \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+    } while (0)
 #define E_PAIR_ISSUE(P, WS, S, SN, NB, J, S2, KN)                                      \
     do {                                                                               \
         E_MMA(P, WS, S, J);                                                            \
@@ -798,20 +807,32 @@ lut6_expanded_gemm_kernel(GemmArgs a)
     for (int j = 0; j < 8; ++j) X[0][j] = read_x(0, 0, j);
 
     // One tile: tile kc in stage ST, its A fragments in set ST (constants).
-    // The barrier before step 3: this wave's copies of tile kc + 1 have
-    // landed (issued a tile ago; only the A fragments issued after them may
-    // be outstanding) and every wave has read its step-3 operands of stage
-    // ST - 1's tile, so after it tile kc + 2 goes to stage (ST + 2) % 3.
+    // Step 0 loads the A fragments of tile kc + 2 into set (ST + 2) % 3,
+    // which tile kc - 1 used.  The barrier before step 3: every load of this
+    // wave is complete (the copies of tile kc + 1, issued a tile ago, and the
+    // A fragments of tile kc + 2), so after the barrier all of tile kc + 1 is
+    // in LDS; and every wave has read its step-3 operands of stage ST, so the
+    // copies of tile kc + 2 can go to stage (ST + 2) % 3.  The wait is for
+    // every outstanding load, not for all but the youngest: register loads
+    // issued after copies into LDS can complete before them (waiting for all
+    // but the eight youngest let the barrier pass early on cold data).
     auto tile_step = [&](auto st_c, int kc) {
         constexpr int ST = decltype(st_c)::value;
         constexpr int S1 = (ST + 1) % T2_NSTAGE, S2 = (ST + 2) % T2_NSTAGE;
         constexpr int so = ST * T2_XBYTES, sn = S1 * T2_XBYTES;
-        E_STEP(0, ST, 0, so, 1);
+        const int kn = min(kc + 2, last);
+        E_PAIR_LOADW(0, ST, 0, so, 1, 0, S2, kn);
+        E_PAIR_LOADW(0, ST, 0, so, 1, 1, S2, kn);
+        E_PAIR_LOADW(0, ST, 0, so, 1, 2, S2, kn);
+        E_PAIR_LOADW(0, ST, 0, so, 1, 3, S2, kn);
+        E_PAIR_LOADW(0, ST, 0, so, 1, 4, S2, kn);
+        E_PAIR_LOADW(0, ST, 0, so, 1, 5, S2, kn);
+        E_PAIR_LOADW(0, ST, 0, so, 1, 6, S2, kn);
+        E_PAIR_LOADW(0, ST, 0, so, 1, 7, S2, kn);
         E_STEP(1, ST, 1, so, 2);
         E_STEP(0, ST, 2, so, 3);
-        __builtin_amdgcn_s_waitcnt(VMCNT8);
+        __builtin_amdgcn_s_waitcnt(VMCNT0);
         lds_barrier();
-        const int kn = min(kc + 2, last);
         E_PAIR_ISSUE(1, ST, 3, sn, 0, 0, S2, kn);
         E_PAIR_ISSUE(1, ST, 3, sn, 0, 1, S2, kn);
         E_PAIR_ISSUE(1, ST, 3, sn, 0, 2, S2, kn);
@@ -820,7 +841,6 @@ lut6_expanded_gemm_kernel(GemmArgs a)
         E_PAIR_ISSUE(1, ST, 3, sn, 0, 5, S2, kn);
         E_PAIR_ISSUE(1, ST, 3, sn, 0, 6, S2, kn);
         E_PAIR_ISSUE(1, ST, 3, sn, 0, 7, S2, kn);
-        load_w(std::integral_constant<int, S2>{}, kn);
     };
     int kc = kc_begin;
     for (; kc + T2_NSTAGE <= kc_end; kc += T2_NSTAGE) {
@@ -831,6 +851,7 @@ lut6_expanded_gemm_kernel(GemmArgs a)
     if (kc < kc_end) tile_step(std::integral_constant<int, 0>{}, kc);
     if (kc + 1 < kc_end) tile_step(std::integral_constant<int, 1>{}, kc + 1);
 #undef E_PAIR_ISSUE
+#undef E_PAIR_LOADW
 #undef E_STEP
 #undef E_PAIR
 #undef E_MMA
