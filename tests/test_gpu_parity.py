@@ -170,6 +170,37 @@ def test_linear_many_tokens(ora, L, K, N, epi, s):
     assert rep.ok, str(rep)
 
 
+# Cold activations, warm weight: every call's activations are evicted from
+# the caches (a 512 MB copy) and the packed weight is read back just before
+# the call.  Copies of the activations into LDS are then slow and loads of the
+# weight into registers fast, so a wait that assumed loads complete in issue
+# order (all but the youngest outstanding) lets a barrier pass before the
+# copies land; this checks that no path relies on that.
+SHAPES_COLD = [(128, 4096, 4096, F16), (40, 1024, 2080, F32), (513, 2048, 160, F16),
+               (1536, 1024, 288, F16), (3072, 8192, 64, F32)]
+
+
+@pytest.mark.parametrize("L,K,N,epi", SHAPES_COLD)
+def test_cold_activation_calls(ora, L, K, N, epi):
+    _say("cold", L, K, N, epi)
+    big = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    big2 = torch.empty_like(big)
+    _, idx, tab = _problem(1, K, N, L + 11 * K + N)
+    packed = lq.pack(idx)
+    pd, td = _dev(packed), _dev(tab)
+    for trial in range(3):
+        x = _problem(L, K, 16, 1000 * trial + L + K)[0]
+        xd = _dev(x)
+        big2.copy_(big)
+        pd.sum()
+        torch.cuda.synchronize()
+        y = lq.linear(xd, pd, td, epilogue=epi)
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()
+        rep = oracle_check(ora, x, idx, tab, epi, 1.0, y.view(np.uint16) if epi != F32 else y)
+        assert rep.ok, f"trial {trial}: {rep}"
+
+
 def test_non_aligned_n_tiles(ora):
     # N = 16 * odd so the last channel tile is partial in both regimes
     for L in (64, 384, 1088):
