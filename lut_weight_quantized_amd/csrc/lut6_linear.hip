@@ -274,77 +274,61 @@ __device__ __forceinline__ int tile_row(int t, int tn, int N)
     }
 }
 
-// Epilogue of the 256 x 256 tiles: lane (r32, h) of a wave whose channels
-// are tile rows 64w + [0, 64) and whose tokens start at tok0 holds token
-// tok0 + 32j + r32 of each 32-token fragment j and channels 8q + 4h + (0..3),
-// q = 0..3, of each 32-row fragment f (tile rows 64w + 32f + ...).  SPLIT:
-// raw FP32 sums of K slice ks into the partial buffer.
-template <int EPI, bool SPLIT, int NJ>
-__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, const f32x16 (&acc)[2][NJ], int tok0, int tn,
-                                              int wave, int r32, int h, int ks)
+// Split-K partial sums through LDS: each wave writes the raw FP32 sums of
+// its 64 accumulator channels (for silu(gate) * up: 32 gate then the 32
+// matching up channels) of 32 * JP tokens into an LDS block with padded rows,
+// then stores whole row segments: 16 bytes per lane, so each store
+// instruction covers whole 128-byte lines (storing straight from the
+// accumulators wrote 32-byte pieces of 32 rows per instruction, and with
+// every workgroup writing its partials at the same moment that took twice
+// as long).  Partial plane ks is [L, N] with the gate columns at [0, N/2)
+// and the up columns at [N/2, N).  The caller has synchronised the
+// workgroup: the pipeline stages are free.
+template <int EPI, int NJ, int JP>
+__device__ __forceinline__ void tile_store_partial(const GemmArgs& a, const f32x16 (&acc)[2][NJ], int tok0,
+                                                   int tn, int w, int lane, uint8_t* lds, int ks)
 {
+    constexpr int ROWB = 64 * 4;                  // one token's 64 sums
+    constexpr int PITCH = ROWB + 16;
+    constexpr int LPR = ROWB / 16;                // lanes per row when reading back
+    constexpr int NREAD = 32 * JP * ROWB / 1024;  // read/store instructions per pass
+    const int r32 = lane & 31, h = lane >> 5;
+    uint8_t* const wl = lds + w * (32 * JP * PITCH);
     const int L = a.L, N = a.N;
+    float* const plane = a.partial + (size_t)ks * L * N;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int tok = tok0 + 32 * j + r32;
-        if (tok >= L) continue;
-        if constexpr (SPLIT) {
-            // raw FP32 sums of this K range; gate rows at j, up rows at N/2 + j
-            float* prow = a.partial + ((size_t)ks * L + tok) * N;
+    for (int p = 0; p < NJ / JP; ++p) {
+#pragma unroll
+        for (int jj = 0; jj < JP; ++jj) {
+            const int j = JP * p + jj;
+            uint8_t* const row = wl + (32 * jj + r32) * PITCH;
 #pragma unroll
             for (int f = 0; f < 2; ++f)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    int n;
-                    bool ok;
-                    if constexpr (EPI == 2) {
-                        const int jj = tn * 128 + 32 * wave + 8 * q + 4 * h;
-                        ok = jj < N / 2;
-                        n = f ? N / 2 + jj : jj;
-                    } else {
-                        n = tn * 256 + 64 * wave + 32 * f + 8 * q + 4 * h;
-                        ok = n < N;
-                    }
-                    if (!ok) continue;
-                    const f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2],
-                                     acc[f][j][4 * q + 3]};
-                    *(f32x4*)(prow + n) = v;
-                }
-        } else if constexpr (EPI == 2) {
+                for (int q = 0; q < 4; ++q)
+                    *(f32x4*)(row + (32 * f + 8 * q + 4 * h) * 4) =
+                        f32x4{acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2], acc[f][j][4 * q + 3]};
+        }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int jj = tn * 128 + 32 * wave + 8 * q + 4 * h;
-                if (jj >= N / 2) continue;
-                f16x4 hv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float gv = acc[0][j][4 * q + e] * a.inv_scale;
-                    const float uv = acc[1][j][4 * q + e] * a.inv_scale;
-                    hv[e] = (_Float16)(silu_f32(gv) * uv);
-                }
-                *(f16x4*)((_Float16*)a.y + (size_t)tok * (N / 2) + jj) = hv;
+        for (int i = 0; i < NREAD; ++i) {
+            const int idx = i * 64 + lane, r = idx / LPR, seg = idx % LPR;
+            const u32x4 v = *(const u32x4*)(wl + r * PITCH + seg * 16);
+            const int tok = tok0 + 32 * JP * p + r;
+            int col;
+            bool ok;
+            if constexpr (EPI == 2) {
+                // segments 0..7: gate channels, 8..15: the matching up channels
+                const int jcol = tn * 128 + 32 * w + (seg & 7) * 4;
+                ok = jcol < N / 2;
+                col = seg < 8 ? jcol : N / 2 + jcol;
+            } else {
+                col = tn * 256 + 64 * w + seg * 4;
+                ok = col < N;
             }
-        } else {
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = tn * 256 + 64 * wave + 32 * f + 8 * q + 4 * h;
-                    if (n >= N) continue;
-                    f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2],
-                               acc[f][j][4 * q + 3]};
-                    v *= a.inv_scale;
-                    if constexpr (EPI == 0) {
-                        *(f32x4*)((float*)a.y + (size_t)tok * N + n) = v;
-                    } else {
-                        f16x4 hv = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-                        *(f16x4*)((_Float16*)a.y + (size_t)tok * N + n) = hv;
-                    }
-                }
+            if (tok < L && ok) *(u32x4*)(plane + (size_t)tok * N + col) = v;
         }
     }
 }
-
 
 // Epilogue through LDS (not split): each wave writes its 64 output channels
 // (32 for silu(gate) * up) of 64 tokens at a time into an LDS block with
@@ -521,6 +505,28 @@ lut6_tile256_kernel(GemmArgs a)
     auto read_xf = [&](int so, int s, int j) -> f16x8 {
         return *(const f16x8*)(lds + so + xoff[s] + j * 4096);
     };
+    // unit u (0..3) of load_pc: fragment u / 2, the 16-byte part (u even) or
+    // the 8-byte part
+    auto load_pc_unit = [&](auto ps_c, int kc, int u) {
+        constexpr int PS = decltype(ps_c)::value;
+        const int f = u >> 1;
+        if (u & 1) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(pr, pgoff[f] + 16, kc * 48, 0);
+            PC[PS][f][4] = v[0];
+            PC[PS][f][5] = v[1];
+        } else {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(pr, pgoff[f], kc * 48, 0);
+            PC[PS][f][0] = v[0];
+            PC[PS][f][1] = v[1];
+            PC[PS][f][2] = v[2];
+            PC[PS][f][3] = v[3];
+        }
+    };
+    auto issue_x1 = [&](int st, int kc, int i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (lds_ptr_t)(lds + T2_TABLES + st * T2_XBYTES + i * 4096 + wave * 1024), 16, xgoff[i],
+            kc * (BK * 2), 0, 0);
+    };
 
     // gather q (0..15) of step NS from packed set PS: fragment q / 8, index
     // 8 NS + q % 8 of the lane's 32
@@ -565,6 +571,31 @@ lut6_tile256_kernel(GemmArgs a)
         W[1 - (P)][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]}); \
         W[1 - (P)][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]}); \
     } while (0)
+    // the same step with one extra memory instruction per MFMA pair: MEM(J)
+#define LUT6_PAIR_M(P, SN, NB, PG, NG, J, MEM)                                         \
+    do {                                                                               \
+        LUT6_MMA(P, J);                                                                \
+        X[1 - (P)][J] = read_xf(SN, NB, J);                                            \
+        LUT6_GATHER(P, PG, NG, 2 * (J));                                               \
+        LUT6_GATHER(P, PG, NG, 2 * (J) + 1);                                           \
+        LUT6_PACK(1 - (P), J);                                                         \
+        MEM(J);                                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                             \
+    } while (0)
+#define LUT6_STEP_M(P, SN, NB, PG, NG, MEM)                                            \
+    do {                                                                               \
+        uint32_t wn[2][4];                                                             \
+        LUT6_PAIR_M(P, SN, NB, PG, NG, 0, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PG, NG, 1, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PG, NG, 2, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PG, NG, 3, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PG, NG, 4, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PG, NG, 5, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PG, NG, 6, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PG, NG, 7, MEM);                                        \
+        W[1 - (P)][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]}); \
+        W[1 - (P)][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]}); \
+    } while (0)
 
     // prologue: activations and packed words of the first two tiles in
     // flight; the first tile's step-0 operands in registers and its step-1
@@ -597,24 +628,32 @@ lut6_tile256_kernel(GemmArgs a)
 
     // One tile: tile kc in stage ST (a constant; its packed words in set ST).
     // Past the end, tiles are fetched again (valid memory, into a stage and a
-    // set that are no longer read).  The barrier before step 3: this wave's
-    // copies of tile kc + 1 landed long ago (its packed words, issued after
-    // them, were already waited for by step 2's gathers); after it, all of
-    // tile kc + 1 is in LDS and every read of the stage that tile kc + 2
-    // refills (tile kc - 1's) has completed.
+    // set that are no longer read).  Memory instructions go one per MFMA
+    // pair: step 0 loads tile kc + 2's packed words into set (ST + 2) % 3
+    // (tile kc - 1's, last read by its step 1's gathers), step 3 copies tile
+    // kc + 2's activations into stage (ST + 2) % 3.  (Issued as a burst of
+    // twelve per wave after the barrier they held up the MFMAs behind them:
+    // about 3,300 cycles per 64-k chunk against 2,850 spread out.)  The
+    // barrier before step 3 waits for every load of this wave (copies of
+    // tile kc + 1, packed words of tile kc + 2); after it, all of tile kc + 1
+    // is in LDS and every read of the stage that tile kc + 2 refills (tile
+    // kc - 1's) has completed.
     auto tile_step = [&](auto st_c, int kc) {
         constexpr int ST = decltype(st_c)::value;
         constexpr int S1 = (ST + 1) % T2_NSTAGE, S2 = (ST + 2) % T2_NSTAGE;
         constexpr int so = T2_TABLES + ST * T2_XBYTES;
         constexpr int sn = T2_TABLES + S1 * T2_XBYTES;
-        LUT6_STEP(0, so, 1, ST, 2);
+        const int kn = min(kc + 2, last);
+#define LUT6_MEM_PC(J) do { if ((J) < 4) load_pc_unit(std::integral_constant<int, S2>{}, kn, (J)); } while (0)
+#define LUT6_MEM_X(J) issue_x1(S2, kn, (J))
+        LUT6_STEP_M(0, so, 1, ST, 2, LUT6_MEM_PC);
         LUT6_STEP(1, so, 2, ST, 3);
         LUT6_STEP(0, so, 3, S1, 0);
         __builtin_amdgcn_s_waitcnt(VMCNT0);
         lds_barrier();
-        issue_x(S2, min(kc + 2, last));
-        load_pc(std::integral_constant<int, S2>{}, min(kc + 2, last));
-        LUT6_STEP(1, sn, 0, S1, 1);
+        LUT6_STEP_M(1, sn, 0, S1, 1, LUT6_MEM_X);
+#undef LUT6_MEM_PC
+#undef LUT6_MEM_X
     };
     int kc = kc_begin;
     for (; kc + T2_NSTAGE <= kc_end; kc += T2_NSTAGE) {
@@ -624,6 +663,8 @@ lut6_tile256_kernel(GemmArgs a)
     }
     if (kc < kc_end) tile_step(std::integral_constant<int, 0>{}, kc);
     if (kc + 1 < kc_end) tile_step(std::integral_constant<int, 1>{}, kc + 1);
+#undef LUT6_STEP_M
+#undef LUT6_PAIR_M
 #undef LUT6_STEP
 #undef LUT6_PAIR
 #undef LUT6_MMA
@@ -633,7 +674,8 @@ lut6_tile256_kernel(GemmArgs a)
     __builtin_amdgcn_s_waitcnt(0);
 
     if constexpr (SPLIT) {
-        tile_epilogue<EPI, SPLIT, 8>(a, acc, m0, tn, wave, r32, h, blockIdx.y);
+        __syncthreads();
+        tile_store_partial<EPI, 8, 2>(a, acc, m0, tn, wave, lane, lds, blockIdx.y);
     } else {
         __syncthreads();
         tile_store_rows<EPI, 8, 2>(a, acc, m0, tn, wave, wave, lane, lds);
@@ -858,7 +900,8 @@ lut6_expanded_gemm_kernel(GemmArgs a)
     __builtin_amdgcn_s_waitcnt(0);
 
     if constexpr (SPLIT) {
-        tile_epilogue<EPI, SPLIT, 8>(a, acc, m0, tn, wave, r32, h, blockIdx.y);
+        __syncthreads();
+        tile_store_partial<EPI, 8, 2>(a, acc, m0, tn, wave, lane, lds, blockIdx.y);
     } else {
         __syncthreads();
         tile_store_rows<EPI, 8, 2>(a, acc, m0, tn, wave, wave, lane, lds);
