@@ -478,6 +478,10 @@ lut6_tile256_kernel(GemmArgs a)
     f16x8 X[2][8];
     f16x8 W[2][2];
     uint32_t G[2][16];
+    // LDS byte offsets of the gathers of a step, computed one step earlier
+    // (by step parity), so a gather never waits for its own address
+    uint32_t GA[2][16];
+    f16x8 XS[2];
 
     // buffer -> LDS copies of the activations of tile kc into stage st
     auto issue_x = [&](int st, int kc) {
@@ -532,67 +536,79 @@ lut6_tile256_kernel(GemmArgs a)
     // 8 NS + q % 8 of the lane's 32
 #define LUT6_GATHER(GP, PS, NS, Q)                                                     \
     G[GP][Q] = *(const uint16_t*)(tlb + entry_off<8 * (NS) + (Q) % 8>(PC[PS][(Q) / 8], (Q) / 8 ? tab1 : tab0))
+#define LUT6_ADDR(AP, PS, NS, Q)                                                       \
+    GA[AP][Q] = entry_off<8 * (NS) + (Q) % 8>(PC[PS][(Q) / 8], (Q) / 8 ? tab1 : tab0)
+#define LUT6_LOAD(GP, Q) G[GP][Q] = *(const uint16_t*)(tlb + GA[GP][Q])
     // pack c (0..7) of the A fragments of the next step: fragment c / 4,
     // dword c % 4 from gathers 2c, 2c + 1
 #define LUT6_PACK(GP, C) wn[(C) / 4][(C) % 4] = G[GP][2 * (C)] | (G[GP][2 * (C) + 1] << 16)
+    // with SCALED the B fragment of pair J was scaled during pair J - 1 (into
+    // XS[J & 1]), so the MFMAs never wait for their own multiplies; pair 7
+    // scales the next step's first fragment, read in this step's pair 0
 #define LUT6_MMA(P, J)                                                                 \
     do {                                                                               \
-        f16x8 xj = X[P][J];                                                            \
-        if constexpr (SCALED) xj = xj * a.scale;                                       \
+        const f16x8 xj = SCALED ? XS[(J) & 1] : X[P][J];                               \
         acc[0][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[P][0], xj, acc[0][J], 0, 0, 0); \
         acc[1][J] = __builtin_amdgcn_mfma_f32_32x32x16_f16(W[P][1], xj, acc[1][J], 0, 0, 0); \
+        if constexpr (SCALED)                                                          \
+            XS[((J) + 1) & 1] = ((J) < 7 ? X[P][((J) + 1) & 7] : X[1 - (P)][0]) * a.scale; \
     } while (0)
     // One step: MFMAs on parity P; B fragments of the next step from stage
-    // byte offset SN (step NB of its tile); gathers for the step after next
-    // (step NG of the tile whose packed words are in set PG); packs of the
-    // entries gathered one step ago.  sched_barrier(0) keeps each MFMA pair
-    // with its share of the other work: left alone the scheduler clusters the
-    // LDS reads.
-#define LUT6_PAIR(P, SN, NB, PG, NG, J)                                                \
+    // byte offset SN (step NB of its tile); the gathers whose addresses the
+    // previous step computed (entries of the step after next); the addresses
+    // of the next step's gathers (step NA of the tile whose packed words are
+    // in set PA); packs of the entries gathered one step ago.
+    // sched_barrier(0) keeps each MFMA pair with its share of the other work:
+    // left alone the scheduler clusters the LDS reads.
+#define LUT6_PAIR(P, SN, NB, PA, NA, J)                                                \
     do {                                                                               \
         LUT6_MMA(P, J);                                                                \
         X[1 - (P)][J] = read_xf(SN, NB, J);                                            \
-        LUT6_GATHER(P, PG, NG, 2 * (J));                                               \
-        LUT6_GATHER(P, PG, NG, 2 * (J) + 1);                                           \
+        LUT6_LOAD(P, 2 * (J));                                                         \
+        LUT6_LOAD(P, 2 * (J) + 1);                                                     \
+        LUT6_ADDR(1 - (P), PA, NA, 2 * (J));                                           \
+        LUT6_ADDR(1 - (P), PA, NA, 2 * (J) + 1);                                       \
         LUT6_PACK(1 - (P), J);                                                         \
         __builtin_amdgcn_sched_barrier(0);                                             \
     } while (0)
-#define LUT6_STEP(P, SN, NB, PG, NG)                                                   \
+#define LUT6_STEP(P, SN, NB, PA, NA)                                                   \
     do {                                                                               \
         uint32_t wn[2][4];                                                             \
-        LUT6_PAIR(P, SN, NB, PG, NG, 0);                                               \
-        LUT6_PAIR(P, SN, NB, PG, NG, 1);                                               \
-        LUT6_PAIR(P, SN, NB, PG, NG, 2);                                               \
-        LUT6_PAIR(P, SN, NB, PG, NG, 3);                                               \
-        LUT6_PAIR(P, SN, NB, PG, NG, 4);                                               \
-        LUT6_PAIR(P, SN, NB, PG, NG, 5);                                               \
-        LUT6_PAIR(P, SN, NB, PG, NG, 6);                                               \
-        LUT6_PAIR(P, SN, NB, PG, NG, 7);                                               \
+        LUT6_PAIR(P, SN, NB, PA, NA, 0);                                               \
+        LUT6_PAIR(P, SN, NB, PA, NA, 1);                                               \
+        LUT6_PAIR(P, SN, NB, PA, NA, 2);                                               \
+        LUT6_PAIR(P, SN, NB, PA, NA, 3);                                               \
+        LUT6_PAIR(P, SN, NB, PA, NA, 4);                                               \
+        LUT6_PAIR(P, SN, NB, PA, NA, 5);                                               \
+        LUT6_PAIR(P, SN, NB, PA, NA, 6);                                               \
+        LUT6_PAIR(P, SN, NB, PA, NA, 7);                                               \
         W[1 - (P)][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]}); \
         W[1 - (P)][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]}); \
     } while (0)
     // the same step with one extra memory instruction per MFMA pair: MEM(J)
-#define LUT6_PAIR_M(P, SN, NB, PG, NG, J, MEM)                                         \
+#define LUT6_PAIR_M(P, SN, NB, PA, NA, J, MEM)                                         \
     do {                                                                               \
         LUT6_MMA(P, J);                                                                \
         X[1 - (P)][J] = read_xf(SN, NB, J);                                            \
-        LUT6_GATHER(P, PG, NG, 2 * (J));                                               \
-        LUT6_GATHER(P, PG, NG, 2 * (J) + 1);                                           \
+        LUT6_LOAD(P, 2 * (J));                                                         \
+        LUT6_LOAD(P, 2 * (J) + 1);                                                     \
+        LUT6_ADDR(1 - (P), PA, NA, 2 * (J));                                           \
+        LUT6_ADDR(1 - (P), PA, NA, 2 * (J) + 1);                                       \
         LUT6_PACK(1 - (P), J);                                                         \
         MEM(J);                                                                        \
         __builtin_amdgcn_sched_barrier(0);                                             \
     } while (0)
-#define LUT6_STEP_M(P, SN, NB, PG, NG, MEM)                                            \
+#define LUT6_STEP_M(P, SN, NB, PA, NA, MEM)                                            \
     do {                                                                               \
         uint32_t wn[2][4];                                                             \
-        LUT6_PAIR_M(P, SN, NB, PG, NG, 0, MEM);                                        \
-        LUT6_PAIR_M(P, SN, NB, PG, NG, 1, MEM);                                        \
-        LUT6_PAIR_M(P, SN, NB, PG, NG, 2, MEM);                                        \
-        LUT6_PAIR_M(P, SN, NB, PG, NG, 3, MEM);                                        \
-        LUT6_PAIR_M(P, SN, NB, PG, NG, 4, MEM);                                        \
-        LUT6_PAIR_M(P, SN, NB, PG, NG, 5, MEM);                                        \
-        LUT6_PAIR_M(P, SN, NB, PG, NG, 6, MEM);                                        \
-        LUT6_PAIR_M(P, SN, NB, PG, NG, 7, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PA, NA, 0, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PA, NA, 1, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PA, NA, 2, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PA, NA, 3, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PA, NA, 4, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PA, NA, 5, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PA, NA, 6, MEM);                                        \
+        LUT6_PAIR_M(P, SN, NB, PA, NA, 7, MEM);                                        \
         W[1 - (P)][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]}); \
         W[1 - (P)][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]}); \
     } while (0)
@@ -611,6 +627,7 @@ lut6_tile256_kernel(GemmArgs a)
         constexpr int so = T2_TABLES;
 #pragma unroll
         for (int j = 0; j < 8; ++j) X[0][j] = read_xf(so, 0, j);
+        if constexpr (SCALED) XS[0] = X[0][0] * a.scale;
         uint32_t wn[2][4];
 #define LUT6_PRO(Q)                                                                    \
     do {                                                                               \
@@ -622,6 +639,12 @@ lut6_tile256_kernel(GemmArgs a)
 #undef LUT6_PRO
         LUT6_PACK(0, 0); LUT6_PACK(0, 1); LUT6_PACK(0, 2); LUT6_PACK(0, 3);
         LUT6_PACK(0, 4); LUT6_PACK(0, 5); LUT6_PACK(0, 6); LUT6_PACK(0, 7);
+        // addresses of the first step's gathers (step 2 of the first tile)
+#define LUT6_PRO_A(Q) LUT6_ADDR(0, 0, 2, Q)
+        LUT6_PRO_A(0); LUT6_PRO_A(1); LUT6_PRO_A(2); LUT6_PRO_A(3); LUT6_PRO_A(4); LUT6_PRO_A(5);
+        LUT6_PRO_A(6); LUT6_PRO_A(7); LUT6_PRO_A(8); LUT6_PRO_A(9); LUT6_PRO_A(10); LUT6_PRO_A(11);
+        LUT6_PRO_A(12); LUT6_PRO_A(13); LUT6_PRO_A(14); LUT6_PRO_A(15);
+#undef LUT6_PRO_A
         W[0][0] = __builtin_bit_cast(f16x8, u32x4{wn[0][0], wn[0][1], wn[0][2], wn[0][3]});
         W[0][1] = __builtin_bit_cast(f16x8, u32x4{wn[1][0], wn[1][1], wn[1][2], wn[1][3]});
     }
@@ -646,12 +669,15 @@ lut6_tile256_kernel(GemmArgs a)
         const int kn = min(kc + 2, last);
 #define LUT6_MEM_PC(J) do { if ((J) < 4) load_pc_unit(std::integral_constant<int, S2>{}, kn, (J)); } while (0)
 #define LUT6_MEM_X(J) issue_x1(S2, kn, (J))
-        LUT6_STEP_M(0, so, 1, ST, 2, LUT6_MEM_PC);
-        LUT6_STEP(1, so, 2, ST, 3);
-        LUT6_STEP(0, so, 3, S1, 0);
+        // steps 0..3 gather entries of (ST, 2), (ST, 3), (S1, 0), (S1, 1) and
+        // compute the addresses of the next step's: (ST, 3), (S1, 0), (S1, 1)
+        // and (S1, 2), the first step of tile kc + 1
+        LUT6_STEP_M(0, so, 1, ST, 3, LUT6_MEM_PC);
+        LUT6_STEP(1, so, 2, S1, 0);
+        LUT6_STEP(0, so, 3, S1, 1);
         __builtin_amdgcn_s_waitcnt(VMCNT0);
         lds_barrier();
-        LUT6_STEP_M(1, sn, 0, S1, 1, LUT6_MEM_X);
+        LUT6_STEP_M(1, sn, 0, S1, 2, LUT6_MEM_X);
 #undef LUT6_MEM_PC
 #undef LUT6_MEM_X
     };
@@ -669,6 +695,8 @@ lut6_tile256_kernel(GemmArgs a)
 #undef LUT6_PAIR
 #undef LUT6_MMA
 #undef LUT6_PACK
+#undef LUT6_LOAD
+#undef LUT6_ADDR
 #undef LUT6_GATHER
     // the last tiles' refetches are still in flight
     __builtin_amdgcn_s_waitcnt(0);
