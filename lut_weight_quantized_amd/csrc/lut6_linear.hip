@@ -181,6 +181,8 @@ constexpr int VMCNT0 = 0x0F70;
 constexpr int VMCNT16 = 0x4F70;
 // lgkmcnt = 0, other counters not waited for
 constexpr int LGKMCNT0 = 0xC07F;
+// lgkmcnt <= 12 (bits 11:8), other counters not waited for
+constexpr int LGKMCNT12 = 0xCC7F;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -1241,9 +1243,13 @@ lut6_stream_kernel(GemmArgs a)
 
     if constexpr (F16) {
         // chunk C computes on fragments read during chunk C - 1 (register
-        // set C % 2); at its start those reads are complete, its slot takes
-        // chunk C + 4, and the fragments of chunk C + 1 are read while its
-        // eight MFMAs run
+        // set C % 2).  Its four MFMA steps each carry a share of the next
+        // chunk's reads (B fragments in steps 0 and 1, then each step's A
+        // gathers) and two of the copies of chunk C + 4 into its slot, so
+        // the MFMAs run while the reads and copies are in flight.  At the
+        // start of chunk C its B reads are complete (LDS returns in order:
+        // at most the twelve gathers issued after them are outstanding), so
+        // its slot can be refilled.
         f16x8 A[2][4], B[2][2][4];
         auto fetch = [&](auto cc) __attribute__((always_inline)) {
             constexpr int C = decltype(cc)::value, RS = C & 1;
@@ -1257,25 +1263,70 @@ lut6_stream_kernel(GemmArgs a)
             A[RS][2] = gather(P16[C], C2{});
             A[RS][3] = gather(P16[C], C3{});
         };
+        // B fragments of steps 2h, 2h + 1 of chunk C
+        auto fetch_b = [&](auto cc, auto hc) __attribute__((always_inline)) {
+            constexpr int C = decltype(cc)::value, RS = C & 1, H = decltype(hc)::value;
+            const uint8_t* const st = slot_base(std::integral_constant<int, C & 3>{});
+#pragma unroll
+            for (int s = 2 * H; s < 2 * H + 2; ++s)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) B[RS][j][s] = *(const f16x8*)(st + 4096 * j + xo[s]);
+        };
+        // copies i and i + 1 of chunk ch into slot SL
+        auto copy_x2 = [&](int ch, auto sc, int i) __attribute__((always_inline)) {
+            uint8_t* const st = slot_base(sc) + wave * S_WAVE_SLOT;
+            const int kc = min(w_begin + ch, kc_last);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(st + (i + u) * 1024), 16, xg[i + u],
+                                                         kc * (BK * 2), 0, 0);
+        };
+        auto scale_b = [&](auto rc, int s) __attribute__((always_inline)) {
+            constexpr int R = decltype(rc)::value;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) B[R][j][s] = B[R][j][s] * a.scale;
+        };
         auto step16 = [&](auto cc) __attribute__((always_inline)) {
-            constexpr int C = decltype(cc)::value, RS = C & 1;
+            constexpr int C = decltype(cc)::value, RS = C & 1, NX = (C + 1) & 1;
+            constexpr bool NEXT = C + 1 < 16, COPY = C + 4 < 16;
+            using SL = std::integral_constant<int, C & 3>;
             __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt(LGKMCNT0);
-            if constexpr (C + 4 < 16) copy_x(C + 4, std::integral_constant<int, C & 3>{});
-            if constexpr (SCALED) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) B[RS][j][s] = B[RS][j][s] * a.scale;
-            }
-            if constexpr (C + 1 < 16) fetch(std::integral_constant<int, C + 1>{});
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_s_waitcnt(LGKMCNT12);
+            __builtin_amdgcn_sched_barrier(0);
+            auto mma = [&](int s) __attribute__((always_inline)) {
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[RS][s], B[RS][0][s], acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[RS][s], B[RS][1][s], acc[1], 0, 0, 0);
-            }
+            };
+            // step 0
+            mma(0);
+            if constexpr (SCALED) scale_b(std::integral_constant<int, RS>{}, 1);
+            if constexpr (NEXT) fetch_b(std::integral_constant<int, C + 1>{}, C0{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (NEXT) A[NX][0] = gather(P16[NEXT ? C + 1 : C], C0{});
+            if constexpr (COPY) copy_x2(C + 4, SL{}, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // step 1
+            mma(1);
+            if constexpr (SCALED) scale_b(std::integral_constant<int, RS>{}, 2);
+            if constexpr (NEXT) fetch_b(std::integral_constant<int, C + 1>{}, C1{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (NEXT) A[NX][1] = gather(P16[NEXT ? C + 1 : C], C1{});
+            if constexpr (COPY) copy_x2(C + 4, SL{}, 2);
+            __builtin_amdgcn_sched_barrier(0);
+            // step 2
+            mma(2);
+            if constexpr (SCALED) scale_b(std::integral_constant<int, RS>{}, 3);
+            if constexpr (NEXT) A[NX][2] = gather(P16[NEXT ? C + 1 : C], C2{});
+            if constexpr (COPY) copy_x2(C + 4, SL{}, 4);
+            __builtin_amdgcn_sched_barrier(0);
+            // step 3
+            mma(3);
+            if constexpr (SCALED && NEXT) scale_b(std::integral_constant<int, NX>{}, 0);
+            if constexpr (NEXT) A[NX][3] = gather(P16[NEXT ? C + 1 : C], C3{});
+            if constexpr (COPY) copy_x2(C + 4, SL{}, 6);
         };
         fetch(C0{});
+        if constexpr (SCALED) scale_b(std::integral_constant<int, 0>{}, 0);
         step16(std::integral_constant<int, 0>{});  step16(std::integral_constant<int, 1>{});
         step16(std::integral_constant<int, 2>{});  step16(std::integral_constant<int, 3>{});
         step16(std::integral_constant<int, 4>{});  step16(std::integral_constant<int, 5>{});
