@@ -4,12 +4,15 @@
 
 Runs ``bench.py --traffic-run`` (one launch of every GEMM of one Gated
 DeltaNet layer and one full-attention layer of the L = 16,384 prefill sweep,
-then a 256 MiB device copy) twice under ``rocprofv3 --pmc``: once for
-FETCH_SIZE, once for WRITE_SIZE (both in KiB per dispatch).  The copy moves
-a known number of bytes, so the counter it reads gives the factor that turns
-counter units into bytes.  Per kernel class (the same classes bench.py uses)
-the result is the average HBM bytes per launch of that class over one sweep
-step: 24 Gated DeltaNet layers and 8 full-attention layers.
+then a 256 MiB device copy) three times under ``rocprofv3 --pmc``: for
+FETCH_SIZE, for WRITE_SIZE (both in KiB per dispatch) and for
+GRBM_GUI_ACTIVE.  The copy moves a known number of bytes, so the counter it
+reads gives the factor that turns counter units into bytes.  Per kernel
+class (the same classes bench.py uses) the result is the average HBM bytes
+per launch of that class over one sweep step (24 Gated DeltaNet layers and 8
+full-attention layers), and the shader clock during that class's GEMM
+dispatches: GRBM_GUI_ACTIVE, which counts busy GPU cycles summed over the 8
+XCDs, divided by 8 and by the dispatch's duration.
 
 Writes gemm_hbm_traffic.json (read by bench.py from profiles/, which
 reports the bytes only while the kernel source hash still matches) and
@@ -35,6 +38,7 @@ OUT = ROOT / "gpurun_out" / "hbm_traffic"
 PROFILES = ROOT / "profiles"
 KERNEL_SOURCES = [ROOT / "lut_weight_quantized_amd" / "csrc" / "lut6_linear.hip"]
 COPY_BYTES = 256 << 20
+NUM_XCD = 8
 LAYER_WEIGHTS = {0: 24, 3: 8}       # layer seen in the run -> layers of its kind per step
 PASS_TIMEOUT_S = 240
 
@@ -101,6 +105,23 @@ def per_dispatch(path: Path, counter: str) -> list[tuple[str, float]]:
     return [(names[d], vals[d]) for d in sorted(vals)]
 
 
+def per_dispatch_clock(path: Path) -> list[tuple[str, float]]:
+    """(kernel name, shader clock in GHz) per dispatch, in dispatch order,
+    from a GRBM_GUI_ACTIVE pass (the counter file carries each dispatch's
+    start and end in ns)."""
+    cyc: dict[int, float] = defaultdict(float)
+    dur: dict[int, int] = {}
+    names: dict[int, str] = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != "GRBM_GUI_ACTIVE":
+            continue
+        d = int(r["Dispatch_Id"])
+        cyc[d] += float(r["Counter_Value"])
+        dur[d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        names[d] = r["Kernel_Name"]
+    return [(names[d], cyc[d] / NUM_XCD / max(dur[d], 1)) for d in sorted(cyc)]
+
+
 def existing(counter: str) -> Path:
     found = list((OUT / counter).rglob("*counter_collection.csv"))
     if not found:
@@ -154,17 +175,34 @@ def main() -> int:
         e["hbm_bytes_per_launch"] = e["read_bytes_per_launch"] + e["write_bytes_per_launch"]
     dominant = max(per_class, key=lambda c: per_class[c]["launches_per_step"])
 
+    # shader clock per class, over its GEMM dispatches (expansions and
+    # reductions excluded), weighted like the bytes
+    clock = [(n, ghz) for n, ghz in per_dispatch_clock(get("GRBM_GUI_ACTIVE"))
+             if classify(n) not in (None, "reduce", "expand")]
+    if len(clock) != 8:
+        raise RuntimeError(f"expected 8 GEMM dispatches in the clock pass, saw {len(clock)}")
+    sums: dict[str, list] = {}
+    for i, (n, ghz) in enumerate(clock):
+        weight = LAYER_WEIGHTS[0] if i < 4 else LAYER_WEIGHTS[3]
+        acc = sums.setdefault(classify(n), [0.0, 0])
+        acc[0] += weight * ghz
+        acc[1] += weight
+    for c, (tot, n) in sums.items():
+        per_class[c]["sclk_ghz"] = round(tot / n, 3)
+
     cmd = "python3 -m lut_weight_quantized_amd.hbm_traffic"
     rec = {
         "kernel_source_sha256": source_sha(),
         "kernel_class": dominant,
         "hbm_bytes_per_launch": per_class[dominant]["hbm_bytes_per_launch"],
+        "sclk_ghz": per_class[dominant].get("sclk_ghz"),
         "per_class": per_class,
         "calibration": {"kernel": copy_name, "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
                         "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)},
         "command": cmd,
         "counter_runs": ["rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --traffic-run",
-                         "rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --traffic-run"],
+                         "rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --traffic-run",
+                         "rocprofv3 --pmc GRBM_GUI_ACTIVE -- python3 bench.py --traffic-run"],
         "date": time.strftime("%Y-%m-%d"),
     }
     dests = [OUT] + ([PROFILES] if "--install" in args else [])
@@ -172,18 +210,22 @@ def main() -> int:
         d.mkdir(parents=True, exist_ok=True)
         (d / "gemm_hbm_traffic.json").write_text(json.dumps(rec, indent=1) + "\n")
 
-    lines = ["# HBM traffic per LUT-6 GEMM launch, prefill sweep at L = 16,384", "",
-             f"Command: `{cmd}` (two counter passes:",
+    lines = ["# HBM traffic and shader clock per LUT-6 GEMM launch, prefill sweep at L = 16,384", "",
+             f"Command: `{cmd}` (three counter passes:",
              "`rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --traffic-run`, then the same with",
-             "`WRITE_SIZE`).  Layers 0 and 3 weighted 24 : 8 as in one sweep step.", "",
+             "`WRITE_SIZE` and with `GRBM_GUI_ACTIVE`).  Layers 0 and 3 weighted 24 : 8 as in one",
+             "sweep step.", "",
              f"Calibration: `{copy_name[:60]}` copying {COPY_BYTES >> 20} MiB reads "
              f"{fetch[-1][1]:.0f} KiB (FETCH_SIZE) and writes {write[-1][1]:.0f} KiB (WRITE_SIZE): "
              f"factors {fetch_factor:.4f} and {write_factor:.4f} bytes per counted byte.", "",
-             "| class | launches/step | read MB/launch | written MB/launch | HBM MB/launch |",
-             "|---|---|---|---|---|"]
+             "Shader clock: `rocprofv3 --pmc GRBM_GUI_ACTIVE -- python3 bench.py --traffic-run`; the",
+             "counter (busy cycles summed over the 8 XCDs) / 8 / each GEMM dispatch's duration.", "",
+             "| class | launches/step | read MB/launch | written MB/launch | HBM MB/launch | clock GHz |",
+             "|---|---|---|---|---|---|"]
     for c, e in sorted(per_class.items()):
         lines.append(f"| {c} | {e['launches_per_step']} | {e['read_bytes_per_launch'] / 1e6:.1f} | "
-                     f"{e['write_bytes_per_launch'] / 1e6:.1f} | {e['hbm_bytes_per_launch'] / 1e6:.1f} |")
+                     f"{e['write_bytes_per_launch'] / 1e6:.1f} | {e['hbm_bytes_per_launch'] / 1e6:.1f} | "
+                     f"{e.get('sclk_ghz', float('nan')):.3f} |")
     lines += ["", "Per dispatch (KiB, raw counters):", "", "| kernel | FETCH_SIZE | WRITE_SIZE |",
               "|---|---|---|"]
     for (n, f), (_, w) in zip(fetch, write):

@@ -176,6 +176,15 @@ WORKLOADS = {
         ((Gemm("qkv|z", 4096, HIDDEN, DN_QKV + DN_Z, EPI_F16),
           Gemm("q|k|v", 4096, HIDDEN, FA_Q + 2 * FA_KV, EPI_F16),
           Gemm("out", 4096, HIDDEN, HIDDEN, EPI_F16, x_tensor=T_A)),)),
+    "hybrid_block_l4096_six": Workload(
+        4, "hybrid_block_l4096_six",
+        "the same block's projections as six launches: qkv, z, out, q, k, v, fp16 out",
+        ((Gemm("qkv", 4096, HIDDEN, DN_QKV, EPI_F16),
+          Gemm("z", 4096, HIDDEN, DN_Z, EPI_F16),
+          Gemm("out", 4096, HIDDEN, HIDDEN, EPI_F16, x_tensor=T_A),
+          Gemm("q", 4096, HIDDEN, FA_Q, EPI_F16),
+          Gemm("k", 4096, HIDDEN, FA_KV, EPI_F16),
+          Gemm("v", 4096, HIDDEN, FA_KV, EPI_F16)),)),
     "prefill_sweep_l16384": Workload(
         5, "prefill_sweep_l16384",
         "all 32 layers' LUT-6 projections and MLPs at L=16384, fp16 out",

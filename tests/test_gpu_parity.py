@@ -225,7 +225,8 @@ def _workload_gemm_check(ora, cfg, layer, proj, g, n_rows):
 
 
 @pytest.mark.parametrize("name,n_rows", [("o_proj_l128", None), ("mlp_gate_up_l512", 24),
-                                         ("mlp_down_l1024", 24), ("hybrid_block_l4096", 12)])
+                                         ("mlp_down_l1024", 24), ("hybrid_block_l4096", 12),
+                                         ("hybrid_block_l4096_six", 12)])
 def test_workload(ora, name, n_rows):
     w = si.WORKLOADS[name]
     for li, pi, g in w.gemms():
