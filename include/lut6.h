@@ -141,9 +141,36 @@ int lut6_linear_path(int64_t L, int64_t K, int64_t N, int epilogue);
 int lut6_dequant(const uint8_t* packed, const void* tables, void* w,
                  int64_t N, int64_t K, hipStream_t stream);
 
+/* Fit the tables and write the packed indices of an FP16 weight [N, K]
+ * (page "Clef-Flash-ANE-LUT6", section "LUT-6 text weights": one 64-entry
+ * table per 16 output channels, from 40 rounds of one-dimensional k-means
+ * started half at quantiles and half evenly between the group's minimum and
+ * maximum).  The steps the page leaves open are fixed as follows, so that
+ * the result is a function of the weight alone (bit for bit, on any run):
+ *   - starting centres: the values of rank floor((2i + 1) n / 64),
+ *     i = 0..31, of the group's n = 16 K values sorted, and
+ *     min + (max - min) * j / 31, j = 0..31, in FP64, sorted;
+ *   - a round assigns each value to its nearest centre (the lower one on a
+ *     tie), replaces each centre by its cluster's mean (kept exactly: a sum
+ *     of FP16 values in 2^-24 units, divided once in FP64), keeps the centre
+ *     of an empty cluster, and sorts the centres;
+ *   - tables[g] is the last centres rounded to FP16 (nearest, ties to
+ *     even), sorted ascending (-0 before +0); each weight's index is its
+ *     nearest entry (the lower one on a tie).
+ * w: device FP16 [N, K], row-major; packed: device uint8 [N, 3K/4] (as
+ * lut6_pack); tables: device FP16 [N/16, 64].  All three 16-byte aligned
+ * (LUT6_E_ALIGN) and not overlapping (LUT6_E_ALIAS).  N % 16 == 0,
+ * K % 64 == 0 and 16 K <= 2^22 (LUT6_E_SHAPE).  Every weight must be
+ * finite; for a group holding inf or NaN the outputs are unspecified.
+ * Enqueued on stream.  The first call allocates a library workspace of
+ * 768 KB per workgroup (at most 256 workgroups: 192 MB), kept until
+ * lut6_release.                                                           */
+int lut6_quantize(const void* w, uint8_t* packed, void* tables, int64_t N, int64_t K,
+                  hipStream_t stream);
+
 /* Free the library's per-device workspaces (after synchronising the
  * devices that hold one).  Optional; safe to call at any time when no
- * lut6_linear call is in flight.                                          */
+ * lut6_linear or lut6_quantize call is in flight.                         */
 int lut6_release(void);
 
 /* Name of a status code ("LUT6_OK", "LUT6_E_SHAPE", ...); never NULL.     */

@@ -30,7 +30,7 @@ STATUS = {0: "LUT6_OK", 1: "LUT6_E_NULL", 2: "LUT6_E_SHAPE", 3: "LUT6_E_ALIGN",
           7: "LUT6_E_DEVICE", 8: "LUT6_E_ALIAS"}
 
 EXPORTS = ("lut6_packed_bytes", "lut6_table_bytes", "lut6_pack", "lut6_unpack",
-           "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_release",
+           "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_quantize", "lut6_release",
            "lut6_status_string")
 
 # kernel paths of lut6_linear (lut6_linear_path)
@@ -75,6 +75,8 @@ def load_library() -> ctypes.CDLL:
     lib.lut6_linear_path.restype = ctypes.c_int
     lib.lut6_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.lut6_dequant.restype = ctypes.c_int
+    lib.lut6_quantize.argtypes = [P, P, P, I64, I64, P]
+    lib.lut6_quantize.restype = ctypes.c_int
     lib.lut6_release.argtypes = []
     lib.lut6_release.restype = ctypes.c_int
     lib.lut6_status_string.argtypes = [ctypes.c_int]
@@ -202,6 +204,29 @@ def dequant(packed, tables, K: int, *, out=None, stream=None):
                                      N, K, _stream_handle(stream))
     _check(st, "lut6_dequant")
     return out
+
+
+def quantize(w, *, packed=None, tables=None, stream=None):
+    """Fit LUT-6 tables to an FP16 weight [N, K] (40 rounds of 1-D k-means per
+    16 rows) and pack its indices; returns (packed uint8 [N, 3K/4], tables
+    float16 [N/16, 64]), both on w's device."""
+    import torch
+    _require(w, torch.float16, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    N, K = w.shape
+    if packed is None:
+        packed = torch.empty((N, K // 4 * 3), dtype=torch.uint8, device=w.device)
+    else:
+        _require(packed, torch.uint8, "packed")
+    if tables is None:
+        tables = torch.empty((N // 16, 64), dtype=torch.float16, device=w.device)
+    else:
+        _require(tables, torch.float16, "tables")
+    st = load_library().lut6_quantize(w.data_ptr(), packed.data_ptr(), tables.data_ptr(),
+                                      N, K, _stream_handle(stream))
+    _check(st, "lut6_quantize")
+    return packed, tables
 
 
 def release() -> None:

@@ -1817,10 +1817,14 @@ extern "C" int lut6_dequant(const uint8_t* packed, const void* tables, void* w, 
     return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
 }
 
+namespace lut6_detail {
+int quantize_release();   // lut6_quantize.hip
+}
+
 extern "C" int lut6_release(void)
 {
+    int status = lut6_detail::quantize_release();
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    int status = LUT6_OK;
     int cur = 0;
     (void)hipGetDevice(&cur);
     for (auto& kv : g_ws) {

@@ -1,0 +1,387 @@
+// LUT-6 table fitting on gfx950: one 64-entry FP16 table per 16 output
+// channels by 40 rounds of one-dimensional k-means, then the packed indices
+// (page "Clef-Flash-ANE-LUT6", section "LUT-6 text weights": 40 rounds per
+// group of 16 channels; half of the starting values are quantiles, the other
+// half spread evenly between the group's minimum and maximum).
+//
+// The page gives nothing finer; the steps follow these readings:
+//   - FP16 weights, all finite; a group is rows 16g .. 16g + 15, n = 16 K
+//     values;
+//   - starting centres: the values of rank floor((2i + 1) n / 64) in the
+//     sorted group (i = 0..31) and min + (max - min) * j / 31 (j = 0..31), in
+//     FP64, sorted;
+//   - a round: boundaries b_i = (c_i + c_{i+1}) / 2; a value v <= b_i and
+//     > b_{i-1} belongs to cluster i; each centre becomes its cluster's mean,
+//     an empty cluster's centre stays; the centres are sorted again;
+//   - sums are exact: FP16 values are integer multiples of 2^-24, so a sum
+//     is a 64-bit count of 2^-24 units and a mean is (double)sum / count *
+//     2^-24;
+//   - the table is the last centres rounded to FP16 (nearest, ties to even),
+//     sorted (-0 before +0); each weight's index is its nearest entry by the
+//     same boundary rule on the FP16 entries.
+//
+// One workgroup per group (a grid of at most Q_MAX_WG workgroups walks the
+// groups).  In one dimension k-means needs no per-value work per round: with
+// the group's values as a histogram over the 65,536 FP16 bit patterns, kept
+// in order-preserving key order, and inclusive prefix counts P and prefix
+// sums S over it, the values <= b are the keys up to the largest key whose
+// value is <= b.  That key is found by a search in registers (the value of a
+// key is computed, not loaded), so a round costs one load of P and one of S
+// per boundary.  The histogram and the prefix arrays live in a library
+// workspace slot of 768 KB per workgroup; they are read through agent-scope
+// loads, so no stale cache line of an earlier group is seen.
+//
+// Compiled for gfx950 only.  No FP contraction in this file: every FP64 step
+// rounds once, as written.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "lut6.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+constexpr int Q_THREADS = 256;
+constexpr int Q_KEYS = 65536;
+constexpr int Q_ROUNDS = 40;
+constexpr int Q_ENTRIES = 64;
+constexpr int Q_MAX_WG = 256;
+// one workspace slot: P (u32) then S (i64) over the 65,536 keys
+constexpr size_t Q_SLOT_BYTES = (size_t)Q_KEYS * 4 + (size_t)Q_KEYS * 8;
+
+// Order-preserving key of an FP16 bit pattern: negative values reversed
+// below 0x8000, positive values above (-0 just below +0).
+__device__ __forceinline__ uint32_t q_key(uint32_t h)
+{
+    return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
+__device__ __forceinline__ uint32_t q_bits(uint32_t key)
+{
+    return (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+}
+// A finite FP16 value in units of 2^-24 (|result| < 2^41).
+__device__ __forceinline__ int64_t q_units(uint32_t h)
+{
+    const int e = (h >> 10) & 31, m = h & 1023;
+    const int64_t u = e == 0 ? (int64_t)m : ((int64_t)(1024 + m) << (e - 1));
+    return (h & 0x8000u) ? -u : u;
+}
+// The value of a finite FP16 pattern as a double (-0 stays -0).
+__device__ __forceinline__ double q_value(uint32_t h)
+{
+    const int e = (h >> 10) & 31, m = h & 1023;
+    const double mag = e == 0 ? ldexp((double)m, -24) : ldexp((double)(1024 + m), e - 25);
+    return (h & 0x8000u) ? -mag : mag;
+}
+// Largest key in [lo_key, hi_key] whose value is <= b, or lo_key - 1 if none
+// (every key in the range is a finite value, increasing with the key).
+__device__ __forceinline__ int q_floor_key(double b, int lo_key, int hi_key)
+{
+    int lo = lo_key - 1, hi = hi_key;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (q_value(q_bits((uint32_t)mid)) <= b) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+// FP16 bit pattern nearest to c, ties to the even pattern; c lies within
+// the values of keys [lo_key, hi_key] (a centre is a mean of the group's
+// values, so it does).
+__device__ __forceinline__ uint32_t q_round_f16(double c, int lo_key, int hi_key)
+{
+    if (c == 0.0) return __builtin_signbit(c) ? 0x8000u : 0u;
+    const int k1 = q_floor_key(c, lo_key, hi_key);
+    const uint32_t h1 = q_bits((uint32_t)k1);
+    const double v1 = q_value(h1);
+    if (v1 == c || k1 >= hi_key) return h1;
+    const uint32_t h2 = q_bits((uint32_t)(k1 + 1));
+    const double d1 = c - v1, d2 = q_value(h2) - c;   // exact: v1 < c < v2, neighbours
+    if (d1 < d2) return h1;
+    if (d2 < d1) return h2;
+    return (h1 & 1u) ? h2 : h1;
+}
+
+template <typename T>
+__device__ __forceinline__ T q_load(const T* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sort 64 doubles in LDS (ascending; of equal values -0 first, then by
+// position): each of 64 threads computes its element's rank.
+__device__ __forceinline__ void q_rank_sort(const double* src, double* dst, int tid)
+{
+    if (tid < Q_ENTRIES) {
+        const double v = src[tid];
+        const bool vneg = __builtin_signbit(v);
+        int rank = 0;
+        for (int j = 0; j < Q_ENTRIES; ++j) {
+            const double u = src[j];
+            const bool before = u < v || (u == v && ((__builtin_signbit(u) && !vneg) ||
+                                                     (__builtin_signbit(u) == vneg && j < tid)));
+            rank += before ? 1 : 0;
+        }
+        dst[rank] = v;
+    }
+}
+
+__global__ void __launch_bounds__(Q_THREADS)
+lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packed,
+                     uint16_t* __restrict__ tables, int N, int K, uint8_t* __restrict__ work)
+{
+    __shared__ uint8_t map[Q_KEYS];                 // key -> index of the final table
+    __shared__ double cen[Q_ENTRIES], tmp[Q_ENTRIES], bnd[Q_ENTRIES];
+    __shared__ uint32_t cle[Q_ENTRIES];
+    __shared__ int64_t sle[Q_ENTRIES];
+    __shared__ uint32_t part_c[Q_THREADS];
+    __shared__ int64_t part_s[Q_THREADS];
+    __shared__ int key_lo, key_hi;
+
+    const int tid = threadIdx.x;
+    uint32_t* const P = (uint32_t*)(work + (size_t)blockIdx.x * Q_SLOT_BYTES);
+    int64_t* const S = (int64_t*)(work + (size_t)blockIdx.x * Q_SLOT_BYTES + (size_t)Q_KEYS * 4);
+    const int groups = N / 16;
+    const int64_t n = 16 * (int64_t)K;
+    const int row_bytes = K / 4 * 3;
+
+    for (int g = blockIdx.x; g < groups; g += gridDim.x) {
+        const uint16_t* const wg = w + (size_t)g * 16 * K;
+
+        // 1. histogram of the group's FP16 patterns, by key
+        for (int i = tid; i < Q_KEYS; i += Q_THREADS) P[i] = 0u;
+        if (tid == 0) { key_lo = Q_KEYS; key_hi = -1; }
+        __threadfence();
+        __syncthreads();
+        for (int64_t i = tid; i < n; i += Q_THREADS)
+            __hip_atomic_fetch_add(P + q_key(wg[i]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __threadfence();
+        __syncthreads();
+
+        // 2. inclusive prefix counts P and exact prefix sums S over the keys:
+        //    thread t owns keys [256 t, 256 t + 256)
+        uint32_t c_own = 0;
+        int64_t s_own = 0;
+        int first = Q_KEYS, lastk = -1;
+        for (int j = 0; j < 256; ++j) {
+            const int key = tid * 256 + j;
+            const uint32_t c = q_load(P + key);
+            if (c) {
+                first = min(first, key);
+                lastk = key;
+                c_own += c;
+                s_own += (int64_t)c * q_units(q_bits((uint32_t)key));
+            }
+        }
+        part_c[tid] = c_own;
+        part_s[tid] = s_own;
+        if (lastk >= 0) {
+            atomicMin(&key_lo, first);
+            atomicMax(&key_hi, lastk);
+        }
+        __syncthreads();
+        // Hillis-Steele inclusive scan of the 256 partials
+        for (int d = 1; d < Q_THREADS; d <<= 1) {
+            const uint32_t ac = tid >= d ? part_c[tid - d] : 0u;
+            const int64_t as = tid >= d ? part_s[tid - d] : 0;
+            __syncthreads();
+            part_c[tid] += ac;
+            part_s[tid] += as;
+            __syncthreads();
+        }
+        {
+            uint32_t run_c = tid ? part_c[tid - 1] : 0u;
+            int64_t run_s = tid ? part_s[tid - 1] : 0;
+            for (int j = 0; j < 256; ++j) {
+                const int key = tid * 256 + j;
+                const uint32_t c = q_load(P + key);
+                run_c += c;
+                run_s += (int64_t)c * (c ? q_units(q_bits((uint32_t)key)) : 0);
+                P[key] = run_c;
+                S[key] = run_s;
+            }
+        }
+        __threadfence();
+        __syncthreads();
+        const int klo = key_lo, khi = key_hi;
+
+        // 3. starting centres: 32 quantiles and 32 evenly spread values
+        if (tid < 32) {
+            // smallest key with P > rank
+            const int64_t rank = ((int64_t)(2 * tid + 1) * n) / 64;
+            int lo = klo, hi = khi;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if ((int64_t)q_load(P + mid) > rank) hi = mid;
+                else lo = mid + 1;
+            }
+            tmp[tid] = q_value(q_bits((uint32_t)lo));
+        } else if (tid < 64) {
+            const double vlo = q_value(q_bits((uint32_t)klo)), vhi = q_value(q_bits((uint32_t)khi));
+            const double span = vhi - vlo;
+            const double step = span * (double)(tid - 32);
+            tmp[tid] = vlo + step / 31.0;
+        }
+        __syncthreads();
+        q_rank_sort(tmp, cen, tid);
+        __syncthreads();
+
+        // 4. Lloyd rounds
+        for (int round = 0; round < Q_ROUNDS; ++round) {
+            if (tid < Q_ENTRIES - 1) {
+                const double b = (cen[tid] + cen[tid + 1]) * 0.5;
+                const int k = q_floor_key(b, klo, khi);
+                // P and S are zero below the smallest key present
+                cle[tid] = k >= klo ? q_load(P + k) : 0u;
+                sle[tid] = k >= klo ? q_load(S + k) : 0;
+            } else if (tid == Q_ENTRIES - 1) {
+                cle[tid] = (uint32_t)n;
+                sle[tid] = q_load(S + khi);
+            }
+            __syncthreads();
+            if (tid < Q_ENTRIES) {
+                const uint32_t num = cle[tid] - (tid ? cle[tid - 1] : 0u);
+                const int64_t sum = sle[tid] - (tid ? sle[tid - 1] : 0);
+                tmp[tid] = num ? ldexp((double)sum / (double)num, -24) : cen[tid];
+            }
+            __syncthreads();
+            q_rank_sort(tmp, cen, tid);
+            __syncthreads();
+        }
+
+        // 5. the FP16 table, sorted, and the final boundaries
+        if (tid < Q_ENTRIES) tmp[tid] = q_value(q_round_f16(cen[tid], klo, khi));
+        __syncthreads();
+        q_rank_sort(tmp, bnd, tid);
+        __syncthreads();
+        if (tid < Q_ENTRIES) {
+            const double t = bnd[tid];
+            const uint32_t h = t == 0.0 ? (__builtin_signbit(t) ? 0x8000u : 0u) : q_round_f16(t, klo, khi);
+            tables[(size_t)g * Q_ENTRIES + tid] = (uint16_t)h;
+            tmp[tid] = t;
+        }
+        __syncthreads();
+        if (tid < Q_ENTRIES - 1) bnd[tid] = (tmp[tid] + tmp[tid + 1]) * 0.5;
+        __syncthreads();
+
+        // 6. key -> index: the number of boundaries below the key's value
+        for (int key = klo + tid; key <= khi; key += Q_THREADS) {
+            const double v = q_value(q_bits((uint32_t)key));
+            int lo = 0, hi = Q_ENTRIES - 1;            // count of bnd[0..62] < v
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (bnd[mid] < v) lo = mid + 1;
+                else hi = mid;
+            }
+            map[key] = (uint8_t)lo;
+        }
+        __syncthreads();
+
+        // 7. pack: 16 consecutive weights of a row -> 12 bytes (three words)
+        const int units_per_row = K / 16;
+        for (int u = tid; u < 16 * units_per_row; u += Q_THREADS) {
+            const int r = u / units_per_row, c = u % units_per_row;
+            const uint16_t* src = wg + (size_t)r * K + 16 * c;
+            uint32_t out[3] = {0u, 0u, 0u};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) word |= (uint32_t)map[q_key(src[4 * q + t])] << (6 * t);
+                // 24-bit little-endian word q at byte 3q of the 12
+#pragma unroll
+                for (int b = 0; b < 3; ++b) {
+                    const int byte = 3 * q + b;
+                    out[byte >> 2] |= ((word >> (8 * b)) & 0xFFu) << (8 * (byte & 3));
+                }
+            }
+            uint32_t* dst = (uint32_t*)(packed + (size_t)(16 * g + r) * row_bytes + 12 * c);
+            dst[0] = out[0];
+            dst[1] = out[1];
+            dst[2] = out[2];
+        }
+        __syncthreads();
+    }
+}
+
+struct QWorkspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_qws_mutex;
+std::map<std::tuple<int, uintptr_t>, QWorkspace> g_qws;   // key: (device, stream)
+
+int q_workspace(hipStream_t stream, size_t bytes, void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LUT6_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_qws_mutex);
+    QWorkspace& ws = g_qws[std::make_tuple(dev, (uintptr_t)stream)];
+    if (ws.bytes < bytes) {
+        if (ws.ptr) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return LUT6_E_DEVICE;
+            (void)hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess) return LUT6_E_DEVICE;
+        ws.ptr = p;
+        ws.bytes = bytes;
+    }
+    *out = ws.ptr;
+    return LUT6_OK;
+}
+
+bool q_overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+extern "C" int lut6_quantize(const void* w, uint8_t* packed, void* tables, int64_t N, int64_t K,
+                             hipStream_t stream)
+{
+    if (!w || !packed || !tables) return LUT6_E_NULL;
+    if (N <= 0 || K <= 0 || N % 16 || K % 64 || 16 * K > (1 << 22) || N > INT32_MAX) return LUT6_E_SHAPE;
+    if (((uintptr_t)w | (uintptr_t)packed | (uintptr_t)tables) & 15u) return LUT6_E_ALIGN;
+    const size_t wb = (size_t)N * K * 2, pb = (size_t)N * (K / 4 * 3), tb = (size_t)(N / 16) * 128;
+    if (q_overlaps(packed, pb, w, wb) || q_overlaps(tables, tb, w, wb) || q_overlaps(packed, pb, tables, tb))
+        return LUT6_E_ALIAS;
+    const int groups = (int)(N / 16);
+    const int wgs = groups < Q_MAX_WG ? groups : Q_MAX_WG;
+    void* work = nullptr;
+    const int st = q_workspace(stream, (size_t)wgs * Q_SLOT_BYTES, &work);
+    if (st != LUT6_OK) return st;
+    hipLaunchKernelGGL(lut6_quantize_kernel, dim3((unsigned)wgs), dim3(Q_THREADS), 0, stream,
+                       (const uint16_t*)w, packed, (uint16_t*)tables, (int)N, (int)K, (uint8_t*)work);
+    return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+}
+
+namespace lut6_detail {
+// Free the table-fitting workspaces (lut6_release calls this), after
+// synchronising the devices that hold one.
+int quantize_release()
+{
+    std::lock_guard<std::mutex> lock(g_qws_mutex);
+    int status = LUT6_OK;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (auto& kv : g_qws) {
+        if (!kv.second.ptr) continue;
+        if (hipSetDevice(std::get<0>(kv.first)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+            status = LUT6_E_DEVICE;
+        (void)hipFree(kv.second.ptr);
+    }
+    g_qws.clear();
+    (void)hipSetDevice(cur);
+    return status;
+}
+}  // namespace lut6_detail

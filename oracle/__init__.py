@@ -69,6 +69,8 @@ class Oracle:
         lib.ora_linear.argtypes = [_P, _P, _P, _I64, _I64, _I64, ctypes.c_double,
                                    ctypes.c_int, _P, _I64, ctypes.c_int, _P, _P]
         lib.ora_linear.restype = ctypes.c_int
+        lib.ora_quantize.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P]
+        lib.ora_quantize.restype = ctypes.c_int
         lib.ora_packed_bytes.argtypes = [_I64, _I64]
         lib.ora_packed_bytes.restype = _I64
         lib.ora_table_bytes.argtypes = [_I64]
@@ -158,6 +160,27 @@ class Oracle:
         if st != OK:
             raise OracleError(f"ora_linear status {st}")
         return y_exact, y_out
+
+
+    # -- table fitting ---------------------------------------------------
+    def quantize(self, w16: np.ndarray, groups=None, with_sse: bool = False):
+        """1-D k-means tables and packed indices of an FP16 weight [N, K].
+
+        Returns (packed uint8 [N, 3K/4], tables uint16 [N/16, 64]), and the
+        41 SSE values of the first group when with_sse; with ``groups`` =
+        (g0, g1) only those groups' rows and tables are computed (the rest
+        are zero)."""
+        w = np.ascontiguousarray(np.asarray(w16).view(np.uint16))
+        n, k = w.shape
+        g0, g1 = (0, n // 16) if groups is None else groups
+        packed = np.zeros((n, 3 * k // 4), np.uint8)
+        tables = np.zeros((n // 16, 64), np.uint16)
+        sse = np.zeros(41, np.float64)
+        st = self.lib.ora_quantize(w.ctypes.data, packed.ctypes.data, tables.ctypes.data, n, k,
+                                   int(g0), int(g1), sse.ctypes.data if with_sse else None)
+        if st != OK:
+            raise OracleError(f"ora_quantize status {st}")
+        return (packed, tables, sse) if with_sse else (packed, tables)
 
 
 _default: Oracle | None = None

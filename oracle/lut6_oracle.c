@@ -373,3 +373,135 @@ int ora_linear(const uint16_t *x, const uint8_t *packed, const uint16_t *tables,
 /* Bytes of a packed [n, k] weight and of its tables (format sizes). */
 int64_t ora_packed_bytes(int64_t n, int64_t k) { return n * (3 * k / 4); }
 int64_t ora_table_bytes(int64_t n) { return (n / 16) * 64 * 2; }
+
+/* ---------------- table fitting: 1-D k-means per 16 channels -------- */
+/*
+ * Page "Clef-Flash-ANE-LUT6", section "LUT-6 text weights": each group of
+ * 16 output channels gets its own 64-value table from 40 rounds of
+ * one-dimensional k-means; half of the starting values are quantiles, the
+ * other half are spread evenly between the group's minimum and maximum.
+ *
+ * Readings taken where the page leaves a step open (the page gives only the
+ * round count and the mix of starting values):
+ *   - the weights arrive as FP16 and every value is finite;
+ *   - the group's n = 16 K values, sorted ascending, give the 32 quantiles
+ *     v[floor((2i + 1) n / 64)], i = 0..31 (the middle of each of 32 equal
+ *     shares), and the 32 evenly spread values min + (max - min) * j / 31,
+ *     j = 0..31 (both ends included), in FP64; the 64 starting centres are
+ *     these, sorted ascending;
+ *   - one round (Lloyd's algorithm): with b_i = (c_i + c_{i+1}) / 2, a value
+ *     v belongs to cluster i when b_{i-1} < v <= b_i (a value exactly on a
+ *     boundary goes to the lower cluster); each centre becomes the mean of
+ *     its cluster; a centre with an empty cluster keeps its value; the
+ *     centres are then sorted again;
+ *   - a cluster's sum is exact: every FP16 value is an integer multiple of
+ *     2^-24, so the sum is kept as a 64-bit integer count of 2^-24 units,
+ *     and the mean is (double)sum / count * 2^-24 (one conversion and one
+ *     division, each rounded to nearest);
+ *   - after the 40th round the centres are rounded to FP16 (to nearest,
+ *     ties to even) and sorted ascending (-0 before +0): that is the table;
+ *   - each weight's index is its nearest table entry, by the same boundary
+ *     rule on the FP16 entries (the lower index on a tie);
+ *   - the indices are packed as by ora_pack.
+ * There is nothing for this to match bit for bit on the page; the tests pin
+ * it with properties k-means has whatever the details (see
+ * tests/test_oracle_pins.py).
+ */
+#define ORA_KM_ROUNDS 40
+#define ORA_KM_ENTRIES 64
+
+/* Ascending by value; of two zeros, -0 first (so sorted FP16 values are in
+ * bit-pattern order, and a table holding both zeros stores -0 first). */
+static int ora_cmp_double(const void *a, const void *b)
+{
+    double x = *(const double *)a, y = *(const double *)b;
+    if (x < y) return -1;
+    if (x > y) return 1;
+    return (signbit(y) != 0) - (signbit(x) != 0);
+}
+
+/* A finite FP16 value in units of 2^-24 (exact: |result| < 2^41). */
+static int64_t ora_f16_units(uint16_t h)
+{
+    int64_t e = (h >> 10) & 31, m = h & 1023;
+    int64_t u = e == 0 ? m : (1024 + m) << (e - 1);
+    return (h & 0x8000) ? -u : u;
+}
+
+/* Cluster of v for sorted centres c[0..63]: the number of boundaries
+ * (c_i + c_{i+1}) / 2 strictly below v. */
+static int ora_km_cluster(double v, const double *c)
+{
+    int i = 0;
+    while (i < ORA_KM_ENTRIES - 1 && (c[i] + c[i + 1]) * 0.5 < v) ++i;
+    return i;
+}
+
+/* Groups [g0, g1) of an FP16 weight [n, k] (n % 16 == 0, k % 4 == 0):
+ * tables[g] (64 FP16) and the packed rows 16g .. 16g + 15.  sse, when not
+ * NULL, receives for group g0 the sum of squared distances to the centres
+ * before round 1 and after each of the 40 rounds (41 values). */
+int ora_quantize(const uint16_t *w, uint8_t *packed, uint16_t *tables, int64_t n, int64_t k,
+                 int64_t g0, int64_t g1, double *sse)
+{
+    if (!w || !packed || !tables) return ORA_E_NULL;
+    if (n <= 0 || k <= 0 || n % 16 || k % 4 || g0 < 0 || g1 > n / 16 || g0 > g1) return ORA_E_SHAPE;
+    const int64_t cnt = 16 * k;
+    double *v = malloc(sizeof(double) * cnt);
+    int64_t *u = malloc(sizeof(int64_t) * cnt);
+    uint8_t *idx = malloc(16 * k);
+    if (!v || !u || !idx) { free(v); free(u); free(idx); return ORA_E_NOMEM; }
+    int status = ORA_OK;
+    for (int64_t g = g0; g < g1 && status == ORA_OK; ++g) {
+        /* the group's values, sorted ascending */
+        for (int64_t r = 0; r < 16; ++r)
+            for (int64_t j = 0; j < k; ++j) {
+                uint16_t h = w[(16 * g + r) * k + j];
+                if (((h >> 10) & 31) == 31) { status = ORA_E_SHAPE; break; }
+                v[r * k + j] = ora_f16_to_f64(h);
+            }
+        if (status != ORA_OK) break;
+        qsort(v, (size_t)cnt, sizeof(double), ora_cmp_double);
+        for (int64_t i = 0; i < cnt; ++i) u[i] = ora_f16_units(ora_f64_to_f16(v[i]));
+
+        /* starting centres */
+        double c[ORA_KM_ENTRIES];
+        const double lo = v[0], hi = v[cnt - 1];
+        for (int i = 0; i < 32; ++i) c[i] = v[((2 * i + 1) * cnt) / 64];
+        for (int j = 0; j < 32; ++j) c[32 + j] = lo + (hi - lo) * (double)j / 31.0;
+        qsort(c, ORA_KM_ENTRIES, sizeof(double), ora_cmp_double);
+
+        for (int round = 0; round <= ORA_KM_ROUNDS; ++round) {
+            if (sse && g == g0) {
+                double s = 0.0;
+                for (int64_t i = 0; i < cnt; ++i) {
+                    double d = v[i] - c[ora_km_cluster(v[i], c)];
+                    s += d * d;
+                }
+                sse[round] = s;
+            }
+            if (round == ORA_KM_ROUNDS) break;
+            int64_t sum[ORA_KM_ENTRIES] = {0}, num[ORA_KM_ENTRIES] = {0};
+            for (int64_t i = 0; i < cnt; ++i) {
+                int q = ora_km_cluster(v[i], c);
+                sum[q] += u[i];
+                num[q] += 1;
+            }
+            for (int q = 0; q < ORA_KM_ENTRIES; ++q)
+                if (num[q]) c[q] = ldexp((double)sum[q] / (double)num[q], -24);
+            qsort(c, ORA_KM_ENTRIES, sizeof(double), ora_cmp_double);
+        }
+
+        /* the table, and each weight's nearest entry */
+        double t[ORA_KM_ENTRIES];
+        for (int q = 0; q < ORA_KM_ENTRIES; ++q) t[q] = ora_f16_to_f64(ora_f64_to_f16(c[q]));
+        qsort(t, ORA_KM_ENTRIES, sizeof(double), ora_cmp_double);
+        for (int q = 0; q < ORA_KM_ENTRIES; ++q) tables[g * ORA_KM_ENTRIES + q] = ora_f64_to_f16(t[q]);
+        for (int64_t r = 0; r < 16; ++r)
+            for (int64_t j = 0; j < k; ++j)
+                idx[r * k + j] = (uint8_t)ora_km_cluster(ora_f16_to_f64(w[(16 * g + r) * k + j]), t);
+        status = ora_pack(idx, packed + 16 * g * (3 * k / 4), 16, k);
+    }
+    free(v); free(u); free(idx);
+    return status;
+}

@@ -144,3 +144,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(lq, "LIB_PATH", tmp_path / "liblut6.so")
     with pytest.raises(RuntimeError, match="missing"):
         lq.load_library()
+
+
+def _quantize(w=X, p=P, t=T, N=4096, K=4096):
+    return lq.load_library().lut6_quantize(w, p, t, N, K, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(w=None), 1), (dict(p=None), 1), (dict(t=None), 1),
+    (dict(N=0), 2), (dict(N=4008), 2), (dict(K=0), 2), (dict(K=100), 2), (dict(K=4032 + 32), 2),
+    (dict(K=2 ** 18 + 64), 2), (dict(N=2 ** 32), 2),
+    (dict(w=X + 2), 3), (dict(p=P + 4), 3), (dict(t=T + 8), 3),
+    (dict(p=X), 8), (dict(t=X + 64), 8), (dict(t=P), 8),
+])
+def test_quantize_validation(kwargs, status):
+    # refusals are decided on the host, before any device call
+    assert _quantize(**kwargs) == status

@@ -313,3 +313,78 @@ def test_mutation_controls(tmp_path, ora, mutant, epi, s):
     bad = oracle.Oracle(oracle.build(tmp_path / f"m{mutant}.so", mutant=mutant))
     # the mutant reads bytes packed by the correct oracle
     assert not oracle_check(bad, x, idx, tab, epi, s, y, packer=ora).ok
+
+
+# ---------------------------------------------------------------------------
+# table fitting: lut6_quantize against the oracle, bit for bit (tables and
+# packed indices)
+# ---------------------------------------------------------------------------
+
+def _q_weights(N, K, seed, kind):
+    g = np.random.default_rng(seed)
+    if kind == "normal":
+        w = g.standard_normal((N, K)) * 0.02
+        w[g.random((N, K)) < 0.02] *= 8.0
+        return w.astype(np.float16)
+    if kind == "edge":
+        # groups of their own kind: constant, two values, zeros of both signs
+        # with subnormals, few distinct values, huge range
+        w = (g.standard_normal((N, K)) * 0.02).astype(np.float16)
+        groups = N // 16
+        for gi in range(groups):
+            blk = w[16 * gi:16 * gi + 16]
+            mode = gi % 5
+            if mode == 0:
+                blk[:] = np.float16(-1.5)
+            elif mode == 1:
+                blk[:] = np.where(g.random(blk.shape) < 0.5, np.float16(0.25), np.float16(-0.0078))
+            elif mode == 2:
+                bits = g.integers(0, 1024, size=blk.shape).astype(np.uint16)
+                bits[g.random(blk.shape) < 0.3] = 0
+                bits |= (g.random(blk.shape) < 0.5).astype(np.uint16) << 15
+                blk[:] = bits.view(np.float16)
+            elif mode == 3:
+                blk[:] = g.choice(np.array([-2.0, -0.5, 0.0, 0.125, 3.0], np.float16), size=blk.shape)
+            else:
+                blk[:] = (g.standard_normal(blk.shape) * 100.0).astype(np.float16)
+        return w
+    raise ValueError(kind)
+
+
+def _gpu_quantize(w16):
+    p, t = lq.quantize(_dev(w16))
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), t.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("N,K,kind", [(16, 64, "normal"), (32, 256, "normal"), (48, 1024, "normal"),
+                                      (80, 128, "edge"), (160, 64, "edge"), (64, 4096, "normal"),
+                                      (16, 12288, "normal")])
+def test_quantize_matches_oracle(ora, N, K, kind):
+    _say("quantize", N, K, kind)
+    w = _q_weights(N, K, N + K, kind)
+    p_gpu, t_gpu = _gpu_quantize(w)
+    p_ora, t_ora = ora.quantize(w)
+    assert np.array_equal(t_gpu, t_ora), "tables"
+    assert np.array_equal(p_gpu, p_ora), "packed indices"
+
+
+def test_quantize_full_layer_sampled_groups(ora):
+    # a 4,096 x 4,096 weight (256 groups, 256 workgroups): four groups
+    # against the oracle, every group twice on the GPU (same bytes)
+    _say("quantize full", 4096, 4096)
+    w = _q_weights(4096, 4096, 77, "normal")
+    wd = _dev(w)
+    p1, t1 = lq.quantize(wd)
+    p2, t2 = lq.quantize(wd)
+    torch.cuda.synchronize()
+    p1, t1 = p1.cpu().numpy(), t1.cpu().numpy().view(np.uint16)
+    assert np.array_equal(p1, p2.cpu().numpy()) and np.array_equal(t1, t2.cpu().numpy().view(np.uint16))
+    for g in (0, 1, 137, 255):
+        p_ora, t_ora = ora.quantize(w, groups=(g, g + 1))
+        assert np.array_equal(t1[g], t_ora[g]), f"table of group {g}"
+        assert np.array_equal(p1[16 * g:16 * g + 16], p_ora[16 * g:16 * g + 16]), f"indices of group {g}"
+    # the fitted tables reproduce the weight to about 6-bit precision
+    back = ora.dequant(p1[:64], t1[:4], 4096).view(np.float16).astype(np.float64)
+    ref = w[:64].astype(np.float64)
+    assert np.sqrt(np.mean((back - ref) ** 2)) < 0.05 * np.sqrt(np.mean(ref ** 2))
