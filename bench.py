@@ -26,6 +26,9 @@ starts.  The line printed is throughput in TFLOP/s, with
     least 512 MB) that the last-level cache cannot hold them: TFLOP/s and
     algorithmic GB/s against the FP16 peak and HBM bandwidth; and, labelled
     warm, the same passes on one buffer set;
+  * quantize: lut6_quantize (table fitting by 1-D k-means) on a 4,096 x 4,096
+    and a 4,096 x 12,288 seeded FP16 weight: time per call, weights per
+    second and algorithmic GB/s, with the oracle on one 16-row group beside;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same step
     (sampled token rows of two layers), on this host's cores;
   * parity_sample: those sampled rows of the GPU result against the oracle.
@@ -167,6 +170,55 @@ def time_workload(lq, si, torch, stream, name: str, launches: int = 20) -> dict:
             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "flops": w.flops, "algorithmic_bytes": w.bytes,
             "buffer_sets_rotated": sets, "warm_us_per_pass": round(us_warm, 2),
             "warm_tflop_s": round(tf_warm, 1), "warm_frac_fp16_peak": round(tf_warm / PEAK_FP16_TFLOPS, 4)}
+
+
+QUANT_SHAPES = (("o_proj", 4096, 4096), ("down", 4096, 12288))
+
+
+def time_quantize(lq, si, torch, stream, no_cpu: bool) -> list:
+    """lut6_quantize (table fitting) on two seeded weights: median of 3 runs
+    of 5 back-to-back calls; algorithmic bytes = the FP16 weight read once
+    plus the packed indices and tables written.  Beside it, the oracle on
+    one 16-row group, scaled to the whole weight."""
+    out = []
+    for name, N, K in QUANT_SHAPES:
+        w16 = si.weights(N, K, (9, 0, K))
+        w = torch.from_numpy(w16).to("cuda")
+        packed = torch.empty((N, K // 4 * 3), dtype=torch.uint8, device="cuda")
+        tables = torch.empty((N // 16, 64), dtype=torch.float16, device="cuda")
+        for _ in range(2):
+            lq.quantize(w, packed=packed, tables=tables, stream=stream)
+        torch.cuda.synchronize()
+        reps = []
+        for r in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                lq.quantize(w, packed=packed, tables=tables, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) * 1e3 / 5)
+        us = sorted(reps)[1]
+        nbytes = N * K * 2 + N * K // 4 * 3 + N // 16 * 128
+        rec = {"weight": f"{name} N={N} K={K}", "us_per_call": round(us, 1),
+               "gweights_per_s": round(N * K / (us * 1e-6) / 1e9, 2),
+               "gb_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+               "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+               "algorithmic_bytes": nbytes, "groups": N // 16}
+        if not no_cpu:
+            import oracle
+            ora = oracle.load()
+            t0 = time.perf_counter()
+            ora.quantize(w16, groups=(0, 1))
+            cpu_s = time.perf_counter() - t0
+            rec["cpu_oracle"] = {"s_per_group": round(cpu_s, 3), "cores": 1, "kind": "oracle",
+                                 "us_per_call_scaled": round(cpu_s * (N // 16) * 1e6, 0),
+                                 "sample": "one 16-row group, single thread, scaled to all groups"}
+        out.append(rec)
+        del w, packed, tables
+    torch.cuda.empty_cache()
+    return out
 
 
 def main() -> int:
@@ -397,6 +449,8 @@ def main() -> int:
     del sets_w
 
     # ---------------- the other workloads ----------------
+    quant = time_quantize(lq, si, torch, stream, args.no_cpu_baseline)
+
     per_config = []
     for name in OTHER_WORKLOADS:
         rec = time_workload(lq, si, torch, stream, name)
@@ -425,6 +479,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "l128_stream": stream_rec,
         "per_config": per_config,
+        "quantize": quant,
         "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)

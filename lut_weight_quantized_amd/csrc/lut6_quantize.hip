@@ -27,9 +27,12 @@
 // sums S over it, the values <= b are the keys up to the largest key whose
 // value is <= b.  That key is found by a search in registers (the value of a
 // key is computed, not loaded), so a round costs one load of P and one of S
-// per boundary.  The histogram and the prefix arrays live in a library
-// workspace slot of 768 KB per workgroup; they are read through agent-scope
-// loads, so no stale cache line of an earlier group is seen.
+// per boundary.  The histogram is counted in LDS, 32,768 keys per pass (one
+// pass covers every FP16 value in [-0.5, 0.5]); P and S go to a library
+// workspace slot of 768 KB per workgroup, written and read back by that
+// workgroup alone, so plain loads see them (a CU's waves share its vector
+// cache).  Agent-scope atomics and loads on that scratch, the first design,
+// went past the per-XCD L2 on every access and took about 1.2 ms per group.
 //
 // Compiled for gfx950 only.  No FP contraction in this file: every FP64 step
 // rounds once, as written.
@@ -51,6 +54,7 @@ constexpr int Q_KEYS = 65536;
 constexpr int Q_ROUNDS = 40;
 constexpr int Q_ENTRIES = 64;
 constexpr int Q_MAX_WG = 256;
+constexpr int Q_CHUNK = 32768;      // histogram keys per LDS pass
 // one workspace slot: P (u32) then S (i64) over the 65,536 keys
 constexpr size_t Q_SLOT_BYTES = (size_t)Q_KEYS * 4 + (size_t)Q_KEYS * 8;
 
@@ -107,12 +111,6 @@ __device__ __forceinline__ uint32_t q_round_f16(double c, int lo_key, int hi_key
     return (h1 & 1u) ? h2 : h1;
 }
 
-template <typename T>
-__device__ __forceinline__ T q_load(const T* p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Sort 64 doubles in LDS (ascending; of equal values -0 first, then by
 // position): each of 64 threads computes its element's rank.
 __device__ __forceinline__ void q_rank_sort(const double* src, double* dst, int tid)
@@ -121,6 +119,7 @@ __device__ __forceinline__ void q_rank_sort(const double* src, double* dst, int 
         const double v = src[tid];
         const bool vneg = __builtin_signbit(v);
         int rank = 0;
+#pragma unroll
         for (int j = 0; j < Q_ENTRIES; ++j) {
             const double u = src[j];
             const bool before = u < v || (u == v && ((__builtin_signbit(u) && !vneg) ||
@@ -135,9 +134,14 @@ __global__ void __launch_bounds__(Q_THREADS)
 lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packed,
                      uint16_t* __restrict__ tables, int N, int K, uint8_t* __restrict__ work)
 {
-    __shared__ uint8_t map[Q_KEYS];                 // key -> index of the final table
+    // 128 KB: a histogram chunk (u32) during the scan, then the key -> index
+    // map of the final table (u8)
+    __shared__ __attribute__((aligned(16))) uint32_t lds_buf[Q_CHUNK];
+    uint32_t* const hist = lds_buf;
+    uint8_t* const map = (uint8_t*)lds_buf;
     __shared__ double cen[Q_ENTRIES], tmp[Q_ENTRIES], bnd[Q_ENTRIES];
     __shared__ uint32_t cle[Q_ENTRIES];
+    __shared__ int fkey[Q_ENTRIES];
     __shared__ int64_t sle[Q_ENTRIES];
     __shared__ uint32_t part_c[Q_THREADS];
     __shared__ int64_t part_s[Q_THREADS];
@@ -153,62 +157,94 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
     for (int g = blockIdx.x; g < groups; g += gridDim.x) {
         const uint16_t* const wg = w + (size_t)g * 16 * K;
 
-        // 1. histogram of the group's FP16 patterns, by key
-        for (int i = tid; i < Q_KEYS; i += Q_THREADS) P[i] = 0u;
+        // 1. the smallest and largest key present
         if (tid == 0) { key_lo = Q_KEYS; key_hi = -1; }
-        __threadfence();
         __syncthreads();
-        for (int64_t i = tid; i < n; i += Q_THREADS)
-            __hip_atomic_fetch_add(P + q_key(wg[i]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __threadfence();
-        __syncthreads();
-
-        // 2. inclusive prefix counts P and exact prefix sums S over the keys:
-        //    thread t owns keys [256 t, 256 t + 256)
-        uint32_t c_own = 0;
-        int64_t s_own = 0;
-        int first = Q_KEYS, lastk = -1;
-        for (int j = 0; j < 256; ++j) {
-            const int key = tid * 256 + j;
-            const uint32_t c = q_load(P + key);
-            if (c) {
-                first = min(first, key);
-                lastk = key;
-                c_own += c;
-                s_own += (int64_t)c * q_units(q_bits((uint32_t)key));
-            }
-        }
-        part_c[tid] = c_own;
-        part_s[tid] = s_own;
-        if (lastk >= 0) {
-            atomicMin(&key_lo, first);
-            atomicMax(&key_hi, lastk);
-        }
-        __syncthreads();
-        // Hillis-Steele inclusive scan of the 256 partials
-        for (int d = 1; d < Q_THREADS; d <<= 1) {
-            const uint32_t ac = tid >= d ? part_c[tid - d] : 0u;
-            const int64_t as = tid >= d ? part_s[tid - d] : 0;
-            __syncthreads();
-            part_c[tid] += ac;
-            part_s[tid] += as;
-            __syncthreads();
-        }
+        const uint4* const wg16 = (const uint4*)wg;       // 8 values per load
+        const int n8 = (int)(n / 8);
         {
-            uint32_t run_c = tid ? part_c[tid - 1] : 0u;
-            int64_t run_s = tid ? part_s[tid - 1] : 0;
-            for (int j = 0; j < 256; ++j) {
-                const int key = tid * 256 + j;
-                const uint32_t c = q_load(P + key);
+            int mn = Q_KEYS, mx = -1;
+            for (int i0 = tid; i0 < n8; i0 += 4 * Q_THREADS) {
+                uint4 v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = i0 + u * Q_THREADS < n8 ? wg16[i0 + u * Q_THREADS] : wg16[i0];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int key = (int)q_key((wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                        mn = min(mn, key);
+                        mx = max(mx, key);
+                    }
+                }
+            }
+            atomicMin(&key_lo, mn);
+            atomicMax(&key_hi, mx);
+        }
+        __syncthreads();
+        const int klo = key_lo, khi = key_hi;
+
+        // 2. histogram (in LDS, Q_CHUNK keys at a time) and the inclusive
+        //    prefix counts P and exact prefix sums S over keys [klo, khi];
+        //    thread t owns keys [c0 + 128 t, c0 + 128 t + 128) of a chunk
+        uint32_t carry_c = 0;
+        int64_t carry_s = 0;
+        for (int c0 = klo; c0 <= khi; c0 += Q_CHUNK) {
+            for (int i = tid; i < Q_CHUNK; i += Q_THREADS) hist[i] = 0u;
+            __syncthreads();
+            for (int i0 = tid; i0 < n8; i0 += 4 * Q_THREADS) {
+                uint4 v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = i0 + u * Q_THREADS < n8 ? wg16[i0 + u * Q_THREADS] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (i0 + u * Q_THREADS >= n8) continue;
+                    const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int rel = (int)q_key((wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) - c0;
+                        if (rel >= 0 && rel < Q_CHUNK) atomicAdd(&hist[rel], 1u);
+                    }
+                }
+            }
+            __syncthreads();
+            uint32_t c_own = 0;
+            int64_t s_own = 0;
+            for (int j = 0; j < Q_CHUNK / Q_THREADS; ++j) {
+                const int rel = tid * (Q_CHUNK / Q_THREADS) + j;
+                const uint32_t c = hist[rel];
+                c_own += c;
+                s_own += (int64_t)c * q_units(q_bits((uint32_t)min(c0 + rel, Q_KEYS - 1)));
+            }
+            part_c[tid] = c_own;
+            part_s[tid] = s_own;
+            __syncthreads();
+            // Hillis-Steele inclusive scan of the 256 partials
+            for (int d = 1; d < Q_THREADS; d <<= 1) {
+                const uint32_t ac = tid >= d ? part_c[tid - d] : 0u;
+                const int64_t as = tid >= d ? part_s[tid - d] : 0;
+                __syncthreads();
+                part_c[tid] += ac;
+                part_s[tid] += as;
+                __syncthreads();
+            }
+            uint32_t run_c = carry_c + (tid ? part_c[tid - 1] : 0u);
+            int64_t run_s = carry_s + (tid ? part_s[tid - 1] : 0);
+            for (int j = 0; j < Q_CHUNK / Q_THREADS; ++j) {
+                const int rel = tid * (Q_CHUNK / Q_THREADS) + j;
+                const int key = c0 + rel;
+                if (key > khi) break;
+                const uint32_t c = hist[rel];
                 run_c += c;
-                run_s += (int64_t)c * (c ? q_units(q_bits((uint32_t)key)) : 0);
+                run_s += (int64_t)c * q_units(q_bits((uint32_t)key));
                 P[key] = run_c;
                 S[key] = run_s;
             }
+            carry_c += part_c[Q_THREADS - 1];
+            carry_s += part_s[Q_THREADS - 1];
+            __syncthreads();
         }
-        __threadfence();
-        __syncthreads();
-        const int klo = key_lo, khi = key_hi;
 
         // 3. starting centres: 32 quantiles and 32 evenly spread values
         if (tid < 32) {
@@ -217,7 +253,7 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
             int lo = klo, hi = khi;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
-                if ((int64_t)q_load(P + mid) > rank) hi = mid;
+                if ((int64_t)P[mid] > rank) hi = mid;
                 else lo = mid + 1;
             }
             tmp[tid] = q_value(q_bits((uint32_t)lo));
@@ -237,11 +273,11 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
                 const double b = (cen[tid] + cen[tid + 1]) * 0.5;
                 const int k = q_floor_key(b, klo, khi);
                 // P and S are zero below the smallest key present
-                cle[tid] = k >= klo ? q_load(P + k) : 0u;
-                sle[tid] = k >= klo ? q_load(S + k) : 0;
+                cle[tid] = k >= klo ? P[k] : 0u;
+                sle[tid] = k >= klo ? S[k] : 0;
             } else if (tid == Q_ENTRIES - 1) {
                 cle[tid] = (uint32_t)n;
-                sle[tid] = q_load(S + khi);
+                sle[tid] = S[khi];
             }
             __syncthreads();
             if (tid < Q_ENTRIES) {
@@ -269,16 +305,28 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
         if (tid < Q_ENTRIES - 1) bnd[tid] = (tmp[tid] + tmp[tid + 1]) * 0.5;
         __syncthreads();
 
-        // 6. key -> index: the number of boundaries below the key's value
-        for (int key = klo + tid; key <= khi; key += Q_THREADS) {
-            const double v = q_value(q_bits((uint32_t)key));
-            int lo = 0, hi = Q_ENTRIES - 1;            // count of bnd[0..62] < v
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (bnd[mid] < v) lo = mid + 1;
-                else hi = mid;
+        // 6. key -> index: a key's value exceeds boundary i exactly when the
+        //    key is above the boundary's floor key, so the index of a key is
+        //    the number of floor keys below it; each thread walks a
+        //    contiguous range of keys
+        if (tid < Q_ENTRIES - 1) fkey[tid] = q_floor_key(bnd[tid], klo, khi);
+        __syncthreads();
+        {
+            const int span = khi - klo + 1;
+            const int per = (span + Q_THREADS - 1) / Q_THREADS;
+            const int k0 = klo + tid * per, k1 = min(khi + 1, k0 + per);
+            if (k0 < k1) {
+                int idx = 0;                           // floor keys below k0
+                while (idx < Q_ENTRIES - 1 && fkey[idx] < k0) ++idx;
+                int next = idx < Q_ENTRIES - 1 ? fkey[idx] : Q_KEYS;
+                for (int key = k0; key < k1; ++key) {
+                    while (next < key) {
+                        ++idx;
+                        next = idx < Q_ENTRIES - 1 ? fkey[idx] : Q_KEYS;
+                    }
+                    map[key] = (uint8_t)idx;
+                }
             }
-            map[key] = (uint8_t)lo;
         }
         __syncthreads();
 

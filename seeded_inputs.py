@@ -31,7 +31,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-T_X, T_A, T_IDX, T_TAB, T_OUTLIER, T_ROWS = 0, 1, 2, 3, 4, 5
+T_X, T_A, T_IDX, T_TAB, T_OUTLIER, T_ROWS, T_W = 0, 1, 2, 3, 4, 5, 6
 EPI_F32, EPI_F16, EPI_SILU_MUL_F16 = 0, 1, 2
 
 
@@ -60,6 +60,17 @@ def tables(N: int, key: tuple[int, int, int], sigma: float = 0.02,
         m = rng(*key, T_OUTLIER).random((N // 16, 64)) < outlier_p
         t = np.where(m, t * outlier_scale, t)
     return np.sort(t.astype(np.float16), axis=1)
+
+
+def weights(N: int, K: int, key: tuple[int, int, int], sigma: float = 0.02,
+            outlier_p: float = 0.02, outlier_scale: float = 8.0) -> np.ndarray:
+    """FP16 weight [N, K] for table fitting: N(0, sigma) with a fraction
+    outlier_p of the entries scaled by outlier_scale (the spread the tables
+    of the workloads model)."""
+    g = rng(*key, T_W)
+    w = g.standard_normal((N, K), dtype=np.float32) * np.float32(sigma)
+    m = g.random((N, K), dtype=np.float32) < outlier_p
+    return np.where(m, w * np.float32(outlier_scale), w).astype(np.float16)
 
 
 def sample_rows(L: int, count: int, key: tuple[int, int, int]) -> np.ndarray:
