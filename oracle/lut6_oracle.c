@@ -403,9 +403,10 @@ int64_t ora_table_bytes(int64_t n) { return (n / 16) * 64 * 2; }
  *   - each weight's index is its nearest table entry, by the same boundary
  *     rule on the FP16 entries (the lower index on a tie);
  *   - the indices are packed as by ora_pack.
- * There is nothing for this to match bit for bit on the page; the tests pin
- * it with properties k-means has whatever the details (see
- * tests/test_oracle_pins.py).
+ * There is nothing for this to match bit for bit on the page: parity
+ * unpinned.  The tests pin it with properties k-means has whatever the
+ * details (see tests/test_oracle_pins.py); a change to one of the readings
+ * above would pass them.
  */
 #define ORA_KM_ROUNDS 40
 #define ORA_KM_ENTRIES 64
