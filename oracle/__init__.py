@@ -69,6 +69,11 @@ class Oracle:
         lib.ora_linear.argtypes = [_P, _P, _P, _I64, _I64, _I64, ctypes.c_double,
                                    ctypes.c_int, _P, _I64, ctypes.c_int, _P, _P]
         lib.ora_linear.restype = ctypes.c_int
+        lib.ora_int8_linear.argtypes = [_P, _P, _P, _I64, _I64, _I64, ctypes.c_double,
+                                        ctypes.c_int, _P, _I64, ctypes.c_int, _P, _P]
+        lib.ora_int8_linear.restype = ctypes.c_int
+        lib.ora_int8_dequant.argtypes = [_P, _P, _P, _I64, _I64]
+        lib.ora_int8_dequant.restype = ctypes.c_int
         lib.ora_quantize.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P]
         lib.ora_quantize.restype = ctypes.c_int
         lib.ora_packed_bytes.argtypes = [_I64, _I64]
@@ -161,6 +166,46 @@ class Oracle:
             raise OracleError(f"ora_linear status {st}")
         return y_exact, y_out
 
+
+    # -- int8 weight-only variant -------------------------------------------
+    def int8_linear(self, x: np.ndarray, q: np.ndarray, scales: np.ndarray, *,
+                    epilogue: int, in_scale: float = 1.0, rows=None, threads: int | None = None):
+        """As linear(), for an int8 weight q [N, K] with FP16 scales [N, K/32]."""
+        x = np.ascontiguousarray(x).view(np.uint16)
+        q = np.ascontiguousarray(q).view(np.int8)
+        scales = np.ascontiguousarray(scales).view(np.uint16)
+        L, K = x.shape
+        N = q.shape[0]
+        if q.shape[1] != K or scales.shape != (N, K // 32):
+            raise OracleError("q / scales shapes do not match x")
+        if rows is None:
+            rows_arr, n_rows, rows_ptr = None, L, None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+            n_rows = rows_arr.size
+            rows_ptr = rows_arr.ctypes.data
+        n_out = N // 2 if epilogue == EPI_SILU_MUL_F16 else N
+        y_exact = np.empty((n_rows, n_out), np.float64)
+        y_out = np.empty((n_rows, n_out), np.float32 if epilogue == EPI_F32 else np.uint16)
+        if threads is None:
+            threads = len(os.sched_getaffinity(0))
+        st = self.lib.ora_int8_linear(x.ctypes.data, q.ctypes.data, scales.ctypes.data,
+                                      L, K, N, float(in_scale), int(epilogue), rows_ptr, n_rows,
+                                      int(threads), y_exact.ctypes.data, y_out.ctypes.data)
+        if st != OK:
+            raise OracleError(f"ora_int8_linear status {st}")
+        return y_exact, y_out
+
+    def int8_dequant(self, q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+        """FP16 bits [N, K]: the weight nearest to q * scale."""
+        q = np.ascontiguousarray(q).view(np.int8)
+        scales = np.ascontiguousarray(scales).view(np.uint16)
+        n, k = q.shape
+        w = np.empty((n, k), np.uint16)
+        st = self.lib.ora_int8_dequant(q.ctypes.data, scales.ctypes.data, w.ctypes.data, n, k)
+        if st != OK:
+            raise OracleError(f"ora_int8_dequant status {st}")
+        return w
 
     # -- table fitting ---------------------------------------------------
     def quantize(self, w16: np.ndarray, groups=None, with_sse: bool = False):

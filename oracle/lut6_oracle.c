@@ -211,10 +211,35 @@ int ora_dequant(const uint8_t *packed, const uint16_t *tables, uint16_t *w,
 
 /* ---------------- the linear layer ---------------- */
 
+/* The FP16 weight an int8 code stands for: the value nearest to q times
+ * its block's scale (one FP16 scale per row and 32 consecutive k; the
+ * product is exact in double, 8 by 11 significant bits). */
+static uint16_t ora_int8_weight(int8_t q, const uint16_t *qs, int64_t r, int64_t c, int64_t k)
+{
+#if ORA_MUTANT == 12
+    const double s = ora_f16_to_f64(qs[r * (k / 32) + (c / 16) % (k / 32)]);
+#else
+    const double s = ora_f16_to_f64(qs[r * (k / 32) + c / 32]);
+#endif
+#if ORA_MUTANT == 13
+    const double v = (double)(uint8_t)q * s;
+#else
+    const double v = (double)q * s;
+#endif
+#if ORA_MUTANT == 14
+    const uint16_t h = ora_f64_to_f16(v);
+    return ora_f16_to_f64(h) != v && fabs(ora_f16_to_f64(h)) > fabs(v) ? (uint16_t)(h - 1) : h;
+#else
+    return ora_f64_to_f16(v);
+#endif
+}
+
 typedef struct {
     const double *xs;        /* [nr][k] scaled, FP16-rounded activations */
-    const uint8_t *packed;
+    const uint8_t *packed;   /* LUT-6 weight, or ... */
     const uint16_t *tables;
+    const int8_t *q;         /* ... int8 weight [n][k] with FP16 scales */
+    const uint16_t *qs;      /* [n][k/32], one per block of 32 along k */
     int64_t k, n, nr;
     int64_t n_begin, n_end;  /* this thread's output channels */
     double *acc;             /* [nr][n] */
@@ -230,9 +255,16 @@ static void *ora_dot_worker(void *arg)
     if (!idx || !wd) { free(idx); free(wd); j->status = ORA_E_NOMEM; return NULL; }
     for (int64_t r = j->n_begin; r < j->n_end; ++r) {
         /* dequantize weight row r */
-        ora_unpack_row(j->packed + r * (3 * k / 4), idx, k);
-        const uint16_t *tab = j->tables + ora_table_of(r) * 64;
-        for (int64_t c = 0; c < k; ++c) wd[c] = ora_f16_to_f64(tab[idx[c]]);
+        if (j->q) {
+            /* int8: the FP16 weight nearest to q * scale (the product is
+             * exact in double: 8 by 11 significant bits) */
+            for (int64_t c = 0; c < k; ++c)
+                wd[c] = ora_f16_to_f64(ora_int8_weight(j->q[r * k + c], j->qs, r, c, k));
+        } else {
+            ora_unpack_row(j->packed + r * (3 * k / 4), idx, k);
+            const uint16_t *tab = j->tables + ora_table_of(r) * 64;
+            for (int64_t c = 0; c < k; ++c) wd[c] = ora_f16_to_f64(tab[idx[c]]);
+        }
         /* one FP64 dot per token row, k ascending */
         for (int64_t l = 0; l < j->nr; ++l) {
             const double *xr = j->xs + l * k;
@@ -261,13 +293,16 @@ static void *ora_dot_worker(void *arg)
  *   n_out = N, or N/2 for the SiLU-multiply epilogue
  * threads <= 0 means one thread.  Returns ORA_OK or an error code.
  */
-int ora_linear(const uint16_t *x, const uint8_t *packed, const uint16_t *tables,
-               int64_t L, int64_t K, int64_t N, double in_scale, int epilogue,
-               const int64_t *rows, int64_t n_rows, int threads,
-               double *y_exact, void *y_out)
+static int ora_linear_any(const uint16_t *x, const uint8_t *packed, const uint16_t *tables,
+                          const int8_t *q, const uint16_t *qs,
+                          int64_t L, int64_t K, int64_t N, double in_scale, int epilogue,
+                          const int64_t *rows, int64_t n_rows, int threads,
+                          double *y_exact, void *y_out)
 {
-    if (!x || !packed || !tables || !y_exact || !y_out) return ORA_E_NULL;
+    if (!x || !y_exact || !y_out) return ORA_E_NULL;
+    if (q ? (!qs) : (!packed || !tables)) return ORA_E_NULL;
     if (L < 0 || K <= 0 || N <= 0 || K % 4 || N % 16) return ORA_E_SHAPE;
+    if (q && K % 32) return ORA_E_SHAPE;
     if (epilogue < 0 || epilogue > 2) return ORA_E_EPILOGUE;
     if (epilogue == ORA_EPI_SILU_MUL_F16 && N % 32) return ORA_E_SHAPE;
     if (!(in_scale > 0.0) || isinf(in_scale)) return ORA_E_SCALE;
@@ -306,7 +341,7 @@ int ora_linear(const uint16_t *x, const uint8_t *packed, const uint16_t *tables,
     char *joined = (char *)calloc((size_t)threads, 1);
     for (int t = 0; t < threads; ++t) {
         ora_job *j = &jobs[t];
-        j->xs = xs; j->packed = packed; j->tables = tables;
+        j->xs = xs; j->packed = packed; j->tables = tables; j->q = q; j->qs = qs;
         j->k = K; j->n = N; j->nr = nr; j->acc = acc;
         j->n_begin = t * per < N ? t * per : N;
         j->n_end = (t + 1) * per < N ? (t + 1) * per : N;
@@ -368,6 +403,46 @@ int ora_linear(const uint16_t *x, const uint8_t *packed, const uint16_t *tables,
     }
     free(xs); free(acc); free(jobs); free(tid);
     return status;
+}
+
+int ora_linear(const uint16_t *x, const uint8_t *packed, const uint16_t *tables,
+               int64_t L, int64_t K, int64_t N, double in_scale, int epilogue,
+               const int64_t *rows, int64_t n_rows, int threads,
+               double *y_exact, void *y_out)
+{
+    return ora_linear_any(x, packed, tables, NULL, NULL, L, K, N, in_scale, epilogue,
+                          rows, n_rows, threads, y_exact, y_out);
+}
+
+/*
+ * int8 weight-only variant (page "clef-flash — Core AI", the bundle list
+ * at the top and section "Precision": int8 per block of 32, weights only,
+ * every other tensor FP16).  Reading: a block is 32 consecutive inputs k of
+ * one output row;
+ * q is an int8 weight [N][K] (two's complement, any value), qs one FP16
+ * scale per row and block of 32 consecutive k, and the weight the layer
+ * uses is FP16, the value nearest to q * scale.  Everything after the
+ * dequantization is ora_linear's.  K % 32 == 0.
+ */
+int ora_int8_linear(const uint16_t *x, const int8_t *q, const uint16_t *qs,
+                    int64_t L, int64_t K, int64_t N, double in_scale, int epilogue,
+                    const int64_t *rows, int64_t n_rows, int threads,
+                    double *y_exact, void *y_out)
+{
+    if (!q) return ORA_E_NULL;
+    return ora_linear_any(x, NULL, NULL, q, qs, L, K, N, in_scale, epilogue,
+                          rows, n_rows, threads, y_exact, y_out);
+}
+
+/* The int8 weight as the layer uses it: FP16 bits [N][K]. */
+int ora_int8_dequant(const int8_t *q, const uint16_t *qs, uint16_t *w, int64_t n, int64_t k)
+{
+    if (!q || !qs || !w) return ORA_E_NULL;
+    if (n <= 0 || k <= 0 || k % 32) return ORA_E_SHAPE;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t c = 0; c < k; ++c)
+            w[r * k + c] = ora_int8_weight(q[r * k + c], qs, r, c, k);
+    return ORA_OK;
 }
 
 /* Bytes of a packed [n, k] weight and of its tables (format sizes). */

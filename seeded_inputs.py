@@ -17,7 +17,8 @@ tables of section "LUT-6 text weights", whose trained weights are not here.
 
 Every stream comes from ``numpy.random.default_rng([2026, cfg, layer, proj,
 tensor])`` (PCG64) with tensor 0 = x, 1 = a second activation, 2 = indices,
-3 = tables, 4 = outlier mask, 5 = sampled rows.  Weights are keyed by
+3 = tables, 4 = outlier mask, 5 = sampled rows, 6 = an FP16 weight to fit
+tables to, 7 = int8 weight codes, 8 = their per-block scales.  Weights are keyed by
 (cfg, layer, projection); activations are shared by every GEMM of a workload
 that reads the same stream at the same width, keyed by (cfg, 0, K): the
 hidden state x, a stand-in `a` for an attention / recurrence output, and a
@@ -31,7 +32,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-T_X, T_A, T_IDX, T_TAB, T_OUTLIER, T_ROWS, T_W = 0, 1, 2, 3, 4, 5, 6
+T_X, T_A, T_IDX, T_TAB, T_OUTLIER, T_ROWS, T_W, T_Q, T_QS = 0, 1, 2, 3, 4, 5, 6, 7, 8
 EPI_F32, EPI_F16, EPI_SILU_MUL_F16 = 0, 1, 2
 
 
@@ -71,6 +72,15 @@ def weights(N: int, K: int, key: tuple[int, int, int], sigma: float = 0.02,
     w = g.standard_normal((N, K), dtype=np.float32) * np.float32(sigma)
     m = g.random((N, K), dtype=np.float32) < outlier_p
     return np.where(m, w * np.float32(outlier_scale), w).astype(np.float16)
+
+
+def int8_weight(N: int, K: int, key: tuple[int, int, int], sigma: float = 0.02):
+    """int8 codes [N, K] uniform on -127..127 and FP16 scales [N, K/32],
+    each sigma * 2.5 / 127 times a log-normal factor (spread 0.25): the
+    shapes of a weight kept as int8 per block of 32 along K."""
+    q = rng(*key, T_Q).integers(-127, 128, size=(N, K), dtype=np.int16).astype(np.int8)
+    f = np.exp(rng(*key, T_QS).standard_normal((N, K // 32)) * 0.25)
+    return q, (f * (sigma * 2.5 / 127.0)).astype(np.float16)
 
 
 def sample_rows(L: int, count: int, key: tuple[int, int, int]) -> np.ndarray:

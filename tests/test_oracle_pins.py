@@ -289,9 +289,62 @@ def pin_in_scale(ora):
     assert np.all(yh.view(np.float16) == np.float16(2048.0)), "largest in-range scale"
 
 
+# -- int8 weight-only variant ------------------------------------------------
+
+def pin_int8_dequant(ora):
+    # the product q * scale is exact in double, so numpy's double -> half
+    # conversion (round to nearest even, overflow to inf) is the definition
+    q, s = si.int8_weight(32, 256, (9, 0, 0))
+    s = s.copy()
+    s[0, 0] = np.float16(600.0)                       # 127 * 600 overflows FP16
+    s[1, 1] = np.float16(6e-8)                        # subnormal products
+    q[0, :32] = np.arange(-128, 128, 8, dtype=np.int16).astype(np.int8)
+    with np.errstate(over="ignore"):
+        want = (q.astype(np.float64) * np.repeat(s.astype(np.float64), 32, axis=1)).astype(np.float16)
+    got = ora.int8_dequant(q, s)
+    assert np.array_equal(got, want.view(np.uint16))
+    assert np.isinf(want[0, 31]) and want[0, 16] == 0.0
+
+
+def pin_int8_as_lut6(ora):
+    # codes -32..31 with one power-of-two scale per 16 rows are exactly a
+    # 64-entry table (entry i = (i - 32) * scale): both variants must give
+    # the same bits, so the LUT-6 pins carry over to the int8 reading
+    N, K, L = 64, 256, 9
+    g = np.random.default_rng(5)
+    idx = g.integers(0, 64, size=(N, K), dtype=np.uint8)
+    e = g.integers(-10, -4, size=N // 16)
+    tab = ((np.arange(64)[None, :] - 32) * np.exp2(e)[:, None]).astype(np.float16)
+    q = (idx.astype(np.int16) - 32).astype(np.int8)
+    s = np.repeat(np.exp2(e), 16)[:, None].repeat(K // 32, axis=1).astype(np.float16)
+    x = si.activations(L, K, 1.0, (9, 0, 1))
+    for epi in (0, 1, 2):
+        for sc in (1.0, 8.0):
+            ya, oa = ora.linear(x, ora.pack(idx), tab, epilogue=epi, in_scale=sc)
+            yb, ob = ora.int8_linear(x, q, s, epilogue=epi, in_scale=sc)
+            assert np.array_equal(ya, yb) and np.array_equal(oa, ob)
+
+
+def pin_int8_block_scale(ora):
+    # doubling one block's scale (exact) adds exactly that block's part of
+    # the dot product once more, for every token row
+    N, K, L = 16, 128, 5
+    q, s = si.int8_weight(N, K, (9, 1, 0))
+    x = si.activations(L, K, 1.0, (9, 1, 1))
+    y0, _ = ora.int8_linear(x, q, s, epilogue=0)
+    s2 = s.copy()
+    s2[3, 2] = s2[3, 2] * np.float16(2)
+    y1, _ = ora.int8_linear(x, q, s2, epilogue=0)
+    w = q[3, 64:96].astype(np.float64) * np.float64(s[3, 2])
+    part = x[:, 64:96].astype(np.float64) @ np.array([np.float64(np.float16(v)) for v in w])
+    assert np.allclose(y1[:, 3] - y0[:, 3], part, rtol=0, atol=1e-12)
+    assert np.array_equal(np.delete(y1, 3, axis=1), np.delete(y0, 3, axis=1))
+
+
 PINS = [pin_pack_worked_examples, pin_pack_exhaustive, pin_storage, pin_f16_decode,
         pin_f16_encode, pin_dequant, pin_linear_bruteforce, pin_linear_silu,
-        pin_special_tables, pin_identity_readout, pin_in_scale]
+        pin_special_tables, pin_identity_readout, pin_in_scale, pin_int8_dequant,
+        pin_int8_as_lut6, pin_int8_block_scale]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -334,7 +387,8 @@ MUTANTS = {1: "big-endian byte order", 2: "index order reversed", 3: "one table 
            4: "no scale-back", 5: "gate and up halves swapped", 6: "SiLU sign error",
            7: "last input column dropped", 8: "ties rounded away from zero",
            9: "subnormal decode off by 2x", 10: "activations read transposed",
-           11: "f32 output truncated"}
+           11: "f32 output truncated", 12: "int8 scale per block of 16",
+           13: "int8 code read unsigned", 14: "int8 product truncated to FP16"}
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m].replace(" ", "_"))
@@ -496,3 +550,4 @@ def test_quantize_group_subset_and_refusals(ora):
         ora.quantize(bad)
     with pytest.raises(oracle.OracleError):
         ora.quantize(w[:8])                                   # N % 16
+
