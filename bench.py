@@ -29,6 +29,8 @@ starts.  The line printed is throughput in TFLOP/s, with
   * quantize: lut6_quantize (table fitting by 1-D k-means) on a 4,096 x 4,096
     and a 4,096 x 12,288 seeded FP16 weight: time per call, weights per
     second and algorithmic GB/s, with the oracle on one 16-row group beside;
+  * int8_variant: the int8 weight-only variant (int8 codes, one FP16 scale
+    per 32 k) beside LUT-6 on the same shapes (L = 128 and 4,096);
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same step
     (sampled token rows of two layers), on this host's cores;
   * parity_sample: those sampled rows of the GPU result against the oracle.
@@ -217,6 +219,59 @@ def time_quantize(lq, si, torch, stream, no_cpu: bool) -> list:
                                  "sample": "one 16-row group, single thread, scaled to all groups"}
         out.append(rec)
         del w, packed, tables
+    torch.cuda.empty_cache()
+    return out
+
+
+INT8_SHAPES = (("o_proj", 128, 4096, 4096), ("o_proj", 4096, 4096, 4096), ("down", 4096, 12288, 4096))
+
+
+def _median_us(fn, torch, stream, calls: int = 5) -> float:
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1) * 1e3 / calls)
+    return sorted(reps)[1]
+
+
+def time_int8(lq, si, torch, stream) -> list:
+    """The int8 weight-only variant (int8 codes, one FP16 scale per 32 k)
+    beside LUT-6 on the same shapes, FP16 output: median of 3 runs of 5
+    back-to-back calls each.  The int8 path expands the weight and runs the
+    FP16 GEMM at every token count."""
+    out = []
+    for name, L, K, N in INT8_SHAPES:
+        x = torch.from_numpy(si.activations(L, K, 1.0, (13, 0, K))).to("cuda")
+        q8, s8 = si.int8_weight(N, K, (13, 1, K))
+        q = torch.from_numpy(q8).to("cuda")
+        sc = torch.from_numpy(s8).to("cuda")
+        packed = torch.from_numpy(lq.pack(si.indices(N, K, (13, 2, K)))).to("cuda")
+        tab = torch.from_numpy(si.tables(N, (13, 2, K))).to("cuda")
+        y = torch.empty((L, N), dtype=torch.float16, device="cuda")
+        us8 = _median_us(lambda: lq.int8_linear(x, q, sc, epilogue=lq.EPI_STORE_F16, out=y, stream=stream),
+                         torch, stream)
+        us6 = _median_us(lambda: lq.linear(x, packed, tab, epilogue=lq.EPI_STORE_F16, out=y, stream=stream),
+                         torch, stream)
+        flops = 2.0 * L * K * N
+        b8 = L * K * 2 + N * K + N * (K // 32) * 2 + L * N * 2
+        b6 = L * K * 2 + N * K // 4 * 3 + N // 16 * 128 + L * N * 2
+        out.append({"gemm": f"{name} L={L} K={K} N={N} f16", "int8_us_per_call": round(us8, 2),
+                    "lut6_us_per_call": round(us6, 2), "int8_over_lut6_time": round(us8 / us6, 3),
+                    "int8_tflop_s": round(flops / (us8 * 1e-6) / 1e12, 1),
+                    "lut6_tflop_s": round(flops / (us6 * 1e-6) / 1e12, 1),
+                    "int8_algorithmic_bytes": b8, "lut6_algorithmic_bytes": b6,
+                    "int8_frac_hbm": round(b8 / (us8 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "lut6_frac_hbm": round(b6 / (us6 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)})
+        del x, q, sc, packed, tab, y
     torch.cuda.empty_cache()
     return out
 
@@ -450,6 +505,7 @@ def main() -> int:
 
     # ---------------- the other workloads ----------------
     quant = time_quantize(lq, si, torch, stream, args.no_cpu_baseline)
+    int8 = time_int8(lq, si, torch, stream)
 
     per_config = []
     for name in OTHER_WORKLOADS:
@@ -480,6 +536,7 @@ def main() -> int:
         "l128_stream": stream_rec,
         "per_config": per_config,
         "quantize": quant,
+        "int8_variant": int8,
         "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)

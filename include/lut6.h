@@ -141,6 +141,22 @@ int lut6_linear_path(int64_t L, int64_t K, int64_t N, int epilogue);
 int lut6_dequant(const uint8_t* packed, const void* tables, void* w,
                  int64_t N, int64_t K, hipStream_t stream);
 
+/* int8 weight-only variant of lut6_linear (page "clef-flash — Core AI",
+ * the bundle list at the top and section "Precision": int8 weights per
+ * block of 32, weights only, activations FP16; the blocks are read as 32
+ * consecutive inputs k of one output row).  The weight the layer uses is FP16, the value nearest
+ * to q[n, k] * scales[n][k / 32]; everything else, including in_scale, the
+ * epilogues and their rules, is as for lut6_linear.
+ * q: device int8 [N, K], row-major; scales: device FP16 [N, K/32]; x, y as
+ * for lut6_linear.  All 16-byte aligned (LUT6_E_ALIGN).  Same shape rules as
+ * lut6_linear (LUT6_E_SHAPE); y must not overlap x, q or scales
+ * (LUT6_E_ALIAS).  Runs the two-pass path at every L: the weight is
+ * expanded into the library's FP16 workspace, then the FP16 GEMM reads it
+ * (split K when few tiles, as lut6_linear).                               */
+int lut6_int8_linear(const void* x, const int8_t* q, const void* scales, void* y,
+                     int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
+                     hipStream_t stream);
+
 /* Fit the tables and write the packed indices of an FP16 weight [N, K]
  * (page "Clef-Flash-ANE-LUT6", section "LUT-6 text weights": one 64-entry
  * table per 16 output channels, from 40 rounds of one-dimensional k-means

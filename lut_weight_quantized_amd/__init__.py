@@ -30,7 +30,8 @@ STATUS = {0: "LUT6_OK", 1: "LUT6_E_NULL", 2: "LUT6_E_SHAPE", 3: "LUT6_E_ALIGN",
           7: "LUT6_E_DEVICE", 8: "LUT6_E_ALIAS"}
 
 EXPORTS = ("lut6_packed_bytes", "lut6_table_bytes", "lut6_pack", "lut6_unpack",
-           "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_quantize", "lut6_release",
+           "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_int8_linear", "lut6_quantize",
+           "lut6_release",
            "lut6_status_string")
 
 # kernel paths of lut6_linear (lut6_linear_path)
@@ -75,6 +76,8 @@ def load_library() -> ctypes.CDLL:
     lib.lut6_linear_path.restype = ctypes.c_int
     lib.lut6_dequant.argtypes = [P, P, P, I64, I64, P]
     lib.lut6_dequant.restype = ctypes.c_int
+    lib.lut6_int8_linear.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_float, ctypes.c_int, P]
+    lib.lut6_int8_linear.restype = ctypes.c_int
     lib.lut6_quantize.argtypes = [P, P, P, I64, I64, P]
     lib.lut6_quantize.restype = ctypes.c_int
     lib.lut6_release.argtypes = []
@@ -203,6 +206,30 @@ def dequant(packed, tables, K: int, *, out=None, stream=None):
     st = load_library().lut6_dequant(packed.data_ptr(), tables.data_ptr(), out.data_ptr(),
                                      N, K, _stream_handle(stream))
     _check(st, "lut6_dequant")
+    return out
+
+
+def int8_linear(x, q, scales, *, epilogue: int = EPI_STORE_F16, in_scale: float = 1.0,
+                out=None, stream=None):
+    """y = epilogue((fp16(x * in_scale) @ W^T) / in_scale) for an int8 weight:
+    W = fp16(q * scales[:, k // 32]); q int8 [N, K], scales float16 [N, K/32]."""
+    import torch
+    _require(x, torch.float16, "x")
+    _require(q, torch.int8, "q")
+    _require(scales, torch.float16, "scales")
+    if x.dim() != 2 or q.dim() != 2:
+        raise ValueError("x and q must be 2-D")
+    L, K = x.shape
+    N = q.shape[0]
+    n_out = N // 2 if epilogue == EPI_SILU_MUL_F16 else N
+    dtype = torch.float32 if epilogue == EPI_STORE_F32 else torch.float16
+    if out is None:
+        out = torch.empty((L, n_out), dtype=dtype, device=x.device)
+    else:
+        _require(out, dtype, "out")
+    st = load_library().lut6_int8_linear(x.data_ptr(), q.data_ptr(), scales.data_ptr(), out.data_ptr(),
+                                         L, K, N, float(in_scale), int(epilogue), _stream_handle(stream))
+    _check(st, "lut6_int8_linear")
     return out
 
 

@@ -1024,6 +1024,62 @@ lut6_expand_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restric
     }
 }
 
+// int8 weight-only variant: the same fragment-order FP16 buffer as
+// lut6_expand_kernel, from an int8 weight q [N, K] and one FP16 scale per
+// row and block of 32 along K (qs [N, K/32]).  A unit (row, 64-k chunk, lane
+// group h) is exactly one block: 32 int8 values and one scale, written as
+// the FP16 value nearest to q * scale (exact in FP32: 8 by 11 significant
+// bits, so the conversion to FP16 is the only rounding).
+template <int EPI>
+__global__ void __launch_bounds__(256)
+lut6_int8_expand_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict__ qs,
+                        uint16_t* __restrict__ w16, int N, int K)
+{
+    const int tn = blockIdx.x, g = blockIdx.y;
+    const int chunks = K / BK;
+    const int nch = min(X_CHUNKS, chunks - g * X_CHUNKS);
+    u32x4 v[X_UNITS][2];
+    uint16_t sc[X_UNITS];
+    int dsto[X_UNITS];
+#pragma unroll
+    for (int i = 0; i < X_UNITS; ++i) {
+        const int uu = threadIdx.x + 256 * i;
+        const int u = uu < 8 * nch * 64 ? uu : 0;
+        const int lane = u & 63, kl = (u >> 6) % nch, wf = (u >> 6) / nch;
+        const int kc = g * X_CHUNKS + kl;
+        const int row = tile_row<EPI>(64 * (wf >> 1) + 32 * (wf & 1) + (lane & 31), tn, N);
+        const int k0 = BK * kc + 32 * (lane >> 5);
+        const u32x4* const src = (const u32x4*)(q + (size_t)row * K + k0);   // 32-byte aligned
+        v[i][0] = src[0];
+        v[i][1] = src[1];
+        sc[i] = qs[(size_t)row * (K / 32) + k0 / 32];
+        dsto[i] = uu < 8 * nch * 64 ? (int)(((size_t)(tn * 8 + wf) * (chunks + 1) + kc) * 2048 + lane * 8) : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < X_UNITS; ++i) {
+        if (dsto[i] < 0) continue;
+        const float s = (float)__builtin_bit_cast(_Float16, sc[i]);
+        const uint32_t wd[8] = {v[i][0][0], v[i][0][1], v[i][0][2], v[i][0][3],
+                                v[i][1][0], v[i][1][1], v[i][1][2], v[i][1][3]};
+        uint16_t* const dst = w16 + (size_t)dsto[i];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            // values 8 st .. 8 st + 7 of the block: words 2 st, 2 st + 1
+            u32x4 out;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t word = wd[2 * st + (j >> 1)];
+                const int sh = 16 * (j & 1);
+                const float a = (float)(int8_t)((word >> sh) & 0xFFu) * s;
+                const float b = (float)(int8_t)((word >> (sh + 8)) & 0xFFu) * s;
+                out[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+            }
+            *(u32x4*)(dst + st * 512) = out;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel for few tokens (L <= 192).  Every weight serves at
 // most 192 tokens here, so streaming the packed weight once from HBM, and
@@ -1797,6 +1853,75 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
         if (st != LUT6_OK) return st;
     }
     launch_tiles(a, two_pass, epilogue, scaled, splits > 1, grid, stream);
+    if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
+    return splits > 1 ? launch_reduce(a, epilogue, splits, stream) : LUT6_OK;
+}
+
+extern "C" int lut6_int8_linear(const void* x, const int8_t* q, const void* scales, void* y,
+                                int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
+                                hipStream_t stream)
+{
+    if (!x || !q || !scales || !y) return LUT6_E_NULL;
+    if (L < 0 || K <= 0 || N <= 0 || K % 64 || N % 16) return LUT6_E_SHAPE;
+    if (L > INT32_MAX || K > INT32_MAX || N > INT32_MAX) return LUT6_E_SHAPE;
+    if (epilogue < 0 || epilogue > 2) return LUT6_E_EPILOGUE;
+    if (epilogue == LUT6_EPI_SILU_MUL_F16 && N % 32) return LUT6_E_SHAPE;
+    if (!(in_scale == 1.0f || in_scale == 2.0f || in_scale == 4.0f || in_scale == 8.0f ||
+          in_scale == 16.0f))
+        return LUT6_E_SCALE;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || !aligned16(y)) return LUT6_E_ALIGN;
+    const size_t x_bytes = (size_t)L * K * 2, q_bytes = (size_t)N * K, s_bytes = (size_t)N * (K / 32) * 2;
+    const size_t y_bytes = (size_t)L * (epilogue == 0 ? N * 4 : epilogue == 1 ? N * 2 : N);
+    if (x_bytes >= ((size_t)1 << 31) || q_bytes >= ((size_t)1 << 31)) return LUT6_E_SHAPE;
+    if (L == 0) return LUT6_OK;
+    if (overlaps(y, y_bytes, x, x_bytes) || overlaps(y, y_bytes, q, q_bytes) || overlaps(y, y_bytes, scales, s_bytes))
+        return LUT6_E_ALIAS;
+
+    GemmArgs a{};
+    a.x = (const uint16_t*)x;
+    a.y = y;
+    a.L = (int)L;
+    a.K = (int)K;
+    a.N = (int)N;
+    a.scale = (_Float16)in_scale;
+    a.inv_scale = 1.0f / in_scale;
+    // the expanded path at every L: weight expansion, then the FP16 GEMM
+    // (split K when the 256 x 256 tiles cannot fill most CUs)
+    const int chunks = (int)(K / BK);
+    const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
+    const int bn_cov = epilogue == 2 ? 128 : 256;
+    const int tiles_m = (int)((L + T2 - 1) / T2);
+    const int tiles_n = (n_half + bn_cov - 1) / bn_cov;
+    const int tiles = tiles_n * tiles_m;
+    int splits = 1;
+    if (tiles < 192) {
+        splits = (256 + tiles - 1) / tiles;
+        const int max_splits = chunks / 8 > 0 ? chunks / 8 : 1;
+        if (splits > max_splits) splits = max_splits;
+    }
+    a.tiles_m = tiles_m;
+    a.n_tiles = tiles;
+    a.k_chunks_per_split = (chunks + splits - 1) / splits;
+    splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
+    const size_t w16_bytes = (size_t)tiles_n * 8 * (chunks + 1) * 4096;
+    if (w16_bytes > (size_t)INT32_MAX) return LUT6_E_SHAPE;
+    void* w16 = nullptr;
+    int st = workspace_for(stream, WS_EXPANDED, w16_bytes, &w16);
+    if (st != LUT6_OK) return st;
+    const dim3 xgrid((unsigned)tiles_n, (unsigned)((chunks + X_CHUNKS - 1) / X_CHUNKS));
+    if (epilogue == 2)
+        hipLaunchKernelGGL(lut6_int8_expand_kernel<2>, xgrid, dim3(256), 0, stream, q,
+                           (const uint16_t*)scales, (uint16_t*)w16, (int)N, (int)K);
+    else
+        hipLaunchKernelGGL(lut6_int8_expand_kernel<0>, xgrid, dim3(256), 0, stream, q,
+                           (const uint16_t*)scales, (uint16_t*)w16, (int)N, (int)K);
+    if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
+    a.w16 = (const uint16_t*)w16;
+    if (splits > 1) {
+        st = workspace_for(stream, WS_PARTIAL, (size_t)splits * L * N * sizeof(float), (void**)&a.partial);
+        if (st != LUT6_OK) return st;
+    }
+    launch_tiles(a, true, epilogue, in_scale != 1.0f, splits > 1, dim3(tiles, splits), stream);
     if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
     return splits > 1 ? launch_reduce(a, epilogue, splits, stream) : LUT6_OK;
 }

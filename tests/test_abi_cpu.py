@@ -22,7 +22,7 @@ HEADER = ROOT / "include" / "lut6.h"
 
 def _declared_functions():
     text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(lut6_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lut6_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -160,3 +160,24 @@ def _quantize(w=X, p=P, t=T, N=4096, K=4096):
 def test_quantize_validation(kwargs, status):
     # refusals are decided on the host, before any device call
     assert _quantize(**kwargs) == status
+
+
+Q, S = 0x50_0000_0000, 0x60_0000_0000
+
+
+def _int8_linear(x=X, q=Q, s=S, y=Y, L=128, K=4096, N=4096, scale=1.0, epi=1):
+    return lq.load_library().lut6_int8_linear(x, q, s, y, L, K, N, scale, epi, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(x=None), 1), (dict(q=None), 1), (dict(s=None), 1), (dict(y=None), 1),
+    (dict(L=-1), 2), (dict(K=0), 2), (dict(K=4000), 2), (dict(K=4064), 2), (dict(N=4008), 2),
+    (dict(N=48, epi=2), 2), (dict(L=2 ** 18), 2), (dict(N=2 ** 19), 2),
+    (dict(epi=3), 5), (dict(scale=3.0), 4), (dict(scale=0.5), 4),
+    (dict(x=X + 8), 3), (dict(q=Q + 8), 3), (dict(s=S + 2), 3), (dict(y=Y + 4), 3),
+    (dict(y=X), 8), (dict(y=Q + 16), 8), (dict(y=S), 8),
+    (dict(L=0), 0),
+])
+def test_int8_linear_validation(kwargs, status):
+    # refusals are decided on the host, before any device call
+    assert _int8_linear(**kwargs) == status

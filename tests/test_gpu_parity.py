@@ -388,3 +388,66 @@ def test_quantize_full_layer_sampled_groups(ora):
     back = ora.dequant(p1[:64], t1[:4], 4096).view(np.float16).astype(np.float64)
     ref = w[:64].astype(np.float64)
     assert np.sqrt(np.mean((back - ref) ** 2)) < 0.05 * np.sqrt(np.mean(ref ** 2))
+
+
+# ---------------------------------------------------------------------------
+# int8 weight-only variant: int8 codes, one FP16 scale per row and 32 k
+# ---------------------------------------------------------------------------
+
+def _gpu_int8(x16, q, s16, epi, s):
+    y = lq.int8_linear(_dev(x16), _dev(q), _dev(s16), epilogue=epi, in_scale=s)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    return y.view(np.uint16) if epi != F32 else y
+
+
+def _int8_check(ora, x16, q, s16, epi, s, y_dev, rows=None):
+    w = ora.int8_dequant(q, s16).view(np.float16)
+    N = q.shape[0]
+    S = tol.row_scale(x16, w, x16.shape[1], rows)
+    yd = y_dev if rows is None else y_dev[np.asarray(rows)]
+    if epi == SILU:
+        h_exact, _ = ora.int8_linear(x16, q, s16, epilogue=oracle.EPI_SILU_MUL_F16, in_scale=s, rows=rows)
+        a_exact, _ = ora.int8_linear(x16, q, s16, epilogue=oracle.EPI_F32, in_scale=s, rows=rows)
+        return tol.check(yd, h_exact, S, fp16=True,
+                         S_elem=tol.silu_scale(a_exact[:, : N // 2], a_exact[:, N // 2:], S))
+    y_exact, _ = ora.int8_linear(x16, q, s16, epilogue=epi, in_scale=s, rows=rows)
+    return tol.check(yd, y_exact, S, fp16=(epi == F16))
+
+
+@pytest.mark.parametrize("s", [1.0, 16.0])
+@pytest.mark.parametrize("K,N", [(64, 32), (256, 96), (1024, 272)])
+def test_int8_identity_readout(ora, K, N, s):
+    # x = I_K: each output is one product, so y = W^T bit for bit, W the
+    # oracle's dequantized int8 weight (including the FP16 rounding of q * s)
+    _say("int8 identity", K, N, s)
+    q, sc = si.int8_weight(N, K, (11, K, N))
+    sc = sc.copy()
+    sc[0, 0] = np.float16(6e-8)                      # subnormal weights
+    y = _gpu_int8(np.eye(K, dtype=np.float16), q, sc, F16, s)
+    assert np.array_equal(y, ora.int8_dequant(q, sc).T)
+
+
+INT8_SHAPES = [(1, 64, 32), (17, 192, 64), (100, 256, 288), (257, 576, 544), (513, 1024, 160),
+               (1029, 4096, 96), (2048, 128, 4128), (64, 12288, 64)]
+
+
+@pytest.mark.parametrize("L,K,N", INT8_SHAPES)
+@pytest.mark.parametrize("epi,s", [(F32, 1.0), (F16, 1.0), (F16, 16.0), (SILU, 1.0), (SILU, 4.0)])
+def test_int8_linear(ora, L, K, N, epi, s):
+    _say("int8", L, K, N, epi, s)
+    q, sc = si.int8_weight(N, K, (11, L, K))
+    x = si.activations(L, K, 1.0, (11, L, N))
+    rep = _int8_check(ora, x, q, sc, epi, s, _gpu_int8(x, q, sc, epi, s))
+    assert rep.ok, rep
+
+
+@pytest.mark.parametrize("L,K,N,epi", [(4096, 4096, 4096, F16), (4096, 4096, 24576, SILU),
+                                       (128, 12288, 4096, F16)])
+def test_int8_full_layer_sampled_rows(ora, L, K, N, epi):
+    _say("int8 full", L, K, N, epi)
+    q, sc = si.int8_weight(N, K, (12, L, N))
+    x = si.activations(L, K, 1.0, (12, L, K))
+    rows = si.sample_rows(L, 12, (12, L, N))
+    rep = _int8_check(ora, x, q, sc, epi, 1.0, _gpu_int8(x, q, sc, epi, 1.0), rows=rows)
+    assert rep.ok, rep
