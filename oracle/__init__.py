@@ -74,6 +74,9 @@ class Oracle:
         lib.ora_int8_linear.restype = ctypes.c_int
         lib.ora_int8_dequant.argtypes = [_P, _P, _P, _I64, _I64]
         lib.ora_int8_dequant.restype = ctypes.c_int
+        lib.ora_attention.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I64,
+                                      _P, _I64, ctypes.c_int, _P, _P, _P, _P]
+        lib.ora_attention.restype = ctypes.c_int
         lib.ora_quantize.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P]
         lib.ora_quantize.restype = ctypes.c_int
         lib.ora_packed_bytes.argtypes = [_I64, _I64]
@@ -206,6 +209,42 @@ class Oracle:
         if st != OK:
             raise OracleError(f"ora_int8_dequant status {st}")
         return w
+
+    # -- full attention -----------------------------------------------------
+    def attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_heads: int,
+                  n_kv_heads: int, head_dim: int, rows=None, threads: int | None = None,
+                  with_bounds: bool = False):
+        """Causal GQA softmax attention of the last L of Lk positions.
+
+        q: FP16 [L, ldq] (head h at columns h*D..), k, v: FP16 [Lk, ld] (head
+        g at columns g*D..).  Returns (o_exact float64, o_out FP16 bits), each
+        [n_rows, n_heads*head_dim], plus (o_abs, v_abs) when with_bounds."""
+        q = np.ascontiguousarray(q).view(np.uint16)
+        k = np.ascontiguousarray(k).view(np.uint16)
+        v = np.ascontiguousarray(v).view(np.uint16)
+        L, Lk = q.shape[0], k.shape[0]
+        if v.shape[0] != Lk:
+            raise OracleError("k and v lengths differ")
+        if rows is None:
+            rows_arr, n_rows, rows_ptr = None, L, None
+        else:
+            rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+            n_rows, rows_ptr = rows_arr.size, rows_arr.ctypes.data
+        W = n_heads * head_dim
+        oe = np.empty((n_rows, W), np.float64)
+        oo = np.empty((n_rows, W), np.uint16)
+        oa = np.empty((n_rows, W), np.float64) if with_bounds else None
+        va = np.empty((n_rows, W), np.float64) if with_bounds else None
+        if threads is None:
+            threads = len(os.sched_getaffinity(0))
+        st = self.lib.ora_attention(q.ctypes.data, q.shape[1], k.ctypes.data, k.shape[1],
+                                    v.ctypes.data, v.shape[1], L, Lk, n_heads, n_kv_heads, head_dim,
+                                    rows_ptr, n_rows, int(threads), oe.ctypes.data, oo.ctypes.data,
+                                    oa.ctypes.data if with_bounds else None,
+                                    va.ctypes.data if with_bounds else None)
+        if st != OK:
+            raise OracleError(f"ora_attention status {st}")
+        return (oe, oo, oa, va) if with_bounds else (oe, oo)
 
     # -- table fitting ---------------------------------------------------
     def quantize(self, w16: np.ndarray, groups=None, with_sse: bool = False):

@@ -581,3 +581,133 @@ int ora_quantize(const uint16_t *w, uint8_t *packed, uint16_t *tables, int64_t n
     free(v); free(u); free(idx);
     return status;
 }
+
+
+/*
+ * Full attention of the attention layers (page "Clef-Flash-ANE-LUT6",
+ * section "Model architecture": 16 query and 4 key-value heads of size 256,
+ * full attention; section "LUT-6 text weights": the probabilities are
+ * scaled by 16 in FP16 and scaled back).  The oracle is the plain
+ * definition, which the FP16 scaling only approximates:
+ *   o[i, h, :] = sum_j p_j v[j, h / (Hq/Hkv), :],
+ *   p = softmax_j(q[i, h, :] . k[j, h / (Hq/Hkv), :] / sqrt(D)), j <= Lk - L + i
+ * Readings: the L queries are the last L positions of the Lk keys (causal,
+ * one chunk of a prefill over a cache); query head h reads key-value head
+ * h / (Hq / Hkv); the softmax scale is 1/sqrt(D); the output is rounded
+ * once to FP16.  Rows are strided: element (t, h, d) of q is
+ * q[t * ldq + h * D + d], likewise k, v and o.
+ * Everything in double, k ascending.  rows (or NULL for all L) lists the
+ * query rows to compute; o_exact / o_out are [n_rows][Hq * D]; o_abs and
+ * v_abs (either may be NULL) receive sum_j p_j |v_j| and sum_j |v_j| over
+ * the visible keys, for the parity bounds.
+ */
+typedef struct {
+    const uint16_t *q, *k, *v;
+    int64_t ldq, ldk, ldv, L, Lk, Hq, Hkv, D;
+    const int64_t *rows;
+    int64_t r_begin, r_end;
+    double *o_exact, *o_abs, *v_abs;
+    uint16_t *o_out;
+    int status;
+} ora_att_job;
+
+static void *ora_att_worker(void *arg)
+{
+    ora_att_job *j = (ora_att_job *)arg;
+    const int64_t D = j->D, Hq = j->Hq, grp = j->Hq / j->Hkv;
+    double *sc = (double *)malloc(sizeof(double) * (size_t)j->Lk);
+    double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!sc || !qd) { free(sc); free(qd); j->status = ORA_E_NOMEM; return NULL; }
+#if ORA_MUTANT == 18
+    const double scale = 1.0 / (double)D;
+#else
+    const double scale = 1.0 / sqrt((double)D);
+#endif
+    for (int64_t r = j->r_begin; r < j->r_end; ++r) {
+        const int64_t i = j->rows ? j->rows[r] : r;
+#if ORA_MUTANT == 17
+        const int64_t last = j->Lk - j->L + i - 1;
+#else
+        const int64_t last = j->Lk - j->L + i;       /* keys 0..last are visible */
+#endif
+        for (int64_t h = 0; h < Hq; ++h) {
+#if ORA_MUTANT == 16
+            const int64_t kh = h % j->Hkv;
+#else
+            const int64_t kh = h / grp;
+#endif
+            for (int64_t d = 0; d < D; ++d) qd[d] = ora_f16_to_f64(j->q[i * j->ldq + h * D + d]);
+            double m = -INFINITY;
+            for (int64_t t = 0; t <= last; ++t) {
+                const uint16_t *kr = j->k + t * j->ldk + kh * D;
+                double acc = 0.0;
+                for (int64_t d = 0; d < D; ++d) acc += qd[d] * ora_f16_to_f64(kr[d]);
+                sc[t] = acc * scale;
+                if (sc[t] > m) m = sc[t];
+            }
+            double l = 0.0;
+            for (int64_t t = 0; t <= last; ++t) { sc[t] = exp(sc[t] - m); l += sc[t]; }
+            double *oe = j->o_exact + r * Hq * D + h * D;
+            double *oa = j->o_abs ? j->o_abs + r * Hq * D + h * D : NULL;
+            double *va = j->v_abs ? j->v_abs + r * Hq * D + h * D : NULL;
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = 0.0, aa = 0.0, vv = 0.0;
+                for (int64_t t = 0; t <= last; ++t) {
+                    const double x = ora_f16_to_f64(j->v[t * j->ldv + kh * D + d]);
+                    acc += sc[t] * x;
+                    aa += sc[t] * fabs(x);
+                    vv += fabs(x);
+                }
+#if ORA_MUTANT == 15
+                oe[d] = acc / (l + 1.0);
+#else
+                oe[d] = acc / l;
+#endif
+                if (oa) oa[d] = aa / l;
+                if (va) va[d] = vv;
+                j->o_out[r * Hq * D + h * D + d] = ora_f64_to_f16(oe[d]);
+            }
+        }
+    }
+    free(sc);
+    free(qd);
+    return NULL;
+}
+
+int ora_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,
+                  const uint16_t *v, int64_t ldv, int64_t L, int64_t Lk, int64_t Hq,
+                  int64_t Hkv, int64_t D, const int64_t *rows, int64_t n_rows, int threads,
+                  double *o_exact, uint16_t *o_out, double *o_abs, double *v_abs)
+{
+    if (!q || !k || !v || !o_exact || !o_out) return ORA_E_NULL;
+    if (L < 0 || Lk < L || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0) return ORA_E_SHAPE;
+    if (ldq < Hq * D || ldk < Hkv * D || ldv < Hkv * D) return ORA_E_SHAPE;
+    if (!rows) n_rows = L;
+    for (int64_t r = 0; rows && r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= L) return ORA_E_SHAPE;
+    if (n_rows == 0) return ORA_OK;
+    if (threads < 1) threads = 1;
+    if (threads > n_rows) threads = (int)n_rows;
+    ora_att_job *jobs = (ora_att_job *)calloc((size_t)threads, sizeof(ora_att_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    char *started = (char *)calloc((size_t)threads, 1);
+    if (!jobs || !tid || !started) { free(jobs); free(tid); free(started); return ORA_E_NOMEM; }
+    const int64_t per = (n_rows + threads - 1) / threads;
+    int status = ORA_OK;
+    for (int t = 0; t < threads; ++t) {
+        ora_att_job *j = &jobs[t];
+        j->q = q; j->k = k; j->v = v; j->ldq = ldq; j->ldk = ldk; j->ldv = ldv;
+        j->L = L; j->Lk = Lk; j->Hq = Hq; j->Hkv = Hkv; j->D = D; j->rows = rows;
+        j->r_begin = t * per < n_rows ? t * per : n_rows;
+        j->r_end = (t + 1) * per < n_rows ? (t + 1) * per : n_rows;
+        j->o_exact = o_exact; j->o_out = o_out; j->o_abs = o_abs; j->v_abs = v_abs;
+        if (pthread_create(&tid[t], NULL, ora_att_worker, j) == 0) started[t] = 1;
+        else ora_att_worker(j);
+    }
+    for (int t = 0; t < threads; ++t) {
+        if (started[t]) pthread_join(tid[t], NULL);
+        if (jobs[t].status != ORA_OK) status = jobs[t].status;
+    }
+    free(jobs); free(tid); free(started);
+    return status;
+}

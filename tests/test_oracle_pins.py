@@ -341,10 +341,67 @@ def pin_int8_block_scale(ora):
     assert np.array_equal(np.delete(y1, 3, axis=1), np.delete(y0, 3, axis=1))
 
 
+# -- full attention ------------------------------------------------------------
+
+def _att_inputs(L, Lk, Hq, Hkv, D, seed, extra=0):
+    g = np.random.default_rng(seed)
+    q = (g.standard_normal((L, Hq * D + extra)) * 0.5).astype(np.float16)
+    k = (g.standard_normal((Lk, Hkv * D + extra)) * 0.5).astype(np.float16)
+    v = g.standard_normal((Lk, Hkv * D + extra)).astype(np.float16)
+    return q, k, v
+
+
+def pin_attention_sdpa(ora):
+    # torch's float64 scaled_dot_product_attention with an explicit mask (the
+    # L queries are the last L of Lk positions) and the key-value heads
+    # repeated for their query heads; strided rows (extra columns) included
+    import torch
+    for L, Lk, Hq, Hkv, D in ((5, 9, 4, 2, 16), (7, 7, 3, 1, 8), (1, 12, 2, 2, 32)):
+        q, k, v = _att_inputs(L, Lk, Hq, Hkv, D, L * 100 + Lk, extra=3)
+        oe, _ = ora.attention(q, k, v, n_heads=Hq, n_kv_heads=Hkv, head_dim=D)
+        tq = torch.from_numpy(q[:, :Hq * D].astype(np.float64)).view(L, Hq, D).transpose(0, 1)
+        tk = torch.from_numpy(k[:, :Hkv * D].astype(np.float64)).view(Lk, Hkv, D).transpose(0, 1)
+        tv = torch.from_numpy(v[:, :Hkv * D].astype(np.float64)).view(Lk, Hkv, D).transpose(0, 1)
+        tk = tk.repeat_interleave(Hq // Hkv, dim=0)
+        tv = tv.repeat_interleave(Hq // Hkv, dim=0)
+        mask = torch.arange(Lk)[None, :] <= (Lk - L + torch.arange(L))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+        ref = ref.transpose(0, 1).reshape(L, Hq * D).numpy()
+        assert np.allclose(oe, ref, rtol=1e-12, atol=1e-13), "attention against torch sdpa"
+
+
+def pin_attention_closed_forms(ora):
+    L, Hq, Hkv, D = 6, 4, 2, 16
+    q, k, v = _att_inputs(L, L, Hq, Hkv, D, 3)
+    oe, oo, oa, va = ora.attention(q, k, v, n_heads=Hq, n_kv_heads=Hkv, head_dim=D, with_bounds=True)
+    # the first query sees one key: its output is that key's value row
+    want0 = np.repeat(v[0].reshape(Hkv, D), Hq // Hkv, axis=0).reshape(-1)
+    assert np.array_equal(oo[0], want0.view(np.uint16)), "single visible key"
+    # zero queries: every visible key equally likely, the mean of the values
+    z = np.zeros_like(q)
+    ez, _ = ora.attention(z, k, v, n_heads=Hq, n_kv_heads=Hkv, head_dim=D)
+    vv = v.astype(np.float64).reshape(L, Hkv, D)
+    for i in range(L):
+        mean = np.repeat(vv[: i + 1].mean(axis=0), Hq // Hkv, axis=0).reshape(-1)
+        assert np.allclose(ez[i], mean, rtol=1e-13, atol=1e-15), "uniform weights"
+    # bounds: sum p |v| between |o| and max |v|; sum |v| over the visible rows
+    assert np.all(oa >= np.abs(oe) - 1e-15)
+    va_want = np.repeat(np.cumsum(np.abs(vv), axis=0), Hq // Hkv, axis=1).reshape(L, -1)
+    assert np.allclose(va, va_want, rtol=1e-14)
+    # softmax shift invariance: a constant added to every score changes
+    # nothing; q scaled so that one key dominates gives that key's value
+    q2 = np.zeros_like(q)
+    q2[:, :D] = (k[1, :D].astype(np.float32) * 64).astype(np.float16)   # head 0 -> kv head 0
+    e2, _ = ora.attention(q2, k, v, n_heads=Hq, n_kv_heads=Hkv, head_dim=D)
+    s = (q2[3, :D].astype(np.float64) @ k[:4, :D].astype(np.float64).T) / np.sqrt(D)
+    if np.argmax(s) == 1 and np.sort(s)[-1] - np.sort(s)[-2] > 60:
+        assert np.allclose(e2[3, :D], v[1, :D].astype(np.float64), rtol=0, atol=1e-20 + 1e-12)
+
+
 PINS = [pin_pack_worked_examples, pin_pack_exhaustive, pin_storage, pin_f16_decode,
         pin_f16_encode, pin_dequant, pin_linear_bruteforce, pin_linear_silu,
         pin_special_tables, pin_identity_readout, pin_in_scale, pin_int8_dequant,
-        pin_int8_as_lut6, pin_int8_block_scale]
+        pin_int8_as_lut6, pin_int8_block_scale, pin_attention_sdpa, pin_attention_closed_forms]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -388,7 +445,9 @@ MUTANTS = {1: "big-endian byte order", 2: "index order reversed", 3: "one table 
            7: "last input column dropped", 8: "ties rounded away from zero",
            9: "subnormal decode off by 2x", 10: "activations read transposed",
            11: "f32 output truncated", 12: "int8 scale per block of 16",
-           13: "int8 code read unsigned", 14: "int8 product truncated to FP16"}
+           13: "int8 code read unsigned", 14: "int8 product truncated to FP16",
+           15: "attention sum off by one", 16: "attention heads interleaved",
+           17: "attention mask one key short", 18: "attention scaled by 1 over D"}
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m].replace(" ", "_"))
