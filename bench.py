@@ -31,6 +31,9 @@ starts.  The line printed is throughput in TFLOP/s, with
     second and algorithmic GB/s, with the oracle on one 16-row group beside;
   * int8_variant: the int8 weight-only variant (int8 codes, one FP16 scale
     per 32 k) beside LUT-6 on the same shapes (L = 128 and 4,096);
+  * attention: the attention layers' full attention (FP16, probabilities
+    x 16) at L = Lk = 16,384 and 4,096, and a 128-query chunk over 16,384
+    keys, in TFLOP/s against the FP16 peak;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same step
     (sampled token rows of two layers), on this host's cores;
   * parity_sample: those sampled rows of the GPU result against the oracle.
@@ -276,6 +279,35 @@ def time_int8(lq, si, torch, stream) -> list:
     return out
 
 
+ATT_SHAPES = ((16384, 16384), (4096, 4096), (128, 16384))
+
+
+def time_attention(lq, torch, stream) -> list:
+    """Full attention of one attention layer (16 query, 4 key-value heads of
+    256; causal, the L queries the last L of Lk positions), reading q, k, v
+    in place from one fused [L, 6144] projection output: median of 3 runs
+    of 5 back-to-back calls.  FLOPs = 4 * 256 * 16 * (visible keys summed
+    over the queries)."""
+    out = []
+    g = torch.Generator(device="cuda").manual_seed(2026)
+    for L, Lk in ATT_SHAPES:
+        qkv = torch.randn((Lk, 6144), generator=g, device="cuda", dtype=torch.float32).to(torch.float16)
+        q = qkv[Lk - L:, :4096]
+        k, v = qkv[:, 4096:5120], qkv[:, 5120:]
+        o = torch.empty((L, 4096), dtype=torch.float16, device="cuda")
+        us = _median_us(lambda: lq.attention(q, k, v, n_heads=16, n_kv_heads=4, out=o, stream=stream),
+                        torch, stream)
+        visible = L * (Lk - L) + L * (L + 1) // 2
+        flops = 4.0 * 256 * 16 * visible
+        tf = flops / (us * 1e-6) / 1e12
+        out.append({"shape": f"L={L} Lk={Lk} heads 16/4 x 256", "us_per_call": round(us, 1),
+                    "tflop_s": round(tf, 1), "frac_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4),
+                    "flops": flops})
+        del qkv, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -506,6 +538,7 @@ def main() -> int:
     # ---------------- the other workloads ----------------
     quant = time_quantize(lq, si, torch, stream, args.no_cpu_baseline)
     int8 = time_int8(lq, si, torch, stream)
+    att = time_attention(lq, torch, stream)
 
     per_config = []
     for name in OTHER_WORKLOADS:
@@ -537,6 +570,7 @@ def main() -> int:
         "per_config": per_config,
         "quantize": quant,
         "int8_variant": int8,
+        "attention": att,
         "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)

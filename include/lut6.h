@@ -157,6 +157,29 @@ int lut6_int8_linear(const void* x, const int8_t* q, const void* scales, void* y
                      int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
                      hipStream_t stream);
 
+/* Full attention of the attention layers, FP16 (page "Clef-Flash-ANE-LUT6",
+ * section "Model architecture": query and key-value heads of size 256, full
+ * attention; section "LUT-6 text weights": the probabilities are scaled up
+ * by 16 in FP16 and scaled back afterwards).
+ * The L queries are the last L of Lk positions: query i sees keys
+ * 0 .. Lk - L + i.  Query head h reads key-value head h / (n_heads /
+ * n_kv_heads).  o = softmax(q k^T / 16) v per head, computed as
+ * (sum_j fp16(16 p_j) v_j) / (16 sum_j p_j) with p_j = exp(s_j - max) in
+ * FP32, then rounded to FP16.
+ * Layouts (device, FP16, row-major with element strides between token
+ * rows): q [L, ldq] with head h at columns h*256 .. h*256+255; k and v
+ * [Lk, ldk / ldv] with key-value head g at columns g*256 ..; o [L, ldo] like
+ * q.  So the fused Q|K|V projection output can be passed in place (q = y,
+ * k = y + 4096, v = y + 5120, ld = 6144).  The caller owns every buffer.
+ * Rules: head_dim == 256, n_heads % n_kv_heads == 0, n_heads <= 4096,
+ * 0 <= L <= Lk < 2^31 - 64, each ld >= its heads * 256 (LUT6_E_SHAPE);
+ * pointers 16-byte aligned and every ld a multiple of 8 (LUT6_E_ALIGN); o
+ * must not overlap q, k or v (LUT6_E_ALIAS).  L == 0 is a no-op.  No
+ * workspace.                                                               */
+int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                   int64_t ldv, void* o, int64_t ldo, int64_t L, int64_t Lk, int64_t n_heads,
+                   int64_t n_kv_heads, int64_t head_dim, hipStream_t stream);
+
 /* Fit the tables and write the packed indices of an FP16 weight [N, K]
  * (page "Clef-Flash-ANE-LUT6", section "LUT-6 text weights": one 64-entry
  * table per 16 output channels, from 40 rounds of one-dimensional k-means

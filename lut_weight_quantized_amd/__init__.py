@@ -30,7 +30,8 @@ STATUS = {0: "LUT6_OK", 1: "LUT6_E_NULL", 2: "LUT6_E_SHAPE", 3: "LUT6_E_ALIGN",
           7: "LUT6_E_DEVICE", 8: "LUT6_E_ALIAS"}
 
 EXPORTS = ("lut6_packed_bytes", "lut6_table_bytes", "lut6_pack", "lut6_unpack",
-           "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_int8_linear", "lut6_quantize",
+           "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_int8_linear", "lut6_attention",
+           "lut6_quantize",
            "lut6_release",
            "lut6_status_string")
 
@@ -78,6 +79,8 @@ def load_library() -> ctypes.CDLL:
     lib.lut6_dequant.restype = ctypes.c_int
     lib.lut6_int8_linear.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_float, ctypes.c_int, P]
     lib.lut6_int8_linear.restype = ctypes.c_int
+    lib.lut6_attention.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I64, I64, P]
+    lib.lut6_attention.restype = ctypes.c_int
     lib.lut6_quantize.argtypes = [P, P, P, I64, I64, P]
     lib.lut6_quantize.restype = ctypes.c_int
     lib.lut6_release.argtypes = []
@@ -230,6 +233,35 @@ def int8_linear(x, q, scales, *, epilogue: int = EPI_STORE_F16, in_scale: float 
     st = load_library().lut6_int8_linear(x.data_ptr(), q.data_ptr(), scales.data_ptr(), out.data_ptr(),
                                          L, K, N, float(in_scale), int(epilogue), _stream_handle(stream))
     _check(st, "lut6_int8_linear")
+    return out
+
+
+def attention(q, k, v, *, n_heads: int, n_kv_heads: int, head_dim: int = 256, out=None,
+              stream=None):
+    """Causal grouped-query attention of the last L of Lk positions.
+
+    q: float16 [L, ldq] (2-D, rows may be strided views such as columns of
+    the Q|K|V projection output), k, v: float16 [Lk, ld]; returns o float16
+    [L, n_heads * head_dim]."""
+    import torch
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a device tensor")
+        if t.dtype != torch.float16 or t.dim() != 2 or t.stride(1) != 1:
+            raise TypeError(f"{name} must be 2-D float16 with unit column stride")
+    L, Lk = q.shape[0], k.shape[0]
+    if v.shape[0] != Lk:
+        raise ValueError("k and v must have the same number of rows")
+    if out is None:
+        out = torch.empty((L, n_heads * head_dim), dtype=torch.float16, device=q.device)
+    elif out.dtype != torch.float16 or out.dim() != 2 or out.stride(1) != 1:
+        raise TypeError("out must be 2-D float16 with unit column stride")
+    def ld(t):
+        return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    st = load_library().lut6_attention(q.data_ptr(), ld(q), k.data_ptr(), ld(k), v.data_ptr(), ld(v),
+                                       out.data_ptr(), ld(out), L, Lk, n_heads, n_kv_heads, head_dim,
+                                       _stream_handle(stream))
+    _check(st, "lut6_attention")
     return out
 
 

@@ -17,7 +17,8 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "liblut6.so"
-SOURCES = [CSRC / "lut6_linear.hip", CSRC / "lut6_quantize.hip", CSRC / "lut6_format.cpp"]
+SOURCES = [CSRC / "lut6_linear.hip", CSRC / "lut6_quantize.hip", CSRC / "lut6_attention.hip",
+           CSRC / "lut6_format.cpp"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,272 @@
+// Full attention of the attention layers on gfx950, FP16 in and out, with
+// the probabilities scaled by 16 before they are rounded to FP16 (page
+// "Clef-Flash-ANE-LUT6", section "Model architecture": 16 query and 4
+// key-value heads of size 256, full attention over the context; section
+// "LUT-6 text weights": attention probabilities are scaled up by 16 in FP16
+// and scaled back afterwards).
+//
+// What one call computes (readings where the page is silent):
+//   - the L queries are the last L positions of the Lk keys: query i sees
+//     keys 0 .. Lk - L + i (causal, one chunk of a prefill over a cache);
+//   - query head h reads key-value head h / (Hq / Hkv);
+//   - softmax scale 1 / sqrt(256) = 1/16;
+//   - o = (sum_j fp16(16 p_j) v_j) / (16 l), p_j = exp(s_j - m) in FP32, l
+//     the FP32 sum of the p_j; one FP16 rounding of o.
+//
+// Design: one workgroup per (query head, 128 queries), four waves of 32
+// queries.  Keys go by blocks of 64 through LDS (K row-major, V transposed)
+// with the next block's loads in flight during the current block's math.
+// Per block a wave computes S^T = K Q^T (keys x queries, so that each lane
+// holds one query and its softmax needs a single cross-lane exchange), the
+// online-softmax update, and O^T += V^T P^T, all on
+// v_mfma_f32_32x32x16_f16.  The P^T values never leave registers: the
+// accumulator layout of S^T, with its k slots permuted consistently in V^T,
+// is the B operand of the second product.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lut6.h"
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int HD = 256;               // head size
+constexpr int BQ = 128;               // queries per workgroup
+constexpr int BKEY = 64;              // keys per block
+constexpr int KS_STRIDE = HD + 8;     // halves per K row in LDS (528 B: rows start on distinct banks)
+constexpr int VT_STRIDE = BKEY + 4;   // halves per V^T row in LDS (136 B)
+
+struct AttArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    int64_t ldq, ldk, ldv, ldo;       // elements between consecutive token rows
+    int L, Lk, Hq, grp, nqb;
+};
+
+__device__ __forceinline__ uint32_t half_of(const u32x4& w, int i)
+{
+    return (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+__global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t ks[BKEY * KS_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[HD * VT_STRIDE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, c = lane & 31;
+    // the query blocks with the most keys start first
+    const int hq = blockIdx.x % a.Hq;
+    const int qb = a.nqb - 1 - (int)(blockIdx.x / a.Hq);
+    const int kh = hq / a.grp;
+    const int q0 = qb * BQ;
+    const int qrow = q0 + 32 * wave + c;
+    const int off = a.Lk - a.L;                                // position of query 0
+    const int pos = off + qrow;                                // this lane's query position
+    const int last = off + min(q0 + BQ - 1, a.L - 1);          // last key the workgroup needs
+    const int nkb = last / BKEY + 1;
+
+    // Q as B fragments of K Q^T: dims 16 j + 8 h .. + 7 of the lane's query
+    // (rows past L read row L - 1 and are never stored)
+    u32x4 qf[16];
+    {
+        const uint16_t* qp = a.q + (size_t)min(qrow, a.L - 1) * a.ldq + (size_t)hq * HD + 8 * h;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qf[j] = *(const u32x4*)(qp + 16 * j);
+    }
+
+    // staging: K as 2,048 16-byte pieces (8 per thread, a row per 32
+    // threads); V as 1,024 units of two keys x 8 dims (4 per thread), written
+    // transposed as key pairs.  Keys past Lk re-read key Lk - 1 (masked).
+    u32x4 kr[8], vr[4][2];
+    auto load_tile = [&](int kb) {
+        const int kbase = kb * BKEY;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int idx = tid + 256 * u, row = idx >> 5, col = idx & 31;
+            const int key = min(kbase + row, a.Lk - 1);
+            kr[u] = *(const u32x4*)(a.k + (size_t)key * a.ldk + (size_t)kh * HD + col * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + 256 * u, kp = idx & 31, dc = idx >> 5;
+            const int k0 = min(kbase + 2 * kp, a.Lk - 1), k1 = min(kbase + 2 * kp + 1, a.Lk - 1);
+            vr[u][0] = *(const u32x4*)(a.v + (size_t)k0 * a.ldv + (size_t)kh * HD + dc * 8);
+            vr[u][1] = *(const u32x4*)(a.v + (size_t)k1 * a.ldv + (size_t)kh * HD + dc * 8);
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int idx = tid + 256 * u, row = idx >> 5, col = idx & 31;
+            *(u32x4*)(ks + row * KS_STRIDE + col * 8) = kr[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + 256 * u, kp = idx & 31, dc = idx >> 5;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *(uint32_t*)(vt + (dc * 8 + i) * VT_STRIDE + 2 * kp) =
+                    half_of(vr[u][0], i) | (half_of(vr[u][1], i) << 16);
+        }
+    };
+
+    f32x16 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+    float m = -__builtin_inff(), l = 0.0f;
+    const float cl = 1.4426950408889634f / 16.0f;              // log2(e) / sqrt(256)
+
+    load_tile(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        store_tile();
+        __syncthreads();
+        if (kb + 1 < nkb) load_tile(kb + 1);
+
+        // S^T for keys 32 st .. 32 st + 31 of the block: lane (c, h), value r
+        // is key 8 (r / 4) + 4 h + r % 4 of the tile, query c
+        f32x16 s[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const f16x8 ka = *(const f16x8*)(ks + (32 * st + c) * KS_STRIDE + 16 * j + 8 * h);
+                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, __builtin_bit_cast(f16x8, qf[j]), s[st], 0, 0, 0);
+            }
+        }
+
+        // online softmax (base 2); masked keys get -inf
+        float bm = -__builtin_inff();
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kb * BKEY + 32 * st + 8 * (r >> 2) + 4 * h + (r & 3);
+                const float t = key <= pos ? s[st][r] * cl : -__builtin_inff();
+                s[st][r] = t;
+                bm = fmaxf(bm, t);
+            }
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m, bm);
+        const float mu = mn == -__builtin_inff() ? 0.0f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m - mu);
+        // P^T x 16 in FP16 as B fragments: step jj of tile st takes values
+        // r = 8 jj .. 8 jj + 7 (keys 16 jj + 4 h + 0..3 and 16 jj + 8 + 4 h + 0..3)
+        u32x4 pf[2][2];
+        float sum = 0.0f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 8 * jj + 2 * e;
+                    const float p0 = __builtin_amdgcn_exp2f(s[st][r] - mu);
+                    const float p1 = __builtin_amdgcn_exp2f(s[st][r + 1] - mu);
+                    sum += p0 + p1;
+                    pf[st][jj][e] = pack_f16(16.0f * p0, 16.0f * p1);
+                }
+        l = l * alpha + sum;
+        m = mn;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+
+        // O^T (dims x queries) += V^T P^T; the A slots follow the same keys
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const uint16_t* vp = vt + (dt * 32 + c) * VT_STRIDE + 32 * st + 16 * jj + 4 * h;
+                    const u32x2 lo = *(const u32x2*)vp;
+                    const u32x2 hi = *(const u32x2*)(vp + 8);
+                    const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
+                                                                   __builtin_bit_cast(f16x8, pf[st][jj]),
+                                                                   o[dt], 0, 0, 0);
+                }
+        __syncthreads();
+    }
+
+    // scale back: o / (16 l), l summed over both lane halves
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = 1.0f / (16.0f * lt);
+    if (qrow < a.L) {
+        uint16_t* op = a.o + (size_t)qrow * a.ldo + (size_t)hq * HD + 4 * h;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const u32x2 w = {pack_f16(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                                 pack_f16(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+                *(u32x2*)(op + dt * 32 + 8 * g) = w;
+            }
+    }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t ldk,
+                              const void* v, int64_t ldv, void* o, int64_t ldo, int64_t L,
+                              int64_t Lk, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                              hipStream_t stream)
+{
+    if (!q || !k || !v || !o) return LUT6_E_NULL;
+    if (head_dim != HD || n_heads <= 0 || n_kv_heads <= 0 || n_heads % n_kv_heads) return LUT6_E_SHAPE;
+    if (n_heads > 4096 || L < 0 || Lk < L || Lk > (int64_t)INT32_MAX - BKEY) return LUT6_E_SHAPE;
+    if (ldq < n_heads * HD || ldo < n_heads * HD || ldk < n_kv_heads * HD || ldv < n_kv_heads * HD)
+        return LUT6_E_SHAPE;
+    if (ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8) return LUT6_E_ALIGN;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LUT6_E_ALIGN;
+    if (L == 0) return LUT6_OK;
+    const size_t qb = ((size_t)(L - 1) * ldq + n_heads * HD) * 2;
+    const size_t ob = ((size_t)(L - 1) * ldo + n_heads * HD) * 2;
+    const size_t kb = ((size_t)(Lk - 1) * ldk + n_kv_heads * HD) * 2;
+    const size_t vb = ((size_t)(Lk - 1) * ldv + n_kv_heads * HD) * 2;
+    if (overlaps(o, ob, q, qb) || overlaps(o, ob, k, kb) || overlaps(o, ob, v, vb)) return LUT6_E_ALIAS;
+
+    AttArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.o = (uint16_t*)o;
+    a.ldq = ldq;
+    a.ldk = ldk;
+    a.ldv = ldv;
+    a.ldo = ldo;
+    a.L = (int)L;
+    a.Lk = (int)Lk;
+    a.Hq = (int)n_heads;
+    a.grp = (int)(n_heads / n_kv_heads);
+    a.nqb = (int)((L + BQ - 1) / BQ);
+    const int64_t blocks = (int64_t)a.nqb * n_heads;
+    if (blocks > INT32_MAX) return LUT6_E_SHAPE;
+    hipLaunchKernelGGL(lut6_attention_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+}

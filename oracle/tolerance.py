@@ -129,3 +129,41 @@ def silu_scale(g_exact: np.ndarray, u_exact: np.ndarray, S_row: np.ndarray) -> n
     with np.errstate(over="ignore"):
         silu = g / (1.0 + np.exp(-g))
     return (1.1 * np.abs(u) + np.abs(silu)) * np.asarray(S_row, np.float64)[:, None]
+
+
+# -- full attention ------------------------------------------------------------
+#
+# The device computes o = (sum_j fp16(16 p_j) v_j) / (16 l) with p_j, l in
+# FP32 against the running maximum.  Against the exact o = sum_j P_j v_j
+# (P the exact softmax) the error is bounded, per output element, by
+#   A * (2^-11 + eps_s + eps_acc) + 2^-29 * V + ulp16(o) / 2 + 2^-23 |o|
+# with A = sum_j P_j |v_j| and V = sum_j |v_j| over the visible keys:
+#   * 2^-11: fp16(16 p) of a normal value is within a relative 2^-11;
+#   * 2^-29 V: a subnormal 16 p is within 2^-25 absolutely, and after the
+#     division by 16 l (l >= 1) each key adds at most 2^-29 |v_j|;
+#   * eps_s = 2^-22 (1.1 S1 + 1): a score is a 256-term FP32 sum (two
+#     levels of at most 16 additions: 32 * 2^-24 relative to
+#     S1 = max_j sum_d |q_d k_jd|); p_j = exp((s_j - s_max) / 16) moves by
+#     the errors of both scores over 16, plus the base-2 exponential's error;
+#   * eps_acc = (16 nkb + 320) 2^-24, nkb = key blocks of 64: the FP32
+#     accumulation chains of o (4 products of 16 per block) and l, and the
+#     per-block rescales, which o and l share, so they only perturb the
+#     weights of the average;
+#   * the FP16 rounding of o, and the FP32 product by 1 / (16 l).
+# S1 is bounded by ||q_row,head||_1 * max|k|.
+
+def attention_bound(o_exact, o_abs, v_abs, s1, nkb: int) -> np.ndarray:
+    o_exact = np.asarray(o_exact, np.float64)
+    eps = 2.0 ** -11 + 2.0 ** -22 * (1.1 * np.asarray(s1, np.float64) + 1.0) + (16 * nkb + 320) * 2.0 ** -24
+    return (np.asarray(o_abs, np.float64) * eps + 2.0 ** -29 * np.asarray(v_abs, np.float64)
+            + 0.5 * ulp16(o_exact) + 2.0 ** -23 * np.abs(o_exact))
+
+
+def check_attention(o_dev16, o_exact, o_abs, v_abs, s1, nkb: int):
+    """(ok, failures, max error / bound) of FP16 device outputs."""
+    val = np.asarray(o_dev16).view(np.float16).astype(np.float64)
+    bound = attention_bound(o_exact, o_abs, v_abs, s1, nkb)
+    err = np.abs(val - np.asarray(o_exact, np.float64))
+    bad = ~(err <= bound)
+    return (not bool(np.any(bad)), int(np.sum(bad)),
+            float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0)

@@ -181,3 +181,21 @@ def _int8_linear(x=X, q=Q, s=S, y=Y, L=128, K=4096, N=4096, scale=1.0, epi=1):
 def test_int8_linear_validation(kwargs, status):
     # refusals are decided on the host, before any device call
     assert _int8_linear(**kwargs) == status
+
+
+def _attention(q=X, ldq=4096, k=P, ldk=1024, v=T, ldv=1024, o=Y, ldo=4096, L=128, Lk=512,
+               hq=16, hkv=4, d=256):
+    return lq.load_library().lut6_attention(q, ldq, k, ldk, v, ldv, o, ldo, L, Lk, hq, hkv, d, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(d=128), 2), (dict(hkv=3), 2), (dict(hkv=0), 2), (dict(hq=0), 2), (dict(L=-1), 2),
+    (dict(Lk=100), 2), (dict(ldq=4088), 2), (dict(ldk=1016), 2), (dict(ldo=256), 2),
+    (dict(ldq=4100), 3), (dict(ldv=1028), 3), (dict(q=X + 8), 3), (dict(o=Y + 2), 3),
+    (dict(o=X + 4096), 8), (dict(o=P), 8), (dict(o=T + 16), 8),
+    (dict(L=0), 0), (dict(L=0, Lk=0), 0),
+])
+def test_attention_validation(kwargs, status):
+    # refusals are decided on the host, before any device call
+    assert _attention(**kwargs) == status

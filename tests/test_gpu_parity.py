@@ -451,3 +451,111 @@ def test_int8_full_layer_sampled_rows(ora, L, K, N, epi):
     rows = si.sample_rows(L, 12, (12, L, N))
     rep = _int8_check(ora, x, q, sc, epi, 1.0, _gpu_int8(x, q, sc, epi, 1.0), rows=rows)
     assert rep.ok, rep
+
+
+# ---------------------------------------------------------------------------
+# full attention: FP16 probabilities x 16, against the exact softmax
+# ---------------------------------------------------------------------------
+
+def _att_s1(q16, k16, rows, Hq, Hkv, D):
+    """Per (row, head) bound on sum_d |q_d k_d|, broadcast over the head's D outputs."""
+    q = np.abs(q16[np.asarray(rows)][:, : Hq * D].astype(np.float64)).reshape(len(rows), Hq, D)
+    kmax = float(np.max(np.abs(k16[:, : Hkv * D].astype(np.float64))))
+    return np.repeat(q.sum(axis=2) * kmax, D, axis=1)
+
+
+def _att_case(ora, q, k, v, Hq, Hkv, rows=None, D=256):
+    """Run the device on torch views q, k, v and check `rows` against the oracle."""
+    L, Lk = q.shape[0], k.shape[0]
+    o = lq.attention(q, k, v, n_heads=Hq, n_kv_heads=Hkv)
+    torch.cuda.synchronize()
+    rows = np.arange(L) if rows is None else np.asarray(rows)
+    qn, kn, vn = (t.cpu().numpy() for t in (q, k, v))
+    oe, _, oa, va = ora.attention(qn, kn, vn, n_heads=Hq, n_kv_heads=Hkv, head_dim=D, rows=rows,
+                                  with_bounds=True)
+    od = o.cpu().numpy()[rows].view(np.uint16)
+    nkb = (Lk - L + int(rows.max())) // 64 + 1
+    return tol.check_attention(od, oe, oa, va, _att_s1(qn, kn, rows, Hq, Hkv, D), nkb), o
+
+
+def _att_inputs(L, Lk, Hq, Hkv, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    D = 256
+    q = (g.standard_normal((L, Hq * D)) * scale).astype(np.float16)
+    k = (g.standard_normal((Lk, Hkv * D)) * scale).astype(np.float16)
+    v = g.standard_normal((Lk, Hkv * D)).astype(np.float16)
+    return _dev(q), _dev(k), _dev(v)
+
+
+ATT_SHAPES = [(1, 1, 16, 4), (5, 5, 2, 1), (37, 37, 4, 4), (128, 128, 16, 4), (130, 200, 4, 2),
+              (300, 1000, 16, 4), (64, 4096, 16, 4), (1024, 1024, 16, 4), (129, 129, 1, 1)]
+
+
+@pytest.mark.parametrize("L,Lk,Hq,Hkv", ATT_SHAPES)
+def test_attention(ora, L, Lk, Hq, Hkv):
+    _say("attention", L, Lk, Hq, Hkv)
+    q, k, v = _att_inputs(L, Lk, Hq, Hkv, L * 7 + Lk)
+    (ok, bad, ratio), _ = _att_case(ora, q, k, v, Hq, Hkv)
+    assert ok, (bad, ratio)
+
+
+@pytest.mark.parametrize("scale", [0.25, 2.0])
+def test_attention_sharp_and_flat_scores(ora, scale):
+    # scale 2: scores of ~64, so one or two keys carry each row; 0.25: near-uniform
+    _say("attention scale", scale)
+    q, k, v = _att_inputs(200, 700, 8, 2, 11, scale=scale)
+    (ok, bad, ratio), _ = _att_case(ora, q, k, v, 8, 2)
+    assert ok, (bad, ratio)
+
+
+def test_attention_reads_fused_qkv_rows(ora):
+    # q, k, v as column ranges of one [L, 6144] projection output
+    _say("attention fused qkv")
+    L = 300
+    g = np.random.default_rng(5)
+    y = _dev(g.standard_normal((L, 6144)).astype(np.float16))
+    q, k, v = y[:, :4096], y[:, 4096:5120], y[:, 5120:]
+    (ok, bad, ratio), o = _att_case(ora, q, k, v, 16, 4)
+    assert ok, (bad, ratio)
+    # the same values in separate contiguous tensors give the same bits
+    o2 = lq.attention(q.contiguous(), k.contiguous(), v.contiguous(), n_heads=16, n_kv_heads=4)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+
+
+def test_attention_tiny_probabilities_keep_their_mass(ora):
+    # key 0 dominates every row: the other 4,095 keys have p = 1.5 * 2^-24
+    # each (16 p = 24 * 2^-24, exact in FP16) and carry the value 1, key 0
+    # the value 0, so the output is their summed mass.  Unscaled, each p is
+    # an FP16 tie between 2^-24 and 2^-23 and loses a third of itself, far
+    # beyond the bound's 2^-29 V term; scaled by 16 it is kept.
+    _say("attention tiny probabilities")
+    Lk, D = 4096, 256
+    q = np.ones((1, D), np.float16)
+    k = np.zeros((Lk, D), np.float16)
+    k[0, :255] = 1.0
+    k[0, 255] = np.float16(16 * (24 * np.log(2) - np.log(1.5)) - 255)   # score gap 259.68
+    v = np.ones((Lk, D), np.float16)
+    v[0] = 0
+    (ok, bad, ratio), o = _att_case(ora, _dev(q), _dev(k), _dev(v), 1, 1)
+    assert ok, (bad, ratio)
+
+
+@pytest.mark.parametrize("L,Lk", [(16384, 16384), (128, 16384)])
+def test_attention_full_size_sampled_rows(ora, L, Lk):
+    # the attention layers at the longest context: the whole prefill, and
+    # the last 128-token chunk over the full cache; q|k|v in one buffer
+    _say("attention full", L, Lk)
+    g = np.random.default_rng(L)
+    kv = _dev(g.standard_normal((Lk, 2048)).astype(np.float16))
+    q = _dev(g.standard_normal((L, 4096)).astype(np.float16))
+    rows = si.sample_rows(L, 8, (14, L, Lk))
+    (ok, bad, ratio), _ = _att_case(ora, q, kv[:, :1024], kv[:, 1024:], 16, 4, rows=rows)
+    assert ok, (bad, ratio)
+
+
+def test_attention_deterministic():
+    q, k, v = _att_inputs(500, 900, 16, 4, 3)
+    a = lq.attention(q, k, v, n_heads=16, n_kv_heads=4)
+    b = lq.attention(q, k, v, n_heads=16, n_kv_heads=4)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
