@@ -14,8 +14,11 @@
 //     the FP32 sum of the p_j; one FP16 rounding of o.
 //
 // Design: one workgroup per (query head, 128 queries), four waves of 32
-// queries.  Keys go by blocks of 64 through LDS (K row-major, V transposed)
-// with the next block's loads in flight during the current block's math.
+// queries.  Keys go by blocks of 64 through two LDS stages (K row-major, V
+// transposed): a block is computed from one stage while the next block,
+// loaded into registers one block ahead, is written to the other; one
+// barrier per block.  Short query chunks over a long cache split the keys
+// over several workgroups, whose partial sums a second kernel combines.
 // Per block a wave computes S^T = K Q^T (keys x queries, so that each lane
 // holds one query and its softmax needs a single cross-lane exchange), the
 // online-softmax update, and O^T += V^T P^T, all on
@@ -39,15 +42,25 @@ constexpr int BQ = 128;               // queries per workgroup
 constexpr int BKEY = 64;              // keys per block
 constexpr int KS_STRIDE = HD + 8;     // halves per K row in LDS (528 B: rows start on distinct banks)
 constexpr int VT_STRIDE = BKEY + 4;   // halves per V^T row in LDS (136 B)
+constexpr int WS_ATTENTION = 2;       // library workspace kind of the key-split partials
 
 struct AttArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
     uint16_t* o;
+    float* part_o;                    // key splits: [split][L][Hq][256] unnormalised sums
+    float* part_ml;                   // key splits: [split][L][Hq][2] (max, sum)
     int64_t ldq, ldk, ldv, ldo;       // elements between consecutive token rows
     int L, Lk, Hq, grp, nqb;
+    int kb_per_split;                 // key blocks per split (key splits only)
 };
+
+// A row's running maximum is raised only when a block's maximum passes it
+// by more than TAU (base-2 units): softmax does not depend on the shift, the
+// probabilities against the older maximum stay below 2^TAU (16 p < 2^12 in
+// FP16), and the 128 accumulators are rescaled only on those blocks.
+constexpr float TAU = 8.0f;
 
 __device__ __forceinline__ uint32_t half_of(const u32x4& w, int i)
 {
@@ -60,10 +73,13 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b)
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
+// one LDS stage: K [64][KS_STRIDE], then V^T [256][VT_STRIDE]
+constexpr int STAGE_HALVES = BKEY * KS_STRIDE + HD * VT_STRIDE;
+
+template <bool SPLIT>
 __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[BKEY * KS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[HD * VT_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE_HALVES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, c = lane & 31;
     // the query blocks with the most keys start first
@@ -75,52 +91,11 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
     const int off = a.Lk - a.L;                                // position of query 0
     const int pos = off + qrow;                                // this lane's query position
     const int last = off + min(q0 + BQ - 1, a.L - 1);          // last key the workgroup needs
-    const int nkb = last / BKEY + 1;
-
-    // Q as B fragments of K Q^T: dims 16 j + 8 h .. + 7 of the lane's query
-    // (rows past L read row L - 1 and are never stored)
-    u32x4 qf[16];
-    {
-        const uint16_t* qp = a.q + (size_t)min(qrow, a.L - 1) * a.ldq + (size_t)hq * HD + 8 * h;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) qf[j] = *(const u32x4*)(qp + 16 * j);
+    int kb0 = 0, kb1 = last / BKEY + 1;
+    if constexpr (SPLIT) {
+        kb0 = min((int)blockIdx.y * a.kb_per_split, kb1);
+        kb1 = min(kb0 + a.kb_per_split, kb1);
     }
-
-    // staging: K as 2,048 16-byte pieces (8 per thread, a row per 32
-    // threads); V as 1,024 units of two keys x 8 dims (4 per thread), written
-    // transposed as key pairs.  Keys past Lk re-read key Lk - 1 (masked).
-    u32x4 kr[8], vr[4][2];
-    auto load_tile = [&](int kb) {
-        const int kbase = kb * BKEY;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int idx = tid + 256 * u, row = idx >> 5, col = idx & 31;
-            const int key = min(kbase + row, a.Lk - 1);
-            kr[u] = *(const u32x4*)(a.k + (size_t)key * a.ldk + (size_t)kh * HD + col * 8);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = tid + 256 * u, kp = idx & 31, dc = idx >> 5;
-            const int k0 = min(kbase + 2 * kp, a.Lk - 1), k1 = min(kbase + 2 * kp + 1, a.Lk - 1);
-            vr[u][0] = *(const u32x4*)(a.v + (size_t)k0 * a.ldv + (size_t)kh * HD + dc * 8);
-            vr[u][1] = *(const u32x4*)(a.v + (size_t)k1 * a.ldv + (size_t)kh * HD + dc * 8);
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int idx = tid + 256 * u, row = idx >> 5, col = idx & 31;
-            *(u32x4*)(ks + row * KS_STRIDE + col * 8) = kr[u];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = tid + 256 * u, kp = idx & 31, dc = idx >> 5;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *(uint32_t*)(vt + (dc * 8 + i) * VT_STRIDE + 2 * kp) =
-                    half_of(vr[u][0], i) | (half_of(vr[u][1], i) << 16);
-        }
-    };
 
     f32x16 o[8];
 #pragma unroll
@@ -128,88 +103,163 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
     float m = -__builtin_inff(), l = 0.0f;
-    const float cl = 1.4426950408889634f / 16.0f;              // log2(e) / sqrt(256)
 
-    load_tile(0);
-    for (int kb = 0; kb < nkb; ++kb) {
-        store_tile();
-        __syncthreads();
-        if (kb + 1 < nkb) load_tile(kb + 1);
-
-        // S^T for keys 32 st .. 32 st + 31 of the block: lane (c, h), value r
-        // is key 8 (r / 4) + 4 h + r % 4 of the tile, query c
-        f32x16 s[2];
+    if (kb0 < kb1) {
+        // Q as B fragments of K Q^T: dims 16 j + 8 h .. + 7 of the lane's
+        // query (rows past L read row L - 1 and are never stored)
+        u32x4 qf[16];
+        {
+            const uint16_t* qp = a.q + (size_t)min(qrow, a.L - 1) * a.ldq + (size_t)hq * HD + 8 * h;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const f16x8 ka = *(const f16x8*)(ks + (32 * st + c) * KS_STRIDE + 16 * j + 8 * h);
-                s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, __builtin_bit_cast(f16x8, qf[j]), s[st], 0, 0, 0);
-            }
+            for (int j = 0; j < 16; ++j) qf[j] = *(const u32x4*)(qp + 16 * j);
         }
 
-        // online softmax (base 2); masked keys get -inf
-        float bm = -__builtin_inff();
+        // staging: K as 2,048 16-byte pieces (8 per thread, a row per 32
+        // threads); V as 1,024 units of two keys x 8 dims (4 per thread),
+        // written transposed as key pairs.  Keys past Lk re-read key Lk - 1
+        // (they are masked).
+        u32x4 kr[8], vr[4][2];
+        auto load_tile = [&](int kb) {
+            const int kbase = kb * BKEY;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kb * BKEY + 32 * st + 8 * (r >> 2) + 4 * h + (r & 3);
-                const float t = key <= pos ? s[st][r] * cl : -__builtin_inff();
-                s[st][r] = t;
-                bm = fmaxf(bm, t);
+            for (int u = 0; u < 8; ++u) {
+                const int idx = tid + 256 * u, row = idx >> 5, col = idx & 31;
+                const int key = min(kbase + row, a.Lk - 1);
+                kr[u] = *(const u32x4*)(a.k + (size_t)key * a.ldk + (size_t)kh * HD + col * 8);
             }
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bm);
-        const float mu = mn == -__builtin_inff() ? 0.0f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m - mu);
-        // P^T x 16 in FP16 as B fragments: step jj of tile st takes values
-        // r = 8 jj .. 8 jj + 7 (keys 16 jj + 4 h + 0..3 and 16 jj + 8 + 4 h + 0..3)
-        u32x4 pf[2][2];
-        float sum = 0.0f;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int u = 0; u < 4; ++u) {
+                const int idx = tid + 256 * u, kp = idx & 31, dc = idx >> 5;
+                const int k0 = min(kbase + 2 * kp, a.Lk - 1), k1 = min(kbase + 2 * kp + 1, a.Lk - 1);
+                vr[u][0] = *(const u32x4*)(a.v + (size_t)k0 * a.ldv + (size_t)kh * HD + dc * 8);
+                vr[u][1] = *(const u32x4*)(a.v + (size_t)k1 * a.ldv + (size_t)kh * HD + dc * 8);
+            }
+        };
+        auto store_tile = [&](int b) {
+            uint16_t* const ks = lds + b * STAGE_HALVES;
+            uint16_t* const vt = ks + BKEY * KS_STRIDE;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+            for (int u = 0; u < 8; ++u) {
+                const int idx = tid + 256 * u, row = idx >> 5, col = idx & 31;
+                *(u32x4*)(ks + row * KS_STRIDE + col * 8) = kr[u];
+            }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 8 * jj + 2 * e;
-                    const float p0 = __builtin_amdgcn_exp2f(s[st][r] - mu);
-                    const float p1 = __builtin_amdgcn_exp2f(s[st][r + 1] - mu);
-                    sum += p0 + p1;
-                    pf[st][jj][e] = pack_f16(16.0f * p0, 16.0f * p1);
-                }
-        l = l * alpha + sum;
-        m = mn;
+            for (int u = 0; u < 4; ++u) {
+                const int idx = tid + 256 * u, kp = idx & 31, dc = idx >> 5;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                for (int i = 0; i < 8; ++i)
+                    *(uint32_t*)(vt + (dc * 8 + i) * VT_STRIDE + 2 * kp) =
+                        half_of(vr[u][0], i) | (half_of(vr[u][1], i) << 16);
+            }
+        };
 
-        // O^T (dims x queries) += V^T P^T; the A slots follow the same keys
+        const float cl = 1.4426950408889634f / 16.0f;          // log2(e) / sqrt(256)
+        load_tile(kb0);
+        store_tile(0);
+        __syncthreads();
+        if (kb0 + 1 < kb1) load_tile(kb0 + 1);
+        for (int kb = kb0; kb < kb1; ++kb) {
+            const int b = (kb - kb0) & 1;
+            const uint16_t* const ks = lds + b * STAGE_HALVES;
+            const uint16_t* const vt = ks + BKEY * KS_STRIDE;
+
+            // S^T for keys 32 st .. 32 st + 31 of the block: lane (c, h),
+            // value r is key 8 (r / 4) + 4 h + r % 4 of the tile, query c
+            f32x16 s[2];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const f16x8 ka = *(const f16x8*)(ks + (32 * st + c) * KS_STRIDE + 16 * j + 8 * h);
+                    s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, __builtin_bit_cast(f16x8, qf[j]),
+                                                                   s[st], 0, 0, 0);
+                }
+            }
+
+            // online softmax (base 2); masked keys get -inf
+            float bm = -__builtin_inff();
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const uint16_t* vp = vt + (dt * 32 + c) * VT_STRIDE + 32 * st + 16 * jj + 4 * h;
-                    const u32x2 lo = *(const u32x2*)vp;
-                    const u32x2 hi = *(const u32x2*)(vp + 8);
-                    const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
-                                                                   __builtin_bit_cast(f16x8, pf[st][jj]),
-                                                                   o[dt], 0, 0, 0);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb * BKEY + 32 * st + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const float t = key <= pos ? s[st][r] * cl : -__builtin_inff();
+                    s[st][r] = t;
+                    bm = fmaxf(bm, t);
                 }
-        __syncthreads();
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const bool raise = bm > m + TAU;                   // also the first finite maximum
+            if (__any(raise)) {
+                const float mn = raise ? bm : m;
+                const float alpha = raise ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                m = mn;
+            }
+            const float mu = m == -__builtin_inff() ? 0.0f : m;
+            // P^T x 16 in FP16 as B fragments: step jj of tile st takes
+            // values r = 8 jj .. 8 jj + 7 (keys 16 jj + 4 h + 0..3 and
+            // 16 jj + 8 + 4 h + 0..3)
+            u32x4 pf[2][2];
+            float sum = 0.0f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 8 * jj + 2 * e;
+                        const float p0 = __builtin_amdgcn_exp2f(s[st][r] - mu);
+                        const float p1 = __builtin_amdgcn_exp2f(s[st][r + 1] - mu);
+                        sum += p0 + p1;
+                        pf[st][jj][e] = pack_f16(16.0f * p0, 16.0f * p1);
+                    }
+            l += sum;
+
+            // O^T (dims x queries) += V^T P^T; the A slots follow the same keys
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const uint16_t* vp = vt + (dt * 32 + c) * VT_STRIDE + 32 * st + 16 * jj + 4 * h;
+                        const u32x2 lo = *(const u32x2*)vp;
+                        const u32x2 hi = *(const u32x2*)(vp + 8);
+                        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
+                                                                       __builtin_bit_cast(f16x8, pf[st][jj]),
+                                                                       o[dt], 0, 0, 0);
+                    }
+            // the other stage was last read before the previous barrier
+            if (kb + 1 < kb1) store_tile(b ^ 1);
+            __syncthreads();
+            if (kb + 2 < kb1) load_tile(kb + 2);
+        }
     }
 
-    // scale back: o / (16 l), l summed over both lane halves
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv = 1.0f / (16.0f * lt);
-    if (qrow < a.L) {
+    const float lt = l + __shfl_xor(l, 32);                    // both lane halves
+    if (qrow >= a.L) return;
+    if constexpr (SPLIT) {
+        // unnormalised sums, the row maximum and the probability sum
+        const size_t row = ((size_t)blockIdx.y * a.L + qrow) * a.Hq + hq;
+        float* op = a.part_o + row * HD + 4 * h;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 w = {o[dt][4 * g], o[dt][4 * g + 1], o[dt][4 * g + 2], o[dt][4 * g + 3]};
+                *(float4*)(op + dt * 32 + 8 * g) = w;
+            }
+        if (h == 0) *(float2*)(a.part_ml + 2 * row) = float2{m, lt};
+    } else {
+        // scale back: o / (16 l)
+        const float inv = 1.0f / (16.0f * lt);
         uint16_t* op = a.o + (size_t)qrow * a.ldo + (size_t)hq * HD + 4 * h;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
@@ -222,6 +272,36 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
     }
 }
 
+// Key splits: o = sum_s 2^(m_s - m) o_s / (16 sum_s 2^(m_s - m) l_s), m the
+// largest m_s; a split that saw no visible key has m_s = -inf, l_s = 0.
+// One thread per (row, head, 4 dims).
+__global__ void __launch_bounds__(256) lut6_attention_combine_kernel(AttArgs a, int splits)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rows = (int64_t)a.L * a.Hq;
+    if (t >= rows * (HD / 4)) return;
+    const int64_t row = t / (HD / 4);
+    const int d4 = (int)(t % (HD / 4));
+    float mx = -__builtin_inff();
+    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, a.part_ml[2 * (s * rows + row)]);
+    float w = 0.0f;
+    float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < splits; ++s) {
+        const float2 ml = *(const float2*)(a.part_ml + 2 * (s * rows + row));
+        const float f = __builtin_amdgcn_exp2f(ml.x - mx);
+        w += f * ml.y;
+        const float4 v = *(const float4*)(a.part_o + (s * rows + row) * HD + 4 * d4);
+        acc.x += f * v.x;
+        acc.y += f * v.y;
+        acc.z += f * v.z;
+        acc.w += f * v.w;
+    }
+    const float inv = 1.0f / (16.0f * w);
+    const int64_t qrow = row / a.Hq, hq = row % a.Hq;
+    const u32x2 out = {pack_f16(acc.x * inv, acc.y * inv), pack_f16(acc.z * inv, acc.w * inv)};
+    *(u32x2*)(a.o + qrow * a.ldo + hq * HD + 4 * d4) = out;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)
@@ -231,6 +311,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 }
 
 }  // namespace
+
+namespace lut6_detail {
+int workspace(hipStream_t stream, int kind, size_t bytes, void** out);   // lut6_linear.hip
+}
 
 extern "C" int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t ldk,
                               const void* v, int64_t ldv, void* o, int64_t ldo, int64_t L,
@@ -267,6 +351,34 @@ extern "C" int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t
     a.nqb = (int)((L + BQ - 1) / BQ);
     const int64_t blocks = (int64_t)a.nqb * n_heads;
     if (blocks > INT32_MAX) return LUT6_E_SHAPE;
-    hipLaunchKernelGGL(lut6_attention_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    // few workgroups (short query chunks over a long cache): split the keys
+    // so that about 256 workgroups run, each over at least 4 key blocks
+    const int nkb = (int)((Lk - 1) / BKEY + 1);
+    int splits = 1;
+    if (blocks < 128 && nkb >= 8) {
+        splits = (int)((256 + blocks - 1) / blocks);
+        if (splits > nkb / 4) splits = nkb / 4;
+    }
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    a.kb_per_split = nkb;
+    if (splits > 1) {
+        a.kb_per_split = (nkb + splits - 1) / splits;
+        splits = (nkb + a.kb_per_split - 1) / a.kb_per_split;
+        const size_t rows = (size_t)L * n_heads * splits;
+        void* ws = nullptr;
+        const int st = lut6_detail::workspace(stream, WS_ATTENTION, rows * (HD + 2) * sizeof(float), &ws);
+        if (st != LUT6_OK) return st;
+        a.part_o = (float*)ws;
+        a.part_ml = a.part_o + rows * HD;
+        hipLaunchKernelGGL(lut6_attention_kernel<true>, dim3((unsigned)blocks, (unsigned)splits), dim3(256),
+                           0, stream, a);
+        if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
+        const int64_t threads = (int64_t)L * n_heads * (HD / 4);
+        hipLaunchKernelGGL(lut6_attention_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                           0, stream, a, splits);
+    } else {
+        hipLaunchKernelGGL(lut6_attention_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
 }

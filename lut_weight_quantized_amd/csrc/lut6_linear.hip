@@ -1618,7 +1618,8 @@ struct Workspace {
     size_t bytes = 0;
 };
 
-// workspace kinds: split-K partial sums, expanded FP16 weight
+// workspace kinds: split-K partial sums, expanded FP16 weight (2: the
+// attention's key-split partials, lut6_attention.hip)
 enum { WS_PARTIAL = 0, WS_EXPANDED = 1 };
 
 std::mutex g_ws_mutex;
@@ -1944,6 +1945,12 @@ extern "C" int lut6_dequant(const uint8_t* packed, const void* tables, void* w, 
 
 namespace lut6_detail {
 int quantize_release();   // lut6_quantize.hip
+
+// the per-(device, stream) workspaces for the other sources (kinds from 2 up)
+int workspace(hipStream_t stream, int kind, size_t bytes, void** out)
+{
+    return workspace_for(stream, kind, bytes, out);
+}
 }
 
 extern "C" int lut6_release(void)
