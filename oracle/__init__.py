@@ -77,6 +77,9 @@ class Oracle:
         lib.ora_attention.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I64,
                                       _P, _I64, ctypes.c_int, _P, _P, _P, _P]
         lib.ora_attention.restype = ctypes.c_int
+        lib.ora_gated_delta.argtypes = [_P, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _I64,
+                                        _I64, _I64, _P, ctypes.c_int, _P, _P, _P, _P]
+        lib.ora_gated_delta.restype = ctypes.c_int
         lib.ora_quantize.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P]
         lib.ora_quantize.restype = ctypes.c_int
         lib.ora_packed_bytes.argtypes = [_I64, _I64]
@@ -245,6 +248,40 @@ class Oracle:
         if st != OK:
             raise OracleError(f"ora_attention status {st}")
         return (oe, oo, oa, va) if with_bounds else (oe, oo)
+
+    # -- Gated DeltaNet recurrence ---------------------------------------------
+    def gated_delta(self, q, k, v, g, beta, *, n_k_heads: int, n_v_heads: int, dk: int = 128,
+                    dv: int = 128, state=None, threads: int | None = None):
+        """Gated delta rule over L tokens (see ora_gated_delta).
+
+        q, k: FP16 [L, ld] (key head at columns kh*dk ..), v: FP16 [L, ld]
+        (value head at h*dv ..), g, beta: float32 [L, n_v_heads], state:
+        float32 [n_v_heads, dk, dv] or None.  Returns (o_exact, o_out bits,
+        o_abs) [L, n_v_heads*dv] and the final state (float64)."""
+        q = np.ascontiguousarray(q).view(np.uint16)
+        k = np.ascontiguousarray(k).view(np.uint16)
+        v = np.ascontiguousarray(v).view(np.uint16)
+        g = np.ascontiguousarray(g, dtype=np.float32)
+        beta = np.ascontiguousarray(beta, dtype=np.float32)
+        L = q.shape[0]
+        if k.shape[0] != L or v.shape[0] != L or g.shape != beta.shape or g.shape[0] != L:
+            raise OracleError("q, k, v, g, beta lengths differ")
+        st_in = None if state is None else np.ascontiguousarray(state, dtype=np.float32)
+        W = n_v_heads * dv
+        oe = np.empty((L, W), np.float64)
+        oo = np.empty((L, W), np.uint16)
+        oa = np.empty((L, W), np.float64)
+        so = np.empty((n_v_heads, dk, dv), np.float64)
+        if threads is None:
+            threads = len(os.sched_getaffinity(0))
+        st = self.lib.ora_gated_delta(q.ctypes.data, q.shape[1], k.ctypes.data, k.shape[1],
+                                      v.ctypes.data, v.shape[1], g.ctypes.data, beta.ctypes.data,
+                                      g.shape[1], L, n_k_heads, n_v_heads, dk, dv,
+                                      None if st_in is None else st_in.ctypes.data, int(threads),
+                                      oe.ctypes.data, oo.ctypes.data, oa.ctypes.data, so.ctypes.data)
+        if st != OK:
+            raise OracleError(f"ora_gated_delta status {st}")
+        return oe, oo, oa, so
 
     # -- table fitting ---------------------------------------------------
     def quantize(self, w16: np.ndarray, groups=None, with_sse: bool = False):

@@ -711,3 +711,125 @@ int ora_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk
     free(jobs); free(tid); free(started);
     return status;
 }
+
+
+/*
+ * Gated DeltaNet recurrence of the linear-attention layers (page
+ * "Clef-Flash-ANE-LUT6", section "Model architecture": 16 key and 32 value
+ * heads of size 128; page "clef-flash — Core AI", the decoder states: a
+ * recurrent state [32, 128, 128] per layer).  The pages name the layer, not
+ * its update; the reading is the gated delta rule, per value head h with
+ * key head h / (Hv / Hk), state S (dk x dv), for t = 0 .. L-1:
+ *   S <- exp(g_t) S;  d = beta_t (v_t - S^T k_t);  S <- S + k_t d^T;
+ *   o_t = S^T q_t / sqrt(dk)
+ * q, k, v FP16 with row strides (head g at columns g*dk / h*dv); g, beta
+ * FP32 [L][Hv] (row stride ldg); state_in FP32 [Hv][dk][dv] (NULL: zeros);
+ * o_exact / o_out [L][Hv*dv] (double / FP16 bits, one rounding); o_abs (may
+ * be NULL) sum_i |S_ij q_i| / sqrt(dk), the size of the terms of each
+ * output; state_out (may be NULL) the final state in double.  Everything in
+ * double, i ascending; threads split the independent heads.
+ */
+typedef struct {
+    const uint16_t *q, *k, *v;
+    const float *g, *beta, *state_in;
+    int64_t ldq, ldk, ldv, ldg, L, Hk, Hv, dk, dv, h_begin, h_end;
+    double *o_exact, *o_abs, *state_out;
+    uint16_t *o_out;
+    int status;
+} ora_gdn_job;
+
+static void *ora_gdn_worker(void *arg)
+{
+    ora_gdn_job *j = (ora_gdn_job *)arg;
+    const int64_t dk = j->dk, dv = j->dv, Hv = j->Hv;
+    double *S = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
+    double *kd = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *qd = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *dl = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!S || !kd || !qd || !dl) { free(S); free(kd); free(qd); free(dl); j->status = ORA_E_NOMEM; return NULL; }
+    const double scale = 1.0 / sqrt((double)dk);
+    for (int64_t h = j->h_begin; h < j->h_end; ++h) {
+#if ORA_MUTANT == 19
+        const int64_t kh = h % j->Hk;
+#else
+        const int64_t kh = h / (Hv / j->Hk);
+#endif
+        for (int64_t e = 0; e < dk * dv; ++e)
+            S[e] = j->state_in ? (double)j->state_in[h * dk * dv + e] : 0.0;
+        for (int64_t t = 0; t < j->L; ++t) {
+            const double a = exp((double)j->g[t * j->ldg + h]);
+#if ORA_MUTANT == 20
+            const double b = 1.0;
+#else
+            const double b = (double)j->beta[t * j->ldg + h];
+#endif
+            for (int64_t i = 0; i < dk; ++i) {
+                kd[i] = ora_f16_to_f64(j->k[t * j->ldk + kh * dk + i]);
+                qd[i] = ora_f16_to_f64(j->q[t * j->ldq + kh * dk + i]);
+            }
+            for (int64_t e = 0; e < dk * dv; ++e) S[e] *= a;
+            for (int64_t c = 0; c < dv; ++c) {
+                double kv = 0.0;
+                for (int64_t i = 0; i < dk; ++i) kv += S[i * dv + c] * kd[i];
+                dl[c] = b * (ora_f16_to_f64(j->v[t * j->ldv + h * dv + c]) - kv);
+            }
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t c = 0; c < dv; ++c) S[i * dv + c] += kd[i] * dl[c];
+            for (int64_t c = 0; c < dv; ++c) {
+                double acc = 0.0, aa = 0.0;
+                for (int64_t i = 0; i < dk; ++i) {
+                    acc += S[i * dv + c] * qd[i];
+                    aa += fabs(S[i * dv + c] * qd[i]);
+                }
+#if ORA_MUTANT == 21
+                const double ov = acc;
+#else
+                const double ov = acc * scale;
+#endif
+                j->o_exact[t * Hv * dv + h * dv + c] = ov;
+                if (j->o_abs) j->o_abs[t * Hv * dv + h * dv + c] = aa * scale;
+                j->o_out[t * Hv * dv + h * dv + c] = ora_f64_to_f16(ov);
+            }
+        }
+        if (j->state_out)
+            for (int64_t e = 0; e < dk * dv; ++e) j->state_out[h * dk * dv + e] = S[e];
+    }
+    free(S); free(kd); free(qd); free(dl);
+    return NULL;
+}
+
+int ora_gated_delta(const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,
+                    const uint16_t *v, int64_t ldv, const float *g, const float *beta,
+                    int64_t ldg, int64_t L, int64_t Hk, int64_t Hv, int64_t dk, int64_t dv,
+                    const float *state_in, int threads, double *o_exact, uint16_t *o_out,
+                    double *o_abs, double *state_out)
+{
+    if (!q || !k || !v || !g || !beta || !o_exact || !o_out) return ORA_E_NULL;
+    if (L < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk || dk <= 0 || dv <= 0) return ORA_E_SHAPE;
+    if (ldq < Hk * dk || ldk < Hk * dk || ldv < Hv * dv || ldg < Hv) return ORA_E_SHAPE;
+    if (threads < 1) threads = 1;
+    if (threads > Hv) threads = (int)Hv;
+    ora_gdn_job *jobs = (ora_gdn_job *)calloc((size_t)threads, sizeof(ora_gdn_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    char *started = (char *)calloc((size_t)threads, 1);
+    if (!jobs || !tid || !started) { free(jobs); free(tid); free(started); return ORA_E_NOMEM; }
+    const int64_t per = (Hv + threads - 1) / threads;
+    int status = ORA_OK;
+    for (int t = 0; t < threads; ++t) {
+        ora_gdn_job *j = &jobs[t];
+        j->q = q; j->k = k; j->v = v; j->g = g; j->beta = beta; j->state_in = state_in;
+        j->ldq = ldq; j->ldk = ldk; j->ldv = ldv; j->ldg = ldg; j->L = L;
+        j->Hk = Hk; j->Hv = Hv; j->dk = dk; j->dv = dv;
+        j->h_begin = t * per < Hv ? t * per : Hv;
+        j->h_end = (t + 1) * per < Hv ? (t + 1) * per : Hv;
+        j->o_exact = o_exact; j->o_abs = o_abs; j->state_out = state_out; j->o_out = o_out;
+        if (pthread_create(&tid[t], NULL, ora_gdn_worker, j) == 0) started[t] = 1;
+        else ora_gdn_worker(j);
+    }
+    for (int t = 0; t < threads; ++t) {
+        if (started[t]) pthread_join(tid[t], NULL);
+        if (jobs[t].status != ORA_OK) status = jobs[t].status;
+    }
+    free(jobs); free(tid); free(started);
+    return status;
+}

@@ -398,10 +398,93 @@ def pin_attention_closed_forms(ora):
         assert np.allclose(e2[3, :D], v[1, :D].astype(np.float64), rtol=0, atol=1e-20 + 1e-12)
 
 
+# -- Gated DeltaNet recurrence ---------------------------------------------------
+
+def _gdn_inputs(L, Hk, Hv, d, seed):
+    g = np.random.default_rng(seed)
+    q = (g.standard_normal((L, Hk * d)) / np.sqrt(d)).astype(np.float16)
+    k = (g.standard_normal((L, Hk * d)) / np.sqrt(d)).astype(np.float16)
+    v = g.standard_normal((L, Hv * d)).astype(np.float16)
+    gl = (-g.random((L, Hv)) * 0.5).astype(np.float32)
+    be = g.random((L, Hv)).astype(np.float32)
+    s0 = (g.standard_normal((Hv, d, d)) * 0.1).astype(np.float32)
+    return q, k, v, gl, be, s0
+
+
+def pin_gated_delta_frozen_state(ora):
+    # beta = 0, g = 0: the state never changes, o_t = S0^T q_t / sqrt(dk)
+    L, Hk, Hv, d = 5, 2, 4, 8
+    q, k, v, gl, be, s0 = _gdn_inputs(L, Hk, Hv, d, 1)
+    oe, _, _, so = ora.gated_delta(q, k, v, np.zeros_like(gl), np.zeros_like(be), n_k_heads=Hk,
+                                   n_v_heads=Hv, dk=d, dv=d, state=s0)
+    qf = q.astype(np.float64).reshape(L, Hk, d)
+    for h in range(Hv):
+        want = qf[:, h // 2] @ s0[h].astype(np.float64) / np.sqrt(d)
+        assert np.allclose(oe[:, h * d:(h + 1) * d], want, rtol=1e-13, atol=1e-15), "frozen state"
+    assert np.array_equal(so, s0.astype(np.float64))
+
+
+def pin_gated_delta_decay_only(ora):
+    # beta = 0: S_t = exp(g_1 + .. + g_t) S0
+    L, Hk, Hv, d = 6, 1, 2, 8
+    q, k, v, gl, be, s0 = _gdn_inputs(L, Hk, Hv, d, 2)
+    _, _, _, so = ora.gated_delta(q, k, v, gl, np.zeros_like(be), n_k_heads=Hk, n_v_heads=Hv,
+                                  dk=d, dv=d, state=s0)
+    for h in range(Hv):
+        f = np.exp(np.sum(gl[:, h].astype(np.float64)))
+        assert np.allclose(so[h], f * s0[h], rtol=1e-12), "decay"
+
+
+def pin_gated_delta_overwrites_unit_keys(ora):
+    # beta = 1 and k_t = e_i: the update replaces row i of the (decayed)
+    # state by v_t, so reading with q = e_i right after gives v_t / sqrt(dk);
+    # every other row only decays
+    L, Hk, Hv, d = 7, 2, 4, 8
+    q, k, v, gl, be, s0 = _gdn_inputs(L, Hk, Hv, d, 3)
+    rows = np.arange(L) % d
+    k = np.zeros_like(k)
+    for t in range(L):
+        for kh in range(Hk):
+            k[t, kh * d + (rows[t] + kh) % d] = 1.0
+    q = k.copy()
+    oe, _, _, so = ora.gated_delta(q, k, v, gl, np.ones_like(be), n_k_heads=Hk, n_v_heads=Hv,
+                                   dk=d, dv=d, state=s0)
+    vf = v.astype(np.float64)
+    assert np.allclose(oe, vf / np.sqrt(d), rtol=1e-13, atol=1e-15), "delta rule overwrite"
+    for h in range(Hv):
+        kh = h // 2
+        last = {}
+        for t in range(L):
+            last[(rows[t] + kh) % d] = t
+        decay = np.exp(np.cumsum(gl[::-1, h].astype(np.float64))[::-1])   # exp(g_t + .. + g_{L-1})
+        for i in range(d):
+            if i in last:
+                t = last[i]
+                want = vf[t, h * d:(h + 1) * d] * (decay[t + 1] if t + 1 < L else 1.0)
+            else:
+                want = s0[h, i].astype(np.float64) * decay[0]
+            assert np.allclose(so[h, i], want, rtol=1e-12, atol=1e-14), "row kept or decayed"
+
+
+def pin_gated_delta_split_sequence(ora):
+    # running [0, a) then [a, L) from the carried state equals one run
+    L, Hk, Hv, d, a = 9, 2, 4, 8, 4
+    q, k, v, gl, be, s0 = _gdn_inputs(L, Hk, Hv, d, 4)
+    oe, _, _, so = ora.gated_delta(q, k, v, gl, be, n_k_heads=Hk, n_v_heads=Hv, dk=d, dv=d, state=s0)
+    o1, _, _, s1 = ora.gated_delta(q[:a], k[:a], v[:a], gl[:a], be[:a], n_k_heads=Hk, n_v_heads=Hv,
+                                   dk=d, dv=d, state=s0)
+    o2, _, _, s2 = ora.gated_delta(q[a:], k[a:], v[a:], gl[a:], be[a:], n_k_heads=Hk, n_v_heads=Hv,
+                                   dk=d, dv=d, state=s1.astype(np.float32))
+    assert np.array_equal(o1, oe[:a])
+    assert np.allclose(o2, oe[a:], rtol=1e-6, atol=1e-7)    # the carried state is rounded to FP32
+
+
 PINS = [pin_pack_worked_examples, pin_pack_exhaustive, pin_storage, pin_f16_decode,
         pin_f16_encode, pin_dequant, pin_linear_bruteforce, pin_linear_silu,
         pin_special_tables, pin_identity_readout, pin_in_scale, pin_int8_dequant,
-        pin_int8_as_lut6, pin_int8_block_scale, pin_attention_sdpa, pin_attention_closed_forms]
+        pin_int8_as_lut6, pin_int8_block_scale, pin_attention_sdpa, pin_attention_closed_forms,
+        pin_gated_delta_frozen_state, pin_gated_delta_decay_only, pin_gated_delta_overwrites_unit_keys,
+        pin_gated_delta_split_sequence]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -447,7 +530,8 @@ MUTANTS = {1: "big-endian byte order", 2: "index order reversed", 3: "one table 
            11: "f32 output truncated", 12: "int8 scale per block of 16",
            13: "int8 code read unsigned", 14: "int8 product truncated to FP16",
            15: "attention sum off by one", 16: "attention heads interleaved",
-           17: "attention mask one key short", 18: "attention scaled by 1 over D"}
+           17: "attention mask one key short", 18: "attention scaled by 1 over D",
+           19: "delta rule heads interleaved", 20: "delta rule beta ignored", 21: "delta rule unscaled"}
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m].replace(" ", "_"))
