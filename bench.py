@@ -34,6 +34,8 @@ starts.  The line printed is throughput in TFLOP/s, with
   * attention: the attention layers' full attention (FP16, probabilities
     x 16) at L = Lk = 16,384 and 4,096, and a 128-query chunk over 16,384
     keys, in TFLOP/s against the FP16 peak;
+  * gated_delta: one linear-attention layer's Gated DeltaNet recurrence
+    (32 value heads, FP32 state) over 4,096 and 16,384 tokens;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same step
     (sampled token rows of two layers), on this host's cores;
   * parity_sample: those sampled rows of the GPU result against the oracle.
@@ -308,6 +310,36 @@ def time_attention(lq, torch, stream) -> list:
     return out
 
 
+GDN_LENGTHS = (4096, 16384)
+
+
+def time_gated_delta(lq, torch, stream) -> list:
+    """Gated DeltaNet recurrence of one linear-attention layer (16 key and
+    32 value heads of 128, state [32, 128, 128] FP32), q|k|v read in place
+    from one fused [L, 8192] projection output: median of 3 runs of 5
+    back-to-back calls.  FLOPs per token and value head: 7 * 128 * 128
+    (decay, S^T k, the rank-one update, S^T q)."""
+    out = []
+    g = torch.Generator(device="cuda").manual_seed(2027)
+    for L in GDN_LENGTHS:
+        qkv = (torch.randn((L, 8192), generator=g, device="cuda", dtype=torch.float32) / 11.3).to(torch.float16)
+        gl = -torch.rand((L, 32), generator=g, device="cuda", dtype=torch.float32) * 0.5
+        be = torch.rand((L, 32), generator=g, device="cuda", dtype=torch.float32)
+        st = torch.zeros((32, 128, 128), dtype=torch.float32, device="cuda")
+        o = torch.empty((L, 4096), dtype=torch.float16, device="cuda")
+        q, k, v = qkv[:, :2048], qkv[:, 2048:4096], qkv[:, 4096:]
+        us = _median_us(lambda: lq.gated_delta(q, k, v, gl, be, st, n_k_heads=16, n_v_heads=32, out=o,
+                                               stream=stream), torch, stream)
+        flops = 7.0 * 128 * 128 * 32 * L
+        out.append({"shape": f"L={L} heads 16/32 x 128", "us_per_call": round(us, 1),
+                    "tokens_per_s": round(L / (us * 1e-6), 0),
+                    "gflop_s": round(flops / (us * 1e-6) / 1e9, 1), "flops": flops,
+                    "note": "token-sequential kernel (the chunked matrix-core form is not built)"})
+        del qkv, gl, be, st, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -539,6 +571,7 @@ def main() -> int:
     quant = time_quantize(lq, si, torch, stream, args.no_cpu_baseline)
     int8 = time_int8(lq, si, torch, stream)
     att = time_attention(lq, torch, stream)
+    gdn = time_gated_delta(lq, torch, stream)
 
     per_config = []
     for name in OTHER_WORKLOADS:
@@ -571,6 +604,7 @@ def main() -> int:
         "quantize": quant,
         "int8_variant": int8,
         "attention": att,
+        "gated_delta": gdn,
         "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)

@@ -180,6 +180,31 @@ int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const
                    int64_t ldv, void* o, int64_t ldo, int64_t L, int64_t Lk, int64_t n_heads,
                    int64_t n_kv_heads, int64_t head_dim, hipStream_t stream);
 
+/* Gated DeltaNet recurrence of the linear-attention layers (page
+ * "Clef-Flash-ANE-LUT6", section "Model architecture": 16 key and 32 value
+ * heads of size 128; page "clef-flash — Core AI", the decoder states: a
+ * recurrent state [32, 128, 128] per layer, carried between calls).
+ * The pages name the layer, not its update; read as the gated delta rule,
+ * per value head h with key head h / (n_v_heads / n_k_heads), tokens in
+ * order:  S <- exp(g_t) S;  d = beta_t (v_t - S^T k_t);  S <- S + k_t d^T;
+ * o_t = S^T q_t / sqrt(128), rounded to FP16.  q and k are used as given
+ * (any normalisation, convolution and gate computation come before).
+ * Layouts (device): q, k FP16 [L, ldq / ldk], key head g at columns
+ * g*128 ..; v FP16 [L, ldv] and o FP16 [L, ldo], value head h at columns
+ * h*128 ..; g (log decay) and beta FP32 [L, ldg], head h at column h;
+ * state FP32 [n_v_heads, 128, 128] (S[h][i][j], i over k, j over v), read
+ * as the initial state and overwritten with the final one.  The caller
+ * owns every buffer.
+ * Rules: dk == dv == 128, n_v_heads % n_k_heads == 0, n_v_heads <= 4096,
+ * 0 <= L < 2^31 - 64, each ld at least its row's width (LUT6_E_SHAPE); q,
+ * k, v, o 16-byte aligned with ldq, ldk, ldv, ldo multiples of 8; g, beta,
+ * state 4-byte aligned (LUT6_E_ALIGN); o and state must not overlap an
+ * input or each other (LUT6_E_ALIAS).  L == 0 is a no-op.  No workspace. */
+int lut6_gated_delta(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                     int64_t ldv, const float* g, const float* beta, int64_t ldg, void* o,
+                     int64_t ldo, float* state, int64_t L, int64_t n_k_heads, int64_t n_v_heads,
+                     int64_t dk, int64_t dv, hipStream_t stream);
+
 /* Fit the tables and write the packed indices of an FP16 weight [N, K]
  * (page "Clef-Flash-ANE-LUT6", section "LUT-6 text weights": one 64-entry
  * table per 16 output channels, from 40 rounds of one-dimensional k-means

@@ -31,6 +31,7 @@ STATUS = {0: "LUT6_OK", 1: "LUT6_E_NULL", 2: "LUT6_E_SHAPE", 3: "LUT6_E_ALIGN",
 
 EXPORTS = ("lut6_packed_bytes", "lut6_table_bytes", "lut6_pack", "lut6_unpack",
            "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_int8_linear", "lut6_attention",
+           "lut6_gated_delta",
            "lut6_quantize",
            "lut6_release",
            "lut6_status_string")
@@ -81,6 +82,9 @@ def load_library() -> ctypes.CDLL:
     lib.lut6_int8_linear.restype = ctypes.c_int
     lib.lut6_attention.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I64, I64, P]
     lib.lut6_attention.restype = ctypes.c_int
+    lib.lut6_gated_delta.argtypes = [P, I64, P, I64, P, I64, P, P, I64, P, I64, P, I64, I64, I64, I64,
+                                     I64, P]
+    lib.lut6_gated_delta.restype = ctypes.c_int
     lib.lut6_quantize.argtypes = [P, P, P, I64, I64, P]
     lib.lut6_quantize.restype = ctypes.c_int
     lib.lut6_release.argtypes = []
@@ -262,6 +266,35 @@ def attention(q, k, v, *, n_heads: int, n_kv_heads: int, head_dim: int = 256, ou
                                        out.data_ptr(), ld(out), L, Lk, n_heads, n_kv_heads, head_dim,
                                        _stream_handle(stream))
     _check(st, "lut6_attention")
+    return out
+
+
+def gated_delta(q, k, v, g, beta, state, *, n_k_heads: int, n_v_heads: int, out=None,
+                stream=None):
+    """Gated delta rule over the L rows (tokens) of q, k, v; updates `state`
+    (float32 [n_v_heads, 128, 128], in place) and returns o float16
+    [L, n_v_heads * 128].  q, k, v: 2-D float16 with unit column stride (row
+    strides allowed); g, beta: float32 [L, >= n_v_heads]."""
+    import torch
+    for t, name, dt in ((q, "q", torch.float16), (k, "k", torch.float16), (v, "v", torch.float16),
+                        (g, "g", torch.float32), (beta, "beta", torch.float32)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a device tensor")
+        if t.dtype != dt or t.dim() != 2 or t.stride(1) != 1:
+            raise TypeError(f"{name} must be 2-D {dt} with unit column stride")
+    _require(state, torch.float32, "state")
+    if g.stride(0) != beta.stride(0) and g.shape[0] > 1:
+        raise ValueError("g and beta must have the same row stride")
+    L = q.shape[0]
+    if out is None:
+        out = torch.empty((L, n_v_heads * 128), dtype=torch.float16, device=q.device)
+    def ld(t):
+        return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    st = load_library().lut6_gated_delta(q.data_ptr(), ld(q), k.data_ptr(), ld(k), v.data_ptr(), ld(v),
+                                         g.data_ptr(), beta.data_ptr(), ld(g), out.data_ptr(), ld(out),
+                                         state.data_ptr(), L, n_k_heads, n_v_heads, 128, 128,
+                                         _stream_handle(stream))
+    _check(st, "lut6_gated_delta")
     return out
 
 

@@ -18,6 +18,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "liblut6.so"
 SOURCES = [CSRC / "lut6_linear.hip", CSRC / "lut6_quantize.hip", CSRC / "lut6_attention.hip",
+           CSRC / "lut6_gated_delta.hip",
            CSRC / "lut6_format.cpp"]
 ARCH = "gfx950"
 

@@ -167,3 +167,33 @@ def check_attention(o_dev16, o_exact, o_abs, v_abs, s1, nkb: int):
     bad = ~(err <= bound)
     return (not bool(np.any(bad)), int(np.sum(bad)),
             float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0)
+
+
+# -- Gated DeltaNet recurrence ---------------------------------------------------
+#
+# The device keeps the state in FP32 and reproduces the gated delta rule
+# token by token.  Each token adds rounding of a few FP32 ulps to every state
+# entry (the decay product, one fused update, and the 128-term dot product
+# S^T k behind d: 8 sequential terms and a 4-level tree), and the token map
+# S -> exp(g) S (I - beta k k^T) does not expand errors for beta |k|^2 in
+# [0, 2].  Taking the per-token roundings as independent, the state error
+# after t tokens grows like sqrt(t); with a wide margin:
+#   |o_t - o_ref| <= ulp16(o_ref) / 2
+#                    + 2^-18 sqrt(t + 1) (A_t + ||q_t||_1 / sqrt(128) * s_rms)
+# A_t = sum_i |S_ij q_i| / sqrt(128) (the oracle returns it) and s_rms the
+# root mean square of the head's final state, a floor for entries near zero.
+
+def gated_delta_bound(o_exact, o_abs, q_l1, s_rms, t) -> np.ndarray:
+    eps = 2.0 ** -18 * np.sqrt(np.asarray(t, np.float64) + 1.0)
+    o_exact = np.asarray(o_exact, np.float64)
+    return (0.5 * ulp16(o_exact)
+            + eps * (np.asarray(o_abs, np.float64) + np.asarray(q_l1, np.float64) / np.sqrt(128.0) * s_rms))
+
+
+def check_gated_delta(o_dev16, o_exact, o_abs, q_l1, s_rms, t):
+    val = np.asarray(o_dev16).view(np.float16).astype(np.float64)
+    bound = gated_delta_bound(o_exact, o_abs, q_l1, s_rms, t)
+    err = np.abs(val - np.asarray(o_exact, np.float64))
+    bad = ~(err <= bound)
+    return (not bool(np.any(bad)), int(np.sum(bad)),
+            float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0)

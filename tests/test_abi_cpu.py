@@ -199,3 +199,26 @@ def _attention(q=X, ldq=4096, k=P, ldk=1024, v=T, ldv=1024, o=Y, ldo=4096, L=128
 def test_attention_validation(kwargs, status):
     # refusals are decided on the host, before any device call
     assert _attention(**kwargs) == status
+
+
+G, B, ST = 0x70_0000_0000, 0x80_0000_0000, 0x90_0000_0000
+
+
+def _gated_delta(q=X, ldq=8192, k=X + 4096, ldk=8192, v=X + 8192, ldv=8192, g=G, be=B, ldg=32,
+                 o=Y, ldo=4096, st=ST, L=64, hk=16, hv=32, dk=128, dv=128):
+    return lq.load_library().lut6_gated_delta(q, ldq, k, ldk, v, ldv, g, be, ldg, o, ldo, st, L,
+                                              hk, hv, dk, dv, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(g=None), 1), (dict(be=None), 1),
+    (dict(o=None), 1), (dict(st=None), 1),
+    (dict(dk=64), 2), (dict(dv=256), 2), (dict(hk=3), 2), (dict(hv=0), 2), (dict(L=-1), 2),
+    (dict(ldq=2040), 2), (dict(ldv=4088), 2), (dict(ldo=4000), 2), (dict(ldg=31), 2),
+    (dict(ldq=8196), 3), (dict(o=Y + 8), 3), (dict(g=G + 2), 3), (dict(st=ST + 1), 3),
+    (dict(o=X + 64), 8), (dict(o=G), 8), (dict(st=X), 8), (dict(st=B + 4), 8), (dict(o=ST), 8),
+    (dict(L=0), 0),
+])
+def test_gated_delta_validation(kwargs, status):
+    # refusals are decided on the host, before any device call
+    assert _gated_delta(**kwargs) == status

@@ -559,3 +559,98 @@ def test_attention_deterministic():
     b = lq.attention(q, k, v, n_heads=16, n_kv_heads=4)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet recurrence: FP32 state, against the FP64 sequential rule
+# ---------------------------------------------------------------------------
+
+def _gdn_problem(L, Hk, Hv, seed, with_state=True):
+    """q|k|v in one [L, 2*Hk*128 + Hv*128] buffer (the projection's layout),
+    g in (-0.5, 0], beta in [0, 1), an optional random initial state."""
+    g = np.random.default_rng(seed)
+    d = 128
+    qkv = np.concatenate([g.standard_normal((L, 2 * Hk * d)) / np.sqrt(d),
+                          g.standard_normal((L, Hv * d))], axis=1).astype(np.float16)
+    gl = (-g.random((L, Hv)) * 0.5).astype(np.float32)
+    be = g.random((L, Hv)).astype(np.float32)
+    s0 = (g.standard_normal((Hv, d, d)) * 0.1).astype(np.float32) if with_state else np.zeros((Hv, d, d), np.float32)
+    return qkv, gl, be, s0
+
+
+def _gdn_run(qkv, gl, be, s0, Hk, Hv):
+    d = 128
+    y = _dev(qkv)
+    st = _dev(s0)
+    o = lq.gated_delta(y[:, : Hk * d], y[:, Hk * d: 2 * Hk * d], y[:, 2 * Hk * d:], _dev(gl), _dev(be), st,
+                       n_k_heads=Hk, n_v_heads=Hv)
+    torch.cuda.synchronize()
+    return o.cpu().numpy().view(np.uint16), st.cpu().numpy()
+
+
+def _gdn_check(ora, qkv, gl, be, s0, Hk, Hv, o_dev, s_dev):
+    d = 128
+    q, k, v = qkv[:, : Hk * d], qkv[:, Hk * d: 2 * Hk * d], qkv[:, 2 * Hk * d:]
+    oe, _, oa, so = ora.gated_delta(q, k, v, gl, be, n_k_heads=Hk, n_v_heads=Hv, state=s0)
+    L = qkv.shape[0]
+    s_rms = np.repeat(np.sqrt(np.mean(so.reshape(Hv, -1) ** 2, axis=1)), d)[None, :]
+    ql1 = np.abs(q.astype(np.float64)).reshape(L, Hk, d).sum(axis=2)
+    ql1 = np.repeat(np.repeat(ql1, Hv // Hk, axis=1), d, axis=1)
+    t = np.arange(L)[:, None]
+    rep = tol.check_gated_delta(o_dev, oe, oa, ql1, s_rms, t)
+    # the final state, entry by entry, within the same allowance at t = L - 1
+    s_err = np.abs(s_dev.astype(np.float64) - so)
+    s_bound = 2.0 ** -18 * np.sqrt(L) * (np.abs(so) + s_rms.reshape(Hv, d)[:, :1, None])
+    return rep, bool(np.all(s_err <= s_bound))
+
+
+GDN_SHAPES = [(1, 1, 1), (5, 2, 4), (63, 1, 2), (64, 2, 2), (65, 16, 32), (200, 16, 32), (1000, 4, 8)]
+
+
+@pytest.mark.parametrize("L,Hk,Hv", GDN_SHAPES)
+def test_gated_delta(ora, L, Hk, Hv):
+    _say("gated delta", L, Hk, Hv)
+    qkv, gl, be, s0 = _gdn_problem(L, Hk, Hv, L + 31 * Hv)
+    o, s = _gdn_run(qkv, gl, be, s0, Hk, Hv)
+    (ok, bad, ratio), s_ok = _gdn_check(ora, qkv, gl, be, s0, Hk, Hv, o, s)
+    assert ok and s_ok, (bad, ratio, s_ok)
+
+
+def test_gated_delta_zero_state_and_unit_keys(ora):
+    # beta = 1 and k_t = e_i: row i of the state becomes v_t, which q = e_i
+    # reads back: o_t = fp16(v_t / sqrt(128)) for every token
+    _say("gated delta unit keys")
+    L, Hk, Hv, d = 300, 2, 4, 128
+    qkv, gl, be, s0 = _gdn_problem(L, Hk, Hv, 5, with_state=False)
+    kq = np.zeros((L, Hk * d), np.float16)
+    for t in range(L):
+        for kh in range(Hk):
+            kq[t, kh * d + (7 * t + kh) % d] = 1.0
+    qkv[:, : Hk * d] = kq
+    qkv[:, Hk * d: 2 * Hk * d] = kq
+    o, s = _gdn_run(qkv, gl, np.ones_like(be), s0, Hk, Hv)
+    want = (qkv[:, 2 * Hk * d:].astype(np.float64) / np.sqrt(d)).astype(np.float16).view(np.uint16)
+    d_ulp = np.abs(o.astype(np.int32) - want.astype(np.int32))
+    assert int(d_ulp.max()) <= 1
+
+
+def test_gated_delta_carried_state_is_exact():
+    # two calls with the state carried between them give the bits of one call
+    _say("gated delta carried state")
+    L, Hk, Hv, a = 333, 16, 32, 130
+    qkv, gl, be, s0 = _gdn_problem(L, Hk, Hv, 9)
+    o_all, s_all = _gdn_run(qkv, gl, be, s0, Hk, Hv)
+    o1, s1 = _gdn_run(qkv[:a], gl[:a], be[:a], s0, Hk, Hv)
+    o2, s2 = _gdn_run(qkv[a:], gl[a:], be[a:], s1, Hk, Hv)
+    assert np.array_equal(np.concatenate([o1, o2]), o_all)
+    assert np.array_equal(s2, s_all)
+
+
+def test_gated_delta_layer_full_size(ora):
+    # one linear-attention layer's recurrence: 16 key and 32 value heads over
+    # a 4,096-token prefill chunk, q|k|v read in place from the projection
+    _say("gated delta full", 4096)
+    qkv, gl, be, s0 = _gdn_problem(4096, 16, 32, 17)
+    o, s = _gdn_run(qkv, gl, be, s0, 16, 32)
+    (ok, bad, ratio), s_ok = _gdn_check(ora, qkv, gl, be, s0, 16, 32, o, s)
+    assert ok and s_ok, (bad, ratio, s_ok)
