@@ -202,13 +202,15 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
                 m = mn;
             }
             const float mu = m == -__builtin_inff() ? 0.0f : m;
-            // P^T x 16 in FP16 as B fragments: step jj of tile st takes
-            // values r = 8 jj .. 8 jj + 7 (keys 16 jj + 4 h + 0..3 and
-            // 16 jj + 8 + 4 h + 0..3)
-            u32x4 pf[2][2];
+            // per 32-key tile: P^T x 16 in FP16 as B fragments (step jj takes
+            // values r = 8 jj .. 8 jj + 7: keys 16 jj + 4 h + 0..3 and
+            // 16 jj + 8 + 4 h + 0..3), then O^T (dims x queries) += V^T P^T
+            // with the A slots on the same keys.  Tile 1's exponentials do
+            // not wait for tile 0's products, so the two can overlap.
             float sum = 0.0f;
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < 2; ++st) {
+                u32x4 pf[2];
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -217,15 +219,10 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
                         const float p0 = __builtin_amdgcn_exp2f(s[st][r] - mu);
                         const float p1 = __builtin_amdgcn_exp2f(s[st][r + 1] - mu);
                         sum += p0 + p1;
-                        pf[st][jj][e] = pack_f16(16.0f * p0, 16.0f * p1);
+                        pf[jj][e] = pack_f16(16.0f * p0, 16.0f * p1);
                     }
-            l += sum;
-
-            // O^T (dims x queries) += V^T P^T; the A slots follow the same keys
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
+                for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
                     for (int jj = 0; jj < 2; ++jj) {
                         const uint16_t* vp = vt + (dt * 32 + c) * VT_STRIDE + 32 * st + 16 * jj + 4 * h;
@@ -233,9 +230,12 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
                         const u32x2 hi = *(const u32x2*)(vp + 8);
                         const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
                         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
-                                                                       __builtin_bit_cast(f16x8, pf[st][jj]),
+                                                                       __builtin_bit_cast(f16x8, pf[jj]),
                                                                        o[dt], 0, 0, 0);
                     }
+            }
+            l += sum;
+
             // the other stage was last read before the previous barrier
             if (kb + 1 < kb1) store_tile(b ^ 1);
             __syncthreads();
