@@ -15,9 +15,9 @@
 // token are 8 FMAs per lane and a 4-step DPP reduction over the 16 lanes.
 // A workgroup holds 16 columns of one head (256 workgroups for 32 heads, one
 // per CU).  Tokens go through LDS 64 at a time in two stages: k and q of the
-// key head, v of the workgroup's columns, g and beta; the next chunk is
-// loaded into registers while the current one is processed, and outputs
-// leave through LDS as 16-byte rows.  The chunked form (products over 64
+// key head (converted to FP32 once there), v of the workgroup's columns, g
+// and beta; the next chunk is loaded into registers while the current one
+// is processed, and outputs leave through LDS as 16-byte rows.  The chunked form (products over 64
 // positions on the matrix cores) is not built.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,8 +58,9 @@ __device__ __forceinline__ float row16_sum(float x)
 
 __global__ void __launch_bounds__(256) lut6_gated_delta_kernel(GdnArgs a)
 {
-    // per stage: k then q [T][DK] halves, v [T][COLS] halves, g and beta [T]
-    __shared__ __attribute__((aligned(16))) uint16_t kq[2][T][2 * DK];
+    // per stage: k then q [T][DK] in FP32 (converted once while staging),
+    // v [T][COLS] halves, g and beta [T]
+    __shared__ __attribute__((aligned(16))) float kq[2][T][2 * DK];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][T][COLS];
     __shared__ float gb[2][2][T];
     __shared__ __attribute__((aligned(16))) uint16_t os[2][T][COLS];
@@ -103,7 +104,10 @@ __global__ void __launch_bounds__(256) lut6_gated_delta_kernel(GdnArgs a)
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int idx = tid + 256 * u, tt = idx >> 5, part = (idx >> 4) & 1, piece = idx & 15;
-            *(u32x4*)(&kq[b][tt][part * DK + piece * 8]) = kqr[u];
+            const f16x8 hv = __builtin_bit_cast(f16x8, kqr[u]);
+            float* const dst = &kq[b][tt][part * DK + piece * 8];
+            *(float4*)dst = float4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
+            *(float4*)(dst + 4) = float4{(float)hv[4], (float)hv[5], (float)hv[6], (float)hv[7]};
         }
         if (tid < 128) *(u32x4*)(&vs[b][tid >> 1][8 * (tid & 1)]) = vr;
         else gb[b][tid < 192 ? 0 : 1][(tid - 128) & 63] = gbr;
@@ -120,14 +124,12 @@ __global__ void __launch_bounds__(256) lut6_gated_delta_kernel(GdnArgs a)
         for (int tt = 0; tt < n; ++tt) {
             const float al = __expf(gb[b][0][tt]);
             const float be = gb[b][1][tt];
-            const f16x8 kh8 = *(const f16x8*)(&kq[b][tt][8 * r]);
-            const f16x8 qh8 = *(const f16x8*)(&kq[b][tt][DK + 8 * r]);
-            float kf[8], qf[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kf[e] = (float)kh8[e];
-                qf[e] = (float)qh8[e];
-            }
+            const float4 k0 = *(const float4*)(&kq[b][tt][8 * r]);
+            const float4 k1 = *(const float4*)(&kq[b][tt][8 * r + 4]);
+            const float4 q0 = *(const float4*)(&kq[b][tt][DK + 8 * r]);
+            const float4 q1 = *(const float4*)(&kq[b][tt][DK + 8 * r + 4]);
+            const float kf[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const float qf[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
             float kv = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) kv = __builtin_fmaf(S[e], kf[e], kv);
