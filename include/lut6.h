@@ -150,9 +150,10 @@ int lut6_dequant(const uint8_t* packed, const void* tables, void* w,
  * q: device int8 [N, K], row-major; scales: device FP16 [N, K/32]; x, y as
  * for lut6_linear.  All 16-byte aligned (LUT6_E_ALIGN).  Same shape rules as
  * lut6_linear (LUT6_E_SHAPE); y must not overlap x, q or scales
- * (LUT6_E_ALIAS).  Runs the two-pass path at every L: the weight is
- * expanded into the library's FP16 workspace, then the FP16 GEMM reads it
- * (split K when few tiles, as lut6_linear).                               */
+ * (LUT6_E_ALIAS).  Up to 192 tokens the codes stream straight into the
+ * products (no workspace); beyond, the weight is expanded into the
+ * library's FP16 workspace and the FP16 GEMM reads it (split K when few
+ * tiles, as lut6_linear).                                                 */
 int lut6_int8_linear(const void* x, const int8_t* q, const void* scales, void* y,
                      int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
                      hipStream_t stream);

@@ -1080,6 +1080,163 @@ lut6_int8_expand_kernel(const int8_t* __restrict__ q, const uint16_t* __restrict
     }
 }
 
+// int8 weight-only variant, few tokens (L <= 192): the weight streams once
+// from HBM straight into MFMA A fragments, with no expanded copy.  A
+// workgroup owns 32 output rows (for silu(gate) * up: 16 gate rows and the
+// matching 16 up rows) and 64 tokens over the whole K range; its four waves
+// take a quarter of the 64-k chunks each and meet in LDS.  In a chunk, lane
+// half h takes the 32 contiguous codes k0 + 32 h .. + 31 of its row, which
+// are exactly one scale block, and step j of the four MFMA steps uses codes
+// 8 j .. 8 j + 7 of them; the B fragments read the activations with the
+// same k order from a per-wave LDS tile filled by whole-row loads (a
+// fragment loaded straight from memory touches 32 rows per instruction).  A code becomes FP16 exactly (0x6400 | (q + 128) is
+// 1152 + q; subtracting 1152 is exact) and one FP16 multiply by the scale
+// rounds q * scale once, as the format defines.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 i8x4_to_f16x4(uint32_t w, f16x2_t sc)
+{
+    const uint32_t t = w ^ 0x80808080u;                     // q + 128 in each byte
+    const uint32_t lo = (t & 0xFFu) | ((t & 0xFF00u) << 8) | 0x64006400u;
+    const uint32_t hi = ((t >> 16) & 0xFFu) | ((t >> 8) & 0xFF0000u) | 0x64006400u;
+    const f16x2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const f16x2_t a = (__builtin_bit_cast(f16x2_t, lo) - bias) * sc;
+    const f16x2_t b = (__builtin_bit_cast(f16x2_t, hi) - bias) * sc;
+    return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
+template <int EPI, bool SCALED>
+__global__ void __launch_bounds__(256)
+lut6_int8_stream_kernel(const uint16_t* __restrict__ x, const int8_t* __restrict__ q,
+                        const uint16_t* __restrict__ qs, void* __restrict__ y, int L, int K, int N,
+                        float in_scale, float inv_scale)
+{
+    __shared__ __attribute__((aligned(16))) float red[3][2][16][64];
+    // per wave, two stages of a 64-token x 64-k activation tile (rows padded
+    // to 144 B so that a fragment's 32 rows start on distinct banks)
+    __shared__ __attribute__((aligned(16))) uint16_t xs[4][2][64][72];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = lane >> 5, rl = lane & 31;
+    const int tn = blockIdx.x, tm = blockIdx.y;
+    // the lane's weight row
+    int row;
+    if constexpr (EPI == 2) {
+        const int j = min(tn * 16 + (rl & 15), N / 2 - 1);
+        row = rl < 16 ? j : N / 2 + j;
+    } else {
+        row = min(tn * 32 + rl, N - 1);
+    }
+    const int8_t* const qrow = q + (size_t)row * K + 32 * h;
+    const uint16_t* const srow = qs + (size_t)row * (K / 32) + h;
+    // activation pieces of this lane: token (lane + 64 i) / 8, 16 bytes at
+    // k offset 8 ((lane + 64 i) % 8) of each chunk (whole 128-byte rows per
+    // instruction)
+    const uint16_t* xrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        xrow[i] = x + (size_t)min(tm * 64 + ((lane + 64 * i) >> 3), L - 1) * K + 8 * (lane & 7);
+    const int chunks = K / 64;
+    const int c0 = wave * chunks / 4, c1 = (wave + 1) * chunks / 4;
+    f32x16 acc[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[f][r] = 0.0f;
+    const _Float16 sh = (_Float16)in_scale;                        // a power of two: exact
+    const f16x8 s8 = {sh, sh, sh, sh, sh, sh, sh, sh};
+    // two register sets: chunk kc + 1's loads are in flight while chunk kc
+    // is converted and multiplied
+    struct Chunk {
+        u32x4 w[2];
+        u32x4 xr[8];
+        uint16_t sc;
+    };
+    auto load = [&](Chunk& c, int kc) {
+        c.w[0] = *(const u32x4*)(qrow + 64 * kc);
+        c.w[1] = *(const u32x4*)(qrow + 64 * kc + 16);
+        c.sc = srow[2 * kc];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c.xr[i] = *(const u32x4*)(xrow[i] + 64 * kc);
+    };
+    // the wave's own LDS tile: LDS instructions of one wave complete in
+    // order, so no barrier is needed between its writes and reads
+    auto stage = [&](const Chunk& c, int b) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *(u32x4*)(&xs[wave][b][(lane + 64 * i) >> 3][8 * (lane & 7)]) = c.xr[i];
+    };
+    auto compute = [&](const Chunk& c, int b) {
+        const _Float16 sc = __builtin_bit_cast(_Float16, c.sc);
+        const f16x2_t sc2 = {sc, sc};
+        const uint32_t wd[8] = {c.w[0][0], c.w[0][1], c.w[0][2], c.w[0][3],
+                                c.w[1][0], c.w[1][1], c.w[1][2], c.w[1][3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x2 a0 = i8x4_to_f16x4(wd[2 * j], sc2), a1 = i8x4_to_f16x4(wd[2 * j + 1], sc2);
+            const u32x4 av = {a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                f16x8 bv = *(const f16x8*)(&xs[wave][b][32 * f + rl][32 * h + 8 * j]);
+                if constexpr (SCALED) bv = bv * s8;                  // fp16(x * s), exact or inf
+                acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av), bv, acc[f],
+                                                                0, 0, 0);
+            }
+        }
+    };
+    Chunk ca, cb;
+    if (c0 < c1) load(ca, c0);
+    for (int kc = c0; kc < c1; kc += 2) {
+        if (kc + 1 < c1) load(cb, kc + 1);
+        stage(ca, 0);
+        compute(ca, 0);
+        if (kc + 2 < c1) load(ca, kc + 2);
+        if (kc + 1 < c1) {
+            stage(cb, 1);
+            compute(cb, 1);
+        }
+    }
+    // waves 1..3 hand their sums to wave 0, which adds them in wave order
+    if (wave > 0) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[wave - 1][f][r][lane] = acc[f][r];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[f][r] += red[w][f][r][lane];
+    // accumulator (f, r) of this lane: row 8 (r / 4) + 4 h + r % 4 of the
+    // tile, token tm * 64 + 32 f + rl
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int tok = tm * 64 + 32 * f + rl;
+        if (tok >= L) continue;
+        if constexpr (EPI == 2) {
+            const int n_out = N / 2;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int ch = tn * 16 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (ch < n_out)
+                    ((_Float16*)y)[(size_t)tok * n_out + ch] =
+                        (_Float16)(silu_f32(acc[f][r] * inv_scale) * (acc[f][r + 8] * inv_scale));
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ch = tn * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (ch >= N) continue;
+                const float v = acc[f][r] * inv_scale;
+                if constexpr (EPI == 0) ((float*)y)[(size_t)tok * N + ch] = v;
+                else ((_Float16*)y)[(size_t)tok * N + ch] = (_Float16)v;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel for few tokens (L <= 192).  Every weight serves at
 // most 192 tokens here, so streaming the packed weight once from HBM, and
@@ -1711,9 +1868,11 @@ void launch_tiles(const GemmArgs& a, bool two_pass, int epilogue, bool scaled, b
 // Which kernels lut6_linear runs for a (valid) shape: the weight-streaming
 // kernel for few tokens, the fused tile kernel, or weight expansion plus the
 // FP16 GEMM for many tokens (when the expanded weight fits 31-bit offsets).
+constexpr int STREAM_MAX_L = 192;   // the weight-streaming kernels up to this many tokens
+
 int choose_path(int64_t L, int64_t K, int64_t N, int epilogue)
 {
-    if (L <= 192) return LUT6_PATH_STREAM;
+    if (L <= STREAM_MAX_L) return LUT6_PATH_STREAM;
     if (L < (K >= DEEP_K ? EXPAND_MIN_L_DEEP_K : EXPAND_MIN_L)) return LUT6_PATH_FUSED;
     const int64_t n_half = epilogue == 2 ? N / 2 : N;
     const int64_t bn_cov = epilogue == 2 ? 128 : 256;
@@ -1878,6 +2037,27 @@ extern "C" int lut6_int8_linear(const void* x, const int8_t* q, const void* scal
     if (overlaps(y, y_bytes, x, x_bytes) || overlaps(y, y_bytes, q, q_bytes) || overlaps(y, y_bytes, scales, s_bytes))
         return LUT6_E_ALIAS;
 
+    if (L <= STREAM_MAX_L) {
+        // few tokens: stream the codes straight into the products
+        const int n_tiles = epilogue == 2 ? (int)(N / 32) : (int)((N + 31) / 32);
+        const dim3 grid((unsigned)n_tiles, (unsigned)((L + 63) / 64));
+        const bool sc = in_scale != 1.0f;
+        const float inv = 1.0f / in_scale;
+#define I8S(E, S) hipLaunchKernelGGL((lut6_int8_stream_kernel<E, S>), grid, dim3(256), 0, stream, \
+                                     (const uint16_t*)x, q, (const uint16_t*)scales, y, (int)L, (int)K, \
+                                     (int)N, in_scale, inv)
+        switch (epilogue * 2 + (sc ? 1 : 0)) {
+        case 0: I8S(0, false); break;
+        case 1: I8S(0, true); break;
+        case 2: I8S(1, false); break;
+        case 3: I8S(1, true); break;
+        case 4: I8S(2, false); break;
+        default: I8S(2, true); break;
+        }
+#undef I8S
+        return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+    }
+
     GemmArgs a{};
     a.x = (const uint16_t*)x;
     a.y = y;
@@ -1886,7 +2066,7 @@ extern "C" int lut6_int8_linear(const void* x, const int8_t* q, const void* scal
     a.N = (int)N;
     a.scale = (_Float16)in_scale;
     a.inv_scale = 1.0f / in_scale;
-    // the expanded path at every L: weight expansion, then the FP16 GEMM
+    // many tokens: weight expansion, then the FP16 GEMM
     // (split K when the 256 x 256 tiles cannot fill most CUs)
     const int chunks = (int)(K / BK);
     const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
