@@ -234,8 +234,10 @@ int lut6_quantize(const void* w, uint8_t* packed, void* tables, int64_t N, int64
                   hipStream_t stream);
 
 /* Free the library's per-device workspaces (after synchronising the
- * devices that hold one).  Optional; safe to call at any time when no
- * lut6_linear or lut6_quantize call is in flight.                         */
+ * devices that hold one): split-K partial sums and the expanded weight
+ * (lut6_linear, lut6_int8_linear), the table-fitting scratch
+ * (lut6_quantize) and the key-split partials (lut6_attention).  Optional;
+ * safe to call at any time when no call of the library is in flight.     */
 int lut6_release(void);
 
 /* Name of a status code ("LUT6_OK", "LUT6_E_SHAPE", ...); never NULL.     */
