@@ -16,8 +16,8 @@ XCDs, divided by 8 and by the dispatch's duration.
 
 Writes gemm_hbm_traffic.json (read by bench.py from profiles/, which
 reports the bytes only while the kernel source hash still matches) and
-gemm_hbm_traffic_prefill_sweep_l16384.md into gpurun_out/hbm_traffic/ and,
-with --install, into profiles/.  ``--from-csv`` skips the runs and re-reads
+gemm_hbm_traffic_prefill_sweep_l16384.md into the raw-output folder (OUT)
+and, with --install, into profiles/.  ``--from-csv`` skips the runs and re-reads
 the counter files of an earlier run.  This process never touches the GPU
 itself; the profiled runs are child processes.
 """
