@@ -492,7 +492,8 @@ def _att_inputs(L, Lk, Hq, Hkv, seed, scale=1.0):
 
 
 ATT_SHAPES = [(1, 1, 16, 4), (5, 5, 2, 1), (37, 37, 4, 4), (128, 128, 16, 4), (130, 200, 4, 2),
-              (300, 1000, 16, 4), (64, 4096, 16, 4), (1024, 1024, 16, 4), (129, 129, 1, 1)]
+              (300, 1000, 16, 4), (64, 4096, 16, 4), (1024, 1024, 16, 4), (129, 129, 1, 1),
+              (1, 4096, 16, 4), (1, 65, 2, 1)]
 
 
 @pytest.mark.parametrize("L,Lk,Hq,Hkv", ATT_SHAPES)
@@ -658,3 +659,21 @@ def test_gated_delta_layer_full_size(ora):
     o, s = _gdn_run(qkv, gl, be, s0, 16, 32)
     (ok, bad, ratio), s_ok = _gdn_check(ora, qkv, gl, be, s0, 16, 32, o, s)
     assert ok and s_ok, (bad, ratio, s_ok)
+
+
+@pytest.mark.parametrize("L", [32, 512])
+def test_int8_overflow_gives_inf(ora, L):
+    # x * 16 = 65536 overflows FP16 in one column: with every weight
+    # positive, every output is +inf on both int8 paths, as in the oracle
+    _say("int8 overflow", L)
+    g = np.random.default_rng(3)
+    x = (g.random((L, 128)) * 0.5).astype(np.float16)
+    x[:, 3] = np.float16(4096.0)
+    q = g.integers(1, 128, size=(64, 128)).astype(np.int8)
+    sc = np.full((64, 4), 0.01, np.float16)
+    for epi in (F32, F16):
+        y = _gpu_int8(x, q, sc, epi, 16.0)
+        yv = y if epi == F32 else y.view(np.float16)
+        _, ref = ora.int8_linear(x, q, sc, epilogue=epi, in_scale=16.0)
+        rv = ref if epi == F32 else ref.view(np.float16)
+        assert np.all(np.isposinf(yv)) and np.all(np.isposinf(rv))
