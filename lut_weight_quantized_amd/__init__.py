@@ -148,9 +148,20 @@ def _stream_handle(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _require(t, dtype, name):
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+
+
+def _is_device(t) -> bool:
     import torch
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    return isinstance(t, torch.Tensor) and t.is_cuda
+
+
+def _require(t, dtype, name):
+    if not _is_device(t):
         raise TypeError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -158,14 +169,8 @@ def _require(t, dtype, name):
         raise TypeError(f"{name} must be contiguous")
 
 
-def linear(x, packed, tables, *, epilogue: int = EPI_STORE_F16, in_scale: float = 1.0,
-           out=None, stream=None):
-    """y = epilogue((fp16(x * in_scale) @ W^T) / in_scale) on the GPU.
-
-    x: float16 [L, K]; packed: uint8 [N, 3K/4]; tables: float16 [N/16, 64];
-    returns float32 [L, N] (EPI_STORE_F32), float16 [L, N] (EPI_STORE_F16) or
-    float16 [L, N/2] (EPI_SILU_MUL_F16: rows [0, N/2) of W gate, the rest up).
-    """
+def _linear_operands(x, packed, tables, epilogue, out):
+    """Check linear's operands; returns (L, K, N, out), allocating out if None."""
     import torch
     _require(x, torch.float16, "x")
     _require(packed, torch.uint8, "packed")
@@ -176,6 +181,7 @@ def linear(x, packed, tables, *, epilogue: int = EPI_STORE_F16, in_scale: float 
     N = packed.shape[0]
     if packed.shape[1] * 4 != 3 * K or tables.numel() * 16 != N * 64:
         raise TypeError("packed / tables do not match x's K and packed's N")
+    _same_device(x, packed, tables)
     n_out = N // 2 if epilogue == EPI_SILU_MUL_F16 else N
     dt = torch.float32 if epilogue == EPI_STORE_F32 else torch.float16
     if out is None:
@@ -184,6 +190,19 @@ def linear(x, packed, tables, *, epilogue: int = EPI_STORE_F16, in_scale: float 
         _require(out, dt, "out")
         if tuple(out.shape) != (L, n_out):
             raise TypeError(f"out must be [{L}, {n_out}]")
+        _same_device(x, out)
+    return L, K, N, out
+
+
+def linear(x, packed, tables, *, epilogue: int = EPI_STORE_F16, in_scale: float = 1.0,
+           out=None, stream=None):
+    """y = epilogue((fp16(x * in_scale) @ W^T) / in_scale) on the GPU.
+
+    x: float16 [L, K]; packed: uint8 [N, 3K/4]; tables: float16 [N/16, 64];
+    returns float32 [L, N] (EPI_STORE_F32), float16 [L, N] (EPI_STORE_F16) or
+    float16 [L, N/2] (EPI_SILU_MUL_F16: rows [0, N/2) of W gate, the rest up).
+    """
+    L, K, N, out = _linear_operands(x, packed, tables, epilogue, out)
     st = load_library().lut6_linear(x.data_ptr(), packed.data_ptr(), tables.data_ptr(),
                                     out.data_ptr(), L, K, N, float(in_scale), int(epilogue),
                                     _stream_handle(stream))
@@ -205,11 +224,19 @@ def dequant(packed, tables, K: int, *, out=None, stream=None):
     import torch
     _require(packed, torch.uint8, "packed")
     _require(tables, torch.float16, "tables")
+    if packed.dim() != 2 or packed.shape[1] * 4 != 3 * K:
+        raise ValueError(f"packed must be [N, {3 * K // 4}] for K = {K}")
     N = packed.shape[0]
+    if tables.numel() * 16 != N * 64:
+        raise ValueError(f"tables must hold {N // 16} x 64 entries for N = {N}")
+    _same_device(packed, tables)
     if out is None:
         out = torch.empty((N, K), dtype=torch.float16, device=packed.device)
     else:
         _require(out, torch.float16, "out")
+        if tuple(out.shape) != (N, K):
+            raise ValueError(f"out must be [{N}, {K}]")
+        _same_device(packed, out)
     st = load_library().lut6_dequant(packed.data_ptr(), tables.data_ptr(), out.data_ptr(),
                                      N, K, _stream_handle(stream))
     _check(st, "lut6_dequant")
@@ -228,42 +255,67 @@ def int8_linear(x, q, scales, *, epilogue: int = EPI_STORE_F16, in_scale: float 
         raise ValueError("x and q must be 2-D")
     L, K = x.shape
     N = q.shape[0]
+    if q.shape[1] != K:
+        raise ValueError(f"q must be [N, {K}] to match x's K")
+    if K % 32 or tuple(scales.shape) != (N, K // 32):
+        raise ValueError(f"scales must be [{N}, K/32] with K % 32 == 0 (K = {K})")
+    _same_device(x, q, scales)
     n_out = N // 2 if epilogue == EPI_SILU_MUL_F16 else N
     dtype = torch.float32 if epilogue == EPI_STORE_F32 else torch.float16
     if out is None:
         out = torch.empty((L, n_out), dtype=dtype, device=x.device)
     else:
         _require(out, dtype, "out")
+        if tuple(out.shape) != (L, n_out):
+            raise ValueError(f"out must be [{L}, {n_out}]")
+        _same_device(x, out)
     st = load_library().lut6_int8_linear(x.data_ptr(), q.data_ptr(), scales.data_ptr(), out.data_ptr(),
                                          L, K, N, float(in_scale), int(epilogue), _stream_handle(stream))
     _check(st, "lut6_int8_linear")
     return out
 
 
+def _rows(t, name, dtype, rows, min_cols):
+    """A 2-D device tensor of `rows` rows, unit column stride (row stride free)
+    and at least `min_cols` columns: what the kernels read from each row."""
+    if not _is_device(t):
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype or t.dim() != 2 or t.stride(1) != 1:
+        raise TypeError(f"{name} must be 2-D {dtype} with unit column stride")
+    if t.shape[0] != rows:
+        raise ValueError(f"{name} must have {rows} rows, got {t.shape[0]}")
+    if t.shape[1] < min_cols:
+        raise ValueError(f"{name} must have at least {min_cols} columns, got {t.shape[1]}")
+    if t.shape[0] > 1 and t.stride(0) < min_cols:
+        raise ValueError(f"{name}'s rows overlap (row stride {t.stride(0)} < {min_cols})")
+
+
+def _ld(t):
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
 def attention(q, k, v, *, n_heads: int, n_kv_heads: int, head_dim: int = 256, out=None,
               stream=None):
     """Causal grouped-query attention of the last L of Lk positions.
 
-    q: float16 [L, ldq] (2-D, rows may be strided views such as columns of
-    the Q|K|V projection output), k, v: float16 [Lk, ld]; returns o float16
-    [L, n_heads * head_dim]."""
+    q: float16 [L, >= n_heads*head_dim] (2-D, rows may be strided views such
+    as columns of the Q|K|V projection output), k, v: float16 [Lk, >=
+    n_kv_heads*head_dim]; returns o float16 [L, n_heads * head_dim]."""
     import torch
-    for t, name in ((q, "q"), (k, "k"), (v, "v")):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise TypeError(f"{name} must be a device tensor")
-        if t.dtype != torch.float16 or t.dim() != 2 or t.stride(1) != 1:
-            raise TypeError(f"{name} must be 2-D float16 with unit column stride")
+    if n_heads <= 0 or n_kv_heads <= 0 or head_dim <= 0:
+        raise ValueError("head counts and head_dim must be positive")
     L, Lk = q.shape[0], k.shape[0]
-    if v.shape[0] != Lk:
-        raise ValueError("k and v must have the same number of rows")
+    _rows(q, "q", torch.float16, L, n_heads * head_dim)
+    _rows(k, "k", torch.float16, Lk, n_kv_heads * head_dim)
+    _rows(v, "v", torch.float16, Lk, n_kv_heads * head_dim)
+    _same_device(q, k, v)
     if out is None:
         out = torch.empty((L, n_heads * head_dim), dtype=torch.float16, device=q.device)
-    elif out.dtype != torch.float16 or out.dim() != 2 or out.stride(1) != 1:
-        raise TypeError("out must be 2-D float16 with unit column stride")
-    def ld(t):
-        return t.stride(0) if t.shape[0] > 1 else t.shape[1]
-    st = load_library().lut6_attention(q.data_ptr(), ld(q), k.data_ptr(), ld(k), v.data_ptr(), ld(v),
-                                       out.data_ptr(), ld(out), L, Lk, n_heads, n_kv_heads, head_dim,
+    else:
+        _rows(out, "out", torch.float16, L, n_heads * head_dim)
+        _same_device(q, out)
+    st = load_library().lut6_attention(q.data_ptr(), _ld(q), k.data_ptr(), _ld(k), v.data_ptr(), _ld(v),
+                                       out.data_ptr(), _ld(out), L, Lk, n_heads, n_kv_heads, head_dim,
                                        _stream_handle(stream))
     _check(st, "lut6_attention")
     return out
@@ -273,25 +325,31 @@ def gated_delta(q, k, v, g, beta, state, *, n_k_heads: int, n_v_heads: int, out=
                 stream=None):
     """Gated delta rule over the L rows (tokens) of q, k, v; updates `state`
     (float32 [n_v_heads, 128, 128], in place) and returns o float16
-    [L, n_v_heads * 128].  q, k, v: 2-D float16 with unit column stride (row
-    strides allowed); g, beta: float32 [L, >= n_v_heads]."""
+    [L, n_v_heads * 128].  q, k: float16 [L, >= n_k_heads*128]; v float16
+    [L, >= n_v_heads*128] (row strides allowed, unit column stride); g, beta:
+    float32 [L, >= n_v_heads] with the same row stride."""
     import torch
-    for t, name, dt in ((q, "q", torch.float16), (k, "k", torch.float16), (v, "v", torch.float16),
-                        (g, "g", torch.float32), (beta, "beta", torch.float32)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise TypeError(f"{name} must be a device tensor")
-        if t.dtype != dt or t.dim() != 2 or t.stride(1) != 1:
-            raise TypeError(f"{name} must be 2-D {dt} with unit column stride")
-    _require(state, torch.float32, "state")
-    if g.stride(0) != beta.stride(0) and g.shape[0] > 1:
-        raise ValueError("g and beta must have the same row stride")
+    if n_k_heads <= 0 or n_v_heads <= 0:
+        raise ValueError("head counts must be positive")
     L = q.shape[0]
+    _rows(q, "q", torch.float16, L, n_k_heads * 128)
+    _rows(k, "k", torch.float16, L, n_k_heads * 128)
+    _rows(v, "v", torch.float16, L, n_v_heads * 128)
+    _rows(g, "g", torch.float32, L, n_v_heads)
+    _rows(beta, "beta", torch.float32, L, n_v_heads)
+    if L > 1 and g.stride(0) != beta.stride(0):
+        raise ValueError("g and beta must have the same row stride")
+    _require(state, torch.float32, "state")
+    if state.numel() != n_v_heads * 128 * 128:
+        raise ValueError(f"state must hold [{n_v_heads}, 128, 128] floats")
+    _same_device(q, k, v, g, beta, state)
     if out is None:
         out = torch.empty((L, n_v_heads * 128), dtype=torch.float16, device=q.device)
-    def ld(t):
-        return t.stride(0) if t.shape[0] > 1 else t.shape[1]
-    st = load_library().lut6_gated_delta(q.data_ptr(), ld(q), k.data_ptr(), ld(k), v.data_ptr(), ld(v),
-                                         g.data_ptr(), beta.data_ptr(), ld(g), out.data_ptr(), ld(out),
+    else:
+        _rows(out, "out", torch.float16, L, n_v_heads * 128)
+        _same_device(q, out)
+    st = load_library().lut6_gated_delta(q.data_ptr(), _ld(q), k.data_ptr(), _ld(k), v.data_ptr(), _ld(v),
+                                         g.data_ptr(), beta.data_ptr(), _ld(g), out.data_ptr(), _ld(out),
                                          state.data_ptr(), L, n_k_heads, n_v_heads, 128, 128,
                                          _stream_handle(stream))
     _check(st, "lut6_gated_delta")
@@ -307,14 +365,21 @@ def quantize(w, *, packed=None, tables=None, stream=None):
     if w.dim() != 2:
         raise ValueError("w must be 2-D [N, K]")
     N, K = w.shape
+    if K % 4 or N % 16:
+        raise ValueError(f"w must be [N, K] with N % 16 == 0 and K % 4 == 0, got [{N}, {K}]")
     if packed is None:
         packed = torch.empty((N, K // 4 * 3), dtype=torch.uint8, device=w.device)
     else:
         _require(packed, torch.uint8, "packed")
+        if tuple(packed.shape) != (N, K // 4 * 3):
+            raise ValueError(f"packed must be [{N}, {K // 4 * 3}]")
     if tables is None:
         tables = torch.empty((N // 16, 64), dtype=torch.float16, device=w.device)
     else:
         _require(tables, torch.float16, "tables")
+        if tuple(tables.shape) != (N // 16, 64):
+            raise ValueError(f"tables must be [{N // 16}, 64]")
+    _same_device(w, packed, tables)
     st = load_library().lut6_quantize(w.data_ptr(), packed.data_ptr(), tables.data_ptr(),
                                       N, K, _stream_handle(stream))
     _check(st, "lut6_quantize")

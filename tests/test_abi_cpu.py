@@ -222,3 +222,119 @@ def _gated_delta(q=X, ldq=8192, k=X + 4096, ldk=8192, v=X + 8192, ldv=8192, g=G,
 def test_gated_delta_validation(kwargs, status):
     # refusals are decided on the host, before any device call
     assert _gated_delta(**kwargs) == status
+
+
+# ---------------------------------------------------------------------------
+# the Python binding's own checks (meta tensors stand in for device memory;
+# every mismatch must raise before the library is called)
+# ---------------------------------------------------------------------------
+
+@pytest.fixture
+def meta_device(monkeypatch):
+    import torch
+    monkeypatch.setattr(lq, "_is_device", lambda t: isinstance(t, torch.Tensor))
+    monkeypatch.setattr(lq, "_stream_handle", lambda stream: None)
+
+    def make(shape, dtype):
+        return torch.empty(shape, dtype=dtype, device="meta")
+    return make
+
+
+def test_binding_linear_shapes(meta_device):
+    import torch
+    f16, u8 = torch.float16, torch.uint8
+    x, p, t = meta_device((8, 64), f16), meta_device((32, 48), u8), meta_device((2, 64), f16)
+    with pytest.raises(TypeError):
+        lq.linear(x, meta_device((32, 40), u8), t)
+    with pytest.raises(TypeError):
+        lq.linear(x, p, meta_device((1, 64), f16))
+    with pytest.raises(TypeError):
+        lq.linear(x, p, t, out=meta_device((8, 16), f16))
+    # well-formed operands reach the library, which refuses the null
+    # pointers of meta tensors without any device work
+    with pytest.raises(lq.Lut6Error) as e:
+        lq.linear(x, p, t)
+    assert e.value.status == "LUT6_E_NULL"
+
+
+def test_binding_dequant_shapes(meta_device):
+    import torch
+    p, t = meta_device((32, 48), torch.uint8), meta_device((2, 64), torch.float16)
+    with pytest.raises(ValueError):
+        lq.dequant(p, t, 128)
+    with pytest.raises(ValueError):
+        lq.dequant(p, meta_device((3, 64), torch.float16), 64)
+    with pytest.raises(ValueError):
+        lq.dequant(p, t, 64, out=meta_device((32, 32), torch.float16))
+    with pytest.raises(lq.Lut6Error):
+        lq.dequant(p, t, 64)
+
+
+def test_binding_int8_shapes(meta_device):
+    import torch
+    f16, i8 = torch.float16, torch.int8
+    x, q, s = meta_device((8, 64), f16), meta_device((32, 64), i8), meta_device((32, 2), f16)
+    with pytest.raises(ValueError):
+        lq.int8_linear(x, meta_device((32, 128), i8), s)
+    with pytest.raises(ValueError):
+        lq.int8_linear(x, q, meta_device((32, 1), f16))
+    with pytest.raises(ValueError):
+        lq.int8_linear(x, q, meta_device((16, 2), f16))
+    with pytest.raises(ValueError):
+        lq.int8_linear(x, q, s, out=meta_device((8, 16), f16))
+    with pytest.raises(lq.Lut6Error):
+        lq.int8_linear(x, q, s)
+
+
+def test_binding_attention_shapes(meta_device):
+    import torch
+    f16 = torch.float16
+    q, k, v = meta_device((4, 1024), f16), meta_device((8, 256), f16), meta_device((8, 256), f16)
+    with pytest.raises(ValueError):       # q narrower than its heads
+        lq.attention(meta_device((4, 768), f16), k, v, n_heads=4, n_kv_heads=1)
+    with pytest.raises(ValueError):       # v rows differ from k rows
+        lq.attention(q, k, meta_device((7, 256), f16), n_heads=4, n_kv_heads=1)
+    with pytest.raises(ValueError):       # k narrower than its heads
+        lq.attention(q, k, v, n_heads=4, n_kv_heads=2)
+    with pytest.raises(ValueError):       # out rows
+        lq.attention(q, k, v, n_heads=4, n_kv_heads=1, out=meta_device((3, 1024), f16))
+    with pytest.raises(TypeError):        # out dtype
+        lq.attention(q, k, v, n_heads=4, n_kv_heads=1, out=meta_device((4, 1024), torch.float32))
+    with pytest.raises(lq.Lut6Error):
+        lq.attention(q, k, v, n_heads=4, n_kv_heads=1)
+
+
+def test_binding_gated_delta_shapes(meta_device):
+    import torch
+    f16, f32 = torch.float16, torch.float32
+    L = 5
+    q, k, v = meta_device((L, 256), f16), meta_device((L, 256), f16), meta_device((L, 512), f16)
+    g, b, st = meta_device((L, 4), f32), meta_device((L, 4), f32), meta_device((4, 128, 128), f32)
+    kw = dict(n_k_heads=2, n_v_heads=4)
+    with pytest.raises(ValueError):       # v narrower than its heads
+        lq.gated_delta(q, k, meta_device((L, 384), f16), g, b, st, **kw)
+    with pytest.raises(ValueError):       # g has too few rows
+        lq.gated_delta(q, k, v, meta_device((L - 1, 4), f32), b, st, **kw)
+    with pytest.raises(ValueError):       # beta narrower than the value heads
+        lq.gated_delta(q, k, v, g, meta_device((L, 3), f32), st, **kw)
+    with pytest.raises(ValueError):       # state too small
+        lq.gated_delta(q, k, v, g, b, meta_device((3, 128, 128), f32), **kw)
+    with pytest.raises(TypeError):        # out dtype
+        lq.gated_delta(q, k, v, g, b, st, out=meta_device((L, 512), f32), **kw)
+    with pytest.raises(ValueError):       # out rows
+        lq.gated_delta(q, k, v, g, b, st, out=meta_device((L + 1, 512), f16), **kw)
+    with pytest.raises(lq.Lut6Error):
+        lq.gated_delta(q, k, v, g, b, st, **kw)
+
+
+def test_binding_quantize_shapes(meta_device):
+    import torch
+    w = meta_device((32, 64), torch.float16)
+    with pytest.raises(ValueError):
+        lq.quantize(meta_device((24, 64), torch.float16))
+    with pytest.raises(ValueError):
+        lq.quantize(w, packed=meta_device((32, 64), torch.uint8))
+    with pytest.raises(ValueError):
+        lq.quantize(w, tables=meta_device((1, 64), torch.float16))
+    with pytest.raises(lq.Lut6Error):
+        lq.quantize(w)
