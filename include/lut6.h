@@ -59,7 +59,9 @@ typedef enum {
     LUT6_E_EPILOGUE = 5,     /* unknown epilogue code                            */
     LUT6_E_INDEX_RANGE = 6,  /* lut6_pack: an index is above 63                  */
     LUT6_E_DEVICE = 7,       /* a HIP call or kernel launch failed               */
-    LUT6_E_ALIAS = 8         /* the output overlaps an input                     */
+    LUT6_E_ALIAS = 8,        /* the output overlaps an input                     */
+    LUT6_E_SCRATCH = 9       /* lut6_linear_noalloc: the shape needs more scratch
+                              * than LUT6_NOALLOC_SCRATCH_BYTES                  */
 } lut6_status;
 
 typedef enum {
@@ -110,6 +112,31 @@ int lut6_unpack(const uint8_t* packed, uint8_t* idx, int64_t N, int64_t K);
 int lut6_linear(const void* x, const uint8_t* packed, const void* tables, void* y,
                 int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
                 hipStream_t stream);
+
+/* Size of the static device array behind lut6_linear_noalloc: 256 MiB per
+ * GPU, held from the library's load until the process ends.               */
+#define LUT6_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* lut6_linear for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, rules, statuses, kernels and results as lut6_linear (the
+ * same path and K split for every shape, so the output is bit-identical);
+ * it never calls hipMalloc or hipFree and never synchronises.  The expanded
+ * weight (LUT6_PATH_EXPANDED) and the split-K partial sums live in one
+ * static device array of LUT6_NOALLOC_SCRATCH_BYTES per GPU instead of the
+ * per-stream workspaces: expanded weight at offset 0, partial sums after it
+ * on a 256-byte boundary.  A shape that needs more than that
+ * (tiles_n * 8 * (K/64 + 1) * 4 KB for the expanded weight, rounded up to
+ * 256 bytes, plus splits * L * N * 4 bytes of partial sums) is refused with
+ * LUT6_E_SCRATCH before anything is launched.  Every shape of the 9B
+ * model's projections fits, at any L.  Nothing in the array needs to start
+ * at zero: each call writes what it reads.  All calls on one GPU share
+ * its array, on any stream: two calls that overlap in time on one GPU race
+ * and give unspecified results, so the caller orders them (one stream, or
+ * events).                                                                */
+int lut6_linear_noalloc(const void* x, const uint8_t* packed, const void* tables, void* y,
+                        int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
+                        hipStream_t stream);
 
 /* Kernel paths of lut6_linear (what lut6_linear_path returns).            */
 typedef enum {

@@ -27,14 +27,18 @@ EPI_SILU_MUL_F16 = 2
 
 STATUS = {0: "LUT6_OK", 1: "LUT6_E_NULL", 2: "LUT6_E_SHAPE", 3: "LUT6_E_ALIGN",
           4: "LUT6_E_SCALE", 5: "LUT6_E_EPILOGUE", 6: "LUT6_E_INDEX_RANGE",
-          7: "LUT6_E_DEVICE", 8: "LUT6_E_ALIAS"}
+          7: "LUT6_E_DEVICE", 8: "LUT6_E_ALIAS", 9: "LUT6_E_SCRATCH"}
+
+# bytes of the static per-GPU array behind lut6_linear_noalloc
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 EXPORTS = ("lut6_packed_bytes", "lut6_table_bytes", "lut6_pack", "lut6_unpack",
            "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_int8_linear", "lut6_attention",
            "lut6_gated_delta",
            "lut6_quantize",
            "lut6_release",
-           "lut6_status_string")
+           "lut6_status_string",
+           "lut6_linear_noalloc")
 
 # kernel paths of lut6_linear (lut6_linear_path)
 PATH_STREAM = 0
@@ -74,6 +78,8 @@ def load_library() -> ctypes.CDLL:
     lib.lut6_unpack.restype = ctypes.c_int
     lib.lut6_linear.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_float, ctypes.c_int, P]
     lib.lut6_linear.restype = ctypes.c_int
+    lib.lut6_linear_noalloc.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_float, ctypes.c_int, P]
+    lib.lut6_linear_noalloc.restype = ctypes.c_int
     lib.lut6_linear_path.argtypes = [I64, I64, I64, ctypes.c_int]
     lib.lut6_linear_path.restype = ctypes.c_int
     lib.lut6_dequant.argtypes = [P, P, P, I64, I64, P]
@@ -207,6 +213,21 @@ def linear(x, packed, tables, *, epilogue: int = EPI_STORE_F16, in_scale: float 
                                     out.data_ptr(), L, K, N, float(in_scale), int(epilogue),
                                     _stream_handle(stream))
     _check(st, "lut6_linear")
+    return out
+
+
+def linear_noalloc(x, packed, tables, out, *, epilogue: int = EPI_STORE_F16,
+                   in_scale: float = 1.0, stream=None):
+    """``linear`` without any device allocation: ``out`` must be given, and
+    the library's scratch is its static per-GPU array (NOALLOC_SCRATCH_BYTES).
+    Calls on one GPU must not overlap in time."""
+    if out is None:
+        raise TypeError("linear_noalloc needs a caller-allocated out")
+    L, K, N, out = _linear_operands(x, packed, tables, epilogue, out)
+    st = load_library().lut6_linear_noalloc(x.data_ptr(), packed.data_ptr(), tables.data_ptr(),
+                                            out.data_ptr(), L, K, N, float(in_scale),
+                                            int(epilogue), _stream_handle(stream))
+    _check(st, "lut6_linear_noalloc")
     return out
 
 

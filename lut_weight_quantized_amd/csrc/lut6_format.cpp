@@ -70,6 +70,7 @@ extern "C" const char* lut6_status_string(int status)
     case LUT6_E_INDEX_RANGE: return "LUT6_E_INDEX_RANGE";
     case LUT6_E_DEVICE: return "LUT6_E_DEVICE";
     case LUT6_E_ALIAS: return "LUT6_E_ALIAS";
+    case LUT6_E_SCRATCH: return "LUT6_E_SCRATCH";
     default: return "LUT6_E_UNKNOWN";
     }
 }

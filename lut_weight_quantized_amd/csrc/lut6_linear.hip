@@ -1894,9 +1894,22 @@ extern "C" int lut6_linear_path(int64_t L, int64_t K, int64_t N, int epilogue)
     return choose_path(L, K, N, epilogue);
 }
 
-extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tables, void* y,
-                           int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
-                           hipStream_t stream)
+namespace {
+
+// Everything lut6_linear decides for one valid shape before it launches.
+struct LinearPlan {
+    int path;                 // lut6_path
+    int splits;               // K slices (1: none)
+    int tiles, tiles_m, tiles_n;
+    int k_chunks_per_split;
+    bool f16;                 // stream path: every wave holds exactly 16 chunks
+    size_t w16_bytes;         // expanded weight (0 unless LUT6_PATH_EXPANDED)
+    size_t partial_bytes;     // split-K partial sums (0 unless splits > 1)
+};
+
+// Host checks of lut6_linear, in the order the header lists them.
+int check_linear(const void* x, const uint8_t* packed, const void* tables, void* y, int64_t L,
+                 int64_t K, int64_t N, float in_scale, int epilogue)
 {
     if (!x || !packed || !tables || !y) return LUT6_E_NULL;
     if (L < 0 || K <= 0 || N <= 0 || K % 64 || N % 16) return LUT6_E_SHAPE;
@@ -1917,7 +1930,62 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
     if (overlaps(y, y_bytes, x, x_bytes) || overlaps(y, y_bytes, packed, p_bytes) ||
         overlaps(y, y_bytes, tables, t_bytes))
         return LUT6_E_ALIAS;
+    return LUT6_OK;
+}
 
+// Path, tiles and K split for a shape check_linear accepted with L > 0.
+int plan_linear(int64_t L, int64_t K, int64_t N, int epilogue, LinearPlan& p)
+{
+    p = LinearPlan{};
+    const int chunks = (int)(K / BK);
+    p.path = choose_path(L, K, N, epilogue);
+    const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
+    if (p.path == LUT6_PATH_STREAM) {
+        // weight-streaming regime: 64-token x 32-channel tiles over the whole
+        // K range; K is split into slices (partial planes, fixed-order sum)
+        // only when the tiles would leave most of the 256 CUs idle
+        const int bn_cov = epilogue == 2 ? S_BN / 2 : S_BN;
+        p.tiles_m = (int)((L + S_BM - 1) / S_BM);
+        p.tiles_n = (n_half + bn_cov - 1) / bn_cov;
+        p.tiles = p.tiles_n * p.tiles_m;
+        int splits = 1;
+        if (p.tiles < 192) {
+            splits = (256 + p.tiles - 1) / p.tiles;
+            const int max_splits = chunks / S_MIN_CHUNKS > 0 ? chunks / S_MIN_CHUNKS : 1;
+            if (splits > max_splits) splits = max_splits;
+        }
+        p.k_chunks_per_split = (chunks + splits - 1) / splits;
+        p.splits = (chunks + p.k_chunks_per_split - 1) / p.k_chunks_per_split;
+        if ((int64_t)p.tiles * p.splits > INT32_MAX) return LUT6_E_SHAPE;
+        p.f16 = p.k_chunks_per_split == 64 && chunks % 64 == 0;
+    } else {
+        // compute regime: 256 x 256 tiles; split K (fixed-order reduction)
+        // when the tiles cannot fill most of the 256 CUs
+        const int bn_cov = epilogue == 2 ? 128 : 256;
+        p.tiles_m = (int)((L + T2 - 1) / T2);
+        p.tiles_n = (n_half + bn_cov - 1) / bn_cov;
+        p.tiles = p.tiles_n * p.tiles_m;
+        int splits = 1;
+        if (p.tiles < 192) {
+            splits = (256 + p.tiles - 1) / p.tiles;
+            const int max_splits = chunks / 8 > 0 ? chunks / 8 : 1;
+            if (splits > max_splits) splits = max_splits;
+        }
+        p.k_chunks_per_split = (chunks + splits - 1) / splits;
+        p.splits = (chunks + p.k_chunks_per_split - 1) / p.k_chunks_per_split;
+        if (p.path == LUT6_PATH_EXPANDED)   // whole tiles, fragment order
+            p.w16_bytes = (size_t)p.tiles_n * 8 * (chunks + 1) * 4096;
+    }
+    p.partial_bytes = p.splits > 1 ? (size_t)p.splits * L * N * sizeof(float) : 0;
+    return LUT6_OK;
+}
+
+// Enqueue the kernels of a plan.  w16 and partial are device buffers of at
+// least p.w16_bytes and p.partial_bytes (unused when those are 0).
+int launch_linear(const LinearPlan& p, const void* x, const uint8_t* packed, const void* tables,
+                  void* y, int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
+                  void* w16, float* partial, hipStream_t stream)
+{
     GemmArgs a{};
     a.x = (const uint16_t*)x;
     a.packed = packed;
@@ -1928,37 +1996,15 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
     a.N = (int)N;
     a.scale = (_Float16)in_scale;
     a.inv_scale = 1.0f / in_scale;
-
-    const int chunks = (int)(K / BK);
-    const int path = choose_path(L, K, N, epilogue);
-    if (path == LUT6_PATH_STREAM) {
-        // weight-streaming regime: 64-token x 32-channel tiles over the whole
-        // K range; K is split into slices (partial planes, fixed-order sum)
-        // only when the tiles would leave most of the 256 CUs idle
-        const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
-        const int bn_cov = epilogue == 2 ? S_BN / 2 : S_BN;
-        const int tiles_m = (int)((L + S_BM - 1) / S_BM);
-        const int tiles = ((n_half + bn_cov - 1) / bn_cov) * tiles_m;
-        int splits = 1;
-        if (tiles < 192) {
-            splits = (256 + tiles - 1) / tiles;
-            const int max_splits = chunks / S_MIN_CHUNKS > 0 ? chunks / S_MIN_CHUNKS : 1;
-            if (splits > max_splits) splits = max_splits;
-        }
-        a.tiles_m = tiles_m;
-        a.n_tiles = tiles;
-        a.k_chunks_per_split = (chunks + splits - 1) / splits;
-        splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
-        if ((int64_t)tiles * splits > INT32_MAX) return LUT6_E_SHAPE;
-        if (splits > 1) {
-            const int st = workspace_for(stream, WS_PARTIAL, (size_t)splits * L * N * sizeof(float), (void**)&a.partial);
-            if (st != LUT6_OK) return st;
-        }
-        const bool scaled = in_scale != 1.0f;
-        const dim3 grid((unsigned)(tiles * splits)), block(256);
-        // every wave holds exactly 16 chunks: the fully preloaded variant
-        const bool f16 = a.k_chunks_per_split == 64 && chunks % 64 == 0;
-        switch (((epilogue * 2 + (scaled ? 1 : 0)) * 2 + (splits > 1 ? 1 : 0)) * 2 + (f16 ? 1 : 0)) {
+    a.tiles_m = p.tiles_m;
+    a.n_tiles = p.tiles;
+    a.k_chunks_per_split = p.k_chunks_per_split;
+    a.partial = p.splits > 1 ? partial : nullptr;
+    const bool scaled = in_scale != 1.0f;
+    const int splits = p.splits;
+    if (p.path == LUT6_PATH_STREAM) {
+        const dim3 grid((unsigned)(p.tiles * splits)), block(256);
+        switch (((epilogue * 2 + (scaled ? 1 : 0)) * 2 + (splits > 1 ? 1 : 0)) * 2 + (p.f16 ? 1 : 0)) {
 #define S8_CASE(I, E, S, P)                                                                                   \
         case 2 * (I): hipLaunchKernelGGL((lut6_stream_kernel<E, S, P, false>), grid, block, 0, stream, a); break; \
         case 2 * (I) + 1: hipLaunchKernelGGL((lut6_stream_kernel<E, S, P, true>), grid, block, 0, stream, a); break;
@@ -1971,34 +2017,13 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
         if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
         return splits > 1 ? launch_reduce(a, epilogue, splits, stream) : LUT6_OK;
     }
-    // compute regime: 256 x 256 tiles; split K (fixed-order reduction) when
-    // the tiles cannot fill most of the 256 CUs
-    const int n_half = epilogue == 2 ? (int)N / 2 : (int)N;
-    const int bn_cov = epilogue == 2 ? 128 : 256;
-    const int tiles_m = (int)((L + T2 - 1) / T2);
-    const int tiles = ((n_half + bn_cov - 1) / bn_cov) * tiles_m;
-    int splits = 1;
-    if (tiles < 192) {
-        splits = (256 + tiles - 1) / tiles;
-        const int max_splits = chunks / 8 > 0 ? chunks / 8 : 1;
-        if (splits > max_splits) splits = max_splits;
-    }
-    a.tiles_m = tiles_m;
-    a.n_tiles = tiles;
-    a.k_chunks_per_split = (chunks + splits - 1) / splits;
-    splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
-    const bool scaled = in_scale != 1.0f;
-    dim3 grid(tiles, splits), block(256);
+    const dim3 grid(p.tiles, splits), block(256);
     // many tokens: expand the weight once, then the FP16 GEMM; otherwise the
     // fused kernel
-    const int tiles_n = tiles / tiles_m;
-    const size_t w16_bytes = (size_t)tiles_n * 8 * (chunks + 1) * 4096;   // whole tiles, fragment order
-    const bool two_pass = path == LUT6_PATH_EXPANDED;
+    const bool two_pass = p.path == LUT6_PATH_EXPANDED;
     if (two_pass) {
-        void* w16 = nullptr;
-        const int st = workspace_for(stream, WS_EXPANDED, w16_bytes, &w16);
-        if (st != LUT6_OK) return st;
-        const dim3 xgrid((unsigned)tiles_n, (unsigned)((chunks + X_CHUNKS - 1) / X_CHUNKS));
+        const int chunks = (int)(K / BK);
+        const dim3 xgrid((unsigned)p.tiles_n, (unsigned)((chunks + X_CHUNKS - 1) / X_CHUNKS));
         switch (epilogue) {
         case 2: hipLaunchKernelGGL(lut6_expand_kernel<2>, xgrid, dim3(256), 0, stream,
                                    packed, (const uint16_t*)tables, (uint16_t*)w16, (int)N, (int)K); break;
@@ -2008,13 +2033,85 @@ extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tab
         if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
         a.w16 = (const uint16_t*)w16;
     }
-    if (splits > 1) {
-        const int st = workspace_for(stream, WS_PARTIAL, (size_t)splits * L * N * sizeof(float), (void**)&a.partial);
-        if (st != LUT6_OK) return st;
-    }
     launch_tiles(a, two_pass, epilogue, scaled, splits > 1, grid, stream);
     if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
     return splits > 1 ? launch_reduce(a, epilogue, splits, stream) : LUT6_OK;
+}
+
+}  // namespace
+
+extern "C" int lut6_linear(const void* x, const uint8_t* packed, const void* tables, void* y,
+                           int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
+                           hipStream_t stream)
+{
+    int st = check_linear(x, packed, tables, y, L, K, N, in_scale, epilogue);
+    if (st != LUT6_OK || L == 0) return st;
+    LinearPlan p;
+    st = plan_linear(L, K, N, epilogue, p);
+    if (st != LUT6_OK) return st;
+    void* w16 = nullptr;
+    float* partial = nullptr;
+    if (p.w16_bytes) {
+        st = workspace_for(stream, WS_EXPANDED, p.w16_bytes, &w16);
+        if (st != LUT6_OK) return st;
+    }
+    if (p.partial_bytes) {
+        st = workspace_for(stream, WS_PARTIAL, p.partial_bytes, (void**)&partial);
+        if (st != LUT6_OK) return st;
+    }
+    return launch_linear(p, x, packed, tables, y, L, K, N, in_scale, epilogue, w16, partial, stream);
+}
+
+// ---------------------------------------------------------------------------
+// lut6_linear_noalloc: the same plan and kernels, with the expanded weight and
+// the split-K partials carved from one static device array per GPU, so that
+// no call allocates.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[LUT6_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mutex;
+std::map<int, void*> g_scratch_addr;   // device -> device address of `scratch`
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept.  The host-side symbol is only a
+// stand-in: kernels and copies get this address, never the symbol.
+int scratch_address(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LUT6_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    auto it = g_scratch_addr.find(dev);
+    if (it == g_scratch_addr.end()) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LUT6_E_DEVICE;
+        it = g_scratch_addr.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return LUT6_OK;
+}
+}  // namespace
+
+extern "C" int lut6_linear_noalloc(const void* x, const uint8_t* packed, const void* tables, void* y,
+                                   int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
+                                   hipStream_t stream)
+{
+    int st = check_linear(x, packed, tables, y, L, K, N, in_scale, epilogue);
+    if (st != LUT6_OK || L == 0) return st;
+    LinearPlan p;
+    st = plan_linear(L, K, N, epilogue, p);
+    if (st != LUT6_OK) return st;
+    // expanded weight first, partial sums after it on a 256-byte boundary
+    const size_t w16_span = (p.w16_bytes + 255) & ~(size_t)255;
+    if (w16_span + p.partial_bytes > LUT6_NOALLOC_SCRATCH_BYTES) return LUT6_E_SCRATCH;
+    void* base = nullptr;
+    if (p.w16_bytes || p.partial_bytes) {
+        st = scratch_address(&base);
+        if (st != LUT6_OK) return st;
+    }
+    void* w16 = p.w16_bytes ? base : nullptr;
+    float* partial = p.partial_bytes ? (float*)((unsigned char*)base + w16_span) : nullptr;
+    return launch_linear(p, x, packed, tables, y, L, K, N, in_scale, epilogue, w16, partial, stream);
 }
 
 extern "C" int lut6_int8_linear(const void* x, const int8_t* q, const void* scales, void* y,

@@ -224,6 +224,31 @@ def test_gated_delta_validation(kwargs, status):
     assert _gated_delta(**kwargs) == status
 
 
+def _linear_noalloc(x=X, p=P, t=T, y=Y, L=128, K=4096, N=4096, s=1.0, epi=1):
+    return lq.load_library().lut6_linear_noalloc(x, p, t, y, L, K, N, s, epi, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(x=None), 1), (dict(y=None), 1), (dict(L=-1), 2), (dict(K=100), 2), (dict(N=4008), 2),
+    (dict(N=48, epi=2), 2), (dict(L=2 ** 18), 2), (dict(epi=3), 5), (dict(s=3.0), 4),
+    (dict(x=X + 8), 3), (dict(y=X), 8), (dict(L=0), 0),
+    # the expanded weight of 65,536 channels at K = 4,096 is 545 MB of scratch
+    (dict(L=2048, N=65536), 9),
+    # deep K (expanded from 3,072 tokens): 15 tiles x 8 x 1,025 chunks x 4 KB
+    (dict(L=3072, K=65536, N=3840), 9),
+])
+def test_linear_noalloc_validation(kwargs, status):
+    # the same host checks as lut6_linear, then LUT6_E_SCRATCH for shapes
+    # whose scratch exceeds the static array; all before any device call
+    assert _linear_noalloc(**kwargs) == status
+
+
+def test_noalloc_scratch_size_is_declared():
+    text = HEADER.read_text()
+    m = re.search(r"#define LUT6_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == lq.NOALLOC_SCRATCH_BYTES
+
+
 # ---------------------------------------------------------------------------
 # the Python binding's own checks (meta tensors stand in for device memory;
 # every mismatch must raise before the library is called)
@@ -250,10 +275,17 @@ def test_binding_linear_shapes(meta_device):
         lq.linear(x, p, meta_device((1, 64), f16))
     with pytest.raises(TypeError):
         lq.linear(x, p, t, out=meta_device((8, 16), f16))
+    with pytest.raises(TypeError):
+        lq.linear_noalloc(x, p, t, None)
+    with pytest.raises(TypeError):
+        lq.linear_noalloc(x, p, t, meta_device((8, 32), torch.float32))
     # well-formed operands reach the library, which refuses the null
     # pointers of meta tensors without any device work
     with pytest.raises(lq.Lut6Error) as e:
         lq.linear(x, p, t)
+    assert e.value.status == "LUT6_E_NULL"
+    with pytest.raises(lq.Lut6Error) as e:
+        lq.linear_noalloc(x, p, t, meta_device((8, 32), f16))
     assert e.value.status == "LUT6_E_NULL"
 
 
