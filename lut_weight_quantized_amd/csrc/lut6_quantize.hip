@@ -1,10 +1,10 @@
 // LUT-6 table fitting on gfx950: one 64-entry FP16 table per 16 output
-// channels by 40 rounds of one-dimensional k-means, then the packed indices
-// (page "Clef-Flash-ANE-LUT6", section "LUT-6 text weights": 40 rounds per
-// group of 16 channels; half of the starting values are quantiles, the other
-// half spread evenly between the group's minimum and maximum).
+// channels by one-dimensional k-means, then the packed indices (page
+// "Clef-Flash-ANE-LUT6", section "LUT-6 text weights").  The page fixes the
+// round count, 40, and the starting centres: 32 at quantiles of the group's
+// values, 32 at even steps from its smallest to its largest value.
 //
-// The page gives nothing finer; the steps follow these readings:
+// Everything finer is a reading:
 //   - FP16 weights, all finite; a group is rows 16g .. 16g + 15, n = 16 K
 //     values;
 //   - starting centres: the values of rank floor((2i + 1) n / 64) in the

@@ -82,6 +82,8 @@ class Oracle:
         lib.ora_gated_delta.restype = ctypes.c_int
         lib.ora_quantize.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P]
         lib.ora_quantize.restype = ctypes.c_int
+        lib.ora_km_centres.argtypes = [_P, _I64, _I64, _I64, ctypes.c_int, _P]
+        lib.ora_km_centres.restype = ctypes.c_int
         lib.ora_packed_bytes.argtypes = [_I64, _I64]
         lib.ora_packed_bytes.restype = _I64
         lib.ora_table_bytes.argtypes = [_I64]
@@ -288,20 +290,32 @@ class Oracle:
         """1-D k-means tables and packed indices of an FP16 weight [N, K].
 
         Returns (packed uint8 [N, 3K/4], tables uint16 [N/16, 64]), and the
-        41 SSE values of the first group when with_sse; with ``groups`` =
-        (g0, g1) only those groups' rows and tables are computed (the rest
-        are zero)."""
+        first group's squared errors when with_sse (before round 1 and after
+        every round: as many values as the oracle ran rounds, plus one); with
+        ``groups`` = (g0, g1) only those groups' rows and tables are computed
+        (the rest are zero)."""
         w = np.ascontiguousarray(np.asarray(w16).view(np.uint16))
         n, k = w.shape
         g0, g1 = (0, n // 16) if groups is None else groups
         packed = np.zeros((n, 3 * k // 4), np.uint8)
         tables = np.zeros((n // 16, 64), np.uint16)
-        sse = np.zeros(41, np.float64)
+        sse = np.full(64, np.nan, np.float64)
         st = self.lib.ora_quantize(w.ctypes.data, packed.ctypes.data, tables.ctypes.data, n, k,
                                    int(g0), int(g1), sse.ctypes.data if with_sse else None)
         if st != OK:
             raise OracleError(f"ora_quantize status {st}")
-        return (packed, tables, sse) if with_sse else (packed, tables)
+        return (packed, tables, sse[~np.isnan(sse)]) if with_sse else (packed, tables)
+
+    def km_centres(self, w16: np.ndarray, group: int, rounds: int) -> np.ndarray:
+        """Group `group`'s 64 FP64 centres after `rounds` Lloyd rounds (0: the
+        starting centres), as ora_quantize computes them."""
+        w = np.ascontiguousarray(np.asarray(w16).view(np.uint16))
+        n, k = w.shape
+        c = np.zeros(64, np.float64)
+        st = self.lib.ora_km_centres(w.ctypes.data, n, k, int(group), int(rounds), c.ctypes.data)
+        if st != OK:
+            raise OracleError(f"ora_km_centres status {st}")
+        return c
 
 
 _default: Oracle | None = None

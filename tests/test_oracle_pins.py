@@ -479,12 +479,121 @@ def pin_gated_delta_split_sequence(ora):
     assert np.allclose(o2, oe[a:], rtol=1e-6, atol=1e-7)    # the carried state is rounded to FP32
 
 
+# ---------------------------------------------------------------------------
+# table fitting: what the page fixes (page "Clef-Flash-ANE-LUT6", section
+# "LUT-6 text weights": 40 rounds of one-dimensional k-means per 16-channel
+# group, half of the starting values at quantiles and half spread evenly
+# from the group's minimum to its maximum).  The Lloyd rounds are recomputed
+# here independently: values as exact integers in 2^-24 units (numpy's FP16
+# conversion), cluster boundaries as exact rational midpoints, means as
+# correctly rounded rationals.
+# ---------------------------------------------------------------------------
+
+def _units(w16) -> np.ndarray:
+    """FP16 values as exact integers in units of 2^-24."""
+    return (np.asarray(w16, np.float16).astype(np.float64) * 2.0 ** 24).astype(np.int64)
+
+
+def _km_assign(u: np.ndarray, c) -> np.ndarray:
+    """Nearest of the sorted centres c for values u (2^-24 units), the lower
+    of two equally near ones: u goes below the exact midpoint m of c_i and
+    c_(i+1) when u <= m, i.e. u <= floor((c_i + c_(i+1)) * 2^23)."""
+    t = np.array([(Fraction(c[i]) + Fraction(c[i + 1])) * 2 ** 23 for i in range(len(c) - 1)])
+    t = np.array([int(v.numerator // v.denominator) for v in t], dtype=np.int64)
+    return np.searchsorted(t, u, side="left")
+
+
+def _km_step(u_sorted: np.ndarray, c) -> list:
+    """One Lloyd round: each centre becomes its cluster's mean (rounded once
+    to the nearest double), an empty cluster keeps its centre, then sort."""
+    cl = _km_assign(u_sorted, c)
+    cnt = np.bincount(cl, minlength=len(c))
+    pref = np.concatenate([[0], np.cumsum(u_sorted)])
+    ends = np.cumsum(cnt)
+    new = []
+    for q in range(len(c)):
+        if cnt[q]:
+            tot = int(pref[ends[q]] - pref[ends[q] - cnt[q]])
+            new.append(float(Fraction(tot, int(cnt[q]))) * 2.0 ** -24)
+        else:
+            new.append(float(c[q]))
+    return sorted(new)
+
+
+def _block_group():
+    """A 16 x 64 group of 32 distinct FP16 values, 32 copies each (shuffled),
+    the two ends far out: every quantile inside one of the 32 equal shares of
+    the sorted values is that share's value, whatever rank is taken."""
+    q = np.concatenate([[-0.5], (np.arange(30) - 14.5) * 0.003, [0.75]]).astype(np.float16)
+    assert np.all(np.diff(q.astype(np.float64)) > 0)
+    vals = np.repeat(q, 32)[np.random.default_rng(11).permutation(1024)]
+    return vals.reshape(16, 64), q.astype(np.float64)
+
+
+def _slow_group(K=1024, seed=12):
+    """N(0, 0.02) with 2% outliers at 8x: k-means is still moving at round 40."""
+    g = np.random.default_rng(seed)
+    w = g.standard_normal((16, K)) * 0.02
+    w[g.random((16, K)) < 0.02] *= 8.0
+    return w.astype(np.float16)
+
+
+def pin_quantize_starts(ora):
+    w, q = _block_group()
+    c0 = ora.km_centres(w, 0, 0)
+    lo, hi = q[0], q[-1]
+    even = lo + (hi - lo) * np.arange(32) / 31.0
+    want = np.sort(np.concatenate([q, even]))
+    # 32 quantiles (one per share) and 32 even steps from min to max, both
+    # ends included; the tolerance only covers the evaluation order
+    assert np.allclose(c0, want, rtol=0, atol=2.0 ** -50), "starting centres"
+    assert c0[0] == lo and c0[-1] == hi
+    # the squared error before the first round, and one value per round
+    _, _, sse = ora.quantize(w, with_sse=True)
+    assert len(sse) == 41, f"{len(sse) - 1} rounds instead of 40"
+    vals = np.repeat(q, 32)
+    d = np.min(np.abs(vals[:, None] - want[None, :]), axis=1)
+    assert abs(sse[0] - float(np.sum(d * d))) <= 1e-12 * float(np.sum(d * d))
+
+
+def pin_quantize_lloyd_step(ora):
+    for w in (_block_group()[0], _slow_group(K=256, seed=13)):
+        u = np.sort(_units(w).reshape(-1))
+        for r in (0, 1, 6):
+            c = ora.km_centres(w, 0, r)
+            nxt = ora.km_centres(w, 0, r + 1)
+            assert list(nxt) == _km_step(u, list(c)), f"Lloyd round {r + 1}"
+
+
+def pin_quantize_forty_rounds(ora):
+    w = _slow_group()
+    K = w.shape[1]
+    u = np.sort(_units(w).reshape(-1))
+    c = list(ora.km_centres(w, 0, 0))          # the starts, pinned above
+    hist = [c]
+    for _ in range(40):
+        c = _km_step(u, c)
+        hist.append(c)
+
+    def table(cs):
+        return np.sort(np.asarray(cs, np.float64).astype(np.float16).astype(np.float64))
+    t39, t40 = table(hist[39]), table(hist[40])
+    assert not np.array_equal(t39, t40), "the group must still move at round 40"
+    packed, tables = ora.quantize(w)
+    got = tables[0].view(np.float16).astype(np.float64)
+    assert np.array_equal(got, t40), "table = the 40th round's centres rounded to FP16"
+    idx = ora.unpack(packed, K).astype(np.int64)
+    want = _km_assign(_units(w).reshape(-1), list(t40)).reshape(16, K)
+    assert np.array_equal(idx, want), "index = nearest entry, the lower on a tie"
+
+
 PINS = [pin_pack_worked_examples, pin_pack_exhaustive, pin_storage, pin_f16_decode,
         pin_f16_encode, pin_dequant, pin_linear_bruteforce, pin_linear_silu,
         pin_special_tables, pin_identity_readout, pin_in_scale, pin_int8_dequant,
         pin_int8_as_lut6, pin_int8_block_scale, pin_attention_sdpa, pin_attention_closed_forms,
         pin_gated_delta_frozen_state, pin_gated_delta_decay_only, pin_gated_delta_overwrites_unit_keys,
-        pin_gated_delta_split_sequence]
+        pin_gated_delta_split_sequence, pin_quantize_starts, pin_quantize_lloyd_step,
+        pin_quantize_forty_rounds]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -531,7 +640,9 @@ MUTANTS = {1: "big-endian byte order", 2: "index order reversed", 3: "one table 
            13: "int8 code read unsigned", 14: "int8 product truncated to FP16",
            15: "attention sum off by one", 16: "attention heads interleaved",
            17: "attention mask one key short", 18: "attention scaled by 1 over D",
-           19: "delta rule heads interleaved", 20: "delta rule beta ignored", 21: "delta rule unscaled"}
+           19: "delta rule heads interleaved", 20: "delta rule beta ignored", 21: "delta rule unscaled",
+           22: "k-means 39 rounds", 23: "k-means starts all quantiles",
+           24: "k-means even starts miss min and max"}
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m].replace(" ", "_"))
@@ -605,9 +716,10 @@ def test_tolerance_accepts_rounded_oracle_and_rejects_drift(ora):
 
 # ---------------------------------------------------------------------------
 # table fitting (1-D k-means, page "Clef-Flash-ANE-LUT6", section "LUT-6 text
-# weights").  The page fixes only the round count and the starting mix, so
-# nothing on it can be matched bit for bit (parity unpinned); these pins are
-# properties that hold for k-means whatever the details.
+# weights").  The page fixes the round count (40) and the starting mix (32
+# quantiles, 32 even steps from the group's minimum to its maximum); the pins
+# above check both.  The tests below are properties that hold for k-means
+# whatever its remaining details.
 # ---------------------------------------------------------------------------
 
 def _q_values(tables_u16: np.ndarray) -> np.ndarray:
