@@ -227,7 +227,17 @@ int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const
  * 0 <= L < 2^31 - 64, each ld at least its row's width (LUT6_E_SHAPE); q,
  * k, v, o 16-byte aligned with ldq, ldk, ldv, ldo multiples of 8; g, beta,
  * state 4-byte aligned (LUT6_E_ALIGN); o and state must not overlap an
- * input or each other (LUT6_E_ALIAS).  L == 0 is a no-op.  No workspace. */
+ * input or each other (LUT6_E_ALIAS).  L == 0 is a no-op.
+ * From L = 64 the rule is evaluated in chunks of 64 positions counted from
+ * the call's first token (page "clef-flash-LiteRT", section "Provenance,
+ * conversion and license": a chunked kernel of 64 positions), on the matrix
+ * cores; below 64, token by token.  The result is the same rule in either
+ * order, within FP32 rounding; two calls with the state carried between
+ * them give the bits of one call when the split falls on a multiple of 64
+ * tokens (or both calls are shorter than 64).  The chunked form uses a
+ * library workspace of n_v_heads x min(ceil(L/64), 128) x 33 KB (at most
+ * 160 MB), created on the first call that needs it and kept until
+ * lut6_release.                                                          */
 int lut6_gated_delta(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
                      int64_t ldv, const float* g, const float* beta, int64_t ldg, void* o,
                      int64_t ldo, float* state, int64_t L, int64_t n_k_heads, int64_t n_v_heads,
@@ -263,7 +273,8 @@ int lut6_quantize(const void* w, uint8_t* packed, void* tables, int64_t N, int64
 /* Free the library's per-device workspaces (after synchronising the
  * devices that hold one): split-K partial sums and the expanded weight
  * (lut6_linear, lut6_int8_linear), the table-fitting scratch
- * (lut6_quantize) and the key-split partials (lut6_attention).  Optional;
+ * (lut6_quantize), the key-split partials (lut6_attention) and the chunk
+ * matrices of the recurrence (lut6_gated_delta).  Optional;
  * safe to call at any time when no call of the library is in flight.     */
 int lut6_release(void);
 

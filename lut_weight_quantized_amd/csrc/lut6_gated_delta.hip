@@ -1,7 +1,9 @@
 // Gated DeltaNet recurrence of the linear-attention layers on gfx950 (page
 // "Clef-Flash-ANE-LUT6", section "Model architecture": 16 key and 32 value
 // heads of size 128; page "clef-flash — Core AI", the decoder states: one
-// recurrent state [32, 128, 128] per layer, carried between calls).
+// recurrent state [32, 128, 128] per layer, carried between calls; page
+// "clef-flash-LiteRT", section "Provenance, conversion and license": the
+// recurrence runs as a chunked kernel of 64 positions).
 //
 // The pages name the layer, not its update; the reading is the gated delta
 // rule.  Per value head h (key head h / (Hv / Hk)), state S (dk x dv, FP32),
@@ -9,16 +11,30 @@
 //   S <- exp(g_t) S;   d = beta_t (v_t - S^T k_t);   S <- S + k_t d^T;
 //   o_t = S^T q_t / sqrt(dk)   (rounded once to FP16)
 //
-// Design (token-sequential): column j of a head's state evolves on its own
-// (it needs only its own S^T k and S^T q entries), so 16 lanes own one
+// Chunked form (L >= 64), an evaluation order of the same rule.  Within a
+// chunk of 64 positions, with G_t = g_1 + .. + g_t (inclusive, FP64),
+// gamma_t = e^G_t, S0 the state before the chunk:
+//   A[t][s] = beta_t e^(G_t - G_s) k_t.k_s  (s < t),   T = (I + A)^-1,
+//   D = T (diag(beta) V - diag(beta gamma) K S0)        (the d_t as rows),
+//   O = (diag(gamma) Q S0 + P D) / sqrt(dk),  P[t][s] = e^(G_t - G_s) q_t.k_s (s <= t),
+//   S  = gamma_63 S0 + K^T diag(eta) D,       eta_s = e^(G_63 - G_s).
+// lut6_gdn_prep_kernel computes T, P and the decay vectors of every (chunk,
+// head) in parallel: K K^T and Q K^T on v_mfma_f32_16x16x32_f16 (the FP16
+// inputs give exact products and FP32 sums), T by substitution.
+// lut6_gdn_chunk_kernel then walks the chunks in order, one workgroup per
+// (head, 16 state columns): every product with the state on
+// v_mfma_f32_16x16x4f32, the state's FP32 columns held in the waves'
+// accumulators and mirrored in LDS as the next chunk's operand.
+//
+// Token-sequential form (L < 64): column j of a head's state evolves on its
+// own (it needs only its own S^T k and S^T q entries), so 16 lanes own one
 // column, 8 rows each, in registers; the two 128-term dot products per
 // token are 8 FMAs per lane and a 4-step DPP reduction over the 16 lanes.
 // A workgroup holds 16 columns of one head (256 workgroups for 32 heads, one
 // per CU).  Tokens go through LDS 64 at a time in two stages: k and q of the
 // key head (converted to FP32 once there), v of the workgroup's columns, g
 // and beta; the next chunk is loaded into registers while the current one
-// is processed, and outputs leave through LDS as 16-byte rows.  The chunked form (products over 64
-// positions on the matrix cores) is not built.
+// is processed, and outputs leave through LDS as 16-byte rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -159,6 +175,354 @@ __global__ void __launch_bounds__(256) lut6_gated_delta_kernel(GdnArgs a)
     for (int e = 0; e < 8; ++e) sp[(size_t)e * DV] = S[e];
 }
 
+// ---------------------------------------------------------------------------
+// chunked form
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;                            // positions per chunk
+constexpr int CB = 16;                            // state columns per recurrence workgroup
+constexpr int WS_T = 0, WS_P = CH * CH;           // workspace layout per (head, chunk), floats
+constexpr int WS_GAMMA = 2 * CH * CH, WS_ETA = WS_GAMMA + CH, WS_BETA = WS_ETA + CH;
+constexpr int WS_FLOATS = 2 * CH * CH + 4 * CH;   // T, P, gamma, eta, beta, pad
+constexpr int WS_GDN = 3;                         // library workspace kind
+constexpr int64_t MAX_WINDOW_CHUNKS = 128;        // chunks per prep + recurrence launch pair
+constexpr size_t WS_BUDGET = (size_t)160 << 20;   // workspace bytes, at most
+
+struct ChunkArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* g;
+    const float* beta;
+    uint16_t* o;
+    float* state;                     // [Hv][DK][DV]
+    float* ws;                        // [Hv][n_chunks][WS_FLOATS]
+    int64_t ldq, ldk, ldv, ldg, ldo;
+    int L;                            // tokens of the call
+    int t_begin;                      // first token of this window
+    int n_chunks;                     // chunks in this window
+    int Hv, grp;
+};
+
+__device__ __forceinline__ float quad_sum(float x)
+{
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    return x;
+}
+
+__device__ __forceinline__ float half_at(const u32x4& w, int i)
+{
+    const uint32_t word = w[i >> 1];
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? word >> 16 : word & 0xffffu));
+}
+
+// One (chunk, value head): T = (I + A)^-1, P and the decay vectors.
+__global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t kh[CH][DK + 8];   // k rows, FP16
+    __shared__ __attribute__((aligned(16))) uint16_t qh[CH][DK + 8];   // q rows, FP16
+    __shared__ float as[CH][CH + 4];                                    // A (zero on and above the diagonal)
+    __shared__ double gl[CH];                                           // G_t
+    __shared__ float bs[CH];                                            // beta_t
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lo = lane & 15, hi = lane >> 4;
+    const int c = blockIdx.x, h = blockIdx.y, kq = h / a.grp;
+    const int t0 = a.t_begin + c * CH;
+    float* const ws = a.ws + ((size_t)h * a.n_chunks + c) * WS_FLOATS;
+
+    // k and q rows of the key head, zero past L
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int idx = tid + 256 * u, row = idx >> 4, piece = idx & 15;
+        const int t = t0 + row;
+        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+        if (t < a.L) {
+            kv = *(const u32x4*)(a.k + (size_t)t * a.ldk + (size_t)kq * DK + piece * 8);
+            qv = *(const u32x4*)(a.q + (size_t)t * a.ldq + (size_t)kq * DK + piece * 8);
+        }
+        *(u32x4*)&kh[row][piece * 8] = kv;
+        *(u32x4*)&qh[row][piece * 8] = qv;
+    }
+    for (int i = tid; i < CH * (CH + 4); i += 256) (&as[0][0])[i] = 0.0f;
+    // the log-decay prefix in FP64 and beta (g = beta = 0 past L)
+    if (wave == 0) {
+        const int t = t0 + lane;
+        double x = 0.0;
+        float be = 0.0f;
+        if (t < a.L) {
+            x = (double)a.g[(size_t)t * a.ldg + h];
+            be = a.beta[(size_t)t * a.ldg + h];
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        gl[lane] = x;
+        bs[lane] = be;
+        const double last = __shfl(x, 63);
+        ws[WS_GAMMA + lane] = expf((float)x);
+        ws[WS_ETA + lane] = expf((float)(last - x));
+        ws[WS_BETA + lane] = be;
+    }
+    __syncthreads();
+
+    // K K^T (tiles on and below the diagonal, into A) and Q K^T (into P):
+    // 20 tiles of 16 x 16, five per wave
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const int job = wave + 4 * j;                       // 0..9: K K^T, 10..19: Q K^T
+        const bool isq = job >= 10;
+        const int tri = isq ? job - 10 : job;               // lower-triangle tile index
+        const int rt = tri >= 6 ? 3 : tri >= 3 ? 2 : tri >= 1 ? 1 : 0;
+        const int st_ = tri - rt * (rt + 1) / 2;
+        const uint16_t (*xa)[DK + 8] = isq ? qh : kh;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const f16x8 av = *(const f16x8*)&xa[16 * rt + lo][32 * kk + 8 * hi];
+            const f16x8 bv = *(const f16x8*)&kh[16 * st_ + lo][32 * kk + 8 * hi];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+        }
+        const int s = 16 * st_ + lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * rt + 4 * hi + e;
+            const float dec = expf((float)(gl[t] - gl[s]));
+            if (isq) ws[WS_P + t * CH + s] = s <= t ? dec * acc[e] : 0.0f;
+            else if (s < t) as[t][s] = bs[t] * dec * acc[e];
+        }
+    }
+    // P above its diagonal tiles is zero
+    for (int i = tid; i < 6 * 256; i += 256) {
+        const int tile = i >> 8, r = (i >> 4) & 15, cc = i & 15;
+        const int rt = tile < 3 ? 0 : tile < 5 ? 1 : 2;
+        const int st_ = tile < 3 ? tile + 1 : tile < 5 ? tile - 1 : 3;
+        ws[WS_P + (16 * rt + r) * CH + 16 * st_ + cc] = 0.0f;
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1 by substitution down each column: column j = 16 wave
+    // + lane / 4, its rows split over four lanes by row % 4
+    {
+        const int j = 16 * wave + (lane >> 2), p = lane & 3;
+        float tc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tc[i] = (4 * i + p == j) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int t = 1; t < CH; ++t) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i <= (t - 1) / 4; ++i) sum = __builtin_fmaf(as[t][4 * i + p], tc[i], sum);
+            sum = quad_sum(sum);
+            if (p == (t & 3) && t > j) tc[t >> 2] = -sum;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ws[WS_T + (4 * i + p) * CH + j] = tc[i];
+    }
+}
+
+// The recurrence over the chunks of a window: one workgroup per (value head,
+// 16 state columns); wave w owns state rows 32 w .. 32 w + 31.  A chunk's
+// operands (k or q rows, v, rows of T and P, the decay vectors) are loaded
+// into registers while the chunk before it is computed.
+__global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float st[CB][DK + 4];     // S^T of the block
+    __shared__ __attribute__((aligned(16))) float ks[CH][DK + 16];    // k rows of the chunk
+    __shared__ float rs[CH][CB + 1];                                  // R = beta (v - gamma K S)
+    __shared__ float ds[CH][CB + 1];                                  // D
+    __shared__ float dh[CH][CB];                                      // eta D
+    __shared__ float vec[2][3][CH];                                   // gamma, eta, beta (two chunks)
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lo = lane & 15, hi = lane >> 4;
+    // the 8 column blocks of a head share its chunk data: keep them on one
+    // XCD (dispatch is round-robin over the 8 XCDs)
+    const int h = blockIdx.x % a.Hv, jb = blockIdx.x / a.Hv;
+    const int kq = h / a.grp;
+    const int col0 = h * DV + jb * CB;
+    float* const sp = a.state + (size_t)h * DK * DV + jb * CB;
+    const float rsq = 0.08838834764831845f;           // 1 / sqrt(128)
+    const bool isq = w >= 2;
+    const uint16_t* const src = (isq ? a.q : a.k) + (size_t)kq * DK + 32 * hi;
+    const int64_t ld = isq ? a.ldq : a.ldk;
+    const float* const wsh = a.ws + (size_t)h * a.n_chunks * WS_FLOATS;
+
+    // S^T tiles r = 2w, 2w + 1: lane holds S[16 r + lo][4 hi + e]
+    f32x4 sacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = 16 * (2 * w + u) + lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sacc[u][e] = sp[(size_t)i * DV + 4 * hi + e];
+            st[4 * hi + e][i] = sacc[u][e];
+        }
+    }
+
+    // one chunk's register operands: k rows (waves 0, 1) or q rows (2, 3)
+    // 32 w' .. 32 w' + 31 (k = 32 hi ..), the wave's T rows, P rows (waves
+    // 2, 3), v (waves 0, 1) and one decay-vector entry (threads < 192)
+    struct Ops {
+        u32x4 xr[2][4];
+        f32x4 tv[4];
+        f32x4 pv[2][4];
+        uint32_t vr[2][4];
+        float vc;
+    };
+    auto load_ops = [&](int c, Ops& op) {
+        const int t0 = a.t_begin + c * CH;
+        const float* const wsc = wsh + (size_t)c * WS_FLOATS;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tg = t0 + 16 * (2 * (w & 1) + u) + lo;
+#pragma unroll
+            for (int z = 0; z < 4; ++z)
+                op.xr[u][z] = tg < a.L ? *(const u32x4*)(src + (size_t)tg * ld + 8 * z) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int z = 0; z < 4; ++z) op.tv[z] = *(const f32x4*)(wsc + WS_T + (16 * w + lo) * CH + 16 * hi + 4 * z);
+        if (isq) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int z = 0; z < 4; ++z)
+                    op.pv[u][z] = *(const f32x4*)(wsc + WS_P + (16 * (2 * (w - 2) + u) + lo) * CH + 16 * hi + 4 * z);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tg = t0 + 16 * (2 * w + u) + 4 * hi + e;
+                    op.vr[u][e] = tg < a.L ? a.v[(size_t)tg * a.ldv + col0 + lo] : 0u;
+                }
+        }
+        op.vc = tid < 3 * CH ? wsc[WS_GAMMA + tid] : 0.0f;
+    };
+
+    Ops cur;
+    load_ops(0, cur);
+    if (tid < 3 * CH) vec[0][tid >> 6][tid & 63] = cur.vc;
+    __syncthreads();
+
+    for (int c = 0; c < a.n_chunks; ++c) {
+        const int t0 = a.t_begin + c * CH, b = c & 1;
+        Ops nxt;
+        load_ops(c + 1 < a.n_chunks ? c + 1 : c, nxt);
+
+        // stage 1: X = [K; Q] S0, rows 32 w .. 32 w + 31 (k rows for waves
+        // 0, 1, q rows for 2, 3); contraction index k = 32 hi + m
+        f32x4 x[2];
+        {
+            float af[2][32];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int z = 0; z < 4; ++z)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) af[u][8 * z + i] = half_at(cur.xr[u][z], i);
+            x[0] = x[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int m4 = 0; m4 < 8; ++m4) {
+                const f32x4 bv = *(const f32x4*)&st[lo][32 * hi + 4 * m4];
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        x[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][4 * m4 + mm], bv[mm], x[u], 0, 0, 0);
+            }
+            if (!isq) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int t = 16 * (2 * w + u) + lo;
+#pragma unroll
+                    for (int z = 0; z < 8; ++z)
+                        *(f32x4*)&ks[t][32 * hi + 4 * z] =
+                            f32x4{af[u][4 * z], af[u][4 * z + 1], af[u][4 * z + 2], af[u][4 * z + 3]};
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * (2 * w + u) + 4 * hi + e;
+                        const float vv = (float)__builtin_bit_cast(_Float16, (uint16_t)cur.vr[u][e]);
+                        rs[t][lo] = vec[b][2][t] * (vv - vec[b][0][t] * x[u][e]);
+                    }
+            }
+        }
+        __syncthreads();
+
+        // stage 2: D rows 16 w .. 16 w + 15 = T R (contraction s = 16 hi + m)
+        {
+            f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                d = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.tv[m >> 2][m & 3], rs[16 * hi + m][lo], d, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * hi + e;
+                ds[t][lo] = d[e];
+                dh[t][lo] = vec[b][1][t] * d[e];
+            }
+        }
+        __syncthreads();
+
+        // stage 3a (waves 2, 3): O = (gamma Q S0 + P D) / sqrt(128), rows
+        // 32 (w - 2) .. + 31; the Q S0 rows are this wave's stage-1 tiles
+        if (isq) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = 2 * (w - 2) + u;
+                f32x4 acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = vec[b][0][16 * r + 4 * hi + e] * x[u][e];
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pv[u][m >> 2][m & 3], ds[16 * hi + m][lo], acc,
+                                                               0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tg = t0 + 16 * r + 4 * hi + e;
+                    if (tg < a.L)
+                        a.o[(size_t)tg * a.ldo + col0 + lo] = __builtin_bit_cast(uint16_t, (_Float16)(acc[e] * rsq));
+                }
+            }
+        }
+
+        // stage 3b: S^T = gamma_63 S0^T + (eta D)^T K for the wave's rows
+        // (contraction s = 4 m + hi)
+        {
+            const float gt = vec[b][0][CH - 1];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = 2 * w + u;
+                f32x4 acc = sacc[u] * gt;
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const int s = 4 * m + hi;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dh[s][lo], ks[s][16 * r + lo], acc, 0, 0, 0);
+                }
+                sacc[u] = acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[4 * hi + e][16 * r + lo] = acc[e];
+            }
+        }
+        // the next chunk's decay vectors (that buffer was last read before
+        // the previous barrier)
+        if (tid < 3 * CH) vec[b ^ 1][tid >> 6][tid & 63] = nxt.vc;
+        __syncthreads();
+        cur = nxt;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = 16 * (2 * w + u) + lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[(size_t)i * DV + 4 * hi + e] = sacc[u][e];
+    }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)
@@ -168,6 +532,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 }
 
 }  // namespace
+
+namespace lut6_detail {
+int workspace(hipStream_t stream, int kind, size_t bytes, void** out);   // lut6_linear.hip
+}
 
 extern "C" int lut6_gated_delta(const void* q, int64_t ldq, const void* k, int64_t ldk,
                                 const void* v, int64_t ldv, const float* g, const float* beta,
@@ -215,7 +583,44 @@ extern "C" int lut6_gated_delta(const void* q, int64_t ldq, const void* k, int64
     a.L = (int)L;
     a.Hv = (int)n_v_heads;
     a.grp = (int)(n_v_heads / n_k_heads);
-    hipLaunchKernelGGL(lut6_gated_delta_kernel, dim3((unsigned)(n_v_heads * (DV / COLS))), dim3(256), 0,
-                       stream, a);
-    return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+    if (L < CH) {
+        hipLaunchKernelGGL(lut6_gated_delta_kernel, dim3((unsigned)(n_v_heads * (DV / COLS))), dim3(256), 0,
+                           stream, a);
+        return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
+    }
+    // chunked: windows of chunks, each a prep launch then a recurrence launch
+    const int64_t chunks = (L + CH - 1) / CH;
+    const size_t per_chunk = (size_t)n_v_heads * WS_FLOATS * sizeof(float);
+    int64_t win = (int64_t)(WS_BUDGET / per_chunk);
+    win = win < 1 ? 1 : win > MAX_WINDOW_CHUNKS ? MAX_WINDOW_CHUNKS : win;
+    if (win > chunks) win = chunks;
+    void* ws = nullptr;
+    const int st = lut6_detail::workspace(stream, WS_GDN, (size_t)win * per_chunk, &ws);
+    if (st != LUT6_OK) return st;
+    ChunkArgs ca;
+    ca.q = a.q;
+    ca.k = a.k;
+    ca.v = a.v;
+    ca.g = g;
+    ca.beta = beta;
+    ca.o = a.o;
+    ca.state = state;
+    ca.ws = (float*)ws;
+    ca.ldq = ldq;
+    ca.ldk = ldk;
+    ca.ldv = ldv;
+    ca.ldg = ldg;
+    ca.ldo = ldo;
+    ca.L = (int)L;
+    ca.Hv = (int)n_v_heads;
+    ca.grp = a.grp;
+    for (int64_t c0 = 0; c0 < chunks; c0 += win) {
+        const int64_t nc = chunks - c0 < win ? chunks - c0 : win;
+        ca.t_begin = (int)(c0 * CH);
+        ca.n_chunks = (int)nc;
+        hipLaunchKernelGGL(lut6_gdn_prep_kernel, dim3((unsigned)nc, (unsigned)n_v_heads), dim3(256), 0, stream, ca);
+        hipLaunchKernelGGL(lut6_gdn_chunk_kernel, dim3((unsigned)(n_v_heads * (DV / CB))), dim3(256), 0, stream, ca);
+        if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
+    }
+    return LUT6_OK;
 }

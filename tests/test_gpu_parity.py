@@ -609,7 +609,10 @@ def _gdn_check(ora, qkv, gl, be, s0, Hk, Hv, o_dev, s_dev):
     return rep, bool(np.all(s_err <= s_bound))
 
 
-GDN_SHAPES = [(1, 1, 1), (5, 2, 4), (63, 1, 2), (64, 2, 2), (65, 16, 32), (200, 16, 32), (1000, 4, 8)]
+# below 64 tokens the token-sequential kernel runs, from 64 the chunked one
+# (64-position chunks; ragged last chunks at 65, 129, 200 and 1,000)
+GDN_SHAPES = [(1, 1, 1), (5, 2, 4), (63, 1, 2), (64, 2, 2), (65, 16, 32), (128, 2, 4), (129, 1, 1),
+              (200, 16, 32), (1000, 4, 8)]
 
 
 @pytest.mark.parametrize("L,Hk,Hv", GDN_SHAPES)
@@ -618,6 +621,7 @@ def test_gated_delta(ora, L, Hk, Hv):
     qkv, gl, be, s0 = _gdn_problem(L, Hk, Hv, L + 31 * Hv)
     o, s = _gdn_run(qkv, gl, be, s0, Hk, Hv)
     (ok, bad, ratio), s_ok = _gdn_check(ora, qkv, gl, be, s0, Hk, Hv, o, s)
+    print(f"[case] gated delta L={L}: failures={bad} max err/bound={ratio:.3f} state ok={s_ok}", flush=True)
     assert ok and s_ok, (bad, ratio, s_ok)
 
 
@@ -639,10 +643,14 @@ def test_gated_delta_zero_state_and_unit_keys(ora):
     assert int(d_ulp.max()) <= 1
 
 
-def test_gated_delta_carried_state_is_exact():
-    # two calls with the state carried between them give the bits of one call
-    _say("gated delta carried state")
-    L, Hk, Hv, a = 333, 16, 32, 130
+@pytest.mark.parametrize("L,a", [(60, 23), (333, 128)])
+def test_gated_delta_carried_state_is_exact(L, a):
+    # two calls with the state carried between them give the bits of one
+    # call: on the token-sequential path at any split, on the chunked path
+    # when the split falls on a chunk boundary (the chunks are counted from
+    # each call's first token)
+    _say("gated delta carried state", L, a)
+    Hk, Hv = 16, 32
     qkv, gl, be, s0 = _gdn_problem(L, Hk, Hv, 9)
     o_all, s_all = _gdn_run(qkv, gl, be, s0, Hk, Hv)
     o1, s1 = _gdn_run(qkv[:a], gl[:a], be[:a], s0, Hk, Hv)
@@ -651,13 +659,29 @@ def test_gated_delta_carried_state_is_exact():
     assert np.array_equal(s2, s_all)
 
 
-def test_gated_delta_layer_full_size(ora):
+def test_gated_delta_carried_state_any_split(ora):
+    # a split off the chunk grid changes the evaluation order, not the
+    # result: both calls together meet the criteria of one
+    _say("gated delta carried state, unaligned split")
+    L, Hk, Hv, a = 333, 16, 32, 130
+    qkv, gl, be, s0 = _gdn_problem(L, Hk, Hv, 9)
+    o1, s1 = _gdn_run(qkv[:a], gl[:a], be[:a], s0, Hk, Hv)
+    o2, s2 = _gdn_run(qkv[a:], gl[a:], be[a:], s1, Hk, Hv)
+    (ok, bad, ratio), s_ok = _gdn_check(ora, qkv, gl, be, s0, Hk, Hv, np.concatenate([o1, o2]), s2)
+    assert ok and s_ok, (bad, ratio, s_ok)
+
+
+@pytest.mark.parametrize("L", [4096, 16384])
+def test_gated_delta_layer_full_size(ora, L):
     # one linear-attention layer's recurrence: 16 key and 32 value heads over
-    # a 4,096-token prefill chunk, q|k|v read in place from the projection
-    _say("gated delta full", 4096)
-    qkv, gl, be, s0 = _gdn_problem(4096, 16, 32, 17)
+    # a 4,096-token prefill chunk and over the whole 16,384-token context,
+    # q|k|v read in place from the projection; every output and the final
+    # state against the FP64 sequential rule
+    _say("gated delta full", L)
+    qkv, gl, be, s0 = _gdn_problem(L, 16, 32, 17)
     o, s = _gdn_run(qkv, gl, be, s0, 16, 32)
     (ok, bad, ratio), s_ok = _gdn_check(ora, qkv, gl, be, s0, 16, 32, o, s)
+    print(f"[case] gated delta L={L}: failures={bad} max err/bound={ratio:.3f} state ok={s_ok}", flush=True)
     assert ok and s_ok, (bad, ratio, s_ok)
 
 
