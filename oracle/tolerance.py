@@ -13,10 +13,14 @@ Criteria, fixed before any device run:
     (for short K and small tables that half ulp exceeds B_row), so for FP16
     outputs the allowance is B_row + ulp16(y_ref) / 2;
   * FP16 outputs: at most 1 unit in the last place from fp16(y_ref)
-    (distance between the ordered bit patterns, +0 == -0).  Where
-    |y_ref| < tau_row = 2^-10 * S_row (S_row = B_row / 2e-3, the natural
-    scale of the row) FP32 summation noise is larger than an FP16 ulp, so
-    the allowance there is the absolute ulp16(tau_row) instead;
+    (distance between the ordered bit patterns, +0 == -0).  Near zero the
+    FP16 ulp falls below the FP32 summation noise of any correct FP32-
+    accumulating kernel, so where |y_ref| < tau_row = 2^-8 * S_row
+    (S_row = B_row / 2e-3, the natural scale of the row) the allowance is
+    the absolute ulp16(tau_row) instead.  An FP32 sum of exact FP16
+    products, added 16 at a time, has errors up to about 2^-20.5 S_row on
+    the full-size workloads (K = 4,096 and 12,288, 262,144 outputs each):
+    up to 1.4 ulp16(2^-10 S_row), and 0.36 ulp16(2^-8 S_row);
   * SiLU(gate) * up: the bound propagates through h = silu(g) * u as
         B_h = (1.1 |u_ref| + |silu(g_ref)|) * B_row     (|silu'| <= 1.1)
     with the same ulp rule on S_h = B_h / 2e-3.
@@ -28,6 +32,7 @@ from dataclasses import dataclass
 import numpy as np
 
 REL = 2e-3
+TAU_REL = 2.0 ** -8                # the near-zero floor, as a fraction of S_row
 
 
 def row_scale(x16: np.ndarray, tables16: np.ndarray, K: int, rows=None) -> np.ndarray:
@@ -63,12 +68,13 @@ class Report:
     strict_ulp_violations: int       # beyond 1 ulp, counted without the floor (diagnostic)
     floor_cases: int
     failures: int
+    floor_max_ratio: float = 0.0     # largest |y - fp16(y_ref)| / ulp16(tau) in the floor (<= 1 passes)
 
     def __str__(self):
         return (f"ok={self.ok} n={self.n} max|err|={self.max_abs_err:.3g} "
                 f"max err/bound={self.max_err_over_bound:.3g} max_ulp={self.max_ulp} "
                 f"strict>1ulp={self.strict_ulp_violations} floor={self.floor_cases} "
-                f"failures={self.failures}")
+                f"floor max/allow={self.floor_max_ratio:.3g} failures={self.failures}")
 
 
 def check(y_dev: np.ndarray, y_exact: np.ndarray, S_row: np.ndarray, *, fp16: bool,
@@ -105,12 +111,14 @@ def check(y_dev: np.ndarray, y_exact: np.ndarray, S_row: np.ndarray, *, fp16: bo
             ref_bits = y_exact.astype(np.float16).view(np.uint16)
         d = np.abs(_ordered(bits) - _ordered(ref_bits))
         d = np.where(special, 0, d)
-        tau = 2.0 ** -10 * S
+        tau = TAU_REL * S
         floor = np.abs(y_exact) < tau
         ref16 = ref_bits.view(np.float16).astype(np.float64)
         with np.errstate(invalid="ignore"):
-            floor_ok = np.abs(val - ref16) <= ulp16(tau)
+            floor_dev = np.abs(val - ref16) / ulp16(tau)
+            floor_ok = floor_dev <= 1.0
         ulp_bad = np.where(floor, ~floor_ok, d > 1)
+        floor_max = float(np.max(floor_dev[floor])) if np.any(floor) else 0.0
         bad = bad | ulp_bad
         max_ulp = int(d[~floor].max()) if np.any(~floor) else 0
         strict = int(np.sum(d > 1))
@@ -119,7 +127,7 @@ def check(y_dev: np.ndarray, y_exact: np.ndarray, S_row: np.ndarray, *, fp16: bo
                   max_abs_err=float(np.max(err)) if err.size else 0.0,
                   max_err_over_bound=float(np.max(ratio)) if ratio.size else 0.0,
                   max_ulp=max_ulp, strict_ulp_violations=strict, floor_cases=floor_cases,
-                  failures=int(np.sum(bad)))
+                  failures=int(np.sum(bad)), floor_max_ratio=floor_max if fp16 else 0.0)
 
 
 def silu_scale(g_exact: np.ndarray, u_exact: np.ndarray, S_row: np.ndarray) -> np.ndarray:

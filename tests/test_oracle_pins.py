@@ -672,6 +672,41 @@ def test_seeded_inputs_are_reproducible():
 # rounding step or more beyond it does not
 # ---------------------------------------------------------------------------
 
+def test_floor_admits_fp32_accumulation(ora):
+    # an FP32-accumulating kernel (exact FP16 products, FP32 sums of 16 at a
+    # time in k order) meets the FP16 criterion, near-zero floor included,
+    # at the deepest K of the workloads (the down projection, K = 12,288,
+    # input scaled by 16); an FP16 output 3 floor allowances off fails
+    from oracle import tolerance as tol
+    L, K, N, s = 48, 12288, 256, 16.0
+    g = np.random.default_rng(21)
+    x = (g.standard_normal((L, K)) * 0.5).astype(np.float16)
+    idx = g.integers(0, 64, size=(N, K), dtype=np.uint8)
+    tab = np.sort((g.standard_normal((N // 16, 64)) * 0.02).astype(np.float16), axis=1)
+    packed = ora.pack(idx)
+    y, _ = ora.linear(x, packed, tab, epilogue=oracle.EPI_F32, in_scale=s)
+    y = np.asarray(y, np.float64)
+    W = ora.dequant(packed, tab, K).view(np.float16).astype(np.float64)
+    xs = (x.astype(np.float64) * s).astype(np.float16).astype(np.float64)
+    acc = np.zeros((L, N), np.float32)
+    for k0 in range(0, K, 16):
+        acc = (acc + (xs[:, k0:k0 + 16] @ W[:, k0:k0 + 16].T).astype(np.float32)).astype(np.float32)
+    y16 = (acc.astype(np.float64) / s).astype(np.float16)
+    S = tol.row_scale(x, tab, K)
+    rep = tol.check(y16, y, S, fp16=True)
+    assert rep.ok and rep.floor_cases > 0, str(rep)
+    # the FP32 error itself stays well inside the floor's allowance (the
+    # FP16 roundings of y and y_ref add at most one step of their own)
+    tau = tol.TAU_REL * S
+    err32 = np.abs(acc.astype(np.float64) / s - y)
+    assert float(np.max(err32 / tol.ulp16(tau)[:, None])) < 0.5
+    # one floor output moved 3 allowances away fails
+    i, j = np.argwhere(np.abs(y) < tau[:, None])[0]
+    bad = y16.copy()
+    bad[i, j] = np.float16(float(y16[i, j]) + 3 * tol.ulp16(tau[i]))
+    assert not tol.check(bad, y, S, fp16=True).ok
+
+
 def test_tolerance_accepts_rounded_oracle_and_rejects_drift(ora):
     from oracle import tolerance as tol
     # K = 64 and no table outliers: half an FP16 ulp of the largest outputs
