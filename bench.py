@@ -14,9 +14,9 @@ starts.  The line printed is throughput in TFLOP/s, with
     call over the call's average time (HIP events around the call on its
     stream, so for the many-token path the weight expansion and the GEMM
     together), against the FP16 dense MFMA peak (2,516.6 TFLOP/s); its HBM
-    traffic and the shader clock during it come from the rocprofv3 counter
-    summary in profiles/ when that summary was taken on the current kernel
-    source, else null;
+    traffic, the shader clock and the MFMA busy share during it come from the
+    rocprofv3 counter record in profiles/ (gemm_counters.py) when that record
+    was taken on the current kernel source, else null;
   * l128_stream: the L = 128 single projection (4,096 -> 4,096, FP32 out) in
     algorithmic HBM GB/s over back-to-back launches, rotating over enough
     weight sets that the 256 MB last-level cache cannot hold them;
@@ -63,9 +63,10 @@ STEP_WORKLOAD = "prefill_sweep_l16384"
 STREAM_WORKLOAD = "o_proj_l128"
 OTHER_WORKLOADS = ("mlp_gate_up_l512", "mlp_down_l1024", "hybrid_block_l4096", "hybrid_block_l4096_six")
 ROTATE_BYTES = 512 << 20           # at least twice the 256 MB last-level cache
-TRAFFIC_FILE = ROOT / "profiles" / "gemm_hbm_traffic.json"
+COUNTER_FILE = ROOT / "profiles" / "gemm_counters.json"
 KERNEL_SOURCES = [ROOT / "lut_weight_quantized_amd" / "csrc" / "lut6_linear.hip"]
-TRAFFIC_LAYERS = (0, 3)            # one Gated DeltaNet and one full-attention layer
+COUNTER_LAYERS = (0, 3)            # one Gated DeltaNet and one full-attention layer
+COUNTER_WORKLOADS = ("o_proj_l128", "mlp_gate_up_l512", "mlp_down_l1024")
 COPY_BYTES = 256 << 20             # calibration copy for the HBM byte counters
 
 
@@ -353,9 +354,10 @@ def main() -> int:
                          "parity sample and the CPU-oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-iters", type=int, default=200)
-    ap.add_argument("--traffic-run", action="store_true",
-                    help="launch the GEMMs of layers 0 and 3 once each, then a 256 MiB copy, "
-                         "and exit (the workload hbm_traffic.py runs under rocprofv3 --pmc)")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="launch the GEMMs of sweep layers 0 and 3 once each, then the L = 128, 512 "
+                         "and 1,024 workloads, then a 256 MiB copy, and exit (the workload "
+                         "gemm_counters.py runs under rocprofv3 --pmc)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -406,17 +408,29 @@ def main() -> int:
     plan = [(li, pi, g, acts[(g.K, g.x_tensor)], weights[li][pi], outs[(g.name, g.n_out)])
             for li, pi, g in w.gemms()]
 
-    if args.traffic_run:
+    if args.counter_run:
         # one launch per GEMM of layers 0 (Gated DeltaNet) and 3 (full attention),
-        # in that order, then the calibration copy: 256 MiB read, 256 MiB written
+        # in that order, then one of each smaller workload, then the calibration
+        # copy: 256 MiB read, 256 MiB written
         for li, pi, g, x, (p, t), y in plan:
-            if li in TRAFFIC_LAYERS:
+            if li in COUNTER_LAYERS:
                 lq.linear(x, p, t, epilogue=g.epilogue, in_scale=g.in_scale, out=y, stream=stream)
+        for name in COUNTER_WORKLOADS:
+            cw = si.WORKLOADS[name]
+            for li, pi, g in cw.gemms():
+                idx, tab = si.gemm_weight(cw.cfg, li, pi, g)
+                xs = torch.from_numpy(si.gemm_activation(cw.cfg, g)).to("cuda")
+                ys = torch.empty((g.L, g.n_out), device="cuda",
+                                 dtype=torch.float32 if g.epilogue == 0 else torch.float16)
+                pw, tw = torch.from_numpy(lq.pack(idx)).to("cuda"), torch.from_numpy(tab).to("cuda")
+                torch.cuda.synchronize()
+                lq.linear(xs, pw, tw, epilogue=g.epilogue, in_scale=g.in_scale, out=ys, stream=stream)
+                torch.cuda.synchronize()
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        log("traffic run done")
+        log("counter run done")
         return 0
 
     def step(events=None):
@@ -463,13 +477,15 @@ def main() -> int:
                     f"{v['flops'] / v['n'] / (v['ms'] / v['n'] * 1e-3) / 1e12:.1f} TFLOP/s"
                     for k, v in sorted(per.items())))
 
-    traffic = None
-    sclk = None
-    if TRAFFIC_FILE.exists():
-        rec = json.loads(TRAFFIC_FILE.read_text())
-        if rec.get("kernel_source_sha256") == kernel_source_sha() and rec.get("kernel_class") == dom_name:
-            traffic = rec.get("hbm_bytes_per_launch")
-            sclk = rec.get("sclk_ghz")
+    # counter record (gemm_counters.py), only while taken on this kernel source
+    counters = {}
+    if COUNTER_FILE.exists():
+        rec = json.loads(COUNTER_FILE.read_text())
+        if rec.get("kernel_source_sha256") == kernel_source_sha():
+            counters = rec.get("per_class", {})
+    dom_c = counters.get(dom_name, {})
+    traffic = dom_c.get("hbm_bytes_per_launch")
+    sclk = dom_c.get("sclk_ghz")
 
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
@@ -483,6 +499,10 @@ def main() -> int:
         # fraction of the dense peak at the clock the counter pass measured
         roofline["sclk_ghz"] = sclk
         roofline["frac_at_sclk"] = round(achieved / (PEAK_FP16_TFLOPS * sclk / 2.4), 4)
+    if dom_c:
+        roofline["mfma_busy_frac"] = dom_c.get("mfma_busy_frac")
+        roofline["mfma_f16_flops_per_launch_counted"] = dom_c.get("mfma_f16_flops_per_launch")
+        roofline["counters"] = "profiles/gemm_counters.json (rocprofv3 --pmc, this kernel source)"
 
     # ---------------- parity sample + CPU baseline (oracle) ----------------
     cpu = None
@@ -571,6 +591,10 @@ def main() -> int:
                   "algorithmic_bytes": sg.bytes, "weight_sets_rotated": sets,
                   "note": (f"median of 3 runs of {args.stream_iters} back-to-back launches; "
                            "spans each call's kernels and the gaps between calls")}
+    sc = counters.get(kernel_class(sg), {})
+    if sc:
+        stream_rec.update(traffic=sc.get("hbm_bytes_per_launch"), mfma_busy_frac=sc.get("mfma_busy_frac"),
+                          sclk_ghz=sc.get("sclk_ghz"))
     log(f"L=128 stream: {us_med:.2f} us, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
     del sets_w
 
@@ -583,6 +607,11 @@ def main() -> int:
     per_config = []
     for name in OTHER_WORKLOADS:
         rec = time_workload(lq, si, torch, stream, name)
+        if name in COUNTER_WORKLOADS:
+            gc = counters.get(kernel_class(si.WORKLOADS[name].layers[0][0]), {})
+            if gc:
+                rec.update(traffic=gc.get("hbm_bytes_per_launch"), mfma_busy_frac=gc.get("mfma_busy_frac"),
+                           sclk_ghz=gc.get("sclk_ghz"))
         per_config.append(rec)
         log(f"{name}: {rec['us_per_pass']:.1f} us, {rec['tflop_s']:.0f} TFLOP/s "
             f"({rec['frac_fp16_peak']:.1%} of FP16 peak)")

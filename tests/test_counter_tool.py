@@ -1,12 +1,13 @@
-"""Host logic of the counter post-processing (no GPU): kernel classes, the
-per-dispatch sums of a counter file, and the clock from GRBM_GUI_ACTIVE."""
+"""Host logic of the counter post-processing in gemm_counters.py (no GPU):
+kernel classes, per-dispatch reductions of a counter file, the clock from
+GRBM_GUI_ACTIVE and the grouping of dispatches into launches."""
 from __future__ import annotations
 
 import csv
 
 import pytest
 
-from lut_weight_quantized_amd import hbm_traffic as ht
+import gemm_counters as ht
 
 COLS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
         "Start_Timestamp", "End_Timestamp"]
@@ -42,7 +43,8 @@ def test_per_dispatch_sums_instances(tmp_path):
 
 
 def test_per_dispatch_clock(tmp_path):
-    # 8 XCDs each busy for 1,000 ns at 1.5 GHz: 8 * 1,500 cycles over 1,000 ns
+    # GRBM_GUI_ACTIVE summed over the 8 XCDs, as one row per XCD or as one
+    # aggregated row: 8 XCDs at 1.5 GHz for 1,000 ns, 8 x 2,400 cycles in 1,000 ns
     p = tmp_path / "g.csv"
     rows = [(1, 7, "gemm", "GRBM_GUI_ACTIVE", 1500.0, 1000, 2000) for _ in range(8)]
     rows.append((2, 8, "copy", "GRBM_GUI_ACTIVE", 8 * 2400.0, 0, 1000))
@@ -51,3 +53,12 @@ def test_per_dispatch_clock(tmp_path):
     assert [n for n, _ in got] == ["gemm", "copy"]
     assert got[0][1] == pytest.approx(1.5)
     assert got[1][1] == pytest.approx(2.4)
+
+
+def test_group_launches():
+    # an expanded launch is expansion + GEMM, a split one GEMM + reduction;
+    # other kernels (copies, torch's) are not part of any launch
+    names = ["at::fill", "lut6_expand_kernel<0>", "lut6_expanded_gemm_kernel<1, false, false>",
+             "lut6_stream_kernel<0, false, false, true>", "lut6_tile256_kernel<1, true, true>",
+             "lut6_reduce_kernel<1>", "__amd_rocclr_copyBuffer"]
+    assert ht.group_launches(names) == [[1, 2], [3], [4, 5]]
