@@ -300,6 +300,9 @@ __device__ __forceinline__ void tile_store_partial(const GemmArgs& a, const f32x
     float* const plane = a.partial + (size_t)ks * L * N;
 #pragma unroll
     for (int p = 0; p < NJ / JP; ++p) {
+        // one pass at a time: hoisting every pass's accumulator reads would
+        // take nearly every register
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int jj = 0; jj < JP; ++jj) {
             const int j = JP * p + jj;
@@ -359,9 +362,20 @@ __device__ __forceinline__ void tile_store_rows(const GemmArgs& a, const f32x16 
     const int n0 = EPI == 2 ? tn * 128 + 32 * w : tn * 256 + 64 * w;
 #pragma unroll
     for (int p = 0; p < NJ / JP; ++p) {
+        // one pass at a time: the pass's fragments are taken out of the
+        // accumulator registers here (the empty asm pins them there until
+        // now), so the reads of every pass are not hoisted together, which
+        // would take nearly every register
+        f32x16 fr[2][JP];
+#pragma unroll
+        for (int jj = 0; jj < JP; ++jj)
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                fr[f][jj] = acc[f][JP * p + jj];
+                asm volatile("" : "+a"(fr[f][jj]));
+            }
 #pragma unroll
         for (int jj = 0; jj < JP; ++jj) {
-            const int j = JP * p + jj;
             uint8_t* const row = wl + (32 * jj + r32) * PITCH;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -369,15 +383,15 @@ __device__ __forceinline__ void tile_store_rows(const GemmArgs& a, const f32x16 
                     f16x4 hv;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float gv = acc[0][j][4 * q + e] * a.inv_scale;
-                        const float uv = acc[1][j][4 * q + e] * a.inv_scale;
+                        const float gv = fr[0][jj][4 * q + e] * a.inv_scale;
+                        const float uv = fr[1][jj][4 * q + e] * a.inv_scale;
                         hv[e] = (_Float16)(silu_f32(gv) * uv);
                     }
                     *(f16x4*)(row + (8 * q + 4 * h) * 2) = hv;
                 } else {
 #pragma unroll
                     for (int f = 0; f < 2; ++f) {
-                        f32x4 v = {acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2], acc[f][j][4 * q + 3]};
+                        f32x4 v = {fr[f][jj][4 * q], fr[f][jj][4 * q + 1], fr[f][jj][4 * q + 2], fr[f][jj][4 * q + 3]};
                         v *= a.inv_scale;
                         const int col = 32 * f + 8 * q + 4 * h;
                         if constexpr (EPI == 0) {
@@ -747,58 +761,76 @@ template <int EPI, bool SCALED, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
 lut6_expanded_gemm_kernel(GemmArgs a)
 {
-    // three activation stages (tables are not needed here)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[T2_NSTAGE * T2_XBYTES];
+    // Persistent: workgroup g computes tiles g, g + G, g + 2G, ... (G =
+    // gridDim.x); tile v is (K slice v / n_tiles, channel x token tile
+    // xcd_remap(v % n_tiles)), so with G a multiple of 8 each workgroup stays
+    // on the tiles its XCD would have run and the tiles in flight at one time
+    // are the same sets as with one workgroup per tile.  Three activation
+    // stages; FP16 and SiLU outputs are staged for the epilogue in a region
+    // of their own, so the next tile's first two chunks are in flight while
+    // this tile's outputs are written (FP32 outputs and split partials stage
+    // in the pipeline region, after which the next tile's loads are issued).
+    constexpr bool OWN_EPI = !SPLIT && EPI != 0;
+    constexpr int EPI_BYTES = OWN_EPI ? 4 * 64 * ((EPI == 2 ? 64 : 128) + 16) : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[T2_NSTAGE * T2_XBYTES + EPI_BYTES];
+    uint8_t* const epi_lds = OWN_EPI ? lds + T2_NSTAGE * T2_XBYTES : lds;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, h = lane >> 5;
     const int K = a.K, N = a.N, L = a.L;
-
-    // tile order as in the large-tile kernel
+    const int chunks = K / BK;
+    const int splits = (chunks + a.k_chunks_per_split - 1) / a.k_chunks_per_split;
+    const int total = a.n_tiles * splits;
     const int tiles_n = a.n_tiles / a.tiles_m;
-    const int t = xcd_remap(blockIdx.x, a.n_tiles);
-    const int group = t / (T2_GROUP_M * tiles_n);
-    const int first_m = group * T2_GROUP_M;
-    const int gm = min(a.tiles_m - first_m, T2_GROUP_M);
-    const int within = t - group * T2_GROUP_M * tiles_n;
-    const int tm = first_m + within % gm, tn = within / gm;
-    const int m0 = tm * T2;
-    const int kc_begin = blockIdx.y * a.k_chunks_per_split;
-    const int kc_end = min(K / BK, kc_begin + a.k_chunks_per_split);
 
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.x, (short)0, (int)((size_t)L * K * 2), RAW_BUFFER_WORD3);
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)a.w16, (short)0, (int)((size_t)tiles_n * 8 * (K / BK + 1) * 4096), RAW_BUFFER_WORD3);
+        (void*)a.w16, (short)0, (int)((size_t)tiles_n * 8 * (chunks + 1) * 4096), RAW_BUFFER_WORD3);
+    const int bstride = (chunks + 1) * 4096;   // one fragment block (see lut6_expand_kernel)
 
-    // activation copies: instruction i of wave w fills rows 32i + 8w .. +8 of
-    // the tile (slot lane & 7 of row 32i + 8w + lane / 8)
-    const int xrow = 8 * wave + (lane >> 3);
-    const int xchunk = (lane & 7) ^ ((xrow >> 1) & 7);
-    int xgoff[8];
+    // per tile: first token, channel tile, K slice and its chunks (uniform)
+    int m0, tn, ks, kc_begin, kc_end, last;
+    auto set_tile = [&](int v) {
+        ks = v / a.n_tiles;
+        const int t = xcd_remap(v - ks * a.n_tiles, a.n_tiles);
+        const int group = t / (T2_GROUP_M * tiles_n);
+        const int first_m = group * T2_GROUP_M;
+        const int gm = min(a.tiles_m - first_m, T2_GROUP_M);
+        const int within = t - group * T2_GROUP_M * tiles_n;
+        m0 = (first_m + within % gm) * T2;
+        tn = within / gm;
+        kc_begin = ks * a.k_chunks_per_split;
+        kc_end = min(chunks, kc_begin + a.k_chunks_per_split);
+        last = kc_end - 1;
+    };
+    // per lane: global offsets of the copies and A-fragment loads, and the
+    // B-fragment offsets inside a stage.  Recomputed from an opaque copy of
+    // the lane id whenever needed, so that none of them stays live through
+    // an epilogue (whose accumulator reads need nearly every register).
+    //  - activation copies: instruction i of wave w fills rows 32i + 8w .. +8
+    //    of the tile (slot lane & 7 of row 32i + 8w + lane / 8);
+    //  - A fragments come straight from the expanded weight, stored in
+    //    fragment order by lut6_expand_kernel: fragment (tile tn, wave w,
+    //    fragment f, chunk kc, step s) is 1 KB, 16 bytes per lane in lane
+    //    order, so each load is contiguous;
+    //  - B fragments: token r32 of each 32-token block, pieces 4h + s.
+    int xgoff[8], wgoff[2], xoff[4];
+    auto set_lane_offsets = [&]() {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int xrow = 8 * wave + (ln >> 3);
+        const int xchunk = (ln & 7) ^ ((xrow >> 1) & 7);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xgoff[i] = min(m0 + 32 * i + xrow, L - 1) * (K * 2) + xchunk * 16;
-    // A fragments straight from the expanded weight, which is stored in
-    // fragment order (lut6_expand_kernel): fragment (tile tn, wave w,
-    // fragment f, chunk kc, step s) is 1 KB, 16 bytes per lane in lane
-    // order, so each load is contiguous
-    const int bstride = (K / BK + 1) * 4096;   // one fragment block (see lut6_expand_kernel)
-    int wgoff[2];
+        for (int i = 0; i < 8; ++i) xgoff[i] = min(m0 + 32 * i + xrow, L - 1) * (K * 2) + xchunk * 16;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) wgoff[f] = ((tn * 4 + wave) * 2 + f) * bstride + lane * 16;
-    // B-fragment offsets inside a stage per step (token r32 of each block)
-    int xoff[4];
+        for (int f = 0; f < 2; ++f) wgoff[f] = ((tn * 4 + wave) * 2 + f) * bstride + ln * 16;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xoff[s] = xswz(r32, 4 * h + s);
+        for (int s = 0; s < 4; ++s) xoff[s] = xswz(ln & 31, 4 * (ln >> 5) + s);
+    };
 
     f32x16 acc[2][8];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
     // B fragments by step parity; A fragments of three tiles (tile
     // kc_begin + i in set i % 3), [step][fragment]
     f16x8 X[2][8];
@@ -818,6 +850,18 @@ lut6_expanded_gemm_kernel(GemmArgs a)
                     f16x8, __builtin_amdgcn_raw_buffer_load_b128(wr, wgoff[f] + 1024 * s, kc * 4096, 0));
     };
     auto read_x = [&](int so, int s, int j) -> f16x8 { return *(const f16x8*)(lds + so + xoff[s] + j * 4096); };
+    // activations (into LDS) and A fragments (into registers) of the tile's
+    // first two chunks in flight
+    auto prologue_x = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) issue_x(0, kc_begin, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) issue_x(1, min(kc_begin + 1, last), i);
+    };
+    auto prologue_w = [&]() {
+        load_w(std::integral_constant<int, 0>{}, kc_begin);
+        load_w(std::integral_constant<int, 1>{}, min(kc_begin + 1, last));
+    };
 
 #define E_MMA(P, WS, S, J)                                                             \
     do {                                                                               \
@@ -862,32 +906,17 @@ lut6_expanded_gemm_kernel(GemmArgs a)
         __builtin_amdgcn_sched_barrier(0);                                             \
     } while (0)
 
-    // prologue: activations and A fragments of the first two tiles in
-    // flight, the first tile's step-0 B fragments in registers
-    const int last = kc_end - 1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) issue_x(0, kc_begin, i);
-    load_w(std::integral_constant<int, 0>{}, kc_begin);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) issue_x(1, min(kc_begin + 1, last), i);
-    load_w(std::integral_constant<int, 1>{}, min(kc_begin + 1, last));
-    // wait for the first tile's copies (tile 2's and the A fragments, issued
-    // after them, may still be in flight)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) X[0][j] = read_x(0, 0, j);
-
-    // One tile: tile kc in stage ST, its A fragments in set ST (constants).
-    // Step 0 loads the A fragments of tile kc + 2 into set (ST + 2) % 3,
-    // which tile kc - 1 used.  The barrier before step 3: every load of this
-    // wave is complete (the copies of tile kc + 1, issued a tile ago, and the
-    // A fragments of tile kc + 2), so after the barrier all of tile kc + 1 is
-    // in LDS; and every wave has read its step-3 operands of stage ST, so the
-    // copies of tile kc + 2 can go to stage (ST + 2) % 3.  The wait is for
-    // every outstanding load, not for all but the youngest: register loads
-    // issued after copies into LDS can complete before them (waiting for all
-    // but the eight youngest let the barrier pass early on cold data).
+    // One 64-k chunk: chunk kc in stage ST, its A fragments in set ST
+    // (constants).  Step 0 loads the A fragments of chunk kc + 2 into set
+    // (ST + 2) % 3, which chunk kc - 1 used.  The barrier before step 3: every
+    // load of this wave is complete (the copies of chunk kc + 1, issued a
+    // chunk ago, and the A fragments of chunk kc + 2), so after the barrier
+    // all of chunk kc + 1 is in LDS; and every wave has read its step-3
+    // operands of stage ST, so the copies of chunk kc + 2 can go to stage
+    // (ST + 2) % 3.  The wait is for every outstanding load, not for all but
+    // the youngest: register loads issued after copies into LDS can complete
+    // before them (waiting for all but the eight youngest let the barrier pass
+    // early on cold data).
     auto tile_step = [&](auto st_c, int kc) {
         constexpr int ST = decltype(st_c)::value;
         constexpr int S1 = (ST + 1) % T2_NSTAGE, S2 = (ST + 2) % T2_NSTAGE;
@@ -914,28 +943,77 @@ lut6_expanded_gemm_kernel(GemmArgs a)
         E_PAIR_ISSUE(1, ST, 3, sn, 0, 6, S2, kn);
         E_PAIR_ISSUE(1, ST, 3, sn, 0, 7, S2, kn);
     };
-    int kc = kc_begin;
-    for (; kc + T2_NSTAGE <= kc_end; kc += T2_NSTAGE) {
-        tile_step(std::integral_constant<int, 0>{}, kc);
-        tile_step(std::integral_constant<int, 1>{}, kc + 1);
-        tile_step(std::integral_constant<int, 2>{}, kc + 2);
+
+    int v = blockIdx.x;
+    set_tile(v);
+    set_lane_offsets();
+    prologue_x();
+    prologue_w();
+    for (;;) {
+        // wait for the tile's first copies (the second chunk's and the A
+        // fragments may still be in flight; on later tiles also the previous
+        // epilogue's stores)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) X[0][j] = read_x(0, 0, j);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[f][j][e] = 0.f;
+
+        int kc = kc_begin;
+        for (; kc + T2_NSTAGE <= kc_end; kc += T2_NSTAGE) {
+            tile_step(std::integral_constant<int, 0>{}, kc);
+            tile_step(std::integral_constant<int, 1>{}, kc + 1);
+            tile_step(std::integral_constant<int, 2>{}, kc + 2);
+        }
+        if (kc < kc_end) tile_step(std::integral_constant<int, 0>{}, kc);
+        if (kc + 1 < kc_end) tile_step(std::integral_constant<int, 1>{}, kc + 1);
+        // every copy and load of this tile has landed, and after the barrier
+        // every wave is done reading the stages
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+
+        const int t_m0 = m0, t_tn = tn, t_ks = ks;
+        const int vn = v + (int)gridDim.x;
+        const bool more = vn < total;
+        if constexpr (OWN_EPI) {
+            // the next tile's copies go out first (they need no registers
+            // while the accumulators are stored), its A fragments after
+            if (more) {
+                set_tile(vn);
+                set_lane_offsets();
+                prologue_x();
+            }
+            tile_store_rows<EPI, 8, 2>(a, acc, t_m0, t_tn, wave, wave, lane, epi_lds);
+            if (more) {
+                set_lane_offsets();
+                prologue_w();
+            }
+        } else {
+            if constexpr (SPLIT)
+                tile_store_partial<EPI, 8, 2>(a, acc, t_m0, t_tn, wave, lane, lds, t_ks);
+            else
+                tile_store_rows<EPI, 8, 2>(a, acc, t_m0, t_tn, wave, wave, lane, lds);
+            if (more) {
+                __syncthreads();          // the staging reads are done
+                set_tile(vn);
+                set_lane_offsets();
+                prologue_x();
+                prologue_w();
+            }
+        }
+        if (!more) break;
+        v = vn;
     }
-    if (kc < kc_end) tile_step(std::integral_constant<int, 0>{}, kc);
-    if (kc + 1 < kc_end) tile_step(std::integral_constant<int, 1>{}, kc + 1);
 #undef E_PAIR_ISSUE
 #undef E_PAIR_LOADW
 #undef E_STEP
 #undef E_PAIR
 #undef E_MMA
-    __builtin_amdgcn_s_waitcnt(0);
-
-    if constexpr (SPLIT) {
-        __syncthreads();
-        tile_store_partial<EPI, 8, 2>(a, acc, m0, tn, wave, lane, lds, blockIdx.y);
-    } else {
-        __syncthreads();
-        tile_store_rows<EPI, 8, 2>(a, acc, m0, tn, wave, wave, lane, lds);
-    }
 }
 
 // Weight expansion for the two-pass path, written in the order the GEMM
@@ -1831,13 +1909,20 @@ int launch_reduce(const GemmArgs& a, int epi, int splits, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
 }
 
-// Launch the 256 x 256 tile kernel, fused or on the expanded weight.
+// Workgroups of the persistent expanded GEMM: one per CU (a multiple of the
+// 8 XCDs, so each workgroup keeps its XCD's tiles).
+constexpr int PERSIST_WGS = 256;
+
+// Launch the 256 x 256 tile kernel, fused (grid: tiles x K slices) or on the
+// expanded weight (persistent: at most PERSIST_WGS workgroups walk the tiles).
 template <bool SPLIT>
 void launch_tiles_t(const GemmArgs& a, bool two_pass, int epilogue, bool scaled, dim3 grid, hipStream_t stream)
 {
     const dim3 block(256);
     const int sel = epilogue * 2 + (scaled ? 1 : 0);
     if (two_pass) {
+        const int64_t total = (int64_t)grid.x * grid.y;
+        grid = dim3((unsigned)(total < PERSIST_WGS ? total : PERSIST_WGS));
         switch (sel) {
         case 0: hipLaunchKernelGGL((lut6_expanded_gemm_kernel<0, false, SPLIT>), grid, block, 0, stream, a); break;
         case 1: hipLaunchKernelGGL((lut6_expanded_gemm_kernel<0, true, SPLIT>), grid, block, 0, stream, a); break;
