@@ -184,6 +184,7 @@ constexpr int CH = 64;                            // positions per chunk
 constexpr int CB = 16;                            // state columns per recurrence workgroup
 constexpr int WS_T = 0, WS_P = CH * CH;           // workspace layout per (head, chunk), floats
 constexpr int WS_GAMMA = 2 * CH * CH, WS_ETA = WS_GAMMA + CH, WS_BETA = WS_ETA + CH;
+constexpr int WS_PAD = WS_BETA + CH;              // 256 bytes never read
 constexpr int WS_FLOATS = 2 * CH * CH + 4 * CH;   // T, P, gamma, eta, beta, pad
 constexpr int WS_GDN = 3;                         // library workspace kind
 constexpr int64_t MAX_WINDOW_CHUNKS = 128;        // chunks per prep + recurrence launch pair
@@ -325,15 +326,19 @@ __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
 }
 
 // The recurrence over the chunks of a window: one workgroup per (value head,
-// 16 state columns); wave w owns state rows 32 w .. 32 w + 31.  A chunk's
-// operands (k or q rows, v, rows of T and P, the decay vectors) are loaded
-// into registers while the chunk before it is computed.
+// 16 state columns).  Per chunk every wave takes one 16-row tile of each
+// product and two of the state: K S0 and Q S0 rows 16 w .. 16 w + 15, then
+// its tile of R = beta (v - gamma K S0), D = T R, the state rows 32 w ..
+// 32 w + 31 and the output rows 16 w .. 16 w + 15, so the four waves carry
+// equal work between the three barriers.  A chunk's operands (its k and q
+// rows, v, rows of T and P, the decay vectors) are loaded into registers
+// while the chunk before it is computed.
 __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
 {
     __shared__ __attribute__((aligned(16))) float st[CB][DK + 4];     // S^T of the block
     __shared__ __attribute__((aligned(16))) float ks[CH][DK + 16];    // k rows of the chunk
-    __shared__ float rs[CH][CB + 1];                                  // R = beta (v - gamma K S)
-    __shared__ float ds[CH][CB + 1];                                  // D
+    __shared__ float rs[CH][CB + 4];                                  // R = beta (v - gamma K S)
+    __shared__ float ds[CH][CB + 4];                                  // D
     __shared__ float dh[CH][CB];                                      // eta D
     __shared__ float vec[2][3][CH];                                   // gamma, eta, beta (two chunks)
 
@@ -345,10 +350,10 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
     const int col0 = h * DV + jb * CB;
     float* const sp = a.state + (size_t)h * DK * DV + jb * CB;
     const float rsq = 0.08838834764831845f;           // 1 / sqrt(128)
-    const bool isq = w >= 2;
-    const uint16_t* const src = (isq ? a.q : a.k) + (size_t)kq * DK + 32 * hi;
-    const int64_t ld = isq ? a.ldq : a.ldk;
-    const float* const wsh = a.ws + (size_t)h * a.n_chunks * WS_FLOATS;
+    const uint16_t* const ksrc = a.k + (size_t)kq * DK + 8 * hi;
+    const uint16_t* const qsrc = a.q + (size_t)kq * DK + 8 * hi;
+    float* const wsh = a.ws + (size_t)h * a.n_chunks * WS_FLOATS;
+    const int trow = 16 * w + lo;                     // this lane's A-operand row of the tiles
 
     // S^T tiles r = 2w, 2w + 1: lane holds S[16 r + lo][4 hi + e]
     f32x4 sacc[2];
@@ -362,44 +367,62 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         }
     }
 
-    // one chunk's register operands: k rows (waves 0, 1) or q rows (2, 3)
-    // 32 w' .. 32 w' + 31 (k = 32 hi ..), the wave's T rows, P rows (waves
-    // 2, 3), v (waves 0, 1) and one decay-vector entry (threads < 192)
+    // one chunk's register operands: the lane's k and q row pieces (row
+    // trow, k = 32 z + 8 hi + i), its T and P row pieces (columns 16 z +
+    // 4 hi + j), v of its R rows (16 w + 4 hi + e) and one decay-vector entry
+    // (threads < 192).  In each load the four lane groups hi = 0..3 of a row
+    // read 64 contiguous bytes, so one instruction touches 16 row segments.
     struct Ops {
-        u32x4 xr[2][4];
-        f32x4 tv[4];
-        f32x4 pv[2][4];
-        uint32_t vr[2][4];
+        u32x4 kr[4], qr[4];
+        f32x4 tv[4], pv[4];
+        uint32_t vr[4];
         float vc;
     };
+    // Every load is unconditional (rows past L re-read row L - 1): with
+    // loads under branches the compiler cannot count the ones in flight, and
+    // its wait for this chunk's operands then also waited for the next
+    // chunk's, a full memory latency per chunk.  Rows past L are zeroed
+    // where the chunk is consumed, not here: any arithmetic on a loaded
+    // register makes the wave wait for that load in the iteration that
+    // issued it.
     auto load_ops = [&](int c, Ops& op) {
         const int t0 = a.t_begin + c * CH;
         const float* const wsc = wsh + (size_t)c * WS_FLOATS;
+        const size_t tr = (size_t)min(t0 + trow, a.L - 1);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tg = t0 + 16 * (2 * (w & 1) + u) + lo;
-#pragma unroll
-            for (int z = 0; z < 4; ++z)
-                op.xr[u][z] = tg < a.L ? *(const u32x4*)(src + (size_t)tg * ld + 8 * z) : u32x4{0u, 0u, 0u, 0u};
+        for (int z = 0; z < 4; ++z) {
+            op.kr[z] = *(const u32x4*)(ksrc + tr * a.ldk + 32 * z);
+            op.qr[z] = *(const u32x4*)(qsrc + tr * a.ldq + 32 * z);
         }
 #pragma unroll
-        for (int z = 0; z < 4; ++z) op.tv[z] = *(const f32x4*)(wsc + WS_T + (16 * w + lo) * CH + 16 * hi + 4 * z);
-        if (isq) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int z = 0; z < 4; ++z)
-                    op.pv[u][z] = *(const f32x4*)(wsc + WS_P + (16 * (2 * (w - 2) + u) + lo) * CH + 16 * hi + 4 * z);
-        } else {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tg = t0 + 16 * (2 * w + u) + 4 * hi + e;
-                    op.vr[u][e] = tg < a.L ? a.v[(size_t)tg * a.ldv + col0 + lo] : 0u;
-                }
+        for (int z = 0; z < 4; ++z) {
+            op.tv[z] = *(const f32x4*)(wsc + WS_T + trow * CH + 16 * z + 4 * hi);
+            op.pv[z] = *(const f32x4*)(wsc + WS_P + trow * CH + 16 * z + 4 * hi);
         }
-        op.vc = tid < 3 * CH ? wsc[WS_GAMMA + tid] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            op.vr[e] = a.v[(size_t)min(t0 + 16 * w + 4 * hi + e, a.L - 1) * a.ldv + col0 + lo];
+        op.vc = wsc[WS_GAMMA + (tid < 3 * CH ? tid : 0)];
+    };
+
+    // A chunk's outputs are stored during the next chunk, after its loads:
+    // stores count in the same in-order counter as loads, so stores issued
+    // just before the barrier made the wait for the next operands also wait
+    // for the write acknowledgements.  Like the loads, the stores are
+    // unconditional: rows past L, and the empty store of chunk 0, go to the
+    // unused pad of a workspace block.
+    uint16_t ob[4] = {0, 0, 0, 0};
+    auto store_o = [&](int cc, bool real) {
+        const int t0c = a.t_begin + cc * CH;
+        uint16_t* const pad = (uint16_t*)(wsh + (size_t)cc * WS_FLOATS + WS_PAD) + lane;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tg = t0c + 16 * w + 4 * hi + e;
+            // both addresses are formed first so that the choice is a select,
+            // not a branch around the multiply
+            uint16_t* const row = a.o + (size_t)min(tg, a.L - 1) * a.ldo + col0 + lo;
+            *(real && tg < a.L ? row : pad) = ob[e];
+        }
     };
 
     Ops cur;
@@ -411,55 +434,63 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         const int t0 = a.t_begin + c * CH, b = c & 1;
         Ops nxt;
         load_ops(c + 1 < a.n_chunks ? c + 1 : c, nxt);
+        store_o(c > 0 ? c - 1 : 0, c > 0);
 
-        // stage 1: X = [K; Q] S0, rows 32 w .. 32 w + 31 (k rows for waves
-        // 0, 1, q rows for 2, 3); contraction index k = 32 hi + m
-        f32x4 x[2];
+        // stage 1: rows 16 w .. 16 w + 15 of K S0 and Q S0 (step n takes
+        // k = 32 (n / 8) + 8 hi + n % 8), the k row to LDS for the state
+        // update, R to LDS
+        f32x4 xk, xq;
         {
-            float af[2][32];
+            float kf[32], qf[32];
+            const uint32_t km = t0 + trow < a.L ? 0xffffffffu : 0u;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int z = 0; z < 4; ++z)
 #pragma unroll
-                for (int z = 0; z < 4; ++z)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) af[u][8 * z + i] = half_at(cur.xr[u][z], i);
-            x[0] = x[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int i = 0; i < 8; ++i) {
+                    kf[8 * z + i] = half_at(cur.kr[z] & km, i);
+                    qf[8 * z + i] = half_at(cur.qr[z] & km, i);
+                }
+            xk = xq = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int m4 = 0; m4 < 8; ++m4) {
-                const f32x4 bv = *(const f32x4*)&st[lo][32 * hi + 4 * m4];
+                const f32x4 bv = *(const f32x4*)&st[lo][32 * (m4 >> 1) + 8 * hi + 4 * (m4 & 1)];
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm)
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        x[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][4 * m4 + mm], bv[mm], x[u], 0, 0, 0);
-            }
-            if (!isq) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int t = 16 * (2 * w + u) + lo;
-#pragma unroll
-                    for (int z = 0; z < 8; ++z)
-                        *(f32x4*)&ks[t][32 * hi + 4 * z] =
-                            f32x4{af[u][4 * z], af[u][4 * z + 1], af[u][4 * z + 2], af[u][4 * z + 3]};
+                for (int mm = 0; mm < 4; ++mm) {
+                    xk = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[4 * m4 + mm], bv[mm], xk, 0, 0, 0);
+                    xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * m4 + mm], bv[mm], xq, 0, 0, 0);
                 }
+            }
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+            for (int z = 0; z < 8; ++z)
+                *(f32x4*)&ks[trow][32 * (z >> 1) + 8 * hi + 4 * (z & 1)] =
+                    f32x4{kf[4 * z], kf[4 * z + 1], kf[4 * z + 2], kf[4 * z + 3]};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * (2 * w + u) + 4 * hi + e;
-                        const float vv = (float)__builtin_bit_cast(_Float16, (uint16_t)cur.vr[u][e]);
-                        rs[t][lo] = vec[b][2][t] * (vv - vec[b][0][t] * x[u][e]);
-                    }
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * w + 4 * hi + e;
+                const uint16_t vb = t0 + t < a.L ? (uint16_t)cur.vr[e] : (uint16_t)0;
+                const float vv = (float)__builtin_bit_cast(_Float16, vb);
+                rs[t][lo] = vec[b][2][t] * (vv - vec[b][0][t] * xk[e]);
+            }
+            // pace the next chunk's 16 row loads (k, q, T, P) one per four
+            // of the 64 matrix instructions: issued back to back they fill
+            // the vector memory path, and the in-order wave then stalls at
+            // each further load while its matrix work waits behind it
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
         }
         __syncthreads();
 
-        // stage 2: D rows 16 w .. 16 w + 15 = T R (contraction s = 16 hi + m)
+        // stage 2: D rows 16 w .. 16 w + 15 = T R (step m takes s = 16 (m / 4)
+        // + 4 hi + m % 4; rows of R 4 apart sit 16 banks apart)
         {
             f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int m = 0; m < 16; ++m)
-                d = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.tv[m >> 2][m & 3], rs[16 * hi + m][lo], d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.tv[m >> 2][m & 3], rs[16 * (m >> 2) + 4 * hi + (m & 3)][lo], d,
+                                                         0, 0, 0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * w + 4 * hi + e;
@@ -469,30 +500,9 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         }
         __syncthreads();
 
-        // stage 3a (waves 2, 3): O = (gamma Q S0 + P D) / sqrt(128), rows
-        // 32 (w - 2) .. + 31; the Q S0 rows are this wave's stage-1 tiles
-        if (isq) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int r = 2 * (w - 2) + u;
-                f32x4 acc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = vec[b][0][16 * r + 4 * hi + e] * x[u][e];
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pv[u][m >> 2][m & 3], ds[16 * hi + m][lo], acc,
-                                                               0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tg = t0 + 16 * r + 4 * hi + e;
-                    if (tg < a.L)
-                        a.o[(size_t)tg * a.ldo + col0 + lo] = __builtin_bit_cast(uint16_t, (_Float16)(acc[e] * rsq));
-                }
-            }
-        }
-
-        // stage 3b: S^T = gamma_63 S0^T + (eta D)^T K for the wave's rows
-        // (contraction s = 4 m + hi)
+        // stage 3: the state rows 32 w .. 32 w + 31, S^T = gamma_63 S0^T +
+        // (eta D)^T K (contraction s = 4 m + hi); then the output rows
+        // 16 w .. 16 w + 15, O = (gamma Q S0 + P D) / sqrt(128)
         {
             const float gt = vec[b][0][CH - 1];
 #pragma unroll
@@ -508,6 +518,15 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) st[4 * hi + e][16 * r + lo] = acc[e];
             }
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = vec[b][0][16 * w + 4 * hi + e] * xq[e];
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                o = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pv[m >> 2][m & 3], ds[16 * (m >> 2) + 4 * hi + (m & 3)][lo], o,
+                                                         0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ob[e] = __builtin_bit_cast(uint16_t, (_Float16)(o[e] * rsq));
         }
         // the next chunk's decay vectors (that buffer was last read before
         // the previous barrier)
@@ -515,6 +534,7 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         __syncthreads();
         cur = nxt;
     }
+    store_o(a.n_chunks - 1, true);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = 16 * (2 * w + u) + lo;
