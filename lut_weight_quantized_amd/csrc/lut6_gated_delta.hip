@@ -222,8 +222,22 @@ __device__ __forceinline__ float half_at(const u32x4& w, int i)
 // One (chunk, value head): T = (I + A)^-1, P and the decay vectors.
 __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t kh[CH][DK + 8];   // k rows, FP16
-    __shared__ __attribute__((aligned(16))) uint16_t qh[CH][DK + 8];   // q rows, FP16
+    // the k and q rows (FP16) while K K^T and Q K^T are formed, then T and
+    // per-wave block products
+    __shared__ __attribute__((aligned(16))) union {
+        struct {
+            uint16_t k[CH][DK + 8];
+            uint16_t q[CH][DK + 8];
+        } rows;
+        struct {
+            float t[CH][CH + 4];
+            float u[4][16][20];
+        } inv;
+    } sh;
+    uint16_t (&kh)[CH][DK + 8] = sh.rows.k;
+    uint16_t (&qh)[CH][DK + 8] = sh.rows.q;
+    float (&ts)[CH][CH + 4] = sh.inv.t;
+    float (&us)[4][16][20] = sh.inv.u;
     __shared__ float as[CH][CH + 4];                                    // A (zero on and above the diagonal)
     __shared__ double gl[CH];                                           // G_t
     __shared__ float bs[CH];                                            // beta_t
@@ -305,23 +319,63 @@ __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by substitution down each column: column j = 16 wave
-    // + lane / 4, its rows split over four lanes by row % 4
+    // T = (I + A)^-1 in 16 x 16 blocks T_ij (unit lower triangular, like
+    // I + A).  The diagonal blocks are (I + A_ii)^-1, wave i by substitution
+    // down each column (column lane / 4, its rows split over four lanes by
+    // row % 4, a quad reduction per row); wave i also clears the blocks
+    // right of its diagonal one.  Row block i of (I + A) T = I then gives,
+    // below the diagonal, T_ij = -T_ii sum_{j <= m < i} A_im T_mj: level
+    // i - j = 1, 2, 3 in turn, one block per wave, on the FP32 matrix unit.
     {
-        const int j = 16 * wave + (lane >> 2), p = lane & 3;
-        float tc[16];
+        const int j = lane >> 2, p = lane & 3, b0 = 16 * wave;
+        float tc[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tc[i] = (4 * i + p == j) ? 1.0f : 0.0f;
+        for (int i = 0; i < 4; ++i) tc[i] = (4 * i + p == j) ? 1.0f : 0.0f;
 #pragma unroll
-        for (int t = 1; t < CH; ++t) {
+        for (int t = 1; t < 16; ++t) {
             float sum = 0.0f;
 #pragma unroll
-            for (int i = 0; i <= (t - 1) / 4; ++i) sum = __builtin_fmaf(as[t][4 * i + p], tc[i], sum);
+            for (int i = 0; i <= (t - 1) / 4; ++i) sum = __builtin_fmaf(as[b0 + t][b0 + 4 * i + p], tc[i], sum);
             sum = quad_sum(sum);
             if (p == (t & 3) && t > j) tc[t >> 2] = -sum;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ws[WS_T + (4 * i + p) * CH + j] = tc[i];
+        for (int i = 0; i < 4; ++i) ts[b0 + 4 * i + p][b0 + j] = tc[i];
+        for (int cb = wave + 1; cb < 4; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ts[b0 + j][16 * cb + 4 * p + e] = 0.0f;
+    }
+    __syncthreads();
+    // C += X Y for 16 x 16 blocks (X, Y row-major with leading dimensions);
+    // lane holds C[4 hi + e][lo]
+    auto mm = [&](const float* x, int ldx, const float* y, int ldy, f32x4 acc) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[lo * ldx + 4 * kk + hi], y[(4 * kk + hi) * ldy + lo], acc, 0,
+                                                     0, 0);
+        return acc;
+    };
+    for (int lvl = 1; lvl < 4; ++lvl) {
+        const bool act = wave < 4 - lvl;
+        const int bi = wave + lvl, bj = wave;
+        if (act) {
+            f32x4 u = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int m = bj; m < bi; ++m) u = mm(&as[16 * bi][16 * m], CH + 4, &ts[16 * m][16 * bj], CH + 4, u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) us[wave][4 * hi + e][lo] = u[e];
+        }
+        __syncthreads();
+        if (act) {
+            const f32x4 t = mm(&ts[16 * bi][16 * bi], CH + 4, &us[wave][0][0], 20, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ts[16 * bi + 4 * hi + e][16 * bj + lo] = -t[e];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int idx = tid + 256 * u, r = idx >> 4, c4 = idx & 15;
+        *(f32x4*)(ws + WS_T + r * CH + 4 * c4) = *(const f32x4*)&ts[r][4 * c4];
     }
 }
 
@@ -337,8 +391,8 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
 {
     __shared__ __attribute__((aligned(16))) float st[CB][DK + 4];     // S^T of the block
     __shared__ __attribute__((aligned(16))) float ks[CH][DK + 16];    // k rows of the chunk
-    __shared__ float rs[CH][CB + 4];                                  // R = beta (v - gamma K S)
-    __shared__ float ds[CH][CB + 4];                                  // D
+    __shared__ __attribute__((aligned(16))) float rt[CB][CH + 4];     // R^T, R = beta (v - gamma K S)
+    __shared__ __attribute__((aligned(16))) float dt[CB][CH + 4];     // D^T
     __shared__ float dh[CH][CB];                                      // eta D
     __shared__ float vec[2][3][CH];                                   // gamma, eta, beta (two chunks)
 
@@ -464,13 +518,15 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
             for (int z = 0; z < 8; ++z)
                 *(f32x4*)&ks[trow][32 * (z >> 1) + 8 * hi + 4 * (z & 1)] =
                     f32x4{kf[4 * z], kf[4 * z + 1], kf[4 * z + 2], kf[4 * z + 3]};
+            f32x4 r4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * w + 4 * hi + e;
                 const uint16_t vb = t0 + t < a.L ? (uint16_t)cur.vr[e] : (uint16_t)0;
                 const float vv = (float)__builtin_bit_cast(_Float16, vb);
-                rs[t][lo] = vec[b][2][t] * (vv - vec[b][0][t] * xk[e]);
+                r4[e] = vec[b][2][t] * (vv - vec[b][0][t] * xk[e]);
             }
+            *(f32x4*)&rt[lo][16 * w + 4 * hi] = r4;
             // pace the next chunk's 16 row loads (k, q, T, P) one per four
             // of the 64 matrix instructions: issued back to back they fill
             // the vector memory path, and the in-order wave then stalls at
@@ -484,17 +540,23 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         __syncthreads();
 
         // stage 2: D rows 16 w .. 16 w + 15 = T R (step m takes s = 16 (m / 4)
-        // + 4 hi + m % 4; rows of R 4 apart sit 16 banks apart)
+        // + 4 hi + m % 4).  R and D are kept transposed in LDS, so a lane's
+        // four entries of one step group are one 16-byte read; two
+        // accumulation chains (even and odd steps).
         {
-            f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4 d2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-            for (int m = 0; m < 16; ++m)
-                d = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.tv[m >> 2][m & 3], rs[16 * (m >> 2) + 4 * hi + (m & 3)][lo], d,
-                                                         0, 0, 0);
+            for (int z = 0; z < 4; ++z) {
+                const f32x4 rv = *(const f32x4*)&rt[lo][16 * z + 4 * hi];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    d2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.tv[z][j], rv[j], d2[j & 1], 0, 0, 0);
+            }
+            const f32x4 d = d2[0] + d2[1];
+            *(f32x4*)&dt[lo][16 * w + 4 * hi] = d;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * w + 4 * hi + e;
-                ds[t][lo] = d[e];
                 dh[t][lo] = vec[b][1][t] * d[e];
             }
         }
@@ -518,13 +580,17 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) st[4 * hi + e][16 * r + lo] = acc[e];
             }
-            f32x4 o;
+            f32x4 o2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = vec[b][0][16 * w + 4 * hi + e] * xq[e];
+            for (int e = 0; e < 4; ++e) o2[0][e] = vec[b][0][16 * w + 4 * hi + e] * xq[e];
 #pragma unroll
-            for (int m = 0; m < 16; ++m)
-                o = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pv[m >> 2][m & 3], ds[16 * (m >> 2) + 4 * hi + (m & 3)][lo], o,
-                                                         0, 0, 0);
+            for (int z = 0; z < 4; ++z) {
+                const f32x4 dv = *(const f32x4*)&dt[lo][16 * z + 4 * hi];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pv[z][j], dv[j], o2[j & 1], 0, 0, 0);
+            }
+            const f32x4 o = o2[0] + o2[1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) ob[e] = __builtin_bit_cast(uint16_t, (_Float16)(o[e] * rsq));
         }
