@@ -40,8 +40,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int HD = 256;               // head size
 constexpr int BQ = 128;               // queries per workgroup
 constexpr int BKEY = 64;              // keys per block
-constexpr int KS_STRIDE = HD + 8;     // halves per K row in LDS (528 B: rows start on distinct banks)
-constexpr int VT_STRIDE = BKEY + 4;   // halves per V^T row in LDS (136 B)
+constexpr int TILE_HALVES = BKEY * HD;  // one K or V tile in LDS: 64 rows of 512 B, unpadded
 constexpr int WS_ATTENTION = 2;       // library workspace kind of the key-split partials
 
 struct AttArgs {
@@ -62,25 +61,35 @@ struct AttArgs {
 // FP16), and the 128 accumulators are rescaled only on those blocks.
 constexpr float TAU = 8.0f;
 
-__device__ __forceinline__ uint32_t half_of(const u32x4& w, int i)
-{
-    return (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-}
-
 __device__ __forceinline__ uint32_t pack_f16(float a, float b)
 {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-// one LDS stage: K [64][KS_STRIDE], then V^T [256][VT_STRIDE]
-constexpr int STAGE_HALVES = BKEY * KS_STRIDE + HD * VT_STRIDE;
+// one LDS stage: K [64][256], then V [64][256], both row-major.  Rows are
+// copied straight from global memory (64 lanes x 16 bytes, two rows per
+// instruction), so instead of padding, the 16-byte pieces of a row are
+// XOR-swizzled: piece p (dims 8 p .. 8 p + 7) of key row r sits in slot
+//   K: p ^ (r & 15): a K-fragment read's 16 lanes per cycle take 16 rows at
+//      one piece, which land on 16 distinct 4-bank groups;
+//   V: p ^ 4 (r & 3): a transposing read's 16 lanes take 4 rows x 4 pieces,
+//      also 16 distinct groups.
+constexpr int STAGE_HALVES = 2 * TILE_HALVES;
+constexpr int VMCNT0 = 0x0F70;        // s_waitcnt: vmcnt = 0, other counters not waited for
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <bool SPLIT>
 __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE_HALVES];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the two stages are separate arrays: the compiler then sees that a copy
+    // into one cannot overwrite what is being read from the other, and does
+    // not drain the outstanding LDS reads before each copy
+    __shared__ __attribute__((aligned(16))) uint16_t lds0[STAGE_HALVES];
+    __shared__ __attribute__((aligned(16))) uint16_t lds1[STAGE_HALVES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, c = lane & 31;
     // the query blocks with the most keys start first
     const int hq = blockIdx.x % a.Hq;
@@ -114,82 +123,90 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
             for (int j = 0; j < 16; ++j) qf[j] = *(const u32x4*)(qp + 16 * j);
         }
 
-        // staging: K as 2,048 16-byte pieces (8 per thread, a row per 32
-        // threads); V as 1,024 units of two keys x 8 dims (4 per thread),
-        // written transposed as key pairs.  Keys past Lk re-read key Lk - 1
-        // (they are masked).
-        u32x4 kr[8], vr[4][2];
-        auto load_tile = [&](int kb) {
-            const int kbase = kb * BKEY;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int idx = tid + 256 * u, row = idx >> 5, col = idx & 31;
-                const int key = min(kbase + row, a.Lk - 1);
-                kr[u] = *(const u32x4*)(a.k + (size_t)key * a.ldk + (size_t)kh * HD + col * 8);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int idx = tid + 256 * u, kp = idx & 31, dc = idx >> 5;
-                const int k0 = min(kbase + 2 * kp, a.Lk - 1), k1 = min(kbase + 2 * kp + 1, a.Lk - 1);
-                vr[u][0] = *(const u32x4*)(a.v + (size_t)k0 * a.ldv + (size_t)kh * HD + dc * 8);
-                vr[u][1] = *(const u32x4*)(a.v + (size_t)k1 * a.ldv + (size_t)kh * HD + dc * 8);
-            }
-        };
-        auto store_tile = [&](int b) {
-            uint16_t* const ks = lds + b * STAGE_HALVES;
-            uint16_t* const vt = ks + BKEY * KS_STRIDE;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int idx = tid + 256 * u, row = idx >> 5, col = idx & 31;
-                *(u32x4*)(ks + row * KS_STRIDE + col * 8) = kr[u];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int idx = tid + 256 * u, kp = idx & 31, dc = idx >> 5;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    *(uint32_t*)(vt + (dc * 8 + i) * VT_STRIDE + 2 * kp) =
-                        half_of(vr[u][0], i) | (half_of(vr[u][1], i) << 16);
-            }
+        // staging: wave w's copy i fills rows 2 (8 w + i) and 2 (8 w + i) + 1
+        // of the K and of the V tile; lane L writes slot L % 32 of row
+        // 2 (8 w + i) + L / 32, so it reads the piece that belongs there.
+        // Keys past Lk re-read key Lk - 1 (they are masked).
+        // copy n (0..15): K (n even) or V (n odd) rows of wave copy i = n / 2
+        auto issue_kv = [&](int kb, uint16_t* kst, int n) {
+            const int i = n >> 1;
+            const int r = 2 * (8 * wave + i) + (lane >> 5), sl = lane & 31;
+            const size_t key = (size_t)min(kb * BKEY + r, a.Lk - 1);
+            if ((n & 1) == 0)
+                __builtin_amdgcn_global_load_lds(a.k + key * a.ldk + (size_t)kh * HD + 8 * (sl ^ (r & 15)),
+                                                 (lds_ptr_t)(kst + (8 * wave + i) * 512), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds(a.v + key * a.ldv + (size_t)kh * HD + 8 * (sl ^ ((r & 3) << 2)),
+                                                 (lds_ptr_t)(kst + TILE_HALVES + (8 * wave + i) * 512), 16, 0, 0);
         };
 
         const float cl = 1.4426950408889634f / 16.0f;          // log2(e) / sqrt(256)
-        load_tile(kb0);
-        store_tile(0);
+#pragma unroll
+        for (int n = 0; n < 16; ++n) issue_kv(kb0, lds0, n);
+        __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
-        if (kb0 + 1 < kb1) load_tile(kb0 + 1);
-        for (int kb = kb0; kb < kb1; ++kb) {
-            const int b = (kb - kb0) & 1;
-            const uint16_t* const ks = lds + b * STAGE_HALVES;
-            const uint16_t* const vt = ks + BKEY * KS_STRIDE;
+        // block kb from stage ks while the next block is copied into nst
+        auto block = [&](int kb, const uint16_t* ks, uint16_t* nst) {
+            const uint16_t* const vs = ks + TILE_HALVES;
+            // the next block goes into the other stage (last read before the
+            // previous barrier), one copy after each pair of the S^T
+            // products below; the last block again on the last iteration
+            const int kn = min(kb + 1, kb1 - 1);
 
             // S^T for keys 32 st .. 32 st + 31 of the block: lane (c, h),
             // value r is key 8 (r / 4) + 4 h + r % 4 of the tile, query c
+            // (the two tiles' products alternate, so that no product waits
+            // for the one before it to finish)
             f32x16 s[2];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const f16x8 ka = *(const f16x8*)(ks + (32 * st + c) * KS_STRIDE + 16 * j + 8 * h);
-                    s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, __builtin_bit_cast(f16x8, qf[j]),
-                                                                   s[st], 0, 0, 0);
-                }
-            }
-
-            // online softmax (base 2); masked keys get -inf
-            float bm = -__builtin_inff();
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb * BKEY + 32 * st + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float t = key <= pos ? s[st][r] * cl : -__builtin_inff();
-                    s[st][r] = t;
-                    bm = fmaxf(bm, t);
-                }
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
+                for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
+            // (issued back to back, the 16 copies fill the vector memory
+            // path and the in-order wave stalls at the later ones with its
+            // products waiting behind them; the copies write LDS, so the
+            // compiler keeps them where they are written)
+            // The K fragments are read two steps ahead: the compiler does
+            // not move an LDS read above a copy into LDS.
+            auto kfrag = [&](int j, int st) {
+                const int kr_ = 32 * st + c;
+                return *(const f16x8*)(ks + kr_ * HD + 8 * ((2 * j + h) ^ (kr_ & 15)));
+            };
+            f16x8 ka[3][2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) ka[j][st] = kfrag(j, st);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j + 2 < 16)
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) ka[(j + 2) % 3][st] = kfrag(j + 2, st);
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[j % 3][st], __builtin_bit_cast(f16x8, qf[j]),
+                                                                   s[st], 0, 0, 0);
+                issue_kv(kn, nst, j);
+            }
+
+            // online softmax (base 2) on the raw scores: masked keys get
+            // -inf, only in blocks that reach past the workgroup's first
+            // query; the block maximum is scaled after the max (cl > 0)
+            float bm = -__builtin_inff();
+            if (kb * BKEY + BKEY - 1 > off + q0) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kb * BKEY + 32 * st + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (key > pos) s[st][r] = -__builtin_inff();
+                    }
+            }
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) bm = fmaxf(bm, s[st][r]);
+            bm = fmaxf(bm, __shfl_xor(bm, 32)) * cl;
             const bool raise = bm > m + TAU;                   // also the first finite maximum
             if (__any(raise)) {
                 const float mn = raise ? bm : m;
@@ -202,6 +219,7 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
                 m = mn;
             }
             const float mu = m == -__builtin_inff() ? 0.0f : m;
+            const float sh = 4.0f - mu;                        // 16 p = 2^(cl s - mu + 4)
             // per 32-key tile: P^T x 16 in FP16 as B fragments (step jj takes
             // values r = 8 jj .. 8 jj + 7: keys 16 jj + 4 h + 0..3 and
             // 16 jj + 8 + 4 h + 0..3), then O^T (dims x queries) += V^T P^T
@@ -216,30 +234,47 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 8 * jj + 2 * e;
-                        const float p0 = __builtin_amdgcn_exp2f(s[st][r] - mu);
-                        const float p1 = __builtin_amdgcn_exp2f(s[st][r + 1] - mu);
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], cl, sh));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r + 1], cl, sh));
                         sum += p0 + p1;
-                        pf[jj][e] = pack_f16(16.0f * p0, 16.0f * p1);
+                        pf[jj][e] = pack_f16(p0, p1);
                     }
+                // (eight accumulators in turn: no product waits for the one
+                // before it)
+                // V^T fragments by transposing reads: in each 16-lane group
+                // (g = lane / 16, i = lane % 16) lane i points at 4 dims of
+                // key K0 + i / 4 and receives keys K0 .. K0 + 3 of dim
+                // 32 dt + 16 (g % 2) + i; K0 = 32 st + 16 jj + 4 h, and + 8
+                // for the second half of the fragment
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        const uint16_t* vp = vt + (dt * 32 + c) * VT_STRIDE + 32 * st + 16 * jj + 4 * h;
-                        const u32x2 lo = *(const u32x2*)vp;
-                        const u32x2 hi = *(const u32x2*)(vp + 8);
-                        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                    for (int dt = 0; dt < 8; ++dt) {
+                        const int gi = lane & 15, vr_ = 32 * st + 16 * jj + 4 * h + (gi >> 2);
+                        const int vp_ = 4 * dt + 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
+                        const uint16_t* vp = vs + vr_ * HD + 8 * (vp_ ^ ((vr_ & 3) << 2)) + 4 * (gi & 1);
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp);
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4*)(vp + 8 * HD));
+                        const u32x4 va = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
                         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
                                                                        __builtin_bit_cast(f16x8, pf[jj]),
                                                                        o[dt], 0, 0, 0);
                     }
             }
-            l += sum;
+            l += sum * 0.0625f;                                // sum holds 16 p
 
-            // the other stage was last read before the previous barrier
-            if (kb + 1 < kb1) store_tile(b ^ 1);
+            // this wave's copies of the next block have landed; after the
+            // barrier, everyone's have
+            __builtin_amdgcn_s_waitcnt(VMCNT0);
             __syncthreads();
-            if (kb + 2 < kb1) load_tile(kb + 2);
+        };
+        for (int kb = kb0; kb < kb1; kb += 2) {
+            block(kb, lds0, lds1);
+            if (kb + 1 < kb1) block(kb + 1, lds1, lds0);
         }
     }
 
