@@ -141,6 +141,17 @@ def per_dispatch_clock(path: Path) -> list[tuple[str, float]]:
             for (n, cyc), ns in zip(per_dispatch(path, "GRBM_GUI_ACTIVE"), durations(path))]
 
 
+MAX_SCLK_GHZ = 2.4    # the MI355X's highest shader clock
+
+
+def clock_or_none(ghz: float) -> float | None:
+    """The clock estimate, or None where it exceeds the chip's highest clock:
+    for a dispatch shorter than rocprofv3's counter window, GRBM_GUI_ACTIVE
+    also counts busy cycles outside the dispatch, so neither the clock nor
+    the MFMA busy share (whose denominator it is) means anything."""
+    return ghz if ghz <= MAX_SCLK_GHZ * 1.01 else None
+
+
 def existing(tag: str) -> Path:
     found = list((OUT / tag).rglob("*counter_collection.csv"))
     if not found:
@@ -164,6 +175,10 @@ def group_launches(names: list[str]) -> list[list[int]]:
             launches.append(pending + [i])
             pending = []
     return launches
+
+
+def fmt(x: float | None) -> str:
+    return "—" if x is None else f"{x:.3f}"
 
 
 def main() -> int:
@@ -194,12 +209,13 @@ def main() -> int:
         gemm = [i for i in idx if classify(names[i]) not in ("reduce", "expand")][0]
         c = classify(names[gemm])
         e = per_class.setdefault(c, {"launches_per_step": 0, "workload": label, "_w": 0, "read": 0.0,
-                                     "written": 0.0, "clock": 0.0, "busy": 0.0, "flops": 0.0})
+                                     "written": 0.0, "clock": 0.0, "busy": 0.0, "flops": 0.0, "window": True})
         e["launches_per_step"] += weight if label.startswith("sweep") else 0
         e["_w"] += weight
         e["read"] += weight * sum(fetch[i][1] for i in idx) * 1024 * fetch_factor
         e["written"] += weight * sum(write[i][1] for i in idx) * 1024 * write_factor
         e["clock"] += weight * clock[gemm][1]
+        e["window"] = e["window"] and clock_or_none(clock[gemm][1]) is not None
         e["busy"] += weight * busy[gemm][1] / (gui[gemm][1] / NUM_XCD * NUM_SIMD)
         e["flops"] += weight * mops[gemm][1] * 512
     for e in per_class.values():
@@ -207,8 +223,11 @@ def main() -> int:
         e["read_bytes_per_launch"] = round(e.pop("read") / w)
         e["write_bytes_per_launch"] = round(e.pop("written") / w)
         e["hbm_bytes_per_launch"] = e["read_bytes_per_launch"] + e["write_bytes_per_launch"]
-        e["sclk_ghz"] = round(e.pop("clock") / w, 3)
-        e["mfma_busy_frac"] = round(e.pop("busy") / w, 4)
+        ok = e.pop("window")
+        e["sclk_ghz"] = round(e.pop("clock") / w, 3) if ok else None
+        e["mfma_busy_frac"] = round(e.pop("busy") / w, 4) if ok else None
+        if not ok:
+            e["note"] = "dispatch shorter than the counter window: no clock or MFMA busy share"
         e["mfma_f16_flops_per_launch"] = round(e.pop("flops") / w)
     sweep = {c: e for c, e in per_class.items() if e["launches_per_step"]}
     dominant = max(sweep, key=lambda c: sweep[c]["launches_per_step"])
@@ -250,15 +269,17 @@ def main() -> int:
     for c, e in sorted(per_class.items()):
         lines.append(f"| {c} | {e['workload']} | {e['launches_per_step']} | {e['read_bytes_per_launch'] / 1e6:.1f} | "
                      f"{e['write_bytes_per_launch'] / 1e6:.1f} | {e['hbm_bytes_per_launch'] / 1e6:.1f} | "
-                     f"{e['sclk_ghz']:.3f} | {e['mfma_busy_frac']:.3f} | "
+                     f"{fmt(e['sclk_ghz'])} | {fmt(e['mfma_busy_frac'])} | "
                      f"{e['mfma_f16_flops_per_launch'] / 1e9:.1f} |")
     lines += ["", "Per dispatch (raw counters; bytes in KiB, cycles as counted):", "",
               "| kernel | FETCH_SIZE | WRITE_SIZE | clock GHz | MFMA busy cycles | MOPS_F16 |",
               "|---|---|---|---|---|---|"]
     for i, n in enumerate(names):
-        lines.append(f"| {n[:70]} | {fetch[i][1]:.0f} | {write[i][1]:.0f} | {clock[i][1]:.3f} | "
+        lines.append(f"| {n[:70]} | {fetch[i][1]:.0f} | {write[i][1]:.0f} | {fmt(clock_or_none(clock[i][1]))} | "
                      f"{busy[i][1]:.0f} | {mops[i][1]:.0f} |")
-    lines += ["", f"Kernel source sha256: {rec['kernel_source_sha256']}", ""]
+    lines += ["", "A dash: the estimate exceeded the chip's 2.4 GHz, because the dispatch is shorter than the",
+              "counter window (GRBM_GUI_ACTIVE then also counts cycles outside it); its MFMA busy share is",
+              "not given either.", "", f"Kernel source sha256: {rec['kernel_source_sha256']}", ""]
     for d in dests:
         (d / "gemm_counters.md").write_text("\n".join(lines))
     print(json.dumps(rec), flush=True)

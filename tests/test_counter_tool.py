@@ -55,6 +55,13 @@ def test_per_dispatch_clock(tmp_path):
     assert got[1][1] == pytest.approx(2.4)
 
 
+def test_clock_beyond_the_chip_is_dropped():
+    # a dispatch shorter than the counter window reads above the top clock
+    assert ht.clock_or_none(1.5) == 1.5
+    assert ht.clock_or_none(2.4) == 2.4
+    assert ht.clock_or_none(3.0) is None
+
+
 def test_group_launches():
     # an expanded launch is expansion + GEMM, a split one GEMM + reduction;
     # other kernels (copies, torch's) are not part of any launch
