@@ -14,17 +14,18 @@
 //     the FP32 sum of the p_j; one FP16 rounding of o.
 //
 // Design: one workgroup per (query head, 128 queries), four waves of 32
-// queries.  Keys go by blocks of 64 through two LDS stages (K row-major, V
-// transposed): a block is computed from one stage while the next block,
-// loaded into registers one block ahead, is written to the other; one
-// barrier per block.  Short query chunks over a long cache split the keys
-// over several workgroups, whose partial sums a second kernel combines.
+// queries.  Keys go by blocks of 64 through two LDS stages, K and V both
+// row-major and copied straight from global memory into LDS: a block is
+// computed from one stage while the next block is copied into the other;
+// one barrier per block.  Short query chunks over a long cache split the
+// keys over several workgroups, whose partial sums a second kernel combines.
 // Per block a wave computes S^T = K Q^T (keys x queries, so that each lane
 // holds one query and its softmax needs a single cross-lane exchange), the
 // online-softmax update, and O^T += V^T P^T, all on
-// v_mfma_f32_32x32x16_f16.  The P^T values never leave registers: the
-// accumulator layout of S^T, with its k slots permuted consistently in V^T,
-// is the B operand of the second product.
+// v_mfma_f32_32x32x16_f16; the V^T fragments come from row-major V through
+// the transposing LDS read.  The P^T values never leave registers: the
+// accumulator layout of S^T, with its k slots read in the same key order
+// from V^T, is the B operand of the second product.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
