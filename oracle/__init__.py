@@ -74,6 +74,8 @@ class Oracle:
         lib.ora_int8_linear.restype = ctypes.c_int
         lib.ora_int8_dequant.argtypes = [_P, _P, _P, _I64, _I64]
         lib.ora_int8_dequant.restype = ctypes.c_int
+        lib.ora_int8_quantize.argtypes = [_P, _P, _P, _I64, _I64]
+        lib.ora_int8_quantize.restype = ctypes.c_int
         lib.ora_attention.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I64,
                                       _P, _I64, ctypes.c_int, _P, _P, _P, _P]
         lib.ora_attention.restype = ctypes.c_int
@@ -214,6 +216,18 @@ class Oracle:
         if st != OK:
             raise OracleError(f"ora_int8_dequant status {st}")
         return w
+
+    def int8_quantize(self, w16: np.ndarray):
+        """Codes int8 [N, K] and FP16 scale bits [N, K/32] of an FP16 weight
+        (symmetric per block of 32, codes clamped to -127..127)."""
+        w = np.ascontiguousarray(w16).view(np.uint16)
+        n, k = w.shape
+        q = np.empty((n, k), np.int8)
+        qs = np.empty((n, max(k // 32, 1)), np.uint16)
+        st = self.lib.ora_int8_quantize(w.ctypes.data, q.ctypes.data, qs.ctypes.data, n, k)
+        if st != OK:
+            raise OracleError(f"ora_int8_quantize status {st}")
+        return q, qs
 
     # -- full attention -----------------------------------------------------
     def attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, *, n_heads: int,

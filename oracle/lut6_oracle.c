@@ -445,6 +445,73 @@ int ora_int8_dequant(const int8_t *q, const uint16_t *qs, uint16_t *w, int64_t n
     return ORA_OK;
 }
 
+/* ---------------- int8 code selection ---------------- */
+
+/* Codes and scales for the int8 variant (page "clef-flash — Core AI",
+ * section "Precision": int8 per block of 32, the mode named symmetric with
+ * clipping, weights only).  The page names the mode and nothing more; the
+ * readings:
+ *   - a block is 32 consecutive inputs k of one output row, as for the
+ *     scales the layer reads;
+ *   - symmetric: no zero point, codes -127..127; the block's scale is its
+ *     largest magnitude divided by 127, rounded once to FP16;
+ *   - with clipping: each code is w / s rounded to the nearest integer (ties
+ *     to even) and clamped to -127..127 (a scale rounded down to FP16 puts
+ *     the largest magnitude's quotient just past 127);
+ *   - the quotient is an integer decision, taken in FP32 as on the device: w
+ *     and s are FP16, exact in FP32, and the FP32 division is correctly
+ *     rounded;
+ *   - a block whose scale rounds to zero (all zero, or too small for an FP16
+ *     scale) gets scale 0 and codes 0.
+ * Weights are finite. */
+int ora_int8_quantize(const uint16_t *w, int8_t *q, uint16_t *qs, int64_t n, int64_t k)
+{
+#if ORA_MUTANT == 29
+    const int bs = 16;
+#else
+    const int bs = 32;
+#endif
+    if (!w || !q || !qs) return ORA_E_NULL;
+    if (n <= 0 || k <= 0 || k % 32) return ORA_E_SHAPE;
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t b = 0; b < k / bs; ++b) {
+            const uint16_t *wb = w + r * k + bs * b;
+            double a = 0.0;
+            for (int i = 0; i < bs; ++i) a = fmax(a, fabs(ora_f16_to_f64(wb[i])));
+#if ORA_MUTANT == 26
+            const uint16_t sh = ora_f64_to_f16(a / 128.0);
+#else
+            const uint16_t sh = ora_f64_to_f16(a / 127.0);
+#endif
+            qs[r * (k / 32) + (b * bs) / 32] = sh;
+#if ORA_MUTANT == 27
+            const float s = (float)(a / 127.0);
+#else
+            const float s = (float)ora_f16_to_f64(sh);
+#endif
+            for (int i = 0; i < bs; ++i) {
+                int code = 0;
+                if (ora_f16_to_f64(sh) != 0.0) {
+                    const float x = (float)ora_f16_to_f64(wb[i]) / s;
+#if ORA_MUTANT == 28
+                    const float v = roundf(x);
+#else
+                    const float v = rintf(x);
+#endif
+#if ORA_MUTANT == 25
+                    code = (int)v;
+#elif ORA_MUTANT == 30
+                    code = v > 127.0f ? 127 : v < -128.0f ? -128 : (int)v;
+#else
+                    code = v > 127.0f ? 127 : v < -127.0f ? -127 : (int)v;
+#endif
+                }
+                q[r * k + bs * b + i] = (int8_t)code;
+            }
+        }
+    return ORA_OK;
+}
+
 /* Bytes of a packed [n, k] weight and of its tables (format sizes). */
 int64_t ora_packed_bytes(int64_t n, int64_t k) { return n * (3 * k / 4); }
 int64_t ora_table_bytes(int64_t n) { return (n / 16) * 64 * 2; }

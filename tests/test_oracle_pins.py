@@ -587,13 +587,96 @@ def pin_quantize_forty_rounds(ora):
     assert np.array_equal(idx, want), "index = nearest entry, the lower on a tie"
 
 
+# ---------------------------------------------------------------------------
+# int8 code selection (page "clef-flash — Core AI", section "Precision": int8
+# per block of 32, symmetric with clipping).  Closed-form blocks: the scale is
+# the largest magnitude over 127 rounded once to FP16, codes are w / s rounded
+# to nearest even and clamped to -127..127.
+# ---------------------------------------------------------------------------
+
+def _i8_block_rows(blocks):
+    """Rows of FP16 values, one 32-wide block per row (zero padded)."""
+    w = np.zeros((len(blocks), 32), np.float16)
+    for r, b in enumerate(blocks):
+        w[r, :len(b)] = np.asarray(b, np.float64).astype(np.float16)
+    return w
+
+
+def pin_int8_quantize_grid(ora):
+    # largest magnitude 127 * 2^-7: the scale is 2^-7 exactly and every
+    # multiple j * 2^-7 (|j| <= 127) is coded as j; only element 0 holds the
+    # maximum, so halves of a block would get other scales
+    g = np.random.default_rng(31)
+    j = g.integers(-126, 127, size=(6, 64))
+    j[:, 0] = np.array([127, -127, 127, -127, 127, -127])
+    j[:, 32] = -j[:, 0]
+    w = (j * 2.0 ** -7).astype(np.float16)
+    q, qs = ora.int8_quantize(w)
+    assert np.array_equal(q.astype(np.int64), j), "codes of an exact grid"
+    assert np.all(qs == np.float16(2.0 ** -7).view(np.uint16)), "scale = max / 127"
+
+
+def pin_int8_quantize_ties(ora):
+    # scale 1 (largest magnitude 127): halves go to the even neighbour
+    w = _i8_block_rows([[127.0, 2.5, -2.5, 3.5, 0.5, -0.5, 1.5, -126.5, 126.5]])
+    q, qs = ora.int8_quantize(w)
+    assert qs[0, 0] == np.float16(1.0).view(np.uint16)
+    assert list(q[0, :9]) == [127, 2, -2, 4, 0, 0, 2, -126, 126], list(q[0, :9])
+
+
+def pin_int8_quantize_clamp_and_fp16_scale(ora):
+    # largest magnitude 2^-17: 2^-17 / 127 = 2^-24 * 128/127 rounds to the
+    # FP16 subnormal 2^-24, so the maximum's quotient is exactly 128 and is
+    # clamped to 127 (and -128 to -127: symmetric).  100 * 2^-24 is coded
+    # 100 against the FP16 scale (99.2 against the unrounded one)
+    t = 2.0 ** -24
+    w = _i8_block_rows([[2.0 ** -17, 100 * t, -3 * t], [-(2.0 ** -17), -100 * t, 3 * t]])
+    q, qs = ora.int8_quantize(w)
+    assert np.all(qs[:, 0] == 1), "scale 2^-24 (FP16 bits 0x0001)"
+    assert list(q[0, :3]) == [127, 100, -3] and list(q[1, :3]) == [-127, -100, 3], (q[0, :3], q[1, :3])
+
+
+def pin_int8_quantize_zero_scales(ora):
+    # an all-zero block and one whose scale rounds to zero (2^-24 / 127)
+    w = _i8_block_rows([[0.0], [2.0 ** -24, -(2.0 ** -24)]])
+    q, qs = ora.int8_quantize(w)
+    assert np.all(qs == 0) and np.all(q == 0)
+
+
+def pin_int8_quantize_round_trip(ora):
+    # any block: the weight the layer uses, fp16(q * s), is within half a
+    # step of w (plus its own FP16 rounding) unless the code was clamped, and
+    # a code is clamped only where |w| is at least 126.5 steps (a scale that
+    # is an FP16 subnormal can be rounded far down); a block whose scale is
+    # an FP16 normal codes its largest magnitude as +-127; q(-w) = -q(w)
+    g = np.random.default_rng(32)
+    w = (g.standard_normal((24, 256)) * 0.02).astype(np.float16)
+    w[3] *= np.float16(1e-3)                                   # a row of tiny blocks
+    q, qs = ora.int8_quantize(w)
+    s = qs.view(np.float16).astype(np.float64).repeat(32, axis=1)
+    wq = ora.int8_dequant(q, qs).view(np.float16).astype(np.float64)
+    wd = w.astype(np.float64)
+    ulp = np.spacing(np.abs(wd).astype(np.float16)).astype(np.float64)
+    inner = np.abs(q.astype(np.int64)) < 127
+    assert np.all((np.abs(wq - wd) <= s / 2 + ulp + 1e-30)[inner]), "within half a step"
+    assert np.all((np.abs(wd) >= 126.5 * s)[~inner]), "clamped only past 126.5 steps"
+    assert np.any(~inner & (np.abs(wd) > 127.5 * s)), "the tiny row has a clamped code"
+    normal = qs.view(np.float16).astype(np.float64) >= 2.0 ** -14
+    top = np.abs(q.astype(np.int64)).reshape(24, -1, 32).max(axis=2)
+    assert np.all(top[normal] == 127), "the largest magnitude codes as 127"
+    qn, qsn = ora.int8_quantize(-w)
+    assert np.array_equal(qn.astype(np.int64), -q.astype(np.int64)) and np.array_equal(qsn, qs)
+
+
 PINS = [pin_pack_worked_examples, pin_pack_exhaustive, pin_storage, pin_f16_decode,
         pin_f16_encode, pin_dequant, pin_linear_bruteforce, pin_linear_silu,
         pin_special_tables, pin_identity_readout, pin_in_scale, pin_int8_dequant,
         pin_int8_as_lut6, pin_int8_block_scale, pin_attention_sdpa, pin_attention_closed_forms,
         pin_gated_delta_frozen_state, pin_gated_delta_decay_only, pin_gated_delta_overwrites_unit_keys,
         pin_gated_delta_split_sequence, pin_quantize_starts, pin_quantize_lloyd_step,
-        pin_quantize_forty_rounds]
+        pin_quantize_forty_rounds, pin_int8_quantize_grid, pin_int8_quantize_ties,
+        pin_int8_quantize_clamp_and_fp16_scale, pin_int8_quantize_zero_scales,
+        pin_int8_quantize_round_trip]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -642,7 +725,10 @@ MUTANTS = {1: "big-endian byte order", 2: "index order reversed", 3: "one table 
            17: "attention mask one key short", 18: "attention scaled by 1 over D",
            19: "delta rule heads interleaved", 20: "delta rule beta ignored", 21: "delta rule unscaled",
            22: "k-means 39 rounds", 23: "k-means starts all quantiles",
-           24: "k-means even starts miss min and max"}
+           24: "k-means even starts miss min and max", 25: "int8 codes not clamped",
+           26: "int8 scale over 128", 27: "int8 quotient on the unrounded scale",
+           28: "int8 ties away from zero", 29: "int8 codes per block of 16",
+           30: "int8 clamp asymmetric"}
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m].replace(" ", "_"))
