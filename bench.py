@@ -36,6 +36,9 @@ starts.  The line printed is throughput in TFLOP/s, with
     keys, in TFLOP/s against the FP16 peak;
   * gated_delta: one linear-attention layer's Gated DeltaNet recurrence
     (32 value heads, FP32 state) over 4,096 and 16,384 tokens;
+  * int8_quantize: lut6_int8_quantize (int8 codes per block of 32) on the
+    24,576 x 4,096 gate|up weight and a 4,096 x 4,096 one, in algorithmic
+    GB/s against HBM;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same step
     (64 sampled token rows of every GEMM of all 32 layers), on this host's
     cores;
@@ -233,6 +236,31 @@ def time_quantize(lq, si, torch, stream, no_cpu: bool) -> list:
 
 
 INT8_SHAPES = (("o_proj", 128, 4096, 4096), ("o_proj", 4096, 4096, 4096), ("down", 4096, 12288, 4096))
+
+
+INT8_QUANT_SHAPES = (("gate|up", 24576, 4096), ("o_proj", 4096, 4096))
+
+
+def time_int8_quantize(lq, si, torch, stream) -> list:
+    """lut6_int8_quantize (int8 codes and scales per block of 32) on seeded
+    FP16 weights: median of 3 runs of 5 back-to-back calls; algorithmic
+    bytes = the weight read once, the codes and the scales written.  The
+    gate|up weight (201 MB read, 101 MB written) exceeds the last-level
+    cache, so its rate is HBM's."""
+    out = []
+    for name, N, K in INT8_QUANT_SHAPES:
+        w = torch.from_numpy(si.weights(N, K, (16, N, K))).to("cuda")
+        q = torch.empty((N, K), dtype=torch.int8, device="cuda")
+        sc = torch.empty((N, K // 32), dtype=torch.float16, device="cuda")
+        us = _median_us(lambda: lq.int8_quantize(w, q=q, scales=sc, stream=stream), torch, stream)
+        nbytes = N * K * 2 + N * K + N * (K // 32) * 2
+        out.append({"weight": f"{name} N={N} K={K}", "us_per_call": round(us, 1),
+                    "gb_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "algorithmic_bytes": nbytes})
+        del w, q, sc
+    torch.cuda.empty_cache()
+    return out
 
 
 def _median_us(fn, torch, stream, calls: int = 5) -> float:
@@ -600,6 +628,7 @@ def main() -> int:
 
     # ---------------- the other workloads ----------------
     quant = time_quantize(lq, si, torch, stream, args.no_cpu_baseline)
+    i8q = time_int8_quantize(lq, si, torch, stream)
     int8 = time_int8(lq, si, torch, stream)
     att = time_attention(lq, torch, stream)
     gdn = time_gated_delta(lq, torch, stream)
@@ -641,6 +670,7 @@ def main() -> int:
         "int8_variant": int8,
         "attention": att,
         "gated_delta": gdn,
+        "int8_quantize": i8q,
         "parity_sample": parity,
     }
     print(json.dumps(line), flush=True)

@@ -185,6 +185,21 @@ int lut6_int8_linear(const void* x, const int8_t* q, const void* scales, void* y
                      int64_t L, int64_t K, int64_t N, float in_scale, int epilogue,
                      hipStream_t stream);
 
+/* int8 code selection for lut6_int8_linear (page "clef-flash — Core AI",
+ * section "Precision": int8 per block of 32, the mode named symmetric with
+ * clipping, weights only).  The page names the mode only; read as: a block
+ * is 32 consecutive inputs k of one row; scales[n][b] = the block's largest
+ * magnitude / 127, rounded to FP16 (nearest, ties to even); q[n, k] = w / s
+ * in FP32, rounded to nearest even and clamped to -127..127; a block whose
+ * scale rounds to zero gets codes 0.  Weights must be finite (otherwise the
+ * outputs are unspecified).
+ * w: device FP16 [N, K], row-major, 16-byte aligned; q: device int8 [N, K],
+ * 16-byte aligned; scales: device FP16 [N, K/32], 2-byte aligned
+ * (LUT6_E_ALIGN); K % 32 == 0 (LUT6_E_SHAPE); no two overlapping
+ * (LUT6_E_ALIAS).  Enqueued on stream; no workspace.                      */
+int lut6_int8_quantize(const void* w, int8_t* q, void* scales, int64_t N, int64_t K,
+                       hipStream_t stream);
+
 /* Full attention of the attention layers, FP16 (page "Clef-Flash-ANE-LUT6",
  * section "Model architecture": query and key-value heads of size 256, full
  * attention; section "LUT-6 text weights": the probabilities are scaled up

@@ -35,7 +35,7 @@ NOALLOC_SCRATCH_BYTES = 256 << 20
 EXPORTS = ("lut6_packed_bytes", "lut6_table_bytes", "lut6_pack", "lut6_unpack",
            "lut6_linear", "lut6_linear_path", "lut6_dequant", "lut6_int8_linear", "lut6_attention",
            "lut6_gated_delta",
-           "lut6_quantize",
+           "lut6_quantize", "lut6_int8_quantize",
            "lut6_release",
            "lut6_status_string",
            "lut6_linear_noalloc")
@@ -93,6 +93,8 @@ def load_library() -> ctypes.CDLL:
     lib.lut6_gated_delta.restype = ctypes.c_int
     lib.lut6_quantize.argtypes = [P, P, P, I64, I64, P]
     lib.lut6_quantize.restype = ctypes.c_int
+    lib.lut6_int8_quantize.argtypes = [P, P, P, I64, I64, P]
+    lib.lut6_int8_quantize.restype = ctypes.c_int
     lib.lut6_release.argtypes = []
     lib.lut6_release.restype = ctypes.c_int
     lib.lut6_status_string.argtypes = [ctypes.c_int]
@@ -405,6 +407,37 @@ def quantize(w, *, packed=None, tables=None, stream=None):
                                       N, K, _stream_handle(stream))
     _check(st, "lut6_quantize")
     return packed, tables
+
+
+def int8_quantize(w, *, q=None, scales=None, stream=None):
+    """int8 codes of an FP16 weight [N, K] for int8_linear: symmetric per
+    block of 32 inputs (scale = largest magnitude / 127 in FP16, codes
+    rounded and clamped to -127..127); returns (q int8 [N, K], scales
+    float16 [N, K/32]), both on w's device."""
+    import torch
+    _require(w, torch.float16, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    N, K = w.shape
+    if K % 32 or N == 0:
+        raise ValueError(f"w must be [N, K] with N > 0 and K % 32 == 0, got [{N}, {K}]")
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.int8, device=w.device)
+    else:
+        _require(q, torch.int8, "q")
+        if tuple(q.shape) != (N, K):
+            raise ValueError(f"q must be [{N}, {K}]")
+    if scales is None:
+        scales = torch.empty((N, K // 32), dtype=torch.float16, device=w.device)
+    else:
+        _require(scales, torch.float16, "scales")
+        if tuple(scales.shape) != (N, K // 32):
+            raise ValueError(f"scales must be [{N}, {K // 32}]")
+    _same_device(w, q, scales)
+    st = load_library().lut6_int8_quantize(w.data_ptr(), q.data_ptr(), scales.data_ptr(), N, K,
+                                           _stream_handle(stream))
+    _check(st, "lut6_int8_quantize")
+    return q, scales
 
 
 def release() -> None:

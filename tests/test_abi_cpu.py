@@ -165,6 +165,21 @@ def test_quantize_validation(kwargs, status):
 Q, S = 0x50_0000_0000, 0x60_0000_0000
 
 
+def _int8_quantize(w=X, q=Q, s=S, N=4096, K=4096):
+    return lq.load_library().lut6_int8_quantize(w, q, s, N, K, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(w=None), 1), (dict(q=None), 1), (dict(s=None), 1),
+    (dict(N=0), 2), (dict(K=0), 2), (dict(K=4016), 2), (dict(N=2 ** 62), 2), (dict(N=2 ** 40, K=32), 2),
+    (dict(w=X + 2), 3), (dict(q=Q + 8), 3), (dict(s=S + 1), 3),
+    (dict(q=X), 8), (dict(s=X + 64), 8), (dict(s=Q + 32), 8),
+])
+def test_int8_quantize_validation(kwargs, status):
+    # refusals are decided on the host, before any device call
+    assert _int8_quantize(**kwargs) == status
+
+
 def _int8_linear(x=X, q=Q, s=S, y=Y, L=128, K=4096, N=4096, scale=1.0, epi=1):
     return lq.load_library().lut6_int8_linear(x, q, s, y, L, K, N, scale, epi, None)
 
@@ -357,6 +372,21 @@ def test_binding_gated_delta_shapes(meta_device):
         lq.gated_delta(q, k, v, g, b, st, out=meta_device((L + 1, 512), f16), **kw)
     with pytest.raises(lq.Lut6Error):
         lq.gated_delta(q, k, v, g, b, st, **kw)
+
+
+def test_binding_int8_quantize_shapes(meta_device):
+    import torch
+    w = meta_device((4, 64), torch.float16)
+    with pytest.raises(ValueError):
+        lq.int8_quantize(meta_device((4, 48), torch.float16))
+    with pytest.raises(ValueError):
+        lq.int8_quantize(w, q=meta_device((4, 32), torch.int8))
+    with pytest.raises(ValueError):
+        lq.int8_quantize(w, scales=meta_device((4, 1), torch.float16))
+    with pytest.raises(TypeError):
+        lq.int8_quantize(meta_device((4, 64), torch.float32))
+    with pytest.raises(lq.Lut6Error):
+        lq.int8_quantize(w)
 
 
 def test_binding_quantize_shapes(meta_device):

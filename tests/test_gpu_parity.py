@@ -477,6 +477,51 @@ def test_int8_full_layer_sampled_rows(ora, L, K, N, epi):
     assert rep.ok, rep
 
 
+# int8 code selection: codes and scales bit-exact against the oracle
+
+@pytest.mark.parametrize("N,K", [(1, 32), (16, 96), (96, 4096), (4096, 4096), (24576, 4096)])
+def test_int8_quantize_matches_oracle(ora, N, K):
+    _say("int8 quantize", N, K)
+    w = si.weights(N, K, (13, N, K))
+    q, sc = lq.int8_quantize(_dev(w))
+    torch.cuda.synchronize()
+    qo, so = ora.int8_quantize(w)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), so)
+
+
+def test_int8_quantize_every_block_maximum(ora):
+    # one block per finite positive FP16 magnitude a (a, -a and 30 seeded
+    # fractions of it) and two zero blocks: every rounding of the scale,
+    # subnormal scales and the clamp included, decided on the device as in
+    # the oracle
+    _say("int8 quantize every maximum")
+    a = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    g = np.random.default_rng(14)
+    f = g.uniform(-1.0, 1.0, size=(a.size, 30))
+    w = np.concatenate([a[:, None], -a[:, None], a[:, None] * f], axis=1).astype(np.float16)
+    w = np.concatenate([w, np.zeros((2, 32), np.float16)], axis=0)
+    q, sc = lq.int8_quantize(_dev(w))
+    torch.cuda.synchronize()
+    qo, so = ora.int8_quantize(w)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_int8_quantize_feeds_int8_linear(ora):
+    # the device's codes and scales drive int8_linear to the oracle's result
+    _say("int8 quantize then linear")
+    L, K, N = 64, 1024, 256
+    w = si.weights(N, K, (15, N, K))
+    q, sc = lq.int8_quantize(_dev(w))
+    x = si.activations(L, K, 1.0, (15, L, N))
+    y = lq.int8_linear(_dev(x), q, sc, epilogue=F16)
+    torch.cuda.synchronize()
+    qo, so = ora.int8_quantize(w)
+    rep = _int8_check(ora, x, qo, so.view(np.float16), F16, 1.0, y.cpu().numpy().view(np.uint16))
+    assert rep.ok, rep
+
+
 # ---------------------------------------------------------------------------
 # full attention: FP16 probabilities x 16, against the exact softmax
 # ---------------------------------------------------------------------------

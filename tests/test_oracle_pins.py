@@ -668,6 +668,17 @@ def pin_int8_quantize_round_trip(ora):
     assert np.array_equal(qn.astype(np.int64), -q.astype(np.int64)) and np.array_equal(qsn, qs)
 
 
+def test_int8_scale_is_one_rounding_in_fp32():
+    # the device takes fp16(fp32(a) / 127) for the block scale, two roundings;
+    # for every finite FP16 magnitude it equals the single rounding of a / 127
+    # (through FP64, whose 53 bits cannot land on an FP16 midpoint here), so
+    # oracle and device agree on every scale
+    a = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)
+    f32 = (a.astype(np.float32) / np.float32(127)).astype(np.float16)
+    f64 = (a.astype(np.float64) / 127.0).astype(np.float16)
+    assert np.array_equal(f32.view(np.uint16), f64.view(np.uint16))
+
+
 PINS = [pin_pack_worked_examples, pin_pack_exhaustive, pin_storage, pin_f16_decode,
         pin_f16_encode, pin_dequant, pin_linear_bruteforce, pin_linear_silu,
         pin_special_tables, pin_identity_readout, pin_in_scale, pin_int8_dequant,
