@@ -29,9 +29,11 @@
  * The library keeps no per-call state.  It owns lazily created device
  * workspaces, one of each kind per (device, stream): split-K partial sums,
  * and the expanded FP16 weight of the many-token path (see
- * lut6_linear_path); each is created on the first call that needs it,
- * grown when a later call needs more (after synchronising that stream) and
- * freed by lut6_release().
+ * lut6_linear_path); each is created on the first call that needs it and
+ * grown when a later call needs more, both in stream order
+ * (hipMallocAsync, and hipFreeAsync of the smaller buffer after the work
+ * already enqueued on that stream: the host is not stopped), and freed by
+ * lut6_release().
  *
  * Errors: every function returns LUT6_OK (0) or a named status, and launches
  * nothing on error.  Arguments are checked on the host; nothing is silently

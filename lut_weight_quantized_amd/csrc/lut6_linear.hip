@@ -1867,15 +1867,17 @@ int workspace_for(hipStream_t stream, int kind, size_t bytes, void** out)
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& w = g_ws[std::make_tuple(dev, (uintptr_t)stream, kind)];
     if (w.bytes < bytes) {
+        // grown in stream order, without stopping the host: the old buffer
+        // is released once the work already enqueued on this stream (which
+        // may still use it) is done, and the new one is valid for the work
+        // enqueued after this call
         if (w.ptr) {
-            // a previous launch on this stream may still use the old buffer
-            if (hipStreamSynchronize(stream) != hipSuccess) return LUT6_E_DEVICE;
-            (void)hipFree(w.ptr);
+            if (hipFreeAsync(w.ptr, stream) != hipSuccess) return LUT6_E_DEVICE;
             w.ptr = nullptr;
             w.bytes = 0;
         }
         void* p = nullptr;
-        if (hipMalloc(&p, bytes) != hipSuccess) return LUT6_E_DEVICE;
+        if (hipMallocAsync(&p, bytes, stream) != hipSuccess) return LUT6_E_DEVICE;
         w.ptr = p;
         w.bytes = bytes;
     }
@@ -2326,7 +2328,10 @@ extern "C" int lut6_release(void)
         const int dev = std::get<0>(kv.first);
         if (hipSetDevice(dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
             status = LUT6_E_DEVICE;
-        (void)hipFree(kv.second.ptr);
+        // stream-ordered allocations, freed on the null stream (the stream
+        // they were made on may no longer exist), the device idle
+        if (hipFreeAsync(kv.second.ptr, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+            status = LUT6_E_DEVICE;
     }
     g_ws.clear();
     (void)hipSetDevice(cur);

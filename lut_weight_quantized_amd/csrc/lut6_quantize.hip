@@ -371,14 +371,15 @@ int q_workspace(hipStream_t stream, size_t bytes, void** out)
     std::lock_guard<std::mutex> lock(g_qws_mutex);
     QWorkspace& ws = g_qws[std::make_tuple(dev, (uintptr_t)stream)];
     if (ws.bytes < bytes) {
+        // grown in stream order (no host synchronisation): the old buffer is
+        // released after the work already enqueued on this stream
         if (ws.ptr) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return LUT6_E_DEVICE;
-            (void)hipFree(ws.ptr);
+            if (hipFreeAsync(ws.ptr, stream) != hipSuccess) return LUT6_E_DEVICE;
             ws.ptr = nullptr;
             ws.bytes = 0;
         }
         void* p = nullptr;
-        if (hipMalloc(&p, bytes) != hipSuccess) return LUT6_E_DEVICE;
+        if (hipMallocAsync(&p, bytes, stream) != hipSuccess) return LUT6_E_DEVICE;
         ws.ptr = p;
         ws.bytes = bytes;
     }
@@ -499,7 +500,8 @@ int quantize_release()
         if (!kv.second.ptr) continue;
         if (hipSetDevice(std::get<0>(kv.first)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
             status = LUT6_E_DEVICE;
-        (void)hipFree(kv.second.ptr);
+        if (hipFreeAsync(kv.second.ptr, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+            status = LUT6_E_DEVICE;
     }
     g_qws.clear();
     (void)hipSetDevice(cur);
