@@ -201,6 +201,41 @@ def test_cold_activation_calls(ora, L, K, N, epi):
         assert rep.ok, f"trial {trial}: {rep}"
 
 
+def test_workspaces_grow_per_stream_and_after_release(ora):
+    # Each call below needs a larger workspace than the stream's previous one
+    # (expanded weight at L >= 1,536, split-K partials at L = 40).  The calls
+    # alternate between two streams and are enqueued with no host wait in
+    # between: a stream's workspace grows in stream order (the smaller buffer
+    # freed behind the work already on it).  After lut6_release they are made
+    # again.  Every result meets the criteria on sampled rows.
+    _say("workspaces")
+    shapes = [(1536, 256, 256, F16), (40, 1024, 2080, F32), (1536, 512, 512, F16),
+              (40, 2048, 4160, F32), (1536, 1024, 1024, F16)]
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def run_all():
+        done = []
+        for i, (L, K, N, epi) in enumerate(shapes):
+            x, idx, tab = _problem(L, K, N, 900 + i)
+            st = side if i % 2 else main
+            with torch.cuda.stream(st):
+                y = lq.linear(_dev(x), _dev(lq.pack(idx)), _dev(tab), epilogue=epi, stream=st)
+            done.append((x, idx, tab, epi, y))
+        torch.cuda.synchronize()
+        for x, idx, tab, epi, y in done:
+            L = x.shape[0]
+            yh = y.cpu().numpy()
+            yh = yh.view(np.uint16) if epi != F32 else yh
+            rows = np.unique(np.concatenate([np.arange(0, L, max(1, L // 24)), [L - 1]]))
+            rep = oracle_check(ora, x, idx, tab, epi, 1.0, yh, rows=rows)
+            assert rep.ok, str(rep)
+
+    run_all()
+    lq.release()
+    run_all()
+
+
 def test_non_aligned_n_tiles(ora):
     # N = 16 * odd so the last channel tile is partial in both regimes
     for L in (64, 384, 1088):
