@@ -129,9 +129,9 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
         // 2 (8 w + i) + L / 32, so it reads the piece that belongs there.
         // Keys past Lk re-read key Lk - 1 (they are masked).
         // copy n (0..15): K (n even) or V (n odd) rows of wave copy i = n / 2
-        auto issue_kv = [&](int kb, uint16_t* kst, int n) {
+        auto issue_kv = [&](int kb, uint16_t* kst, int n, int ln) {
             const int i = n >> 1;
-            const int r = 2 * (8 * wave + i) + (lane >> 5), sl = lane & 31;
+            const int r = 2 * (8 * wave + i) + (ln >> 5), sl = ln & 31;
             const size_t key = (size_t)min(kb * BKEY + r, a.Lk - 1);
             if ((n & 1) == 0)
                 __builtin_amdgcn_global_load_lds(a.k + key * a.ldk + (size_t)kh * HD + 8 * (sl ^ (r & 15)),
@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
 
         const float cl = 1.4426950408889634f / 16.0f;          // log2(e) / sqrt(256)
 #pragma unroll
-        for (int n = 0; n < 16; ++n) issue_kv(kb0, lds0, n);
+        for (int n = 0; n < 16; ++n) issue_kv(kb0, lds0, n, lane);
         __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
         // block kb from stage ks while the next block is copied into nst
@@ -153,6 +153,11 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
             // previous barrier), one copy after each pair of the S^T
             // products below; the last block again on the last iteration
             const int kn = min(kb + 1, kb1 - 1);
+            // every LDS and global address below is derived from an opaque
+            // copy of the lane id, so the compiler recomputes them per block
+            // (hoisted, about 70 of them stayed live through the loop)
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
 
             // S^T for keys 32 st .. 32 st + 31 of the block: lane (c, h),
             // value r is key 8 (r / 4) + 4 h + r % 4 of the tile, query c
@@ -170,8 +175,8 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
             // The K fragments are read two steps ahead: the compiler does
             // not move an LDS read above a copy into LDS.
             auto kfrag = [&](int j, int st) {
-                const int kr_ = 32 * st + c;
-                return *(const f16x8*)(ks + kr_ * HD + 8 * ((2 * j + h) ^ (kr_ & 15)));
+                const int kr_ = 32 * st + (ln & 31);
+                return *(const f16x8*)(ks + kr_ * HD + 8 * ((2 * j + (ln >> 5)) ^ (kr_ & 15)));
             };
             f16x8 ka[3][2];
 #pragma unroll
@@ -187,7 +192,7 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
                 for (int st = 0; st < 2; ++st)
                     s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[j % 3][st], __builtin_bit_cast(f16x8, qf[j]),
                                                                    s[st], 0, 0, 0);
-                issue_kv(kn, nst, j);
+                issue_kv(kn, nst, j, ln);
             }
 
             // online softmax (base 2) on the raw scores: masked keys get
@@ -251,8 +256,8 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
                 for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                     for (int dt = 0; dt < 8; ++dt) {
-                        const int gi = lane & 15, vr_ = 32 * st + 16 * jj + 4 * h + (gi >> 2);
-                        const int vp_ = 4 * dt + 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
+                        const int gi = ln & 15, vr_ = 32 * st + 16 * jj + 4 * (ln >> 5) + (gi >> 2);
+                        const int vp_ = 4 * dt + 2 * ((ln >> 4) & 1) + ((gi & 3) >> 1);
                         const uint16_t* vp = vs + vr_ * HD + 8 * (vp_ ^ ((vr_ & 3) << 2)) + 4 * (gi & 1);
                         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp);
                         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
