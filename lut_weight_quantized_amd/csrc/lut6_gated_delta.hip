@@ -505,13 +505,18 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
                     qf[8 * z + i] = half_at(cur.qr[z] & km, i);
                 }
             xk = xq = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            // each group's S0 column piece is read one group ahead, so that
+            // no product waits for an LDS round trip
+            f32x4 bv[2];
+            bv[0] = *(const f32x4*)&st[lo][8 * hi];
 #pragma unroll
             for (int m4 = 0; m4 < 8; ++m4) {
-                const f32x4 bv = *(const f32x4*)&st[lo][32 * (m4 >> 1) + 8 * hi + 4 * (m4 & 1)];
+                if (m4 + 1 < 8)
+                    bv[(m4 + 1) & 1] = *(const f32x4*)&st[lo][32 * ((m4 + 1) >> 1) + 8 * hi + 4 * ((m4 + 1) & 1)];
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm) {
-                    xk = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[4 * m4 + mm], bv[mm], xk, 0, 0, 0);
-                    xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * m4 + mm], bv[mm], xq, 0, 0, 0);
+                    xk = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[4 * m4 + mm], bv[m4 & 1][mm], xk, 0, 0, 0);
+                    xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * m4 + mm], bv[m4 & 1][mm], xq, 0, 0, 0);
                 }
             }
 #pragma unroll
@@ -530,9 +535,15 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
             // pace the next chunk's 16 row loads (k, q, T, P) one per four
             // of the 64 matrix instructions: issued back to back they fill
             // the vector memory path, and the in-order wave then stalls at
-            // each further load while its matrix work waits behind it
+            // each further load while its matrix work waits behind it.  The
+            // S0 pieces are read one group of 8 products ahead (left to
+            // itself the compiler reads each just before its products).
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < 8; ++i) {
+                if (i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
@@ -545,13 +556,17 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         // accumulation chains (even and odd steps).
         {
             f32x4 d2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+            // all four R pieces are read before the first product
+            f32x4 rv[4];
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                const f32x4 rv = *(const f32x4*)&rt[lo][16 * z + 4 * hi];
+            for (int z = 0; z < 4; ++z) rv[z] = *(const f32x4*)&rt[lo][16 * z + 4 * hi];
+#pragma unroll
+            for (int z = 0; z < 4; ++z)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    d2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.tv[z][j], rv[j], d2[j & 1], 0, 0, 0);
-            }
+                    d2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.tv[z][j], rv[z][j], d2[j & 1], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
             const f32x4 d = d2[0] + d2[1];
             *(f32x4*)&dt[lo][16 * w + 4 * hi] = d;
 #pragma unroll
@@ -583,13 +598,15 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
             f32x4 o2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
             for (int e = 0; e < 4; ++e) o2[0][e] = vec[b][0][16 * w + 4 * hi + e] * xq[e];
+            // all four D pieces are read before the first product
+            f32x4 dv[4];
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                const f32x4 dv = *(const f32x4*)&dt[lo][16 * z + 4 * hi];
+            for (int z = 0; z < 4; ++z) dv[z] = *(const f32x4*)&dt[lo][16 * z + 4 * hi];
+#pragma unroll
+            for (int z = 0; z < 4; ++z)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    o2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pv[z][j], dv[j], o2[j & 1], 0, 0, 0);
-            }
+                    o2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pv[z][j], dv[z][j], o2[j & 1], 0, 0, 0);
             const f32x4 o = o2[0] + o2[1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) ob[e] = __builtin_bit_cast(uint16_t, (_Float16)(o[e] * rsq));
