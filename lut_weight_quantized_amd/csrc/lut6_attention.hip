@@ -14,7 +14,8 @@
 //     the FP32 sum of the p_j; one FP16 rounding of o.
 //
 // Design: one workgroup per (query head, 128 queries), four waves of 32
-// queries.  Keys go by blocks of 64 through two LDS stages, K and V both
+// queries.  Keys go by blocks of 64 (or of 32, with two workgroups per CU,
+// when a launch has many workgroups) through two LDS stages, K and V both
 // row-major and copied straight from global memory into LDS: a block is
 // computed from one stage while the next block is copied into the other;
 // one barrier per block.  Short query chunks over a long cache split the
@@ -40,8 +41,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int HD = 256;               // head size
 constexpr int BQ = 128;               // queries per workgroup
-constexpr int BKEY = 64;              // keys per block
-constexpr int TILE_HALVES = BKEY * HD;  // one K or V tile in LDS: 64 rows of 512 B, unpadded
+constexpr int BKEY = 64;              // keys per block (key splits and fewer workgroups)
+constexpr int BKEY_SMALL = 32;        // keys per block with two workgroups per CU
+// Launches of at least this many workgroups (and no key split) use 32-key
+// blocks: 64 KB of LDS and at most 256 registers per lane, so two
+// workgroups share a CU and each SIMD runs two waves.  With fewer, the
+// causal work is too uneven for the pairs to pay.
+constexpr int64_t SMALL_BLOCK_MIN_WGS = 768;
 constexpr int WS_ATTENTION = 2;       // library workspace kind of the key-split partials
 
 struct AttArgs {
@@ -68,7 +74,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b)
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-// one LDS stage: K [64][256], then V [64][256], both row-major.  Rows are
+// one LDS stage: K [BK][256], then V [BK][256], both row-major.  Rows are
 // copied straight from global memory (64 lanes x 16 bytes, two rows per
 // instruction), so instead of padding, the 16-byte pieces of a row are
 // XOR-swizzled: piece p (dims 8 p .. 8 p + 7) of key row r sits in slot
@@ -76,14 +82,17 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b)
 //      one piece, which land on 16 distinct 4-bank groups;
 //   V: p ^ 4 (r & 3): a transposing read's 16 lanes take 4 rows x 4 pieces,
 //      also 16 distinct groups.
-constexpr int STAGE_HALVES = 2 * TILE_HALVES;
 constexpr int VMCNT0 = 0x0F70;        // s_waitcnt: vmcnt = 0, other counters not waited for
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <bool SPLIT>
-__global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
+template <bool SPLIT, int BK>
+__global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_kernel(AttArgs a)
 {
+    constexpr int NST = BK / 32;                   // 32-key tiles per block
+    constexpr int NCOPY = BK / 4;                  // copies per wave and block (K and V)
+    constexpr int TILE_HALVES = BK * HD;           // one K or V tile in LDS, unpadded
+    constexpr int STAGE_HALVES = 2 * TILE_HALVES;
     // the two stages are separate arrays: the compiler then sees that a copy
     // into one cannot overwrite what is being read from the other, and does
     // not drain the outstanding LDS reads before each copy
@@ -101,7 +110,7 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
     const int off = a.Lk - a.L;                                // position of query 0
     const int pos = off + qrow;                                // this lane's query position
     const int last = off + min(q0 + BQ - 1, a.L - 1);          // last key the workgroup needs
-    int kb0 = 0, kb1 = last / BKEY + 1;
+    int kb0 = 0, kb1 = last / BK + 1;
     if constexpr (SPLIT) {
         kb0 = min((int)blockIdx.y * a.kb_per_split, kb1);
         kb1 = min(kb0 + a.kb_per_split, kb1);
@@ -124,26 +133,27 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
             for (int j = 0; j < 16; ++j) qf[j] = *(const u32x4*)(qp + 16 * j);
         }
 
-        // staging: wave w's copy i fills rows 2 (8 w + i) and 2 (8 w + i) + 1
-        // of the K and of the V tile; lane L writes slot L % 32 of row
-        // 2 (8 w + i) + L / 32, so it reads the piece that belongs there.
-        // Keys past Lk re-read key Lk - 1 (they are masked).
-        // copy n (0..15): K (n even) or V (n odd) rows of wave copy i = n / 2
+        // staging: wave w's copy i fills rows 2 (C w + i) and 2 (C w + i) + 1
+        // of the K and of the V tile (C = NCOPY / 2 copies per wave and
+        // tile); lane L writes slot L % 32 of row 2 (C w + i) + L / 32, so it
+        // reads the piece that belongs there.  Keys past Lk re-read key
+        // Lk - 1 (they are masked).
+        // copy n (0..NCOPY-1): K (n even) or V (n odd) rows of wave copy i = n / 2
         auto issue_kv = [&](int kb, uint16_t* kst, int n, int ln) {
             const int i = n >> 1;
-            const int r = 2 * (8 * wave + i) + (ln >> 5), sl = ln & 31;
-            const size_t key = (size_t)min(kb * BKEY + r, a.Lk - 1);
+            const int r = 2 * (NCOPY / 2 * wave + i) + (ln >> 5), sl = ln & 31;
+            const size_t key = (size_t)min(kb * BK + r, a.Lk - 1);
             if ((n & 1) == 0)
                 __builtin_amdgcn_global_load_lds(a.k + key * a.ldk + (size_t)kh * HD + 8 * (sl ^ (r & 15)),
-                                                 (lds_ptr_t)(kst + (8 * wave + i) * 512), 16, 0, 0);
+                                                 (lds_ptr_t)(kst + (NCOPY / 2 * wave + i) * 512), 16, 0, 0);
             else
                 __builtin_amdgcn_global_load_lds(a.v + key * a.ldv + (size_t)kh * HD + 8 * (sl ^ ((r & 3) << 2)),
-                                                 (lds_ptr_t)(kst + TILE_HALVES + (8 * wave + i) * 512), 16, 0, 0);
+                                                 (lds_ptr_t)(kst + TILE_HALVES + (NCOPY / 2 * wave + i) * 512), 16, 0, 0);
         };
 
         const float cl = 1.4426950408889634f / 16.0f;          // log2(e) / sqrt(256)
 #pragma unroll
-        for (int n = 0; n < 16; ++n) issue_kv(kb0, lds0, n, lane);
+        for (int n = 0; n < NCOPY; ++n) issue_kv(kb0, lds0, n, lane);
         __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
         // block kb from stage ks while the next block is copied into nst
@@ -163,9 +173,9 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
             // value r is key 8 (r / 4) + 4 h + r % 4 of the tile, query c
             // (the two tiles' products alternate, so that no product waits
             // for the one before it to finish)
-            f32x16 s[2];
+            f32x16 s[NST];
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
             // (issued back to back, the 16 copies fill the vector memory
@@ -178,38 +188,38 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
                 const int kr_ = 32 * st + (ln & 31);
                 return *(const f16x8*)(ks + kr_ * HD + 8 * ((2 * j + (ln >> 5)) ^ (kr_ & 15)));
             };
-            f16x8 ka[3][2];
+            f16x8 ka[3][NST];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int st = 0; st < 2; ++st) ka[j][st] = kfrag(j, st);
+                for (int st = 0; st < NST; ++st) ka[j][st] = kfrag(j, st);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 if (j + 2 < 16)
 #pragma unroll
-                    for (int st = 0; st < 2; ++st) ka[(j + 2) % 3][st] = kfrag(j + 2, st);
+                    for (int st = 0; st < NST; ++st) ka[(j + 2) % 3][st] = kfrag(j + 2, st);
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
+                for (int st = 0; st < NST; ++st)
                     s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[j % 3][st], __builtin_bit_cast(f16x8, qf[j]),
                                                                    s[st], 0, 0, 0);
-                issue_kv(kn, nst, j, ln);
+                if (j % (16 / NCOPY) == 0) issue_kv(kn, nst, j / (16 / NCOPY), ln);
             }
 
             // online softmax (base 2) on the raw scores: masked keys get
             // -inf, only in blocks that reach past the workgroup's first
             // query; the block maximum is scaled after the max (cl > 0)
             float bm = -__builtin_inff();
-            if (kb * BKEY + BKEY - 1 > off + q0) {
+            if (kb * BK + BK - 1 > off + q0) {
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
+                for (int st = 0; st < NST; ++st)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = kb * BKEY + 32 * st + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const int key = kb * BK + 32 * st + 8 * (r >> 2) + 4 * h + (r & 3);
                         if (key > pos) s[st][r] = -__builtin_inff();
                     }
             }
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) bm = fmaxf(bm, s[st][r]);
             bm = fmaxf(bm, __shfl_xor(bm, 32)) * cl;
@@ -233,7 +243,7 @@ __global__ void __launch_bounds__(256) lut6_attention_kernel(AttArgs a)
             // not wait for tile 0's products, so the two can overlap.
             float sum = 0.0f;
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+            for (int st = 0; st < NST; ++st) {
                 u32x4 pf[2];
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
@@ -412,14 +422,16 @@ extern "C" int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t
         if (st != LUT6_OK) return st;
         a.part_o = (float*)ws;
         a.part_ml = a.part_o + rows * HD;
-        hipLaunchKernelGGL(lut6_attention_kernel<true>, dim3((unsigned)blocks, (unsigned)splits), dim3(256),
+        hipLaunchKernelGGL((lut6_attention_kernel<true, BKEY>), dim3((unsigned)blocks, (unsigned)splits), dim3(256),
                            0, stream, a);
         if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
         const int64_t threads = (int64_t)L * n_heads * (HD / 4);
         hipLaunchKernelGGL(lut6_attention_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256),
                            0, stream, a, splits);
+    } else if (blocks >= SMALL_BLOCK_MIN_WGS) {
+        hipLaunchKernelGGL((lut6_attention_kernel<false, BKEY_SMALL>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     } else {
-        hipLaunchKernelGGL(lut6_attention_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((lut6_attention_kernel<false, BKEY>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? LUT6_OK : LUT6_E_DEVICE;
 }

@@ -156,7 +156,9 @@ def silu_scale(g_exact: np.ndarray, u_exact: np.ndarray, S_row: np.ndarray) -> n
 #   * eps_acc = (16 nkb + 320) 2^-24, nkb = key blocks of 64: the FP32
 #     accumulation chains of o (4 products of 16 per block) and l, and the
 #     per-block rescales, which o and l share, so they only perturb the
-#     weights of the average;
+#     weights of the average (a device that takes keys in blocks of 32 has
+#     the same chains per 64 keys and at most one more rescale, within the
+#     16 counted per block);
 #   * the FP16 rounding of o, and the FP32 product by 1 / (16 l).
 # S1 is bounded by ||q_row,head||_1 * max|k|.
 

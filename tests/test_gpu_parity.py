@@ -645,10 +645,13 @@ def test_attention_tiny_probabilities_keep_their_mass(ora):
     assert ok, (bad, ratio)
 
 
-@pytest.mark.parametrize("L,Lk", [(16384, 16384), (128, 16384)])
+@pytest.mark.parametrize("L,Lk", [(16384, 16384), (128, 16384), (6200, 6200), (6208, 7000)])
 def test_attention_full_size_sampled_rows(ora, L, Lk):
     # the attention layers at the longest context: the whole prefill, and
-    # the last 128-token chunk over the full cache; q|k|v in one buffer
+    # the last 128-token chunk over the full cache; q|k|v in one buffer.
+    # 16,384 and the two shapes of about 6,200 queries (784 workgroups, a
+    # ragged last query block, one over a longer cache) take 32-key blocks
+    # with two workgroups per CU; 128 queries split the keys
     _say("attention full", L, Lk)
     g = np.random.default_rng(L)
     kv = _dev(g.standard_normal((Lk, 2048)).astype(np.float16))
