@@ -380,14 +380,17 @@ __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
 }
 
 // The recurrence over the chunks of a window: one workgroup per (value head,
-// 16 state columns).  Per chunk every wave takes one 16-row tile of each
-// product and two of the state: K S0 and Q S0 rows 16 w .. 16 w + 15, then
-// its tile of R = beta (v - gamma K S0), D = T R, the state rows 32 w ..
-// 32 w + 31 and the output rows 16 w .. 16 w + 15, so the four waves carry
-// equal work between the three barriers.  A chunk's operands (its k and q
-// rows, v, rows of T and P, the decay vectors) are loaded into registers
-// while the chunk before it is computed.
-__global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
+// 16 state columns), eight waves, two per SIMD.  Wave w has the role p = w / 4
+// (0: K, 1: Q) on the row block r = w % 4 of the chunk: per chunk a K wave
+// takes rows 16 r .. 16 r + 15 of K S0, then of R = beta (v - gamma K S0) and
+// D = T R; a Q wave the same rows of Q S0, then of the output O = gamma Q S0
+// + P D; and every wave one 16-row tile of the state update (tile w).  Both
+// roles run the same loads and the same first product on their own rows (k
+// and T rows, or q and P rows), so the compiler's counts of loads in flight
+// are exact on both, and the two waves on a SIMD fill each other's stalls.
+// A chunk's operands are loaded into registers while the chunk before it is
+// computed.
+__global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
 {
     __shared__ __attribute__((aligned(16))) float st[CB][DK + 4];     // S^T of the block
     __shared__ __attribute__((aligned(16))) float ks[CH][DK + 16];    // k rows of the chunk
@@ -396,7 +399,9 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
     __shared__ float dh[CH][CB];                                      // eta D
     __shared__ float vec[2][3][CH];                                   // gamma, eta, beta (two chunks)
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lo = lane & 15, hi = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, lo = lane & 15, hi = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int role = w >> 2, r = w & 3;
     // the 8 column blocks of a head share its chunk data: keep them on one
     // XCD (dispatch is round-robin over the 8 XCDs)
     const int h = blockIdx.x % a.Hv, jb = blockIdx.x / a.Hv;
@@ -404,31 +409,34 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
     const int col0 = h * DV + jb * CB;
     float* const sp = a.state + (size_t)h * DK * DV + jb * CB;
     const float rsq = 0.08838834764831845f;           // 1 / sqrt(128)
-    const uint16_t* const ksrc = a.k + (size_t)kq * DK + 8 * hi;
-    const uint16_t* const qsrc = a.q + (size_t)kq * DK + 8 * hi;
+    // this wave's row operand: k rows and T rows (K waves), q rows and P rows
+    // (Q waves)
+    const uint16_t* const xsrc = (role ? a.q : a.k) + (size_t)kq * DK + 8 * hi;
+    const int64_t ldx = role ? a.ldq : a.ldk;
+    const int wsm = role ? WS_P : WS_T;
     float* const wsh = a.ws + (size_t)h * a.n_chunks * WS_FLOATS;
-    const int trow = 16 * w + lo;                     // this lane's A-operand row of the tiles
+    const int trow = 16 * r + lo;                     // this lane's A-operand row of the tiles
 
-    // S^T tiles r = 2w, 2w + 1: lane holds S[16 r + lo][4 hi + e]
-    f32x4 sacc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = 16 * (2 * w + u) + lo;
+    // S^T tile w: lane holds S[16 w + lo][4 hi + e]
+    f32x4 sacc;
+    {
+        const int i = 16 * w + lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            sacc[u][e] = sp[(size_t)i * DV + 4 * hi + e];
-            st[4 * hi + e][i] = sacc[u][e];
+            sacc[e] = sp[(size_t)i * DV + 4 * hi + e];
+            st[4 * hi + e][i] = sacc[e];
         }
     }
 
-    // one chunk's register operands: the lane's k and q row pieces (row
-    // trow, k = 32 z + 8 hi + i), its T and P row pieces (columns 16 z +
-    // 4 hi + j), v of its R rows (16 w + 4 hi + e) and one decay-vector entry
-    // (threads < 192).  In each load the four lane groups hi = 0..3 of a row
-    // read 64 contiguous bytes, so one instruction touches 16 row segments.
+    // one chunk's register operands: the lane's k or q row pieces (row trow,
+    // k = 32 z + 8 hi + i), its T or P row pieces (columns 16 z + 4 hi + j),
+    // v of its R rows (16 r + 4 hi + e; used by K waves) and one
+    // decay-vector entry (threads < 192).  In each row load the four lane
+    // groups hi = 0..3 of a row read 64 contiguous bytes, so one instruction
+    // touches 16 row segments.
     struct Ops {
-        u32x4 kr[4], qr[4];
-        f32x4 tv[4], pv[4];
+        u32x4 xr[4];
+        f32x4 mv[4];
         uint32_t vr[4];
         float vc;
     };
@@ -444,18 +452,12 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         const float* const wsc = wsh + (size_t)c * WS_FLOATS;
         const size_t tr = (size_t)min(t0 + trow, a.L - 1);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) {
-            op.kr[z] = *(const u32x4*)(ksrc + tr * a.ldk + 32 * z);
-            op.qr[z] = *(const u32x4*)(qsrc + tr * a.ldq + 32 * z);
-        }
+        for (int z = 0; z < 4; ++z) op.xr[z] = *(const u32x4*)(xsrc + tr * ldx + 32 * z);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) {
-            op.tv[z] = *(const f32x4*)(wsc + WS_T + trow * CH + 16 * z + 4 * hi);
-            op.pv[z] = *(const f32x4*)(wsc + WS_P + trow * CH + 16 * z + 4 * hi);
-        }
+        for (int z = 0; z < 4; ++z) op.mv[z] = *(const f32x4*)(wsc + wsm + trow * CH + 16 * z + 4 * hi);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            op.vr[e] = a.v[(size_t)min(t0 + 16 * w + 4 * hi + e, a.L - 1) * a.ldv + col0 + lo];
+            op.vr[e] = a.v[(size_t)min(t0 + 16 * r + 4 * hi + e, a.L - 1) * a.ldv + col0 + lo];
         op.vc = wsc[WS_GAMMA + (tid < 3 * CH ? tid : 0)];
     };
 
@@ -463,19 +465,19 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
     // stores count in the same in-order counter as loads, so stores issued
     // just before the barrier made the wait for the next operands also wait
     // for the write acknowledgements.  Like the loads, the stores are
-    // unconditional: rows past L, and the empty store of chunk 0, go to the
-    // unused pad of a workspace block.
+    // unconditional: K waves, rows past L and the empty store of chunk 0 go
+    // to the unused pad of a workspace block.
     uint16_t ob[4] = {0, 0, 0, 0};
     auto store_o = [&](int cc, bool real) {
         const int t0c = a.t_begin + cc * CH;
         uint16_t* const pad = (uint16_t*)(wsh + (size_t)cc * WS_FLOATS + WS_PAD) + lane;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int tg = t0c + 16 * w + 4 * hi + e;
+            const int tg = t0c + 16 * r + 4 * hi + e;
             // both addresses are formed first so that the choice is a select,
             // not a branch around the multiply
             uint16_t* const row = a.o + (size_t)min(tg, a.L - 1) * a.ldo + col0 + lo;
-            *(real && tg < a.L ? row : pad) = ob[e];
+            *(real && role == 1 && tg < a.L ? row : pad) = ob[e];
         }
     };
 
@@ -490,21 +492,18 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         load_ops(c + 1 < a.n_chunks ? c + 1 : c, nxt);
         store_o(c > 0 ? c - 1 : 0, c > 0);
 
-        // stage 1: rows 16 w .. 16 w + 15 of K S0 and Q S0 (step n takes
-        // k = 32 (n / 8) + 8 hi + n % 8), the k row to LDS for the state
-        // update, R to LDS
-        f32x4 xk, xq;
+        // stage 1: rows 16 r .. 16 r + 15 of K S0 (K waves) or Q S0 (Q
+        // waves), step n taking k = 32 (n / 8) + 8 hi + n % 8; K waves then
+        // put the k row in LDS for the state update and R in LDS
+        f32x4 x;
         {
-            float kf[32], qf[32];
+            float xf[32];
             const uint32_t km = t0 + trow < a.L ? 0xffffffffu : 0u;
 #pragma unroll
             for (int z = 0; z < 4; ++z)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    kf[8 * z + i] = half_at(cur.kr[z] & km, i);
-                    qf[8 * z + i] = half_at(cur.qr[z] & km, i);
-                }
-            xk = xq = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int i = 0; i < 8; ++i) xf[8 * z + i] = half_at(cur.xr[z] & km, i);
+            x = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             // each group's S0 column piece is read one group ahead, so that
             // no product waits for an LDS round trip
             f32x4 bv[2];
@@ -514,29 +513,14 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
                 if (m4 + 1 < 8)
                     bv[(m4 + 1) & 1] = *(const f32x4*)&st[lo][32 * ((m4 + 1) >> 1) + 8 * hi + 4 * ((m4 + 1) & 1)];
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    xk = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[4 * m4 + mm], bv[m4 & 1][mm], xk, 0, 0, 0);
-                    xq = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * m4 + mm], bv[m4 & 1][mm], xq, 0, 0, 0);
-                }
+                for (int mm = 0; mm < 4; ++mm)
+                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[4 * m4 + mm], bv[m4 & 1][mm], x, 0, 0, 0);
             }
-#pragma unroll
-            for (int z = 0; z < 8; ++z)
-                *(f32x4*)&ks[trow][32 * (z >> 1) + 8 * hi + 4 * (z & 1)] =
-                    f32x4{kf[4 * z], kf[4 * z + 1], kf[4 * z + 2], kf[4 * z + 3]};
-            f32x4 r4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * w + 4 * hi + e;
-                const uint16_t vb = t0 + t < a.L ? (uint16_t)cur.vr[e] : (uint16_t)0;
-                const float vv = (float)__builtin_bit_cast(_Float16, vb);
-                r4[e] = vec[b][2][t] * (vv - vec[b][0][t] * xk[e]);
-            }
-            *(f32x4*)&rt[lo][16 * w + 4 * hi] = r4;
-            // pace the next chunk's 16 row loads (k, q, T, P) one per four
-            // of the 64 matrix instructions: issued back to back they fill
+            // pace the next chunk's 8 row loads (k or q, T or P) one per four
+            // of the 32 matrix instructions: issued back to back they fill
             // the vector memory path, and the in-order wave then stalls at
             // each further load while its matrix work waits behind it.  The
-            // S0 pieces are read one group of 8 products ahead (left to
+            // S0 pieces are read one group of 4 products ahead (left to
             // itself the compiler reads each just before its products).
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
@@ -544,17 +528,30 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
                 if (i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            }
+            if (role == 0) {
+#pragma unroll
+                for (int z = 0; z < 8; ++z)
+                    *(f32x4*)&ks[trow][32 * (z >> 1) + 8 * hi + 4 * (z & 1)] =
+                        f32x4{xf[4 * z], xf[4 * z + 1], xf[4 * z + 2], xf[4 * z + 3]};
+                f32x4 r4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * r + 4 * hi + e;
+                    const uint16_t vb = t0 + t < a.L ? (uint16_t)cur.vr[e] : (uint16_t)0;
+                    const float vv = (float)__builtin_bit_cast(_Float16, vb);
+                    r4[e] = vec[b][2][t] * (vv - vec[b][0][t] * x[e]);
+                }
+                *(f32x4*)&rt[lo][16 * r + 4 * hi] = r4;
             }
         }
         __syncthreads();
 
-        // stage 2: D rows 16 w .. 16 w + 15 = T R (step m takes s = 16 (m / 4)
-        // + 4 hi + m % 4).  R and D are kept transposed in LDS, so a lane's
-        // four entries of one step group are one 16-byte read; two
+        // stage 2 (K waves): D rows 16 r .. 16 r + 15 = T R (step m takes s =
+        // 16 (m / 4) + 4 hi + m % 4).  R and D are kept transposed in LDS, so
+        // a lane's four entries of one step group are one 16-byte read; two
         // accumulation chains (even and odd steps).
-        {
+        if (role == 0) {
             f32x4 d2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
             // all four R pieces are read before the first product
             f32x4 rv[4];
@@ -564,52 +561,50 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
             for (int z = 0; z < 4; ++z)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    d2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.tv[z][j], rv[z][j], d2[j & 1], 0, 0, 0);
+                    d2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.mv[z][j], rv[z][j], d2[j & 1], 0, 0, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
             const f32x4 d = d2[0] + d2[1];
-            *(f32x4*)&dt[lo][16 * w + 4 * hi] = d;
+            *(f32x4*)&dt[lo][16 * r + 4 * hi] = d;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = 16 * w + 4 * hi + e;
+                const int t = 16 * r + 4 * hi + e;
                 dh[t][lo] = vec[b][1][t] * d[e];
             }
         }
         __syncthreads();
 
-        // stage 3: the state rows 32 w .. 32 w + 31, S^T = gamma_63 S0^T +
-        // (eta D)^T K (contraction s = 4 m + hi); then the output rows
-        // 16 w .. 16 w + 15, O = (gamma Q S0 + P D) / sqrt(128)
+        // stage 3: the state rows 16 w .. 16 w + 15, S^T = gamma_63 S0^T +
+        // (eta D)^T K (contraction s = 4 m + hi); then (Q waves) the output
+        // rows 16 r .. 16 r + 15, O = (gamma Q S0 + P D) / sqrt(128)
         {
             const float gt = vec[b][0][CH - 1];
+            f32x4 acc = sacc * gt;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int r = 2 * w + u;
-                f32x4 acc = sacc[u] * gt;
-#pragma unroll
-                for (int m = 0; m < 16; ++m) {
-                    const int s = 4 * m + hi;
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dh[s][lo], ks[s][16 * r + lo], acc, 0, 0, 0);
-                }
-                sacc[u] = acc;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) st[4 * hi + e][16 * r + lo] = acc[e];
+            for (int m = 0; m < 16; ++m) {
+                const int s = 4 * m + hi;
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dh[s][lo], ks[s][16 * w + lo], acc, 0, 0, 0);
             }
-            f32x4 o2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+            sacc = acc;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o2[0][e] = vec[b][0][16 * w + 4 * hi + e] * xq[e];
-            // all four D pieces are read before the first product
-            f32x4 dv[4];
+            for (int e = 0; e < 4; ++e) st[4 * hi + e][16 * w + lo] = acc[e];
+            if (role == 1) {
+                f32x4 o2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-            for (int z = 0; z < 4; ++z) dv[z] = *(const f32x4*)&dt[lo][16 * z + 4 * hi];
+                for (int e = 0; e < 4; ++e) o2[0][e] = vec[b][0][16 * r + 4 * hi + e] * x[e];
+                // all four D pieces are read before the first product
+                f32x4 dv[4];
 #pragma unroll
-            for (int z = 0; z < 4; ++z)
+                for (int z = 0; z < 4; ++z) dv[z] = *(const f32x4*)&dt[lo][16 * z + 4 * hi];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pv[z][j], dv[z][j], o2[j & 1], 0, 0, 0);
-            const f32x4 o = o2[0] + o2[1];
+                for (int z = 0; z < 4; ++z)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ob[e] = __builtin_bit_cast(uint16_t, (_Float16)(o[e] * rsq));
+                    for (int j = 0; j < 4; ++j)
+                        o2[j & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.mv[z][j], dv[z][j], o2[j & 1], 0, 0, 0);
+                const f32x4 o = o2[0] + o2[1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ob[e] = __builtin_bit_cast(uint16_t, (_Float16)(o[e] * rsq));
+            }
         }
         // the next chunk's decay vectors (that buffer was last read before
         // the previous barrier)
@@ -618,11 +613,10 @@ __global__ void __launch_bounds__(256) lut6_gdn_chunk_kernel(ChunkArgs a)
         cur = nxt;
     }
     store_o(a.n_chunks - 1, true);
+    {
+        const int i = 16 * w + lo;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = 16 * (2 * w + u) + lo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sp[(size_t)i * DV + 4 * hi + e] = sacc[u][e];
+        for (int e = 0; e < 4; ++e) sp[(size_t)i * DV + 4 * hi + e] = sacc[e];
     }
 }
 
@@ -722,7 +716,7 @@ extern "C" int lut6_gated_delta(const void* q, int64_t ldq, const void* k, int64
         ca.t_begin = (int)(c0 * CH);
         ca.n_chunks = (int)nc;
         hipLaunchKernelGGL(lut6_gdn_prep_kernel, dim3((unsigned)nc, (unsigned)n_v_heads), dim3(256), 0, stream, ca);
-        hipLaunchKernelGGL(lut6_gdn_chunk_kernel, dim3((unsigned)(n_v_heads * (DV / CB))), dim3(256), 0, stream, ca);
+        hipLaunchKernelGGL(lut6_gdn_chunk_kernel, dim3((unsigned)(n_v_heads * (DV / CB))), dim3(512), 0, stream, ca);
         if (hipGetLastError() != hipSuccess) return LUT6_E_DEVICE;
     }
     return LUT6_OK;
