@@ -160,7 +160,7 @@ __global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_
         auto block = [&](int kb, const uint16_t* ks, uint16_t* nst) {
             const uint16_t* const vs = ks + TILE_HALVES;
             // the next block goes into the other stage (last read before the
-            // previous barrier), one copy after each pair of the S^T
+            // previous barrier), its NCOPY copies spread evenly over the S^T
             // products below; the last block again on the last iteration
             const int kn = min(kb + 1, kb1 - 1);
             // every LDS and global address below is derived from an opaque
@@ -171,15 +171,15 @@ __global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_
 
             // S^T for keys 32 st .. 32 st + 31 of the block: lane (c, h),
             // value r is key 8 (r / 4) + 4 h + r % 4 of the tile, query c
-            // (the two tiles' products alternate, so that no product waits
-            // for the one before it to finish)
+            // (with two tiles their products alternate, so that no product
+            // waits for the one before it to finish)
             f32x16 s[NST];
 #pragma unroll
             for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[st][r] = 0.0f;
-            // (issued back to back, the 16 copies fill the vector memory
-            // path and the in-order wave stalls at the later ones with its
+            // (issued back to back, the copies fill the vector memory path
+            // and the in-order wave stalls at the later ones with its
             // products waiting behind them; the copies write LDS, so the
             // compiler keeps them where they are written)
             // The K fragments are read two steps ahead: the compiler does
