@@ -217,10 +217,14 @@ int lut6_int8_quantize(const void* w, int8_t* q, void* scales, int64_t N, int64_
  * q.  So the fused Q|K|V projection output can be passed in place (q = y,
  * k = y + 4096, v = y + 5120, ld = 6144).  The caller owns every buffer.
  * Rules: head_dim == 256, n_heads % n_kv_heads == 0, n_heads <= 4096,
- * 0 <= L <= Lk < 2^31 - 64, each ld >= its heads * 256 (LUT6_E_SHAPE);
- * pointers 16-byte aligned and every ld a multiple of 8 (LUT6_E_ALIGN); o
- * must not overlap q, k or v (LUT6_E_ALIAS).  L == 0 is a no-op.  No
- * workspace.                                                               */
+ * 0 <= L <= Lk < 2^31 - 64, each ld >= its heads * 256, ldk and ldv at
+ * most 2^24 (LUT6_E_SHAPE); pointers 16-byte aligned and every ld a
+ * multiple of 8 (LUT6_E_ALIGN); o must not overlap q, k or v
+ * (LUT6_E_ALIAS).  L == 0 is a no-op.  A call with fewer than 128
+ * (query block of 128, head) pairs over at least 8 blocks of 64 keys
+ * splits the keys over several workgroups; their partial sums go to a
+ * library workspace of L x n_heads x splits x 1,032 bytes (splits <= 256),
+ * created on the first call that needs it and kept until lut6_release.  */
 int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
                    int64_t ldv, void* o, int64_t ldo, int64_t L, int64_t Lk, int64_t n_heads,
                    int64_t n_kv_heads, int64_t head_dim, hipStream_t stream);

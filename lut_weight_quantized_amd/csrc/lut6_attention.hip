@@ -26,7 +26,11 @@
 // v_mfma_f32_32x32x16_f16; the V^T fragments come from row-major V through
 // the transposing LDS read.  The P^T values never leave registers: the
 // accumulator layout of S^T, with its k slots read in the same key order
-// from V^T, is the B operand of the second product.
+// from V^T, is the B operand of the second product.  Every address in the
+// key loop is a uniform base plus a lane offset computed once (the K
+// fragment offsets from a single base by XOR), so that the loop's vector
+// instructions go to the softmax, and the K and V fragments are read two
+// products ahead of their use.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,6 +52,7 @@ constexpr int BKEY_SMALL = 32;        // keys per block with two workgroups per 
 // workgroups share a CU and each SIMD runs two waves.  With fewer, the
 // causal work is too uneven for the pairs to pay.
 constexpr int64_t SMALL_BLOCK_MIN_WGS = 768;
+constexpr int64_t MAX_KV_LD = int64_t(1) << 24;   // largest k / v row stride, elements
 constexpr int WS_ATTENTION = 2;       // library workspace kind of the key-split partials
 
 struct AttArgs {
@@ -136,24 +141,69 @@ __global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_
         // staging: wave w's copy i fills rows 2 (C w + i) and 2 (C w + i) + 1
         // of the K and of the V tile (C = NCOPY / 2 copies per wave and
         // tile); lane L writes slot L % 32 of row 2 (C w + i) + L / 32, so it
-        // reads the piece that belongs there.  Keys past Lk re-read key
-        // Lk - 1 (they are masked).
+        // reads the piece that belongs there.  A copy's address is a uniform
+        // base (the block's first row) plus the lane's byte offset kco / vco
+        // (32-bit: the host bounds the row strides).  Keys past Lk re-read
+        // key Lk - 1 (they are masked): only the last block can hold such
+        // keys, so the offsets are pulled back once, when that block is the
+        // next one to copy.
+        uint32_t kco[NCOPY / 2], vco[NCOPY / 2];
+#pragma unroll
+        for (int i = 0; i < NCOPY / 2; ++i) {
+            const int r = 2 * (NCOPY / 2 * wave + i) + h;
+            kco[i] = 2u * ((uint32_t)r * (uint32_t)a.ldk + 8u * (uint32_t)(c ^ (r & 15)));
+            vco[i] = 2u * ((uint32_t)r * (uint32_t)a.ldv + 8u * (uint32_t)(c ^ ((r & 3) << 2)));
+        }
+        bool clamped = false;
+        auto clamp_tail = [&](int kb) {
+            if (!clamped && kb * BK + BK > a.Lk) {
+#pragma unroll
+                for (int i = 0; i < NCOPY / 2; ++i) {
+                    const int r = 2 * (NCOPY / 2 * wave + i) + h;
+                    const uint32_t d = (uint32_t)max(kb * BK + r - (a.Lk - 1), 0);
+                    kco[i] -= 2u * d * (uint32_t)a.ldk;
+                    vco[i] -= 2u * d * (uint32_t)a.ldv;
+                }
+                clamped = true;
+            }
+        };
         // copy n (0..NCOPY-1): K (n even) or V (n odd) rows of wave copy i = n / 2
-        auto issue_kv = [&](int kb, uint16_t* kst, int n, int ln) {
+        auto issue_kv = [&](int kb, uint16_t* kst, int n) {
             const int i = n >> 1;
-            const int r = 2 * (NCOPY / 2 * wave + i) + (ln >> 5), sl = ln & 31;
-            const size_t key = (size_t)min(kb * BK + r, a.Lk - 1);
+            // (the offset goes through a local: with the array element
+            // written inside the builtin's argument, the host pass of this
+            // compiler emitted no launch stub for the kernel)
+            const uint32_t lo = (n & 1) ? vco[i] : kco[i];
+            const size_t row0 = (size_t)kb * BK;
             if ((n & 1) == 0)
-                __builtin_amdgcn_global_load_lds(a.k + key * a.ldk + (size_t)kh * HD + 8 * (sl ^ (r & 15)),
+                __builtin_amdgcn_global_load_lds((const char*)(a.k + row0 * a.ldk + (size_t)kh * HD) + lo,
                                                  (lds_ptr_t)(kst + (NCOPY / 2 * wave + i) * 512), 16, 0, 0);
             else
-                __builtin_amdgcn_global_load_lds(a.v + key * a.ldv + (size_t)kh * HD + 8 * (sl ^ ((r & 3) << 2)),
+                __builtin_amdgcn_global_load_lds((const char*)(a.v + row0 * a.ldv + (size_t)kh * HD) + lo,
                                                  (lds_ptr_t)(kst + TILE_HALVES + (NCOPY / 2 * wave + i) * 512), 16, 0, 0);
         };
+        // LDS byte offsets of the lane's fragments within a stage, whose
+        // other parts are immediates.  K: row c of a 32-key tile at piece
+        // (2 j + h) ^ (c & 15); for j = 0..7 that is kfo0 ^ 32 j (the piece
+        // bits lie between the row's and the lane half's), and j + 8 is 256
+        // bytes further.  V: the transposing read for dims 32 dt .. with
+        // dt = 0..3 (dt + 4: 256 bytes further), key rows 4 h + i / 4
+        // (i = lane % 16).
+        uint32_t vfo[4];
+        const uint32_t kfo0 = 2u * (uint32_t)(c * HD + 8 * (h ^ (c & 15)));
+        {
+            const int gi = lane & 15, vr = 4 * h + (gi >> 2);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const int vp = 4 * dt + 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
+                vfo[dt] = 2u * (uint32_t)(vr * HD + 8 * (vp ^ ((vr & 3) << 2)) + 4 * (gi & 1));
+            }
+        }
 
         const float cl = 1.4426950408889634f / 16.0f;          // log2(e) / sqrt(256)
+        clamp_tail(kb0);
 #pragma unroll
-        for (int n = 0; n < NCOPY; ++n) issue_kv(kb0, lds0, n, lane);
+        for (int n = 0; n < NCOPY; ++n) issue_kv(kb0, lds0, n);
         __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
         // block kb from stage ks while the next block is copied into nst
@@ -163,11 +213,12 @@ __global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_
             // previous barrier), its NCOPY copies spread evenly over the S^T
             // products below; the last block again on the last iteration
             const int kn = min(kb + 1, kb1 - 1);
-            // every LDS and global address below is derived from an opaque
-            // copy of the lane id, so the compiler recomputes them per block
-            // (hoisted, about 70 of them stayed live through the loop)
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
+            clamp_tail(kn);
+            // (an opaque copy: the seven other K offsets are formed per block
+            // by one XOR each, not kept in registers through the loop; a
+            // lane needs every register it can keep for the prefetches)
+            uint32_t k0 = kfo0;
+            asm volatile("" : "+v"(k0));
 
             // S^T for keys 32 st .. 32 st + 31 of the block: lane (c, h),
             // value r is key 8 (r / 4) + 4 h + r % 4 of the tile, query c
@@ -185,8 +236,7 @@ __global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_
             // The K fragments are read two steps ahead: the compiler does
             // not move an LDS read above a copy into LDS.
             auto kfrag = [&](int j, int st) {
-                const int kr_ = 32 * st + (ln & 31);
-                return *(const f16x8*)(ks + kr_ * HD + 8 * ((2 * j + (ln >> 5)) ^ (kr_ & 15)));
+                return *(const f16x8*)((const char*)ks + (k0 ^ (32u * (j & 7))) + 256 * (j >> 3) + 2 * 32 * HD * st);
             };
             f16x8 ka[3][NST];
 #pragma unroll
@@ -202,7 +252,7 @@ __global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_
                 for (int st = 0; st < NST; ++st)
                     s[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[j % 3][st], __builtin_bit_cast(f16x8, qf[j]),
                                                                    s[st], 0, 0, 0);
-                if (j % (16 / NCOPY) == 0) issue_kv(kn, nst, j / (16 / NCOPY), ln);
+                if (j % (16 / NCOPY) == 0) issue_kv(kn, nst, j / (16 / NCOPY));
             }
 
             // online softmax (base 2) on the raw scores: masked keys get
@@ -222,7 +272,13 @@ __global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_
             for (int st = 0; st < NST; ++st)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) bm = fmaxf(bm, s[st][r]);
-            bm = fmaxf(bm, __shfl_xor(bm, 32)) * cl;
+            {
+                // the other half's maximum (lanes L and L ^ 32 hold the same
+                // query), exchanged in registers rather than through LDS
+                const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, bm),
+                                                                 __builtin_bit_cast(uint32_t, bm), false, false);
+                bm = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1])) * cl;
+            }
             const bool raise = bm > m + TAU;                   // also the first finite maximum
             if (__any(raise)) {
                 const float mn = raise ? bm : m;
@@ -236,50 +292,57 @@ __global__ void __launch_bounds__(256, BK == BKEY_SMALL ? 2 : 1) lut6_attention_
             }
             const float mu = m == -__builtin_inff() ? 0.0f : m;
             const float sh = 4.0f - mu;                        // 16 p = 2^(cl s - mu + 4)
-            // per 32-key tile: P^T x 16 in FP16 as B fragments (step jj takes
-            // values r = 8 jj .. 8 jj + 7: keys 16 jj + 4 h + 0..3 and
+            // per 32-key tile and half jj: P^T x 16 in FP16 as the B fragment
+            // (values r = 8 jj .. 8 jj + 7: keys 16 jj + 4 h + 0..3 and
             // 16 jj + 8 + 4 h + 0..3), then O^T (dims x queries) += V^T P^T
-            // with the A slots on the same keys.  Tile 1's exponentials do
-            // not wait for tile 0's products, so the two can overlap.
+            // with the A slots on the same keys; a half's exponentials come
+            // just before its eight products, so fewer values are live.
+            // V^T fragments by transposing reads: in each 16-lane group
+            // (g = lane / 16, i = lane % 16) lane i points at 4 dims of key
+            // K0 + i / 4 and receives keys K0 .. K0 + 3 of dim
+            // 32 dt + 16 (g % 2) + i; K0 = 32 st + 16 jj + 4 h, and + 8 for
+            // the second half of the fragment.  Fragment n = (st, jj, dt) in
+            // product order; they are read two products ahead, the first two
+            // before the exponentials.
+            auto vfrag = [&](int n) {
+                const int st = n >> 4, jj = (n >> 3) & 1, dt = n & 7;
+                const char* vp = (const char*)vs + vfo[dt & 3] + 256 * (dt >> 2) + 2 * (32 * st + 16 * jj) * HD;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vp + 2 * 8 * HD));
+                const u32x4 va = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                                  __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+                return __builtin_bit_cast(f16x8, va);
+            };
+            constexpr int NV = 16 * NST;
+            f16x8 vb[3];
+            vb[0] = vfrag(0);
+            vb[1] = vfrag(1);
+            __builtin_amdgcn_sched_barrier(0);
             float sum = 0.0f;
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
-                u32x4 pf[2];
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
+                for (int jj = 0; jj < 2; ++jj) {
+                    u32x4 pf;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 8 * jj + 2 * e;
                         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r], cl, sh));
                         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][r + 1], cl, sh));
                         sum += p0 + p1;
-                        pf[jj][e] = pack_f16(p0, p1);
+                        pf[e] = pack_f16(p0, p1);
                     }
-                // (eight accumulators in turn: no product waits for the one
-                // before it)
-                // V^T fragments by transposing reads: in each 16-lane group
-                // (g = lane / 16, i = lane % 16) lane i points at 4 dims of
-                // key K0 + i / 4 and receives keys K0 .. K0 + 3 of dim
-                // 32 dt + 16 (g % 2) + i; K0 = 32 st + 16 jj + 4 h, and + 8
-                // for the second half of the fragment
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                     for (int dt = 0; dt < 8; ++dt) {
-                        const int gi = ln & 15, vr_ = 32 * st + 16 * jj + 4 * (ln >> 5) + (gi >> 2);
-                        const int vp_ = 4 * dt + 2 * ((ln >> 4) & 1) + ((gi & 3) >> 1);
-                        const uint16_t* vp = vs + vr_ * HD + 8 * (vp_ ^ ((vr_ & 3) << 2)) + 4 * (gi & 1);
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp);
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4*)(vp + 8 * HD));
-                        const u32x4 va = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
-                                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
-                                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
-                                          __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va),
-                                                                       __builtin_bit_cast(f16x8, pf[jj]),
+                        const int n = 16 * st + 8 * jj + dt;
+                        if (n + 2 < NV) vb[(n + 2) % 3] = vfrag(n + 2);
+                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb[n % 3], __builtin_bit_cast(f16x8, pf),
                                                                        o[dt], 0, 0, 0);
                     }
+                }
             }
             l += sum * 0.0625f;                                // sum holds 16 p
 
@@ -377,6 +440,8 @@ extern "C" int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t
     if (n_heads > 4096 || L < 0 || Lk < L || Lk > (int64_t)INT32_MAX - BKEY) return LUT6_E_SHAPE;
     if (ldq < n_heads * HD || ldo < n_heads * HD || ldk < n_kv_heads * HD || ldv < n_kv_heads * HD)
         return LUT6_E_SHAPE;
+    // the key loop's copy offsets are 32-bit: up to 63 rows of k and v
+    if (ldk > MAX_KV_LD || ldv > MAX_KV_LD) return LUT6_E_SHAPE;
     if (ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8) return LUT6_E_ALIGN;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return LUT6_E_ALIGN;
     if (L == 0) return LUT6_OK;

@@ -207,6 +207,7 @@ def _attention(q=X, ldq=4096, k=P, ldk=1024, v=T, ldv=1024, o=Y, ldo=4096, L=128
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
     (dict(d=128), 2), (dict(hkv=3), 2), (dict(hkv=0), 2), (dict(hq=0), 2), (dict(L=-1), 2),
     (dict(Lk=100), 2), (dict(ldq=4088), 2), (dict(ldk=1016), 2), (dict(ldo=256), 2),
+    (dict(ldk=(1 << 24) + 8), 2), (dict(ldv=(1 << 24) + 8), 2),
     (dict(ldq=4100), 3), (dict(ldv=1028), 3), (dict(q=X + 8), 3), (dict(o=Y + 2), 3),
     (dict(o=X + 4096), 8), (dict(o=P), 8), (dict(o=T + 16), 8),
     (dict(L=0), 0), (dict(L=0, Lk=0), 0),
