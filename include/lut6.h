@@ -245,7 +245,8 @@ int lut6_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const
  * as the initial state and overwritten with the final one.  The caller
  * owns every buffer.
  * Rules: dk == dv == 128, n_v_heads % n_k_heads == 0, n_v_heads <= 4096,
- * 0 <= L < 2^31 - 64, each ld at least its row's width (LUT6_E_SHAPE); q,
+ * 0 <= L < 2^31 - 64, each ld at least its row's width and ldq, ldk, ldv,
+ * ldo at most 2^24 (LUT6_E_SHAPE); q,
  * k, v, o 16-byte aligned with ldq, ldk, ldv, ldo multiples of 8; g, beta,
  * state 4-byte aligned (LUT6_E_ALIGN); o and state must not overlap an
  * input or each other (LUT6_E_ALIAS).  L == 0 is a no-op.

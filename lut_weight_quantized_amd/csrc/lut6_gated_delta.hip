@@ -189,6 +189,7 @@ constexpr int WS_FLOATS = 2 * CH * CH + 4 * CH;   // T, P, gamma, eta, beta, pad
 constexpr int WS_GDN = 3;                         // library workspace kind
 constexpr int64_t MAX_WINDOW_CHUNKS = 128;        // chunks per prep + recurrence launch pair
 constexpr size_t WS_BUDGET = (size_t)160 << 20;   // workspace bytes, at most
+constexpr int64_t MAX_LD = int64_t(1) << 24;      // largest row stride, elements (32-bit lane offsets)
 
 struct ChunkArgs {
     const uint16_t* q;
@@ -389,7 +390,7 @@ __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
 // and T rows, or q and P rows), so the compiler's counts of loads in flight
 // are exact on both, and the two waves on a SIMD fill each other's stalls.
 // A chunk's operands are loaded into registers while the chunk before it is
-// computed.
+// computed, with the two operand sets swapped every chunk.
 __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
 {
     __shared__ __attribute__((aligned(16))) float st[CB][DK + 4];     // S^T of the block
@@ -411,7 +412,7 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
     const float rsq = 0.08838834764831845f;           // 1 / sqrt(128)
     // this wave's row operand: k rows and T rows (K waves), q rows and P rows
     // (Q waves)
-    const uint16_t* const xsrc = (role ? a.q : a.k) + (size_t)kq * DK + 8 * hi;
+    const uint16_t* const xbase = (role ? a.q : a.k) + (size_t)kq * DK;
     const int64_t ldx = role ? a.ldq : a.ldk;
     const int wsm = role ? WS_P : WS_T;
     float* const wsh = a.ws + (size_t)h * a.n_chunks * WS_FLOATS;
@@ -440,57 +441,97 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
         uint32_t vr[4];
         float vc;
     };
+    // Every load and store address is a uniform base, formed per chunk on
+    // the scalar unit, plus one of these lane byte offsets, formed once
+    // (32-bit: the host bounds the row strides): k or q row, T or P row, the
+    // four v rows, the decay entry, the four o rows and the pad slot.
+    uint32_t ox = 2u * ((uint32_t)trow * (uint32_t)ldx + 8u * (uint32_t)hi);
+    uint32_t om = 4u * (uint32_t)(trow * CH + 4 * hi);
+    uint32_t oc = 4u * (uint32_t)(WS_GAMMA + (tid < 3 * CH ? tid : 0));
+    uint32_t opad = 4u * (uint32_t)WS_PAD + 2u * (uint32_t)lane;
+    uint32_t ov[4], os[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t row = (uint32_t)(16 * r + 4 * hi + e);
+        ov[e] = 2u * (row * (uint32_t)a.ldv + (uint32_t)lo);
+        os[e] = 2u * (row * (uint32_t)a.ldo + (uint32_t)lo);
+    }
     // Every load is unconditional (rows past L re-read row L - 1): with
     // loads under branches the compiler cannot count the ones in flight, and
     // its wait for this chunk's operands then also waited for the next
-    // chunk's, a full memory latency per chunk.  Rows past L are zeroed
-    // where the chunk is consumed, not here: any arithmetic on a loaded
-    // register makes the wave wait for that load in the iteration that
-    // issued it.
+    // chunk's, a full memory latency per chunk.  Only the call's last chunk
+    // can hold rows past L, so the row offsets are pulled back once, when it
+    // is the next chunk to load.  Rows past L are zeroed where the chunk is
+    // consumed, not here: any arithmetic on a loaded register makes the wave
+    // wait for that load in the iteration that issued it.
+    bool clamped = false;
+    auto clamp_tail = [&](int c) {
+        const int t0 = a.t_begin + c * CH;
+        if (!clamped && t0 + CH > a.L) {
+            ox -= 2u * (uint32_t)max(t0 + trow - (a.L - 1), 0) * (uint32_t)ldx;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ov[e] -= 2u * (uint32_t)max(t0 + 16 * r + 4 * hi + e - (a.L - 1), 0) * (uint32_t)a.ldv;
+            clamped = true;
+        }
+    };
     auto load_ops = [&](int c, Ops& op) {
         const int t0 = a.t_begin + c * CH;
-        const float* const wsc = wsh + (size_t)c * WS_FLOATS;
-        const size_t tr = (size_t)min(t0 + trow, a.L - 1);
+        const char* const xb = (const char*)(xbase + (size_t)t0 * ldx);
+        const char* const mb = (const char*)(wsh + (size_t)c * WS_FLOATS + wsm);
+        const char* const vb = (const char*)(a.v + (size_t)t0 * a.ldv + col0);
+        const char* const gb = (const char*)(wsh + (size_t)c * WS_FLOATS);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) op.xr[z] = *(const u32x4*)(xsrc + tr * ldx + 32 * z);
+        for (int z = 0; z < 4; ++z) op.xr[z] = *(const u32x4*)(xb + ox + 64 * z);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) op.mv[z] = *(const f32x4*)(wsc + wsm + trow * CH + 16 * z + 4 * hi);
+        for (int z = 0; z < 4; ++z) op.mv[z] = *(const f32x4*)(mb + om + 64 * z);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            op.vr[e] = a.v[(size_t)min(t0 + 16 * r + 4 * hi + e, a.L - 1) * a.ldv + col0 + lo];
-        op.vc = wsc[WS_GAMMA + (tid < 3 * CH ? tid : 0)];
+        for (int e = 0; e < 4; ++e) op.vr[e] = *(const uint16_t*)(vb + ov[e]);
+        op.vc = *(const float*)(gb + oc);
     };
 
     // A chunk's outputs are stored during the next chunk, after its loads:
     // stores count in the same in-order counter as loads, so stores issued
     // just before the barrier made the wait for the next operands also wait
-    // for the write acknowledgements.  Like the loads, the stores are
-    // unconditional: K waves, rows past L and the empty store of chunk 0 go
-    // to the unused pad of a workspace block.
+    // for the write acknowledgements.  Every path stores four times: K
+    // waves, the empty store of chunk 0 and rows past L go to the unused pad
+    // of a workspace block.
     uint16_t ob[4] = {0, 0, 0, 0};
     auto store_o = [&](int cc, bool real) {
         const int t0c = a.t_begin + cc * CH;
-        uint16_t* const pad = (uint16_t*)(wsh + (size_t)cc * WS_FLOATS + WS_PAD) + lane;
+        if (real && role == 1 && t0c + CH <= a.L) {
+            char* const orow = (char*)(a.o + (size_t)t0c * a.ldo + col0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int tg = t0c + 16 * r + 4 * hi + e;
-            // both addresses are formed first so that the choice is a select,
-            // not a branch around the multiply
-            uint16_t* const row = a.o + (size_t)min(tg, a.L - 1) * a.ldo + col0 + lo;
-            *(real && role == 1 && tg < a.L ? row : pad) = ob[e];
+            for (int e = 0; e < 4; ++e) *(uint16_t*)(orow + os[e]) = ob[e];
+        } else if (real && role == 1) {
+            uint16_t* const pad = (uint16_t*)(wsh + (size_t)cc * WS_FLOATS + WS_PAD) + lane;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tg = t0c + 16 * r + 4 * hi + e;
+                // both addresses are formed first so that the choice is a
+                // select, not a branch around the multiply
+                uint16_t* const row = a.o + (size_t)min(tg, a.L - 1) * a.ldo + col0 + lo;
+                *(tg < a.L ? row : pad) = ob[e];
+            }
+        } else {
+            char* const pad = (char*)(wsh + (size_t)cc * WS_FLOATS);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *(uint16_t*)(pad + opad) = ob[e];
         }
     };
 
-    Ops cur;
-    load_ops(0, cur);
-    if (tid < 3 * CH) vec[0][tid >> 6][tid & 63] = cur.vc;
-    __syncthreads();
-
-    for (int c = 0; c < a.n_chunks; ++c) {
+    // chunk c from the operands in cur while the next chunk's are loaded
+    // into nxt (the loop runs two chunks per pass with the two sets swapped,
+    // so that no set is copied)
+    auto chunk = [&](int c, const Ops& cur, Ops& nxt) {
         const int t0 = a.t_begin + c * CH, b = c & 1;
-        Ops nxt;
-        load_ops(c + 1 < a.n_chunks ? c + 1 : c, nxt);
-        store_o(c > 0 ? c - 1 : 0, c > 0);
+        const int cn = c + 1 < a.n_chunks ? c + 1 : c;
+        // (opaque per chunk: hoisted, the offsets were widened to 64 bits
+        // once and every access then added them on the vector unit)
+        asm volatile("" : "+v"(om), "+v"(oc), "+v"(opad), "+v"(os[0]), "+v"(os[1]), "+v"(os[2]), "+v"(os[3]));
+        asm volatile("" : "+v"(ox), "+v"(ov[0]), "+v"(ov[1]), "+v"(ov[2]), "+v"(ov[3]));
+        clamp_tail(cn);
+        load_ops(cn, nxt);
 
         // stage 1: rows 16 r .. 16 r + 15 of K S0 (K waves) or Q S0 (Q
         // waves), step n taking k = 32 (n / 8) + 8 hi + n % 8; K waves then
@@ -498,6 +539,9 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
         f32x4 x;
         {
             float xf[32];
+            // rows past L read as zero (a select, not a branch: the next
+            // chunk's loads above and these products must stay in one
+            // scheduling region for their pacing)
             const uint32_t km = t0 + trow < a.L ? 0xffffffffu : 0u;
 #pragma unroll
             for (int z = 0; z < 4; ++z)
@@ -529,6 +573,9 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
+            // the previous chunk's outputs (after the loads, so no wait for
+            // this chunk's operands waits for a write acknowledgement)
+            store_o(c > 0 ? c - 1 : 0, c > 0);
             if (role == 0) {
 #pragma unroll
                 for (int z = 0; z < 8; ++z)
@@ -546,7 +593,6 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
             }
         }
         __syncthreads();
-
         // stage 2 (K waves): D rows 16 r .. 16 r + 15 = T R (step m takes s =
         // 16 (m / 4) + 4 hi + m % 4).  R and D are kept transposed in LDS, so
         // a lane's four entries of one step group are one 16-byte read; two
@@ -610,7 +656,16 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
         // the previous barrier)
         if (tid < 3 * CH) vec[b ^ 1][tid >> 6][tid & 63] = nxt.vc;
         __syncthreads();
-        cur = nxt;
+    };
+
+    Ops opa, opb;
+    clamp_tail(0);
+    load_ops(0, opa);
+    if (tid < 3 * CH) vec[0][tid >> 6][tid & 63] = opa.vc;
+    __syncthreads();
+    for (int c = 0; c < a.n_chunks; c += 2) {
+        chunk(c, opa, opb);
+        if (c + 1 < a.n_chunks) chunk(c + 1, opb, opa);
     }
     store_o(a.n_chunks - 1, true);
     {
@@ -647,6 +702,7 @@ extern "C" int lut6_gated_delta(const void* q, int64_t ldq, const void* k, int64
     if (ldq < n_k_heads * DK || ldk < n_k_heads * DK || ldv < n_v_heads * DV || ldo < n_v_heads * DV ||
         ldg < n_v_heads)
         return LUT6_E_SHAPE;
+    if (ldq > MAX_LD || ldk > MAX_LD || ldv > MAX_LD || ldo > MAX_LD) return LUT6_E_SHAPE;
     if (ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8) return LUT6_E_ALIGN;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)g & 3) ||
         ((uintptr_t)beta & 3) || ((uintptr_t)state & 3))

@@ -231,6 +231,7 @@ def _gated_delta(q=X, ldq=8192, k=X + 4096, ldk=8192, v=X + 8192, ldv=8192, g=G,
     (dict(o=None), 1), (dict(st=None), 1),
     (dict(dk=64), 2), (dict(dv=256), 2), (dict(hk=3), 2), (dict(hv=0), 2), (dict(L=-1), 2),
     (dict(ldq=2040), 2), (dict(ldv=4088), 2), (dict(ldo=4000), 2), (dict(ldg=31), 2),
+    (dict(ldk=(1 << 24) + 8), 2), (dict(ldo=(1 << 24) + 8), 2),
     (dict(ldq=8196), 3), (dict(o=Y + 8), 3), (dict(g=G + 2), 3), (dict(st=ST + 1), 3),
     (dict(o=X + 64), 8), (dict(o=G), 8), (dict(st=X), 8), (dict(st=B + 4), 8), (dict(o=ST), 8),
     (dict(L=0), 0),
