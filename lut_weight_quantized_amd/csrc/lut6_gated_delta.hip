@@ -394,10 +394,15 @@ __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
 __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
 {
     __shared__ __attribute__((aligned(16))) float st[CB][DK + 4];     // S^T of the block
-    __shared__ __attribute__((aligned(16))) float ks[CH][DK + 16];    // k rows of the chunk
+    // k rows of the chunk; column c of row i is stored at c ^ 4 ((i / 4) % 4):
+    // the stride suits the state update's reads (rows 4 m + hi, columns
+    // 16 w + lo: one bank per lane), and the swizzle spreads the row writes,
+    // whose 16 lanes (rows 16 r + lo) would otherwise share four 16-byte
+    // bank groups
+    __shared__ __attribute__((aligned(16))) float ks[CH][DK + 16];
     __shared__ __attribute__((aligned(16))) float rt[CB][CH + 4];     // R^T, R = beta (v - gamma K S)
     __shared__ __attribute__((aligned(16))) float dt[CB][CH + 4];     // D^T
-    __shared__ float dh[CH][CB];                                      // eta D
+    __shared__ __attribute__((aligned(16))) float dh[CB][CH + 4];     // (eta D)^T, like D^T
     __shared__ float vec[2][3][CH];                                   // gamma, eta, beta (two chunks)
 
     const int tid = threadIdx.x, lane = tid & 63, lo = lane & 15, hi = lane >> 4;
@@ -579,7 +584,7 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
             if (role == 0) {
 #pragma unroll
                 for (int z = 0; z < 8; ++z)
-                    *(f32x4*)&ks[trow][32 * (z >> 1) + 8 * hi + 4 * (z & 1)] =
+                    *(f32x4*)&ks[trow][32 * (z >> 1) + ((8 * hi + 4 * (z & 1)) ^ (4 * ((lo >> 2) & 3)))] =
                         f32x4{xf[4 * z], xf[4 * z + 1], xf[4 * z + 2], xf[4 * z + 3]};
                 f32x4 r4;
 #pragma unroll
@@ -612,11 +617,10 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
             __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
             const f32x4 d = d2[0] + d2[1];
             *(f32x4*)&dt[lo][16 * r + 4 * hi] = d;
+            f32x4 dhe;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * r + 4 * hi + e;
-                dh[t][lo] = vec[b][1][t] * d[e];
-            }
+            for (int e = 0; e < 4; ++e) dhe[e] = vec[b][1][16 * r + 4 * hi + e] * d[e];
+            *(f32x4*)&dh[lo][16 * r + 4 * hi] = dhe;
         }
         __syncthreads();
 
@@ -629,7 +633,8 @@ __global__ void __launch_bounds__(512) lut6_gdn_chunk_kernel(ChunkArgs a)
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 const int s = 4 * m + hi;
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dh[s][lo], ks[s][16 * w + lo], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(dh[lo][s], ks[s][16 * w + (lo ^ (4 * (m & 3)))], acc, 0,
+                                                           0, 0);
             }
             sacc = acc;
 #pragma unroll
