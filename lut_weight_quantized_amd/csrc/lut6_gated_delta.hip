@@ -248,18 +248,25 @@ __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
     const int t0 = a.t_begin + c * CH;
     float* const ws = a.ws + ((size_t)h * a.n_chunks + c) * WS_FLOATS;
 
-    // k and q rows of the key head, zero past L
+    // k and q rows of the key head, zero past L: the eight loads go out
+    // together (rows past L re-read row L - 1 and are zeroed on the way to
+    // LDS; under a branch each pair of loads waited for the one before)
+    {
+        u32x4 kv[4], qv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int idx = tid + 256 * u, row = idx >> 4, piece = idx & 15;
-        const int t = t0 + row;
-        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-        if (t < a.L) {
-            kv = *(const u32x4*)(a.k + (size_t)t * a.ldk + (size_t)kq * DK + piece * 8);
-            qv = *(const u32x4*)(a.q + (size_t)t * a.ldq + (size_t)kq * DK + piece * 8);
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + 256 * u, row = idx >> 4, piece = idx & 15;
+            const size_t t = (size_t)min(t0 + row, a.L - 1);
+            kv[u] = *(const u32x4*)(a.k + t * a.ldk + (size_t)kq * DK + piece * 8);
+            qv[u] = *(const u32x4*)(a.q + t * a.ldq + (size_t)kq * DK + piece * 8);
         }
-        *(u32x4*)&kh[row][piece * 8] = kv;
-        *(u32x4*)&qh[row][piece * 8] = qv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + 256 * u, row = idx >> 4, piece = idx & 15;
+            const uint32_t m = t0 + row < a.L ? 0xffffffffu : 0u;
+            *(u32x4*)&kh[row][piece * 8] = kv[u] & m;
+            *(u32x4*)&qh[row][piece * 8] = qv[u] & m;
+        }
     }
     for (int i = tid; i < CH * (CH + 4); i += 256) (&as[0][0])[i] = 0.0f;
     // the log-decay prefix in FP64 and beta (g = beta = 0 past L)
@@ -286,7 +293,12 @@ __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
     __syncthreads();
 
     // K K^T (tiles on and below the diagonal, into A) and Q K^T (into P):
-    // 20 tiles of 16 x 16, five per wave
+    // 20 tiles of 16 x 16, five per wave.  All five tiles' products first,
+    // then per tile its decays from one read of the four G_t and beta_t and
+    // stores without per-element branches (entries of A on or above the
+    // diagonal get the zero they already hold): with a branch around each
+    // element, each decay waited for its own LDS round trips.
+    f32x4 acc[5];
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
         const int job = wave + 4 * j;                       // 0..9: K K^T, 10..19: Q K^T
@@ -295,20 +307,35 @@ __global__ void __launch_bounds__(256) lut6_gdn_prep_kernel(ChunkArgs a)
         const int rt = tri >= 6 ? 3 : tri >= 3 ? 2 : tri >= 1 ? 1 : 0;
         const int st_ = tri - rt * (rt + 1) / 2;
         const uint16_t (*xa)[DK + 8] = isq ? qh : kh;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const f16x8 av = *(const f16x8*)&xa[16 * rt + lo][32 * kk + 8 * hi];
             const f16x8 bv = *(const f16x8*)&kh[16 * st_ + lo][32 * kk + 8 * hi];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[j], 0, 0, 0);
         }
-        const int s = 16 * st_ + lo;
+    }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const int job = wave + 4 * j;
+        const bool isq = job >= 10;
+        const int tri = isq ? job - 10 : job;
+        const int rt = tri >= 6 ? 3 : tri >= 3 ? 2 : tri >= 1 ? 1 : 0;
+        const int st_ = tri - rt * (rt + 1) / 2;
+        const int s = 16 * st_ + lo, tb = 16 * rt + 4 * hi;
+        const double gs = gl[s];
+        float dec[4], bt[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = 16 * rt + 4 * hi + e;
-            const float dec = expf((float)(gl[t] - gl[s]));
-            if (isq) ws[WS_P + t * CH + s] = s <= t ? dec * acc[e] : 0.0f;
-            else if (s < t) as[t][s] = bs[t] * dec * acc[e];
+            dec[e] = expf((float)(gl[tb + e] - gs));
+            bt[e] = bs[tb + e];
+        }
+        if (isq) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ws[WS_P + (tb + e) * CH + s] = s <= tb + e ? dec[e] * acc[j][e] : 0.0f;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) as[tb + e][s] = s < tb + e ? bt[e] * dec[e] * acc[j][e] : 0.0f;
         }
     }
     // P above its diagonal tiles is zero
