@@ -14,9 +14,9 @@
 //     the FP32 sum of the p_j; one FP16 rounding of o.
 //
 // Design: one workgroup per (query head, 128 queries), four waves of 32
-// queries.  Keys go by blocks of 64 (or of 32, with two workgroups per CU,
-// when a launch has many workgroups) through two LDS stages, K and V both
-// row-major and copied straight from global memory into LDS: a block is
+// queries.  Keys go by blocks of 32, two workgroups per CU (of 64, one per
+// CU, for small launches and key splits), through two LDS stages, K and V
+// both row-major and copied straight from global memory into LDS: a block is
 // computed from one stage while the next block is copied into the other;
 // one barrier per block.  Short query chunks over a long cache split the
 // keys over several workgroups, whose partial sums a second kernel combines.
@@ -49,9 +49,10 @@ constexpr int BKEY = 64;              // keys per block (key splits and fewer wo
 constexpr int BKEY_SMALL = 32;        // keys per block with two workgroups per CU
 // Launches of at least this many workgroups (and no key split) use 32-key
 // blocks: 64 KB of LDS and at most 256 registers per lane, so two
-// workgroups share a CU and each SIMD runs two waves.  With fewer, the
-// causal work is too uneven for the pairs to pay.
-constexpr int64_t SMALL_BLOCK_MIN_WGS = 768;
+// workgroups share a CU and each SIMD runs two waves.  Measured from 128
+// workgroups up (1,024 queries with 16 heads, chunks over a longer cache
+// included) that form is as fast or faster; below, the 64-key form.
+constexpr int64_t SMALL_BLOCK_MIN_WGS = 128;
 constexpr int64_t MAX_KV_LD = int64_t(1) << 24;   // largest k / v row stride, elements
 constexpr int WS_ATTENTION = 2;       // library workspace kind of the key-split partials
 
