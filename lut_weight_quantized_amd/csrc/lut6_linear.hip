@@ -1260,16 +1260,26 @@ lut6_int8_stream_kernel(const uint16_t* __restrict__ x, const int8_t* __restrict
             }
         }
     };
+    // chunks in pairs with no branch inside the loop (the load of the chunk
+    // after next is clamped to the last one: at most one spare load per
+    // wave), an odd last chunk after it.  (With the second chunk's work
+    // under a branch, the accumulators went through vector registers and
+    // back on every pass.)
     Chunk ca, cb;
-    if (c0 < c1) load(ca, c0);
-    for (int kc = c0; kc < c1; kc += 2) {
-        if (kc + 1 < c1) load(cb, kc + 1);
-        stage(ca, 0);
-        compute(ca, 0);
-        if (kc + 2 < c1) load(ca, kc + 2);
-        if (kc + 1 < c1) {
+    if (c0 < c1) {
+        load(ca, c0);
+        int kc = c0;
+        for (; kc + 1 < c1; kc += 2) {
+            load(cb, kc + 1);
+            stage(ca, 0);
+            compute(ca, 0);
+            load(ca, min(kc + 2, c1 - 1));
             stage(cb, 1);
             compute(cb, 1);
+        }
+        if (kc < c1) {
+            stage(ca, 0);
+            compute(ca, 0);
         }
     }
     // waves 1..3 hand their sums to wave 0, which adds them in wave order
@@ -1354,7 +1364,9 @@ lut6_stream_kernel(GemmArgs a)
     // the wave's in-order load queue.
     //
     // pair tables (slot s: tile rows 16s .. 16s+15), then the four ring slots
-    __shared__ __attribute__((aligned(1024))) uint8_t s_pair[2 * 16384];
+    // (the largest alignment: the pair tables go first, at LDS address 0, so
+    // a lookup's offset is its address and needs no add)
+    __shared__ __attribute__((aligned(16384))) uint8_t s_pair[2 * 16384];
     __shared__ __attribute__((aligned(1024))) uint8_t s_x0[S_SLOT];
     __shared__ __attribute__((aligned(1024))) uint8_t s_x1[S_SLOT];
     __shared__ __attribute__((aligned(1024))) uint8_t s_x2[S_SLOT];
