@@ -483,8 +483,12 @@ def test_int8_identity_readout(ora, K, N, s):
     assert np.array_equal(y, ora.int8_dequant(q, sc).T)
 
 
+# K = 4,160 is 65 chunks of 64: for L <= 192 three waves take 16 chunks and one
+# takes 17 (pairs, then an odd last chunk); K = 64, 192 and 256 give one chunk
+# per busy wave, K = 512 two.
 INT8_SHAPES = [(1, 64, 32), (17, 192, 64), (100, 256, 288), (130, 64, 48), (192, 512, 4112),
-               (257, 576, 544), (513, 1024, 160), (1029, 4096, 96), (2048, 128, 4128), (64, 12288, 64)]
+               (150, 4160, 96), (257, 576, 544), (513, 1024, 160), (1029, 4096, 96), (2048, 128, 4128),
+               (64, 12288, 64)]
 
 
 @pytest.mark.parametrize("L,K,N", INT8_SHAPES)
