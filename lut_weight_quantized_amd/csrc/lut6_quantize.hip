@@ -25,9 +25,9 @@
 // the group's values as a histogram over the 65,536 FP16 bit patterns, kept
 // in order-preserving key order, and inclusive prefix counts P and prefix
 // sums S over it, the values <= b are the keys up to the largest key whose
-// value is <= b.  That key is found by a search in registers (the value of a
-// key is computed, not loaded), so a round costs one load of P and one of S
-// per boundary.  The histogram is counted in LDS, 32,768 keys per pass (one
+// value is <= b.  That key is computed from b alone (FP16 values are whole
+// numbers of 2^-24 units: b rounded down onto them), so a round costs one
+// load of P and one of S per boundary, in one wave.  The histogram is counted in LDS, 32,768 keys per pass (one
 // pass covers every FP16 value in [-0.5, 0.5]); P and S go to a library
 // workspace slot of 768 KB per workgroup, written and read back by that
 // workgroup alone, so plain loads see them (a CU's waves share its vector
@@ -82,17 +82,39 @@ __device__ __forceinline__ double q_value(uint32_t h)
     const double mag = e == 0 ? ldexp((double)m, -24) : ldexp((double)(1024 + m), e - 25);
     return (h & 0x8000u) ? -mag : mag;
 }
+// Pattern of the FP16 magnitude nearest to u (a whole number of 2^-24 units,
+// 0 <= u <= 65,504 * 2^24) from below (up = false) or from above (up = true).
+// Below 1,024 units (the subnormals) every whole number is a value; above,
+// the binade of u has 1,024 values spaced 2^(ex - 11) units apart, ex being
+// frexp's exponent of u, and rounding up from its last value reaches the
+// first value of the next binade.
+__device__ __forceinline__ uint32_t q_mag_bits(double u, bool up)
+{
+    if (u < 1024.0) return (uint32_t)u;
+    int ex;
+    (void)frexp(u, &ex);
+    const double mq = up ? ceil(ldexp(u, 11 - ex)) : floor(ldexp(u, 11 - ex));
+    return mq == 2048.0 ? (uint32_t)(ex - 9) << 10 : ((uint32_t)(ex - 10) << 10) | ((uint32_t)mq - 1024u);
+}
 // Largest key in [lo_key, hi_key] whose value is <= b, or lo_key - 1 if none
-// (every key in the range is a finite value, increasing with the key).
+// (every key in the range is a finite value, increasing with the key).  The
+// FP16 values are whole numbers of 2^-24 units, so the largest one <= b is
+// b's units rounded down onto that grid: the magnitude truncated for b >= 0
+// (-0 included: +0 is the larger key of value 0), rounded up for b < 0.
 __device__ __forceinline__ int q_floor_key(double b, int lo_key, int hi_key)
 {
-    int lo = lo_key - 1, hi = hi_key;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (q_value(q_bits((uint32_t)mid)) <= b) lo = mid;
-        else hi = mid - 1;
+    const double F16_MAX_UNITS = 65504.0 * 16777216.0;
+    const double t = ldexp(b, 24);                      // exact
+    uint32_t h;
+    if (t >= 0.0) {
+        h = q_mag_bits(fmin(floor(t), F16_MAX_UNITS), false);
+    } else {
+        const double c = ceil(-t);
+        if (c > F16_MAX_UNITS) return lo_key - 1;
+        h = q_mag_bits(c, true) | 0x8000u;
     }
-    return lo;
+    const int k = (int)q_key(h);
+    return k > hi_key ? hi_key : (k < lo_key ? lo_key - 1 : k);
 }
 // FP16 bit pattern nearest to c, ties to the even pattern; c lies within
 // the values of keys [lo_key, hi_key] (a centre is a mean of the group's
@@ -109,6 +131,15 @@ __device__ __forceinline__ uint32_t q_round_f16(double c, int lo_key, int hi_key
     if (d1 < d2) return h1;
     if (d2 < d1) return h2;
     return (h1 & 1u) ? h2 : h1;
+}
+
+// Orders one wave's LDS accesses before and after it (the lanes of a wave
+// run in step; this keeps the compiler from moving accesses across).
+__device__ __forceinline__ void q_wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Sort 64 doubles in LDS (ascending; of equal values -0 first, then by
@@ -267,28 +298,48 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
         q_rank_sort(tmp, cen, tid);
         __syncthreads();
 
-        // 4. Lloyd rounds
-        for (int round = 0; round < Q_ROUNDS; ++round) {
-            if (tid < Q_ENTRIES - 1) {
-                const double b = (cen[tid] + cen[tid + 1]) * 0.5;
-                const int k = q_floor_key(b, klo, khi);
-                // P and S are zero below the smallest key present
-                cle[tid] = k >= klo ? P[k] : 0u;
-                sle[tid] = k >= klo ? S[k] : 0;
-            } else if (tid == Q_ENTRIES - 1) {
-                cle[tid] = (uint32_t)n;
-                sle[tid] = S[khi];
+        // 4. Lloyd rounds, all in wave 0: lane i holds centre i, its
+        //    neighbours come by lane shifts.  The new centres are already in
+        //    the sort's order whenever each comes after its left neighbour
+        //    (a mean lies between its cluster's boundaries, an empty cluster
+        //    keeps its centre); then the rank sort would leave them in place
+        //    and is skipped.  Otherwise (equal zeros of opposite sign) they go
+        //    through it in LDS.
+        if (tid < Q_ENTRIES) {
+            double c = cen[tid];
+            const int64_t s_all = S[khi];
+            for (int round = 0; round < Q_ROUNDS; ++round) {
+                const double c_next = __shfl_down(c, 1);
+                uint32_t cnt = (uint32_t)n;
+                int64_t sum = s_all;
+                if (tid < Q_ENTRIES - 1) {
+                    const int k = q_floor_key((c + c_next) * 0.5, klo, khi);
+                    // P and S are zero below the smallest key present
+                    cnt = k >= klo ? P[k] : 0u;
+                    sum = k >= klo ? S[k] : 0;
+                }
+                uint32_t cnt_prev = __shfl_up(cnt, 1);
+                int64_t sum_prev = __shfl_up(sum, 1);
+                if (tid == 0) { cnt_prev = 0u; sum_prev = 0; }
+                const uint32_t num = cnt - cnt_prev;
+                const double v = num ? ldexp((double)(sum - sum_prev) / (double)num, -24) : c;
+                const double u = __shfl_up(v, 1);
+                const bool after = tid == 0 || u < v ||
+                                   (u == v && !(!__builtin_signbit(u) && __builtin_signbit(v)));
+                if (__all(after)) {
+                    c = v;
+                } else {
+                    tmp[tid] = v;
+                    q_wave_sync();
+                    q_rank_sort(tmp, cen, tid);
+                    q_wave_sync();
+                    c = cen[tid];
+                    q_wave_sync();
+                }
             }
-            __syncthreads();
-            if (tid < Q_ENTRIES) {
-                const uint32_t num = cle[tid] - (tid ? cle[tid - 1] : 0u);
-                const int64_t sum = sle[tid] - (tid ? sle[tid - 1] : 0);
-                tmp[tid] = num ? ldexp((double)sum / (double)num, -24) : cen[tid];
-            }
-            __syncthreads();
-            q_rank_sort(tmp, cen, tid);
-            __syncthreads();
+            cen[tid] = c;
         }
+        __syncthreads();
 
         // 5. the FP16 table, sorted, and the final boundaries
         if (tid < Q_ENTRIES) tmp[tid] = q_value(q_round_f16(cen[tid], klo, khi));

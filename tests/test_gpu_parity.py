@@ -412,6 +412,10 @@ def _gpu_quantize(w16):
     return p.cpu().numpy(), t.cpu().numpy().view(np.uint16)
 
 
+# The "edge" weights include groups whose new centres come out of the sort's
+# order in some rounds (equal zeros of opposite sign: the oracle re-sorts in 2
+# rounds of the 80 x 128 weight and 4 of the 160 x 64 one), so both the
+# kernel's in-order shortcut and its full rank sort are compared.
 @pytest.mark.parametrize("N,K,kind", [(16, 64, "normal"), (32, 256, "normal"), (48, 1024, "normal"),
                                       (80, 128, "edge"), (160, 64, "edge"), (64, 4096, "normal"),
                                       (16, 12288, "normal")])
