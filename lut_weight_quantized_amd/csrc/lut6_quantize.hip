@@ -55,6 +55,7 @@ constexpr int Q_ROUNDS = 40;
 constexpr int Q_ENTRIES = 64;
 constexpr int Q_MAX_WG = 256;
 constexpr int Q_CHUNK = 32768;      // histogram keys per LDS pass
+constexpr int Q_WAVE_KEYS = Q_CHUNK / (Q_THREADS / 64);   // keys per wave in the scan
 // one workspace slot: P (u32) then S (i64) over the 65,536 keys
 constexpr size_t Q_SLOT_BYTES = (size_t)Q_KEYS * 4 + (size_t)Q_KEYS * 8;
 
@@ -131,6 +132,51 @@ __device__ __forceinline__ uint32_t q_round_f16(double c, int lo_key, int hi_key
     if (d1 < d2) return h1;
     if (d2 < d1) return h2;
     return (h1 & 1u) ? h2 : h1;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// within each row of 16 lanes (lanes shifted in from outside the row add
+// 0), then the last lane of row 0 into row 1 and of row 2 into row 3, then
+// lane 31 into rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t q_dpp(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int64_t q_dpp64(int64_t x)
+{
+    const uint32_t lo = q_dpp<CTRL, ROWS>((uint32_t)x), hi = q_dpp<CTRL, ROWS>((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t q_wave_scan(uint32_t x)
+{
+    x += q_dpp<0x111, 0xf>(x);      // row_shr:1
+    x += q_dpp<0x112, 0xf>(x);      // row_shr:2
+    x += q_dpp<0x114, 0xf>(x);      // row_shr:4
+    x += q_dpp<0x118, 0xf>(x);      // row_shr:8
+    x += q_dpp<0x142, 0xa>(x);      // row_bcast:15 into rows 1 and 3
+    x += q_dpp<0x143, 0xc>(x);      // row_bcast:31 into rows 2 and 3
+    return x;
+}
+__device__ __forceinline__ int64_t q_wave_scan64(int64_t x)
+{
+    x += q_dpp64<0x111, 0xf>(x);
+    x += q_dpp64<0x112, 0xf>(x);
+    x += q_dpp64<0x114, 0xf>(x);
+    x += q_dpp64<0x118, 0xf>(x);
+    x += q_dpp64<0x142, 0xa>(x);
+    x += q_dpp64<0x143, 0xc>(x);
+    return x;
+}
+__device__ __forceinline__ uint32_t q_lane63(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ int64_t q_lane63_64(int64_t x)
+{
+    const uint32_t lo = q_lane63((uint32_t)x), hi = q_lane63((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Orders one wave's LDS accesses before and after it (the lanes of a wave
@@ -217,12 +263,11 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
         const int klo = key_lo, khi = key_hi;
 
         // 2. histogram (in LDS, Q_CHUNK keys at a time) and the inclusive
-        //    prefix counts P and exact prefix sums S over keys [klo, khi];
-        //    thread t owns keys [c0 + 128 t, c0 + 128 t + 128) of a chunk
+        //    prefix counts P and exact prefix sums S over keys [klo, khi]
         uint32_t carry_c = 0;
         int64_t carry_s = 0;
         for (int c0 = klo; c0 <= khi; c0 += Q_CHUNK) {
-            for (int i = tid; i < Q_CHUNK; i += Q_THREADS) hist[i] = 0u;
+            for (int i = tid; i < Q_CHUNK / 4; i += Q_THREADS) ((uint4*)hist)[i] = make_uint4(0, 0, 0, 0);
             __syncthreads();
             for (int i0 = tid; i0 < n8; i0 += 4 * Q_THREADS) {
                 uint4 v[4];
@@ -240,40 +285,50 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
                 }
             }
             __syncthreads();
-            uint32_t c_own = 0;
-            int64_t s_own = 0;
-            for (int j = 0; j < Q_CHUNK / Q_THREADS; ++j) {
-                const int rel = tid * (Q_CHUNK / Q_THREADS) + j;
+            // wave w takes keys [w Q_WAVE_KEYS, (w + 1) Q_WAVE_KEYS) of the
+            // chunk in blocks of 64, lane l key l of a block: first each
+            // wave's totals, then the inclusive prefixes block by block (an
+            // in-wave scan plus the running carry), stored coalesced.  The
+            // sums are integers, so any order gives the same P and S.
+            const int wave = tid >> 6, lane = tid & 63;
+            uint32_t wc = 0;
+            int64_t wsum = 0;
+            for (int b = 0; b < Q_WAVE_KEYS; b += 64) {
+                const int rel = wave * Q_WAVE_KEYS + b + lane;
                 const uint32_t c = hist[rel];
-                c_own += c;
-                s_own += (int64_t)c * q_units(q_bits((uint32_t)min(c0 + rel, Q_KEYS - 1)));
+                wc += c;
+                wsum += (int64_t)c * q_units(q_bits((uint32_t)min(c0 + rel, Q_KEYS - 1)));
             }
-            part_c[tid] = c_own;
-            part_s[tid] = s_own;
+            wc = q_wave_scan(wc);
+            wsum = q_wave_scan64(wsum);
+            if (lane == 63) {
+                part_c[wave] = wc;
+                part_s[wave] = wsum;
+            }
             __syncthreads();
-            // Hillis-Steele inclusive scan of the 256 partials
-            for (int d = 1; d < Q_THREADS; d <<= 1) {
-                const uint32_t ac = tid >= d ? part_c[tid - d] : 0u;
-                const int64_t as = tid >= d ? part_s[tid - d] : 0;
-                __syncthreads();
-                part_c[tid] += ac;
-                part_s[tid] += as;
-                __syncthreads();
+            uint32_t run_c = carry_c;
+            int64_t run_s = carry_s;
+            for (int v = 0; v < wave; ++v) {
+                run_c += part_c[v];
+                run_s += part_s[v];
             }
-            uint32_t run_c = carry_c + (tid ? part_c[tid - 1] : 0u);
-            int64_t run_s = carry_s + (tid ? part_s[tid - 1] : 0);
-            for (int j = 0; j < Q_CHUNK / Q_THREADS; ++j) {
-                const int rel = tid * (Q_CHUNK / Q_THREADS) + j;
+            for (int b = 0; b < Q_WAVE_KEYS && c0 + wave * Q_WAVE_KEYS + b <= khi; b += 64) {
+                const int rel = wave * Q_WAVE_KEYS + b + lane;
                 const int key = c0 + rel;
-                if (key > khi) break;
                 const uint32_t c = hist[rel];
-                run_c += c;
-                run_s += (int64_t)c * q_units(q_bits((uint32_t)key));
-                P[key] = run_c;
-                S[key] = run_s;
+                const uint32_t x = q_wave_scan(c);
+                const int64_t y = q_wave_scan64((int64_t)c * q_units(q_bits((uint32_t)min(key, Q_KEYS - 1))));
+                if (key <= khi) {
+                    P[key] = run_c + x;
+                    S[key] = run_s + y;
+                }
+                run_c += q_lane63(x);
+                run_s += q_lane63_64(y);
             }
-            carry_c += part_c[Q_THREADS - 1];
-            carry_s += part_s[Q_THREADS - 1];
+            for (int v = 0; v < Q_THREADS / 64; ++v) {
+                carry_c += part_c[v];
+                carry_s += part_s[v];
+            }
             __syncthreads();
         }
 
