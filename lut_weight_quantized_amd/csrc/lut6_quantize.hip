@@ -169,6 +169,16 @@ __device__ __forceinline__ int64_t q_wave_scan64(int64_t x)
     x += q_dpp64<0x143, 0xc>(x);
     return x;
 }
+// A wave's values moved one lane up (lane i gets lane i - 1's, lane 0 gets 0)
+// or down (lane i gets lane i + 1's, lane 63 gets 0): whole-wave DPP shifts.
+__device__ __forceinline__ uint64_t q_up1(uint64_t x)
+{
+    return ((uint64_t)q_dpp<0x138, 0xf>((uint32_t)(x >> 32)) << 32) | q_dpp<0x138, 0xf>((uint32_t)x);
+}
+__device__ __forceinline__ uint64_t q_down1(uint64_t x)
+{
+    return ((uint64_t)q_dpp<0x130, 0xf>((uint32_t)(x >> 32)) << 32) | q_dpp<0x130, 0xf>((uint32_t)x);
+}
 __device__ __forceinline__ uint32_t q_lane63(uint32_t x)
 {
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
@@ -354,7 +364,7 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
         __syncthreads();
 
         // 4. Lloyd rounds, all in wave 0: lane i holds centre i, its
-        //    neighbours come by lane shifts.  The new centres are already in
+        //    neighbours come by whole-wave DPP shifts.  The new centres are already in
         //    the sort's order whenever each comes after its left neighbour
         //    (a mean lies between its cluster's boundaries, an empty cluster
         //    keeps its centre); then the rank sort would leave them in place
@@ -364,7 +374,7 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
             double c = cen[tid];
             const int64_t s_all = S[khi];
             for (int round = 0; round < Q_ROUNDS; ++round) {
-                const double c_next = __shfl_down(c, 1);
+                const double c_next = __builtin_bit_cast(double, q_down1(__builtin_bit_cast(uint64_t, c)));
                 uint32_t cnt = (uint32_t)n;
                 int64_t sum = s_all;
                 if (tid < Q_ENTRIES - 1) {
@@ -373,12 +383,11 @@ lut6_quantize_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ packe
                     cnt = k >= klo ? P[k] : 0u;
                     sum = k >= klo ? S[k] : 0;
                 }
-                uint32_t cnt_prev = __shfl_up(cnt, 1);
-                int64_t sum_prev = __shfl_up(sum, 1);
-                if (tid == 0) { cnt_prev = 0u; sum_prev = 0; }
+                const uint32_t cnt_prev = q_dpp<0x138, 0xf>(cnt);           // 0 in lane 0
+                const int64_t sum_prev = (int64_t)q_up1((uint64_t)sum);
                 const uint32_t num = cnt - cnt_prev;
                 const double v = num ? ldexp((double)(sum - sum_prev) / (double)num, -24) : c;
-                const double u = __shfl_up(v, 1);
+                const double u = __builtin_bit_cast(double, q_up1(__builtin_bit_cast(uint64_t, v)));
                 const bool after = tid == 0 || u < v ||
                                    (u == v && !(!__builtin_signbit(u) && __builtin_signbit(v)));
                 if (__all(after)) {
